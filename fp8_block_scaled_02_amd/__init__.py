@@ -1,0 +1,314 @@
+"""libfp8w: FP8 (e4m3fn) weights for the decode path on MI355X (gfx950).
+
+A thin ctypes binding over the C ABI of ``include/fp8w.h``.  Every function
+here only checks and marshals arguments; all arithmetic runs in the HIP
+kernels of ``libfp8w.so``.  PyTorch supplies device memory and the stream.
+There is no CPU fallback: importing works on any host (so the symbol table
+can be checked), but every call needs a ROCm GPU and the built library, and
+fails loudly otherwise.
+
+Functions carry the names of the C entry points:
+
+* ``fp8w_quantize_block(w) -> (codes, scales)``   bf16 [n,k] -> u8 [n,k], f32 grid
+* ``fp8w_quantize_mx(w) -> (codes, e8m0)``        bf16 [n,k] -> u8 [n,k], u8 [n,ceil(k/32)]
+* ``fp8w_gemv_block(x, codes, scales) -> y``      bf16 [m,k] -> bf16 [m,n]
+* ``fp8w_gemv_mx(x, codes, e8m0) -> y``
+* ``fp8w_grouped_plan_init(xs, codes, scales) -> plan`` and
+  ``fp8w_gemv_grouped(plan) -> ys``: many independent GEMVs in one launch
+
+plus ``Fp8Weight``, a format-tagged weight whose GEMV asserts the format
+before dispatch (a scale buffer of the wrong format cannot be detected by a
+kernel: "quantize_fp8_bs.rs", Atlas weight_map, module notes).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp8w.so")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_OVERLAP, ERR_HIP = range(7)
+ROUTE_AUTO, ROUTE_VALU, ROUTE_MFMA = 0, 1, 2
+MAX_M = 32
+TILE = 128
+MX_GROUP = 32
+
+# name -> (restype, argtypes); the exported C ABI, mirrored from include/fp8w.h
+_P, _I64, _I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+SIGNATURES = {
+    "fp8w_quantize_block": (_I, [_P, _I64, _I64, _P, _P, _P]),
+    "fp8w_quantize_mx": (_I, [_P, _I64, _I64, _P, _P, _P]),
+    "fp8w_gemv_block": (_I, [_P, _I64, _P, _P, _I64, _I64, _P, _P]),
+    "fp8w_gemv_mx": (_I, [_P, _I64, _P, _P, _I64, _I64, _P, _P]),
+    "fp8w_gemv_block_route": (_I, [_P, _I64, _P, _P, _I64, _I64, _P, _I, _P]),
+    "fp8w_gemv_mx_route": (_I, [_P, _I64, _P, _P, _I64, _I64, _P, _I, _P]),
+    "fp8w_grouped_table_bytes": (_I64, [_I64]),
+    "fp8w_grouped_plan_init": (_I, [_P, _I64, _I64, _I, _I, _P, _P]),
+    "fp8w_gemv_grouped": (_I, [_P, _P]),
+    "fp8w_block_scale_count": (_I64, [_I64, _I64]),
+    "fp8w_mx_scale_count": (_I64, [_I64, _I64]),
+    "fp8w_status_string": (ctypes.c_char_p, [_I]),
+    "fp8w_version": (_I, []),
+}
+
+FORMAT_BLOCK, FORMAT_MX = 0, 1
+
+
+class GemvDesc(ctypes.Structure):
+    """fp8w_gemv_desc of include/fp8w.h."""
+    _fields_ = [("x", _P), ("codes", _P), ("scales", _P), ("y", _P),
+                ("n", _I64), ("k", _I64)]
+
+
+class GroupedPlanC(ctypes.Structure):
+    """fp8w_grouped_plan of include/fp8w.h."""
+    _fields_ = [("table", _P), ("count", ctypes.c_int32), ("m", ctypes.c_int32),
+                ("format", ctypes.c_int32), ("route", ctypes.c_int32), ("blocks", _I64)]
+
+
+_lib = None
+
+
+class Fp8wError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)}")
+
+
+def lib() -> ctypes.CDLL:
+    """Load ``libfp8w.so`` (built by ``__graft_entry__.build()``), or raise."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m fp8_block_scaled_02_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = handle
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().fp8w_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != OK:
+        raise Fp8wError(status, what)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream) -> Optional[int]:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _require(t, dtypes, what: str, dims: int):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what}: expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what}: must be a GPU tensor (libfp8w has no CPU path)")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{what}: dtype {t.dtype} not in {dtypes}")
+    if t.dim() != dims or not t.is_contiguous():
+        raise ValueError(f"{what}: expected a contiguous {dims}-d tensor")
+    return t
+
+
+def _bf16_like(torch):
+    return (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def block_scale_shape(n: int, k: int):
+    return ((n + TILE - 1) // TILE, (k + TILE - 1) // TILE)
+
+
+def mx_scale_shape(n: int, k: int):
+    return (n, (k + MX_GROUP - 1) // MX_GROUP)
+
+
+# --------------------------------------------------------------- quantize --
+
+def fp8w_quantize_block(w, codes=None, scales=None, stream=None):
+    """bf16 W [n,k] -> (e4m3fn codes u8 [n,k], fp32 scales [ceil(n/128), ceil(k/128)])."""
+    torch = _torch()
+    _require(w, _bf16_like(torch), "w", 2)
+    n, k = w.shape
+    if codes is None:
+        codes = torch.empty((n, k), dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty(block_scale_shape(n, k), dtype=torch.float32, device=w.device)
+    _require(codes, (torch.uint8,), "codes", 2)
+    _require(scales, (torch.float32,), "scales", 2)
+    if tuple(codes.shape) != (n, k) or tuple(scales.shape) != block_scale_shape(n, k):
+        raise ValueError("fp8w_quantize_block: output shapes do not match w")
+    _check(lib().fp8w_quantize_block(w.data_ptr(), n, k, codes.data_ptr(), scales.data_ptr(),
+                                     _stream_handle(stream)), "fp8w_quantize_block")
+    return codes, scales
+
+
+def fp8w_quantize_mx(w, codes=None, e8m0=None, stream=None):
+    """bf16 W [n,k] -> (e4m3fn codes u8 [n,k], e8m0 u8 [n, ceil(k/32)])."""
+    torch = _torch()
+    _require(w, _bf16_like(torch), "w", 2)
+    n, k = w.shape
+    if codes is None:
+        codes = torch.empty((n, k), dtype=torch.uint8, device=w.device)
+    if e8m0 is None:
+        e8m0 = torch.empty(mx_scale_shape(n, k), dtype=torch.uint8, device=w.device)
+    _require(codes, (torch.uint8,), "codes", 2)
+    _require(e8m0, (torch.uint8,), "e8m0", 2)
+    if tuple(codes.shape) != (n, k) or tuple(e8m0.shape) != mx_scale_shape(n, k):
+        raise ValueError("fp8w_quantize_mx: output shapes do not match w")
+    _check(lib().fp8w_quantize_mx(w.data_ptr(), n, k, codes.data_ptr(), e8m0.data_ptr(),
+                                  _stream_handle(stream)), "fp8w_quantize_mx")
+    return codes, e8m0
+
+
+# ------------------------------------------------------------------- GEMV --
+
+def _gemv(fn_name, x, codes, scale_t, scale_shape, scale_dtype, y, route, stream):
+    torch = _torch()
+    _require(x, _bf16_like(torch), "x", 2)
+    _require(codes, (torch.uint8,), "codes", 2)
+    _require(scale_t, (scale_dtype,), "scales", 2)
+    m, k = x.shape
+    n, k2 = codes.shape
+    if k != k2:
+        raise ValueError(f"{fn_name}: x has K={k}, codes have K={k2}")
+    if tuple(scale_t.shape) != scale_shape(n, k):
+        raise ValueError(f"{fn_name}: scale grid {tuple(scale_t.shape)} != {scale_shape(n, k)}")
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    _require(y, _bf16_like(torch), "y", 2)
+    if tuple(y.shape) != (m, n):
+        raise ValueError(f"{fn_name}: y must be [{m}, {n}]")
+    fn = getattr(lib(), fn_name + "_route")
+    _check(fn(x.data_ptr(), m, codes.data_ptr(), scale_t.data_ptr(), n, k, y.data_ptr(),
+              int(route), _stream_handle(stream)), fn_name)
+    return y
+
+
+def fp8w_gemv_block(x, codes, scales, y=None, route=ROUTE_AUTO, stream=None):
+    """y[m,n] = x[m,k] . deq(W)^T with 128x128 fp32 block scales (bf16 out)."""
+    torch = _torch()
+    return _gemv("fp8w_gemv_block", x, codes, scales, block_scale_shape, torch.float32, y,
+                 route, stream)
+
+
+def fp8w_gemv_mx(x, codes, e8m0, y=None, route=ROUTE_AUTO, stream=None):
+    """y[m,n] = x[m,k] . deq(W)^T with per-32 e8m0 scales (bf16 out)."""
+    torch = _torch()
+    return _gemv("fp8w_gemv_mx", x, codes, e8m0, mx_scale_shape, torch.uint8, y, route, stream)
+
+
+# ---------------------------------------------------------------- grouped --
+
+class GroupedPlan:
+    """A group of independent GEMVs launched as one kernel.
+
+    Holds the device table and references to every buffer it names, so the
+    buffers stay alive as long as the plan.  ``y`` tensors are allocated here
+    when not given.
+    """
+
+    def __init__(self, xs, codes, scales, ys=None, fmt: str = "block", route=ROUTE_AUTO):
+        torch = _torch()
+        if not (len(xs) == len(codes) == len(scales)) or not xs:
+            raise ValueError("xs, codes and scales must be non-empty lists of equal length")
+        fmt_id = {"block": FORMAT_BLOCK, "mx": FORMAT_MX}[fmt]
+        sdt, sshape = ((torch.float32, block_scale_shape) if fmt_id == FORMAT_BLOCK
+                       else (torch.uint8, mx_scale_shape))
+        m = int(xs[0].shape[0])
+        if ys is None:
+            ys = [torch.empty((m, int(c.shape[0])), dtype=torch.bfloat16, device=c.device) for c in codes]
+        descs = (GemvDesc * len(xs))()
+        for i, (x, c, s, y) in enumerate(zip(xs, codes, scales, ys)):
+            _require(x, _bf16_like(torch), "x", 2)
+            _require(c, (torch.uint8,), "codes", 2)
+            _require(s, (sdt,), "scales", 2)
+            _require(y, _bf16_like(torch), "y", 2)
+            n, k = c.shape
+            if x.shape[0] != m or x.shape[1] != k or tuple(s.shape) != sshape(n, k) \
+                    or tuple(y.shape) != (m, n):
+                raise ValueError(f"grouped GEMV {i}: inconsistent shapes")
+            descs[i] = GemvDesc(x.data_ptr(), c.data_ptr(), s.data_ptr(), y.data_ptr(), n, k)
+        nbytes = int(lib().fp8w_grouped_table_bytes(len(xs)))
+        self.table = torch.empty(nbytes, dtype=torch.uint8, device=codes[0].device)
+        self.plan = GroupedPlanC()
+        _check(lib().fp8w_grouped_plan_init(descs, len(xs), m, fmt_id, int(route),
+                                            self.table.data_ptr(), ctypes.byref(self.plan)),
+               "fp8w_grouped_plan_init")
+        self.xs, self.codes, self.scales, self.ys = list(xs), list(codes), list(scales), list(ys)
+        self.m, self.fmt = m, fmt
+
+    @property
+    def blocks(self) -> int:
+        return int(self.plan.blocks)
+
+    @property
+    def route(self) -> int:
+        return int(self.plan.route)
+
+
+def fp8w_grouped_plan_init(xs, codes, scales, ys=None, fmt="block", route=ROUTE_AUTO) -> GroupedPlan:
+    """Validate a group of GEMVs and write its device table (set-up call)."""
+    return GroupedPlan(xs, codes, scales, ys, fmt, route)
+
+
+def fp8w_gemv_grouped(plan: GroupedPlan, stream=None):
+    """Enqueue every GEMV of ``plan`` in one launch; returns the ``y`` list."""
+    _check(lib().fp8w_gemv_grouped(ctypes.byref(plan.plan), _stream_handle(stream)),
+           "fp8w_gemv_grouped")
+    return plan.ys
+
+
+# ----------------------------------------------------------- tagged weight --
+
+BLOCK128, MX32 = "block128", "mx32"
+
+
+@dataclass
+class Fp8Weight:
+    """Quantized weight with its scale format fixed at construction."""
+    codes: object
+    scales: object
+    n: int
+    k: int
+    fmt: str
+
+    @classmethod
+    def quantize(cls, w, fmt: str = BLOCK128, stream=None) -> "Fp8Weight":
+        if fmt == BLOCK128:
+            c, s = fp8w_quantize_block(w, stream=stream)
+        elif fmt == MX32:
+            c, s = fp8w_quantize_mx(w, stream=stream)
+        else:
+            raise ValueError(f"unknown scale format {fmt!r}")
+        return cls(c, s, int(w.shape[0]), int(w.shape[1]), fmt)
+
+    def check_format(self) -> None:
+        """The single place that decides which scale layout a weight carries."""
+        torch = _torch()
+        want = ((torch.float32, block_scale_shape(self.n, self.k)) if self.fmt == BLOCK128 else
+                (torch.uint8, mx_scale_shape(self.n, self.k)) if self.fmt == MX32 else None)
+        if want is None or self.scales.dtype != want[0] or tuple(self.scales.shape) != want[1]:
+            raise ValueError(f"Fp8Weight: scales do not match format {self.fmt!r}")
+
+    def gemv(self, x, y=None, route=ROUTE_AUTO, stream=None):
+        self.check_format()
+        if self.fmt == BLOCK128:
+            return fp8w_gemv_block(x, self.codes, self.scales, y, route, stream)
+        return fp8w_gemv_mx(x, self.codes, self.scales, y, route, stream)

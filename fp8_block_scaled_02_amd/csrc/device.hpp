@@ -1,0 +1,89 @@
+// device.hpp -- device helpers shared by the libfp8w kernels (gfx950 only).
+//
+// bf16 <-> fp32 bit helpers, the e4m3fn encoder, the e8m0 exponent rule and
+// wavefront reductions.  Nothing here is shared with the CPU oracle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8w {
+
+constexpr int kWave = 64;       // CDNA wavefront width
+constexpr int kTile = 128;      // block-scale tile edge, both axes
+constexpr int kGroup = 32;      // elements per e8m0 scale, along K
+constexpr uint32_t kF32Bits448 = 0x43E00000u;   // 448.0f
+constexpr uint32_t kF32BitsMinNormalE4M3 = 0x3C800000u;   // 2^-6
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// bf16 halves of a packed dword, widened exactly to fp32.
+__device__ __forceinline__ float bf16_lo(uint32_t d) { return __uint_as_float(d << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// e4m3fn encoder: round |q| to the nearest representable magnitude with ties
+// to even, saturate at 448, keep the sign bit.  Works on the fp32 bit
+// pattern: in the normal range (|q| >= 2^-6) the top three mantissa bits are
+// kept and the 20 dropped bits round to nearest even, the carry ripples into
+// the exponent, and the exponent is rebiased from 127 to 7; below 2^-6 the
+// e4m3 grid is uniform with step 2^-9, so the code is |q| * 512 rounded to
+// the nearest even integer (0..8, where 8 is the smallest normal, 2^-6).
+// Inputs must not be NaN.
+__device__ __forceinline__ uint32_t e4m3_encode(float q) {
+  const uint32_t u = __float_as_uint(q);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a >= kF32Bits448) {
+    code = 0x7Eu;
+  } else if (a >= kF32BitsMinNormalE4M3) {
+    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    code = (r >> 20) - (120u << 3);
+  } else {
+    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  }
+  return sign | code;
+}
+
+// MX exponent of a group from its amax (the fp32 bit pattern of a
+// non-negative value): the smallest e with amax <= 448 * 2^e, clamped to
+// [-127, 127].  With amax = 2^x * 1.f and 448 = 2^8 * 1.75, e = x - 8 when
+// 1.f <= 1.75 and x - 7 otherwise.  fp32 subnormals and zero land below
+// -127 and clamp there; no finite amax reaches 127.
+__device__ __forceinline__ int e8m0_exponent(uint32_t amax_bits) {
+  const int field = (int)(amax_bits >> 23);
+  if (field == 0) return -127;
+  const int e = field - 127 - 8 + ((amax_bits & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return e < -127 ? -127 : e;
+}
+
+// Sum over aligned groups of `width` consecutive lanes (width a power of two
+// <= 64).  Every lane of the group ends with the group's sum.
+template <int width>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int off = width / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, width);
+  return v;
+}
+
+template <int width>
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = width / 2; off > 0; off >>= 1) {
+    const uint32_t o = (uint32_t)__shfl_xor((int)v, off, width);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+}  // namespace fp8w

@@ -1,0 +1,36 @@
+// internal.hpp -- launchers behind the C ABI (not exported).
+//
+// Each launcher assumes its arguments were validated by the caller (api.cpp)
+// and returns the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8w {
+
+// One GEMV y[m, n] = x[m, k] . deq(codes)^T.  The same layout is the row of
+// a grouped launch's device table (fp8w_grouped_plan_init writes it).
+struct GemvJob {
+  const uint16_t* x;        // bf16 [m, k]
+  const uint8_t* codes;     // e4m3fn [n, k]
+  const void* scales;       // fp32 [ceil(n/128), ceil(k/128)] or e8m0 [n, ceil(k/32)]
+  uint16_t* y;              // bf16 [m, n]
+  int32_t n, k;             // validated to fit int32 on the host
+  int32_t item0;            // first workgroup of this job in a grouped launch
+  int32_t reserved;
+};
+static_assert(sizeof(GemvJob) == 48, "device table row");
+
+hipError_t launch_quantize_block(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,
+                                 float* scales, hipStream_t stream);
+hipError_t launch_quantize_mx(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,
+                              uint8_t* e8m0, hipStream_t stream);
+
+// route: 1 = VALU (m <= 8), 2 = MFMA (m <= 32).
+int gemv_rows_per_block(int route, int m, bool grouped);
+hipError_t launch_gemv(const GemvJob& job, int m, bool mx, int route, hipStream_t stream);
+hipError_t launch_gemv_grouped(const GemvJob* device_table, int njobs, int64_t blocks, int m,
+                               bool mx, int route, hipStream_t stream);
+
+}  // namespace fp8w

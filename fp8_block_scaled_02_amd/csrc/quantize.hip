@@ -1,0 +1,216 @@
+// quantize.hip -- load-time bf16 -> e4m3fn quantizers for gfx950.
+//
+// Block format: one fp32 scale per 128x128 tile, scale = amax/448 and
+// code = enc(w/scale) with both divisions correctly rounded in fp32
+// ("quantize_fp8_bs.rs", Atlas weight_map: one byte per weight, one f32 per
+// [128,128] tile, a ceil(k/128) x ceil(n/128) grid of 256-thread blocks).
+// MX format: one e8m0 exponent per 32 elements along K, e = ceil(log2(
+// amax/448)), code = enc(w * 2^-e) ("Load-time MXFP8 requantization ..."
+// issue, Proposed solution).  The issue's 32 MB row-chunked fp32 transient
+// bounds host memory in a torch implementation; the result is the same for
+// any chunking, so the kernel streams rows with no transient.
+#include <hip/hip_runtime.h>
+
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace fp8w {
+namespace {
+
+constexpr int kThreads = 256;
+
+// Largest |bf16| of a packed pair, compared as bit patterns: for
+// non-negative finite values the bit order is the value order.
+__device__ __forceinline__ uint32_t abs_max_pair(uint32_t d, uint32_t acc) {
+  const uint32_t lo = d & 0x7FFFu, hi = (d >> 16) & 0x7FFFu;
+  acc = lo > acc ? lo : acc;
+  return hi > acc ? hi : acc;
+}
+
+// Four codes of four packed bf16 (two dwords) divided by `scale`.
+__device__ __forceinline__ uint32_t encode4_div(uint32_t d0, uint32_t d1, float scale) {
+  return e4m3_encode(bf16_lo(d0) / scale) | (e4m3_encode(bf16_hi(d0) / scale) << 8) |
+         (e4m3_encode(bf16_lo(d1) / scale) << 16) | (e4m3_encode(bf16_hi(d1) / scale) << 24);
+}
+
+// Four codes of four packed bf16 multiplied by a power of two.
+__device__ __forceinline__ uint32_t encode4_mul(uint32_t d0, uint32_t d1, float mul) {
+  return e4m3_encode(bf16_lo(d0) * mul) | (e4m3_encode(bf16_hi(d0) * mul) << 8) |
+         (e4m3_encode(bf16_lo(d1) * mul) << 16) | (e4m3_encode(bf16_hi(d1) * mul) << 24);
+}
+
+// Block-wide max of a per-thread value (256 threads = 4 waves).
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v) {
+  __shared__ uint32_t partial[kThreads / kWave];
+  v = group_max_u32<kWave>(v);
+  if ((threadIdx.x & (kWave - 1)) == 0) partial[threadIdx.x / kWave] = v;
+  __syncthreads();
+  uint32_t r = partial[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / kWave; ++i) r = partial[i] > r ? partial[i] : r;
+  return r;
+}
+
+// One 256-thread block per 128x128 tile; flat block index b -> tile
+// (b / tiles_k, b % tiles_k).  Vector path: k % 8 == 0, w 16-B aligned and
+// codes 8-B aligned.  Thread t owns columns 8*(t%16) .. +7 of rows
+// t/16 + 16*i (i = 0..7): each row of the tile is read as 16 x 16 B and
+// written as 16 x 8 B, and the tile stays in registers between the amax and
+// the encode pass (the bf16 source is read from HBM once).
+__global__ __launch_bounds__(kThreads) void k_quant_block_vec(const uint16_t* __restrict__ w,
+                                                              uint8_t* __restrict__ codes,
+                                                              float* __restrict__ scales, int n,
+                                                              int k, int tiles_k) {
+  const int ti = blockIdx.x / tiles_k, tj = blockIdx.x % tiles_k;
+  const int col = tj * kTile + (threadIdx.x & 15) * 8;
+  const int row0 = ti * kTile + (threadIdx.x >> 4);
+  const bool col_ok = col < k;
+  uint4 v[8];
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = row0 + 16 * i;
+    v[i] = make_uint4(0, 0, 0, 0);
+    if (col_ok && row < n) v[i] = *reinterpret_cast<const uint4*>(w + (size_t)row * k + col);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    amax = abs_max_pair(v[i].x, amax);
+    amax = abs_max_pair(v[i].y, amax);
+    amax = abs_max_pair(v[i].z, amax);
+    amax = abs_max_pair(v[i].w, amax);
+  }
+  amax = block_max_u32(amax);
+  const float amax_f = __uint_as_float(amax << 16);
+  const float scale = amax_f > 0.0f ? amax_f / 448.0f : 1.0f;
+  if (threadIdx.x == 0) scales[blockIdx.x] = scale;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = row0 + 16 * i;
+    if (col_ok && row < n) {
+      uint2 out;
+      out.x = encode4_div(v[i].x, v[i].y, scale);
+      out.y = encode4_div(v[i].z, v[i].w, scale);
+      *reinterpret_cast<uint2*>(codes + (size_t)row * k + col) = out;
+    }
+  }
+}
+
+// Any shape and alignment: element e = t + 256*j (j = 0..63) of the tile,
+// row e/128, column e%128, 2-byte loads and 1-byte stores.
+__global__ __launch_bounds__(kThreads) void k_quant_block_any(const uint16_t* __restrict__ w,
+                                                              uint8_t* __restrict__ codes,
+                                                              float* __restrict__ scales, int n,
+                                                              int k, int tiles_k) {
+  const int ti = blockIdx.x / tiles_k, tj = blockIdx.x % tiles_k;
+  uint16_t v[64];
+  uint32_t amax = 0;
+#pragma unroll
+  for (int j = 0; j < 64; ++j) {
+    const int e = threadIdx.x + kThreads * j;
+    const int row = ti * kTile + (e >> 7), col = tj * kTile + (e & 127);
+    v[j] = 0;
+    if (row < n && col < k) v[j] = w[(size_t)row * k + col];
+    const uint32_t a = v[j] & 0x7FFFu;
+    amax = a > amax ? a : amax;
+  }
+  amax = block_max_u32(amax);
+  const float amax_f = __uint_as_float(amax << 16);
+  const float scale = amax_f > 0.0f ? amax_f / 448.0f : 1.0f;
+  if (threadIdx.x == 0) scales[blockIdx.x] = scale;
+#pragma unroll
+  for (int j = 0; j < 64; ++j) {
+    const int e = threadIdx.x + kThreads * j;
+    const int row = ti * kTile + (e >> 7), col = tj * kTile + (e & 127);
+    if (row < n && col < k)
+      codes[(size_t)row * k + col] = (uint8_t)e4m3_encode(__uint_as_float((uint32_t)v[j] << 16) / scale);
+  }
+}
+
+// 2^-e as an fp32 (e in [-127, 120], so the result is a normal number).
+__device__ __forceinline__ float pow2_neg(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
+
+// MX vector path: k % 32 == 0, w 16-B aligned, codes 8-B aligned.  With k a
+// multiple of 32 the groups tile the flat [n*k] array, so thread t takes
+// elements 8t .. 8t+7 and the four lanes 4g .. 4g+3 form group g.
+__global__ __launch_bounds__(kThreads) void k_quant_mx_vec(const uint16_t* __restrict__ w,
+                                                           uint8_t* __restrict__ codes,
+                                                           uint8_t* __restrict__ e8m0,
+                                                           size_t threads_total) {
+  const size_t t = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  const bool ok = t < threads_total;
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (ok) v = *reinterpret_cast<const uint4*>(w + 8 * t);
+  uint32_t amax = abs_max_pair(v.x, 0);
+  amax = abs_max_pair(v.y, amax);
+  amax = abs_max_pair(v.z, amax);
+  amax = abs_max_pair(v.w, amax);
+  amax = group_max_u32<4>(amax);
+  const int e = e8m0_exponent(amax << 16);
+  if (!ok) return;
+  if ((t & 3) == 0) e8m0[t >> 2] = (uint8_t)(e + 127);
+  const float mul = pow2_neg(e);
+  uint2 out;
+  out.x = encode4_mul(v.x, v.y, mul);
+  out.y = encode4_mul(v.z, v.w, mul);
+  *reinterpret_cast<uint2*>(codes + 8 * t) = out;
+}
+
+// MX, any shape: one thread per (row, group), 2-byte loads.
+__global__ __launch_bounds__(kThreads) void k_quant_mx_any(const uint16_t* __restrict__ w,
+                                                           uint8_t* __restrict__ codes,
+                                                           uint8_t* __restrict__ e8m0, int n,
+                                                           int k, int groups) {
+  const size_t t = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (t >= (size_t)n * groups) return;
+  const size_t row = t / groups;
+  const int c0 = (int)(t % groups) * kGroup;
+  const int c1 = c0 + kGroup < k ? c0 + kGroup : k;
+  const uint16_t* src = w + row * k;
+  uint32_t amax = 0;
+  for (int c = c0; c < c1; ++c) {
+    const uint32_t a = src[c] & 0x7FFFu;
+    amax = a > amax ? a : amax;
+  }
+  const int e = e8m0_exponent(amax << 16);
+  e8m0[t] = (uint8_t)(e + 127);
+  const float mul = pow2_neg(e);
+  for (int c = c0; c < c1; ++c)
+    codes[row * k + c] = (uint8_t)e4m3_encode(__uint_as_float((uint32_t)src[c] << 16) * mul);
+}
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+hipError_t launch_quantize_block(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,
+                                 float* scales, hipStream_t stream) {
+  const int64_t tiles_n = (n + kTile - 1) / kTile, tiles_k = (k + kTile - 1) / kTile;
+  const dim3 grid((unsigned)(tiles_n * tiles_k)), block(kThreads);
+  if (k % 8 == 0 && aligned(w, 16) && aligned(codes, 8))
+    hipLaunchKernelGGL(k_quant_block_vec, grid, block, 0, stream, w, codes, scales, (int)n, (int)k,
+                       (int)tiles_k);
+  else
+    hipLaunchKernelGGL(k_quant_block_any, grid, block, 0, stream, w, codes, scales, (int)n, (int)k,
+                       (int)tiles_k);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_mx(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,
+                              uint8_t* e8m0, hipStream_t stream) {
+  const int64_t groups = (k + kGroup - 1) / kGroup;
+  if (k % kGroup == 0 && aligned(w, 16) && aligned(codes, 8)) {
+    const size_t threads_total = (size_t)n * k / 8;
+    const dim3 grid((unsigned)((threads_total + kThreads - 1) / kThreads));
+    hipLaunchKernelGGL(k_quant_mx_vec, grid, dim3(kThreads), 0, stream, w, codes, e8m0,
+                       threads_total);
+  } else {
+    const size_t total = (size_t)n * groups;
+    const dim3 grid((unsigned)((total + kThreads - 1) / kThreads));
+    hipLaunchKernelGGL(k_quant_mx_any, grid, dim3(kThreads), 0, stream, w, codes, e8m0, (int)n,
+                       (int)k, (int)groups);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fp8w

@@ -1,0 +1,225 @@
+/*
+ * fp8w.h -- C ABI of libfp8w: FP8 (OCP e4m3fn) weights for the decode path
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * Two operations, each in two scale formats:
+ *
+ *   quantize  bf16 W[n,k]  ->  e4m3fn codes[n,k] + a scale grid
+ *   GEMV      y[m,n] = x[m,k] . deq(W)^T, bf16 in, bf16 out, fp32 accumulate
+ *
+ * Scale formats:
+ *   block : one fp32 scale per 128x128 tile, grid [ceil(n/128), ceil(k/128)]
+ *           row-major; scale = amax/448 (1.0 for an all-zero tile) and
+ *           deq = dec(code) * scale.  Format of "quantize_fp8_bs.rs" (Atlas
+ *           spark_model/weight_map: one byte per weight, one f32 per
+ *           [128,128] tile) and of the 128x128 block checkpoints of "feat: add
+ *           FP8 blockwise weight quantization and FP8(E4M3) KV cache support"
+ *           (Summary); the per-block quantizer of "feat(quant): opt-in
+ *           fp8-block QAT for the lm_head" (Changes).
+ *   mx    : one e8m0 byte per 32 elements along K, grid [n, ceil(k/32)]
+ *           row-major; exponent e = ceil(log2(amax/448)) clamped to
+ *           [-127, 127], byte = e + 127 (an all-zero group stores 0), and
+ *           deq = dec(code) * 2^(byte - 127).  "Load-time MXFP8
+ *           requantization of bf16 dense, hyper-connection and lm_head
+ *           weights" (Proposed solution).
+ *
+ * Encoding (both formats): the quotient w/scale (fp32, correctly rounded),
+ * or w * 2^-e, is rounded to the nearest e4m3fn value with ties to the even
+ * code, saturating at +-448; the sign is kept (negative values that round to
+ * zero give 0x80).  NaN codes (0x7F, 0xFF) are never produced.
+ *
+ * Data types: bf16 tensors are passed as their raw 16-bit patterns
+ * (uint16_t), since C has no bf16 type.  All matrices are dense row-major.
+ *
+ * Memory and ownership: every tensor pointer is a DEVICE pointer on the
+ * current HIP device.  The caller allocates and frees every buffer; the
+ * library keeps no pointer after a call returns and never allocates.
+ *
+ * Execution: every call only enqueues work on `stream` (a hipStream_t;
+ * NULL means the default stream) and returns without synchronizing.  Calls
+ * never read tensor values on the host, and the kernel chosen depends on the
+ * shape only, so the calls may be captured in a HIP graph.  Results are
+ * bitwise reproducible run to run (no atomics, fixed reduction order).
+ *
+ * Errors: arguments are checked on the host before anything is enqueued; on
+ * any error nothing is launched and no output byte is written.  A fault
+ * during execution surfaces at the caller's next synchronization of
+ * `stream`.  Non-finite inputs are outside the contract: the calls do not
+ * fault on them but their outputs are unspecified.  Mis-shaped calls fail
+ * loudly instead of miscomputing, as the bounds contract of "feat: add FP8
+ * blockwise weight quantization ..." (Security and Safety) asks.
+ */
+#ifndef FP8W_H_
+#define FP8W_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fp8w_status {
+  FP8W_OK = 0,
+  FP8W_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  FP8W_ERR_SHAPE = 2,       /* n, k or m out of range (n, k >= 1; m in 1..32)   */
+  FP8W_ERR_ALIGN = 3,       /* GEMV: k % 16 != 0 or x / codes not 16-B aligned, */
+                            /* or a scale pointer not 4-B aligned               */
+  FP8W_ERR_UNSUPPORTED = 4, /* the requested route cannot serve this m          */
+  FP8W_ERR_OVERLAP = 5,     /* an output byte range overlaps another buffer     */
+  FP8W_ERR_HIP = 6          /* the HIP runtime rejected the launch              */
+} fp8w_status;
+
+/* GEMV kernel family.  AUTO picks VALU for m <= 8 and MFMA for m >= 9, the
+ * split measured for the fused W8A16 GEMM in "feat: add FP8 blockwise weight
+ * quantization ..." (Summary; Notes for Reviewers: SIMT for M <= 8,
+ * tensor-core mma for 9 <= M <= 32).  VALU serves 1 <= m <= 8 only; MFMA
+ * serves 1 <= m <= 32.  Every route meets the same error bound.          */
+typedef enum fp8w_route {
+  FP8W_ROUTE_AUTO = 0,
+  FP8W_ROUTE_VALU = 1,
+  FP8W_ROUTE_MFMA = 2
+} fp8w_route;
+
+/* Largest m (activation rows) served by the GEMV calls.  Larger batches are
+ * prefill work, served elsewhere ("feat: add FP8 blockwise weight
+ * quantization ...", Summary: M > 32 uses dequantize + dense GEMM). */
+#define FP8W_MAX_M 32
+
+/* ------------------------------------------------------------ quantize -- */
+
+/* Block quantization, load time.
+ *   w      : bf16 [n, k] (2-byte aligned)                          input
+ *   codes  : u8   [n, k]                                           output
+ *   scales : f32  [ceil(n/128), ceil(k/128)] (4-byte aligned)      output
+ * Per tile: amax = max |w| over the tile's valid elements; scale =
+ * amax/448 in fp32 (1.0 if amax == 0); code = enc(w/scale) in fp32.
+ * Tiles at the bottom/right edges are partial.  Any n, k >= 1.
+ * Errors: NULL, SHAPE (n < 1, k < 1, n or k > 2^31 - 1), ALIGN, OVERLAP, HIP. */
+fp8w_status fp8w_quantize_block(const uint16_t* w, int64_t n, int64_t k,
+                                uint8_t* codes, float* scales, void* stream);
+
+/* MX quantization, load time.
+ *   w     : bf16 [n, k]                        input
+ *   codes : u8   [n, k]                        output
+ *   e8m0  : u8   [n, ceil(k/32)]               output
+ * Per row and 32-element group along K (the last group may be partial):
+ * e = smallest integer with amax <= 448 * 2^e, clamped to [-127, 127]
+ * (-127 if amax == 0); byte = e + 127; code = enc(w * 2^-e).  The result
+ * does not depend on how rows are chunked, so no transient is needed.
+ * Errors: NULL, SHAPE, OVERLAP, HIP. */
+fp8w_status fp8w_quantize_mx(const uint16_t* w, int64_t n, int64_t k,
+                             uint8_t* codes, uint8_t* e8m0, void* stream);
+
+/* ---------------------------------------------------------------- GEMV -- */
+
+/* Block-scaled W8A16 GEMV / skinny GEMM.
+ *   x      : bf16 [m, k], 16-byte aligned                   input
+ *   codes  : u8   [n, k], 16-byte aligned                   input
+ *   scales : f32  [ceil(n/128), ceil(k/128)], 4-B aligned    input
+ *   y      : bf16 [m, n]                                    output
+ * y[i][j] = bf16_rne( sum_k x[i][k] * dec(codes[j][k]) * scale[j/128][k/128] )
+ * accumulated in fp32.  Bound met for every output, with y_ref in fp64:
+ * |y - y_ref| <= 2^-7 * sum_k |x[i][k]| |deq[j][k]| + 1e-6.
+ * Requires 1 <= m <= 32, n >= 1, k >= 16 and k % 16 == 0.
+ * Errors: NULL, SHAPE, ALIGN, UNSUPPORTED, OVERLAP, HIP. */
+fp8w_status fp8w_gemv_block(const uint16_t* x, int64_t m, const uint8_t* codes,
+                            const float* scales, int64_t n, int64_t k,
+                            uint16_t* y, void* stream);
+
+/* MX-scaled W8A16 GEMV: as fp8w_gemv_block with
+ * deq[j][k] = dec(codes[j][k]) * 2^(e8m0[j][k/32] - 127).
+ *   e8m0 : u8 [n, ceil(k/32)]   input (no alignment requirement) */
+fp8w_status fp8w_gemv_mx(const uint16_t* x, int64_t m, const uint8_t* codes,
+                         const uint8_t* e8m0, int64_t n, int64_t k,
+                         uint16_t* y, void* stream);
+
+/* The same two GEMVs with an explicit kernel family, for A/B measurement
+ * and for testing every route at every m.  FP8W_ROUTE_AUTO is identical to
+ * the calls above. */
+fp8w_status fp8w_gemv_block_route(const uint16_t* x, int64_t m,
+                                  const uint8_t* codes, const float* scales,
+                                  int64_t n, int64_t k, uint16_t* y,
+                                  fp8w_route route, void* stream);
+fp8w_status fp8w_gemv_mx_route(const uint16_t* x, int64_t m,
+                               const uint8_t* codes, const uint8_t* e8m0,
+                               int64_t n, int64_t k, uint16_t* y,
+                               fp8w_route route, void* stream);
+
+/* ------------------------------------------------------------- grouped -- */
+
+/* A group of independent GEMVs served by one kernel launch: the fixed cost
+ * of a launch (about 1.7 us on MI355X) is paid once instead of per GEMV,
+ * which matters when each GEMV streams only a few microseconds of weights
+ * (the 96-GEMV decode pass of "feat(qwen4_exp): load-time per-tensor FP8
+ * dense projections", Why; the grouped expert GEMM that reads [N/128,
+ * K/128] fp32 block scales in "quantize_fp8_bs.rs", Atlas weight_map).  The
+ * GEMVs of a group must not depend on one another (no y of one is the x of
+ * another); all share m, the scale format and the route.  Each GEMV meets
+ * the same error bound as the single call (the summation order may differ,
+ * so the last bit of y may too). */
+
+typedef enum fp8w_format {
+  FP8W_FORMAT_BLOCK = 0, /* fp32 scales, one per 128x128 tile */
+  FP8W_FORMAT_MX = 1     /* e8m0 bytes, one per 32 elements along K */
+} fp8w_format;
+
+/* One GEMV of a group; the same layout rules as fp8w_gemv_block /
+ * fp8w_gemv_mx.  scales is `const float*` (block) or `const uint8_t*` (mx). */
+typedef struct fp8w_gemv_desc {
+  const uint16_t* x;     /* bf16 [m, k], 16-byte aligned       */
+  const uint8_t* codes;  /* e4m3fn [n, k], 16-byte aligned     */
+  const void* scales;    /* block: f32 grid (4-B aligned); mx: e8m0 bytes */
+  uint16_t* y;           /* bf16 [m, n], output                */
+  int64_t n, k;          /* n >= 1, k >= 16, k % 16 == 0       */
+} fp8w_gemv_desc;
+
+/* What fp8w_grouped_plan_init fills in; pass it to fp8w_gemv_grouped. */
+typedef struct fp8w_grouped_plan {
+  const void* table; /* the caller's device table buffer          */
+  int32_t count;     /* GEMVs in the group                        */
+  int32_t m;         /* activation rows, shared by the group      */
+  int32_t format;    /* fp8w_format                               */
+  int32_t route;     /* fp8w_route resolved for m (VALU or MFMA)  */
+  int64_t blocks;    /* workgroups of one launch                  */
+} fp8w_grouped_plan;
+
+/* Bytes of device memory a table for `count` GEMVs needs (0 if count < 1). */
+int64_t fp8w_grouped_table_bytes(int64_t count);
+
+/* Set-up call (not for graph capture): validates every descriptor as the
+ * single call would, rejects any output that overlaps another GEMV's
+ * inputs or outputs, and writes the group's table into `device_table`
+ * (caller-owned device memory of fp8w_grouped_table_bytes(count) bytes,
+ * 16-byte aligned) with a blocking host-to-device copy.  The descriptors are
+ * not retained.  Errors: NULL, SHAPE (count < 1, m out of range, too many
+ * workgroups), ALIGN, UNSUPPORTED, OVERLAP, HIP. */
+fp8w_status fp8w_grouped_plan_init(const fp8w_gemv_desc* descs, int64_t count, int64_t m,
+                                   fp8w_format format, fp8w_route route, void* device_table,
+                                   fp8w_grouped_plan* plan);
+
+/* Enqueue every GEMV of the plan in one launch on `stream`.  Asynchronous,
+ * allocation-free and safe to capture in a HIP graph; the buffers the
+ * descriptors named must still be live.  Errors: NULL, SHAPE (a plan not
+ * produced by fp8w_grouped_plan_init), HIP. */
+fp8w_status fp8w_gemv_grouped(const fp8w_grouped_plan* plan, void* stream);
+
+/* ------------------------------------------------------------- helpers -- */
+
+/* Number of fp32 block scales for [n, k]: ceil(n/128) * ceil(k/128); 0 if
+ * n < 1 or k < 1. */
+int64_t fp8w_block_scale_count(int64_t n, int64_t k);
+
+/* Number of e8m0 bytes for [n, k]: n * ceil(k/32); 0 if n < 1 or k < 1. */
+int64_t fp8w_mx_scale_count(int64_t n, int64_t k);
+
+/* Static, NUL-terminated name of a status code. */
+const char* fp8w_status_string(fp8w_status status);
+
+/* Library version, as major * 10000 + minor * 100 + patch. */
+int fp8w_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8W_H_ */

@@ -1,0 +1,135 @@
+"""C-ABI checks that need no GPU: libfp8w.so loads, exports exactly the
+functions include/fp8w.h declares, and rejects invalid arguments on the host
+before anything is enqueued (no compute call is made here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8w.h")
+
+
+@pytest.fixture(scope="module")
+def F():
+    import fp8_block_scaled_02_amd as fp8w
+    if not os.path.exists(fp8w.LIB_PATH):
+        from fp8_block_scaled_02_amd import build
+        build.build()
+    fp8w.lib()
+    return fp8w
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp8w_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls_of_the_path():
+    names = declared_functions()
+    for n in ("fp8w_quantize_block", "fp8w_quantize_mx", "fp8w_gemv_block", "fp8w_gemv_mx"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol_and_nothing_else(F):
+    out = subprocess.run(["nm", "-D", "--defined-only", F.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = sorted({line.split()[-1] for line in out.splitlines()
+                       if " T " in line and line.split()[-1].startswith("fp8w_")})
+    assert exported == declared_functions()
+    for name in declared_functions():
+        assert hasattr(F.lib(), name)
+    assert set(F.SIGNATURES) == set(declared_functions())
+
+
+def test_helpers(F):
+    L = F.lib()
+    assert L.fp8w_block_scale_count(129, 257) == 2 * 3
+    assert L.fp8w_block_scale_count(128, 128) == 1
+    assert L.fp8w_block_scale_count(0, 5) == 0
+    assert L.fp8w_mx_scale_count(3, 33) == 3 * 2
+    assert L.fp8w_mx_scale_count(3, -1) == 0
+    assert L.fp8w_grouped_table_bytes(96) == 96 * 48
+    assert L.fp8w_grouped_table_bytes(0) == 0
+    assert L.fp8w_version() >= 100
+    for st in range(7):
+        assert F.status_string(st).startswith("FP8W_")
+
+
+# Fake, well-aligned "device" addresses: every call below fails validation
+# before any HIP call, so they are never dereferenced.
+A, B, C, D = 0x10000, 0x2000000, 0x4000000, 0x8000000
+
+
+def test_quantize_argument_errors(F):
+    L = F.lib()
+    assert L.fp8w_quantize_block(None, 4, 4, B, C, None) == F.ERR_NULL
+    assert L.fp8w_quantize_block(A, 0, 4, B, C, None) == F.ERR_SHAPE
+    assert L.fp8w_quantize_block(A, 4, -1, B, C, None) == F.ERR_SHAPE
+    assert L.fp8w_quantize_block(A, 1 << 31, 4, B, C, None) == F.ERR_SHAPE
+    assert L.fp8w_quantize_block(A + 1, 4, 4, B, C, None) == F.ERR_ALIGN
+    assert L.fp8w_quantize_block(A, 4, 4, B, C + 2, None) == F.ERR_ALIGN
+    assert L.fp8w_quantize_block(A, 64, 64, A + 100, C, None) == F.ERR_OVERLAP   # codes inside w
+    assert L.fp8w_quantize_block(A, 64, 64, B, B + 100, None) == F.ERR_OVERLAP   # scales inside codes
+    assert L.fp8w_quantize_mx(A, 4, 4, None, C, None) == F.ERR_NULL
+    assert L.fp8w_quantize_mx(A, 4, 0, B, C, None) == F.ERR_SHAPE
+    assert L.fp8w_quantize_mx(A, 64, 64, B, B + 64, None) == F.ERR_OVERLAP
+
+
+def test_gemv_argument_errors(F):
+    L = F.lib()
+    g = L.fp8w_gemv_block
+    assert g(None, 1, B, C, 16, 16, D, None) == F.ERR_NULL
+    assert g(A, 0, B, C, 16, 16, D, None) == F.ERR_SHAPE
+    assert g(A, 33, B, C, 16, 16, D, None) == F.ERR_SHAPE
+    assert g(A, 1, B, C, 0, 16, D, None) == F.ERR_SHAPE
+    assert g(A, 1, B, C, 16, 8, D, None) == F.ERR_SHAPE          # k < 16
+    assert g(A, 1, B, C, 16, 40, D, None) == F.ERR_ALIGN         # k % 16
+    assert g(A + 8, 1, B, C, 16, 16, D, None) == F.ERR_ALIGN     # x alignment
+    assert g(A, 1, B + 4, C, 16, 16, D, None) == F.ERR_ALIGN     # codes alignment
+    assert g(A, 1, B, C + 2, 16, 16, D, None) == F.ERR_ALIGN     # scale alignment
+    assert g(A, 1, B, C, 16, 16, A + 16, None) == F.ERR_OVERLAP  # y over x
+    assert g(A, 1, B, C, 16, 16, C, None) == F.ERR_OVERLAP       # y over scales
+    r = L.fp8w_gemv_block_route
+    assert r(A, 9, B, C, 16, 16, D, F.ROUTE_VALU, None) == F.ERR_UNSUPPORTED
+    assert r(A, 1, B, C, 16, 16, D, 7, None) == F.ERR_UNSUPPORTED
+    m = L.fp8w_gemv_mx_route
+    assert m(A, 1, B, None, 16, 16, D, F.ROUTE_AUTO, None) == F.ERR_NULL
+    # e8m0 needs no alignment: an odd scale pointer passes the alignment
+    # check and the call is then rejected for the overlap (nothing enqueued)
+    assert m(A, 1, B, C + 1, 16, 16, A + 16, F.ROUTE_AUTO, None) == F.ERR_OVERLAP
+
+
+def test_grouped_argument_errors(F):
+    L = F.lib()
+    descs = (F.GemvDesc * 2)(F.GemvDesc(A, B, C, D, 16, 16), F.GemvDesc(A, B, C, D + 4096, 16, 16))
+    plan = F.GroupedPlanC()
+    T = 0x10000000
+    init = L.fp8w_grouped_plan_init
+    assert init(None, 2, 1, F.FORMAT_BLOCK, 0, T, ctypes.byref(plan)) == F.ERR_NULL
+    assert init(descs, 0, 1, F.FORMAT_BLOCK, 0, T, ctypes.byref(plan)) == F.ERR_SHAPE
+    assert init(descs, 2, 1, 5, 0, T, ctypes.byref(plan)) == F.ERR_UNSUPPORTED
+    assert init(descs, 2, 1, F.FORMAT_BLOCK, 0, T + 8, ctypes.byref(plan)) == F.ERR_ALIGN
+    assert init(descs, 2, 40, F.FORMAT_BLOCK, 0, T, ctypes.byref(plan)) == F.ERR_SHAPE
+    clash = (F.GemvDesc * 2)(F.GemvDesc(A, B, C, D, 16, 16), F.GemvDesc(A, B, C, D + 8, 16, 16))
+    assert init(clash, 2, 1, F.FORMAT_BLOCK, 0, T, ctypes.byref(plan)) == F.ERR_OVERLAP
+    into_table = (F.GemvDesc * 1)(F.GemvDesc(A, B, C, T + 16, 16, 16))
+    assert init(into_table, 1, 1, F.FORMAT_BLOCK, 0, T, ctypes.byref(plan)) == F.ERR_OVERLAP
+    assert L.fp8w_gemv_grouped(None, None) == F.ERR_NULL
+    bad = F.GroupedPlanC(T, 1, 1, 0, 1, 0)        # zero blocks: not from plan_init
+    assert L.fp8w_gemv_grouped(ctypes.byref(bad), None) == F.ERR_SHAPE
+    bad = F.GroupedPlanC(T, 1, 9, 0, 1, 4)        # VALU route with m = 9
+    assert L.fp8w_gemv_grouped(ctypes.byref(bad), None) == F.ERR_SHAPE
+
+
+def test_binding_refuses_cpu_tensors(F):
+    import torch
+    w = torch.zeros((4, 4), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        F.fp8w_quantize_block(w)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        F.fp8w_gemv_block(torch.zeros((1, 16), dtype=torch.bfloat16),
+                          torch.zeros((16, 16), dtype=torch.uint8), torch.ones((1, 1)))

@@ -1,0 +1,121 @@
+"""GPU parity of the grouped GEMV (many independent GEMVs in one launch)
+against the CPU oracle, its argument checks, and HIP-graph replays."""
+import numpy as np
+import pytest
+
+from fp8_block_scaled_02_amd import workloads as W
+from gpu_util import assert_within_bound, bf16_to_f64, to_dev, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+# ragged N, K multiples of 16 that are not multiples of 128, several jobs per K
+SHAPES = [(300, 1008), (130, 272), (1024, 1024), (257, 2560), (129, 4112), (64, 16), (2560, 3072)]
+
+
+@pytest.fixture(scope="module")
+def fp8w():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    import fp8_block_scaled_02_amd as F
+    F.lib()
+    return F
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def _jobs(oracle_mod, fmt, seed):
+    out = []
+    for i, (n, k) in enumerate(SHAPES):
+        bits = W.gaussian_weight(30 + seed, i, n, k, outlier_rows=fmt == "block", heavy_tail=fmt == "mx")
+        codes, sc = oracle_mod.quantize_block(bits) if fmt == "block" else oracle_mod.quantize_mx(bits)
+        out.append((n, k, codes, sc))
+    return out
+
+
+@pytest.mark.parametrize("fmt", ["block", "mx"])
+@pytest.mark.parametrize("m", [1, 2, 5, 8, 9, 16, 17, 32])
+def test_grouped_matches_oracle(fp8w, oracle_mod, fmt, m):
+    jobs = _jobs(oracle_mod, fmt, 0)
+    xs_h = [W.activation(31, m, k) for (_, k, _, _) in jobs]
+    plan = fp8w.fp8w_grouped_plan_init([to_dev_bf16(x) for x in xs_h],
+                                       [to_dev(c) for (_, _, c, _) in jobs],
+                                       [to_dev(s) for (_, _, _, s) in jobs], fmt=fmt)
+    assert plan.route == (fp8w.ROUTE_VALU if m <= 8 else fp8w.ROUTE_MFMA)
+    ys = fp8w.fp8w_gemv_grouped(plan)
+    _sync()
+    ref = oracle_mod.gemv_block_f64 if fmt == "block" else oracle_mod.gemv_mx_f64
+    for (n, k, c, s), x, y in zip(jobs, xs_h, ys):
+        y_ref, bound = ref(x, c, s)
+        assert_within_bound(bf16_to_f64(y), y_ref, bound, f"grouped {fmt} m={m} [{n}x{k}]")
+
+
+def test_grouped_mfma_route_at_small_m(fp8w, oracle_mod):
+    jobs = _jobs(oracle_mod, "block", 1)
+    for m in (1, 4, 8):
+        xs_h = [W.activation(32, m, k) for (_, k, _, _) in jobs]
+        plan = fp8w.fp8w_grouped_plan_init([to_dev_bf16(x) for x in xs_h],
+                                           [to_dev(c) for (_, _, c, _) in jobs],
+                                           [to_dev(s) for (_, _, _, s) in jobs],
+                                           route=fp8w.ROUTE_MFMA)
+        ys = fp8w.fp8w_gemv_grouped(plan)
+        _sync()
+        for (n, k, c, s), x, y in zip(jobs, xs_h, ys):
+            y_ref, bound = oracle_mod.gemv_block_f64(x, c, s)
+            assert_within_bound(bf16_to_f64(y), y_ref, bound, f"grouped mfma m={m} [{n}x{k}]")
+
+
+def test_grouped_rejects_overlapping_outputs(fp8w, oracle_mod):
+    import torch
+    jobs = _jobs(oracle_mod, "block", 2)[:2]
+    xs = [to_dev_bf16(W.activation(33, 1, k)) for (_, k, _, _) in jobs]
+    cs = [to_dev(c) for (_, _, c, _) in jobs]
+    ss = [to_dev(s) for (_, _, _, s) in jobs]
+    big = torch.empty((1, 4096), dtype=torch.bfloat16, device="cuda")
+    ys = [big[:, :jobs[0][0]], big[:, 100:100 + jobs[1][0]]]        # overlapping views
+    with pytest.raises(fp8w.Fp8wError) as e:
+        fp8w.fp8w_grouped_plan_init(xs, cs, ss, ys=ys)
+    assert e.value.status == fp8w.ERR_OVERLAP
+
+
+def test_grouped_and_single_calls_replay_in_a_graph(fp8w, oracle_mod):
+    """Capture single and grouped calls in one HIP graph; replay it several
+    times with eager work and synchronizations in between; every replay must
+    equal the eager result bit for bit."""
+    import torch
+    jobs = _jobs(oracle_mod, "block", 3)
+    m = 3
+    xs = [to_dev_bf16(W.activation(34, m, k)) for (_, k, _, _) in jobs]
+    cs = [to_dev(c) for (_, _, c, _) in jobs]
+    ss = [to_dev(s) for (_, _, _, s) in jobs]
+    plan = fp8w.fp8w_grouped_plan_init(xs, cs, ss)
+    ys_single = [torch.empty((m, c.shape[0]), dtype=torch.bfloat16, device="cuda") for c in cs]
+
+    def run():
+        fp8w.fp8w_gemv_grouped(plan)
+        for x, c, s, y in zip(xs, cs, ss, ys_single):
+            fp8w.fp8w_gemv_block(x, c, s, y=y)
+
+    run()
+    _sync()
+    eager_g = [y.clone() for y in plan.ys]
+    eager_s = [y.clone() for y in ys_single]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    _sync()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(4):
+        for y in plan.ys + ys_single:
+            y.fill_(float(rep + 7))                       # eager work between replays
+        _sync()
+        g.replay()
+        _sync()
+        for a, b in zip(plan.ys + ys_single, eager_g + eager_s):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"replay {rep}"

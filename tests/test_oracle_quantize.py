@@ -11,6 +11,7 @@ import pytest
 import torch
 
 from fp8_block_scaled_02_amd import workloads as W
+from cases import edge_case_weight
 from pagevalues import page_values
 
 TILE = page_values()["block_tile"]
@@ -66,24 +67,6 @@ def independent_mx_quant(bits: np.ndarray):
     e = exact_e8m0(amax)
     q = np.ldexp(w, -np.repeat(e, GROUP, axis=1)[:, :k]).astype(np.float32)
     return fp8_cast(q), (e + 127).astype(np.uint8)
-
-
-def edge_case_weight() -> np.ndarray:
-    """[384 x 300] bf16 with hand-made tiles: all zero, a single nonzero,
-    a subnormal amax, an exact +-448, huge values, negative zeros."""
-    rng = np.random.default_rng(3)
-    w = (rng.standard_normal((384, 300)) * 0.02).astype(np.float32)
-    w[0:128, 0:128] = 0.0                                   # all-zero tile
-    w[0:128, 128:256] = 0.0
-    w[5, 130] = -0.75                                       # single nonzero
-    w[128:256, 0:128] = rng.standard_normal((128, 128)) * 1e-39   # subnormal amax
-    w[128:256, 128:256] = np.clip(rng.standard_normal((128, 128)) * 200, -448, 448)
-    w[130, 140], w[131, 141] = 448.0, -448.0
-    w[256:384, 0:128] *= 1e36                               # huge values
-    w[256:300, 256:300] = -0.0                              # negative zeros in the tail tile
-    bits = W._to_bf16(w)
-    assert np.isfinite(f32(bits)).all()
-    return bits
 
 
 SHAPES = [(1, 1), (1, 127), (127, 129), (130, 260), (300, 1000), (129, 4100)]

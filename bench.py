@@ -88,16 +88,21 @@ class Timer:
     def hold(self, ms):
         self.torch.cuda._sleep(int(self.cycles_per_ms * ms))
 
-    def run(self, fn, reps, warmup, hold_ms=30.0):
-        """Per-rep ms (event pair around each call of fn) and total ms."""
+    def run(self, fn, reps, warmup, hold_ms=0.0):
+        """Per-rep ms (event pair around each call of fn) and total ms.
+
+        hold_ms > 0 queues a spin kernel first, for sequences whose host-side
+        enqueue is slower than their GPU time (un-graphed launches); graph
+        replays are cheap to enqueue and run right after their warmup."""
         t = self.torch
-        for _ in range(warmup):
-            fn()
-        t.cuda.synchronize()
         starts = [t.cuda.Event(enable_timing=True) for _ in range(reps)]
         ends = [t.cuda.Event(enable_timing=True) for _ in range(reps)]
         t0, t1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
-        self.hold(hold_ms)
+        if hold_ms > 0:
+            t.cuda.synchronize()
+            self.hold(hold_ms)
+        for _ in range(warmup):
+            fn()
         t0.record()
         for i in range(reps):
             starts[i].record()

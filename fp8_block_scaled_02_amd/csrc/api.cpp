@@ -167,20 +167,38 @@ FP8W_API fp8w_status fp8w_grouped_plan_init(const fp8w_gemv_desc* descs, int64_t
   if (any_overlap(outs.data(), (int)outs.size(), ins.data(), (int)ins.size()))
     return FP8W_ERR_OVERLAP;
   const int r = resolve_route(route, m);
-  const int rows = fp8w::gemv_rows_per_block(r, (int)m, true);
+  int64_t max_k = 0;
+  for (int64_t i = 0; i < count; ++i) max_k = descs[i].k > max_k ? descs[i].k : max_k;
+  // m = 1 on the VALU route with every K in one segment: the streaming
+  // kernel (contiguous runs of tiles per workgroup); otherwise one tile per
+  // workgroup.
+  const bool stream = r == 1 && m == 1 && max_k <= fp8w::gemv_stream_max_k();
+  const int rows = stream ? fp8w::gemv_stream_rows() : fp8w::gemv_rows_per_block(r, (int)m, true);
   std::vector<fp8w::GemvJob> table((size_t)count);
-  int64_t blocks = 0;
+  int64_t tiles = 0;
   for (int64_t i = 0; i < count; ++i) {
     const fp8w_gemv_desc& d = descs[i];
     table[i] = fp8w::GemvJob{d.x, d.codes, d.scales, d.y, (int32_t)d.n, (int32_t)d.k,
-                             (int32_t)blocks, 0};
-    blocks += (d.n + rows - 1) / rows;
-    if (blocks > kMaxDim) return FP8W_ERR_SHAPE;
+                             (int32_t)tiles, 0};
+    tiles += (d.n + rows - 1) / rows;
+    if (tiles > kMaxDim) return FP8W_ERR_SHAPE;
+  }
+  int64_t blocks = tiles;
+  int32_t per_block = 0;
+  if (stream) {
+    int slots = 0;
+    if (fp8w::gemv_stream_slots(!block, &slots) != hipSuccess) return FP8W_ERR_HIP;
+    // about four workgroups per resident slot: short runs keep the tail of
+    // the launch small
+    const int64_t want = (int64_t)4 * slots;
+    per_block = (int32_t)((tiles + want - 1) / want);
+    blocks = (tiles + per_block - 1) / per_block;
   }
   if (hipMemcpy(device_table, table.data(), table_bytes, hipMemcpyHostToDevice) != hipSuccess)
     return FP8W_ERR_HIP;
   *plan = fp8w_grouped_plan{device_table, (int32_t)count, (int32_t)m, (int32_t)format,
-                            (int32_t)(r == 1 ? FP8W_ROUTE_VALU : FP8W_ROUTE_MFMA), blocks};
+                            (int32_t)(r == 1 ? FP8W_ROUTE_VALU : FP8W_ROUTE_MFMA), blocks, tiles,
+                            per_block, 0};
   return FP8W_OK;
 }
 
@@ -189,13 +207,23 @@ FP8W_API fp8w_status fp8w_gemv_grouped(const fp8w_grouped_plan* plan, void* stre
   const bool route_ok = (plan->route == FP8W_ROUTE_VALU && plan->m <= kValuMaxM) ||
                         plan->route == FP8W_ROUTE_MFMA;
   if (plan->count < 1 || plan->m < 1 || plan->m > FP8W_MAX_M || !route_ok || plan->blocks < 1 ||
-      plan->blocks > kMaxDim ||
+      plan->blocks > kMaxDim || plan->tiles < plan->blocks || plan->tiles > kMaxDim ||
+      plan->tiles_per_block < 0 ||
       (plan->format != FP8W_FORMAT_BLOCK && plan->format != FP8W_FORMAT_MX))
     return FP8W_ERR_SHAPE;
-  return from_hip(fp8w::launch_gemv_grouped(
-      static_cast<const fp8w::GemvJob*>(plan->table), plan->count, plan->blocks, plan->m,
-      plan->format == FP8W_FORMAT_MX, plan->route == FP8W_ROUTE_VALU ? 1 : 2,
-      static_cast<hipStream_t>(stream)));
+  const bool mx = plan->format == FP8W_FORMAT_MX;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const fp8w::GemvJob* table = static_cast<const fp8w::GemvJob*>(plan->table);
+  if (plan->tiles_per_block > 0) {
+    if (plan->route != FP8W_ROUTE_VALU || plan->m != 1 ||
+        plan->blocks * (int64_t)plan->tiles_per_block < plan->tiles)
+      return FP8W_ERR_SHAPE;
+    return from_hip(fp8w::launch_gemv_stream(table, plan->count, plan->blocks, plan->tiles,
+                                             plan->tiles_per_block, mx, s));
+  }
+  if (plan->blocks != plan->tiles) return FP8W_ERR_SHAPE;
+  return from_hip(fp8w::launch_gemv_grouped(table, plan->count, plan->blocks, plan->m, mx,
+                                            plan->route == FP8W_ROUTE_VALU ? 1 : 2, s));
 }
 
 // ------------------------------------------------------------- helpers --

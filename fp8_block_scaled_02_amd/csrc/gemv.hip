@@ -15,7 +15,8 @@
 //    x^T padded to 16 or 32 columns.
 //
 // Each call is a few microseconds of HBM traffic, so latency decides the
-// time: every kernel issues a K segment's weight loads first, then stages x
+// time: every kernel issues a K segment's weight loads first (non-temporal:
+// each code byte is read once), then stages x
 // (and the block-scale row) in LDS while those loads are in flight.  Segments
 // are sized so that the common K (up to a few thousand) is one segment.
 //
@@ -35,6 +36,7 @@
 // weights must be finite in fp32 (|deq| < 2^128): only e8m0 bytes >= 247,
 // i.e. weights within 0.4 % of the bf16 maximum, can break that.
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 
 #include "device.hpp"
 #include "internal.hpp"
@@ -113,12 +115,19 @@ __device__ __forceinline__ void find_job(const GemvJob& arg, const GemvJob* __re
   int lo = 0, hi = njobs - 1;   // last job whose first workgroup is <= b
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (jobs[mid].item0 <= b)
+    if (ld_global<int32_t>(jobs, (size_t)mid * sizeof(GemvJob) + offsetof(GemvJob, item0)) <= b)
       lo = mid;
     else
       hi = mid - 1;
   }
-  job = jobs[lo];
+  const size_t row = (size_t)lo * sizeof(GemvJob);
+  job.x = (const uint16_t*)ld_global<uint64_t>(jobs, row + offsetof(GemvJob, x));
+  job.codes = (const uint8_t*)ld_global<uint64_t>(jobs, row + offsetof(GemvJob, codes));
+  job.scales = (const void*)ld_global<uint64_t>(jobs, row + offsetof(GemvJob, scales));
+  job.y = (uint16_t*)ld_global<uint64_t>(jobs, row + offsetof(GemvJob, y));
+  job.n = ld_global<int32_t>(jobs, row + offsetof(GemvJob, n));
+  job.k = ld_global<int32_t>(jobs, row + offsetof(GemvJob, k));
+  job.item0 = ld_global<int32_t>(jobs, row + offsetof(GemvJob, item0));
   tile = b - job.item0;
 }
 
@@ -132,7 +141,7 @@ __device__ __forceinline__ void stage_x(const uint16_t* __restrict__ x, int rows
   for (int u = threadIdx.x; u < rows_pad * units; u += kThreads) {
     const int r = u / units, c = (u % units) * 8;
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (r < rows && c < len) v = *reinterpret_cast<const uint4*>(x + (size_t)r * k + seg0 + c);
+    if (r < rows && c < len) v = ld_global_u4(x, ((size_t)r * k + seg0 + c) * 2);
     *reinterpret_cast<uint4*>(xs + r * ld + c) = v;
   }
 }
@@ -168,8 +177,8 @@ __device__ __forceinline__ void valu_load(const GemvJob& j, int row0, int seg0, 
       wv[r][c] = make_uint4(0, 0, 0, 0);
       ws[r][c] = 0.0f;
       if (ch < nch && row < j.n) {
-        wv[r][c] = *reinterpret_cast<const uint4*>(j.codes + (size_t)row * j.k + seg0 + ch * 16);
-        if (MX) ws[r][c] = mx_scale(e8[(size_t)row * groups + (seg0 + ch * 16) / kGroup]);
+        wv[r][c] = ld_stream_u4(j.codes, (size_t)row * j.k + seg0 + ch * 16);
+        if (MX) ws[r][c] = mx_scale(ld_global<uint8_t>(e8, (size_t)row * groups + (seg0 + ch * 16) / kGroup));
       }
     }
   }
@@ -210,11 +219,10 @@ __global__ __launch_bounds__(kThreads) void k_gemv_valu(GemvJob arg, const GemvJ
     stage_x(j.x, M, M, j.k, seg0, len, len, xs, S::kSeg);
     if (!MX) {
       const int nkb = (len + kTile - 1) / kTile;
-      if ((int)threadIdx.x < nkb) ss[threadIdx.x] = srow[seg0 / kTile + threadIdx.x];
+      if ((int)threadIdx.x < nkb) ss[threadIdx.x] = ld_global<float>(srow, (size_t)(seg0 / kTile + threadIdx.x) * 4);
     }
     __syncthreads();
 
-#pragma unroll
     for (int c = 0; c < C; ++c) {
       const int ch = lane + kWave * c;
       if (ch < nch) {
@@ -244,8 +252,160 @@ __global__ __launch_bounds__(kThreads) void k_gemv_valu(GemvJob arg, const GemvJ
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       const float v = wave_sum(acc[r][m]);
-      if (lane == 0 && row < j.n) j.y[(size_t)m * j.n + row] = (uint16_t)f32_to_bf16_rne(v);
+      if (lane == 0 && row < j.n) st_global<uint16_t>(j.y, ((size_t)m * j.n + row) * 2, (uint16_t)f32_to_bf16_rne(v));
     }
+  }
+}
+
+// ------------------------------------------------------- VALU streaming --
+//
+// Grouped launches at M = 1 whose GEMVs all have K <= 1024*C: each
+// workgroup owns a contiguous run of row tiles (across job boundaries) and
+// requests tile t+1's codes and scales before computing tile t, so the weight
+// stream never waits for a workgroup to start, look up its job or stage x.
+// x is restaged in LDS only when the run crosses into the next job.
+template <int R, int C, bool MX>
+struct TileRegs {
+  uint4 w[R][C];
+  float s[R][C];   // MX: per row and chunk; block: row 0 holds the chunk scales
+};
+
+__device__ __forceinline__ void load_job_row(const GemvJob* __restrict__ jobs, int jn, GemvJob& job) {
+  const size_t row = (size_t)jn * sizeof(GemvJob);
+  job.x = (const uint16_t*)ld_global<uint64_t>(jobs, row + offsetof(GemvJob, x));
+  job.codes = (const uint8_t*)ld_global<uint64_t>(jobs, row + offsetof(GemvJob, codes));
+  job.scales = (const void*)ld_global<uint64_t>(jobs, row + offsetof(GemvJob, scales));
+  job.y = (uint16_t*)ld_global<uint64_t>(jobs, row + offsetof(GemvJob, y));
+  job.n = ld_global<int32_t>(jobs, row + offsetof(GemvJob, n));
+  job.k = ld_global<int32_t>(jobs, row + offsetof(GemvJob, k));
+  job.item0 = ld_global<int32_t>(jobs, row + offsetof(GemvJob, item0));
+}
+
+__device__ __forceinline__ int next_item0(const GemvJob* __restrict__ jobs, int jn, int njobs) {
+  return jn + 1 < njobs
+             ? ld_global<int32_t>(jobs, (size_t)(jn + 1) * sizeof(GemvJob) + offsetof(GemvJob, item0))
+             : 0x7FFFFFFF;
+}
+
+template <int R, int C, bool MX>
+__device__ __forceinline__ void stream_issue(const GemvJob& j, int tile, TileRegs<R, C, MX>& t) {
+  constexpr int kRows = kWaves * R;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int row0 = tile * kRows + wave * R;
+  const int nch = j.k / 16;
+  const int tiles_k = (j.k + kTile - 1) / kTile;
+  const int groups = (j.k + kGroup - 1) / kGroup;
+  const float* __restrict__ srow =
+      MX ? nullptr : static_cast<const float*>(j.scales) + (size_t)(tile * kRows / kTile) * tiles_k;
+  const uint8_t* __restrict__ e8 = static_cast<const uint8_t*>(j.scales);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int row = row0 + r;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int ch = lane + kWave * c;
+      t.w[r][c] = make_uint4(0, 0, 0, 0);
+      t.s[r][c] = 0.0f;
+      if (ch < nch && row < j.n) {
+        t.w[r][c] = ld_stream_u4(j.codes, (size_t)row * j.k + ch * 16);
+        if (MX) t.s[r][c] = mx_scale(ld_global<uint8_t>(e8, (size_t)row * groups + ch / 2));
+      }
+    }
+  }
+  if (!MX) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int ch = lane + kWave * c;
+      t.s[0][c] = ch < nch ? ld_global<float>(srow, (size_t)(ch >> 3) * 4) : 0.0f;
+    }
+  }
+}
+
+template <int R, int C, bool MX>
+__global__ __launch_bounds__(kThreads) void k_gemv_valu_stream(const GemvJob* __restrict__ jobs,
+                                                               int njobs, int total_tiles,
+                                                               int tiles_per_block) {
+  constexpr int kRows = kWaves * R, kSeg = 1024 * C;
+  static_assert(kTile % kRows == 0, "a tile must stay inside one 128-row block");
+  __shared__ __align__(16) uint16_t xs[kSeg];
+  const int t_begin = blockIdx.x * tiles_per_block;
+  const int t_end = min(total_tiles, t_begin + tiles_per_block);
+  if (t_begin >= t_end) return;   // whole workgroup: no barrier is skipped by part of it
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+
+  int jn = 0;
+  {
+    int lo = 0, hi = njobs - 1;   // last job whose first tile is <= t_begin
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (ld_global<int32_t>(jobs, (size_t)mid * sizeof(GemvJob) + offsetof(GemvJob, item0)) <= t_begin)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    jn = lo;
+  }
+  GemvJob j;
+  load_job_row(jobs, jn, j);
+  int boundary = next_item0(jobs, jn, njobs);
+
+  TileRegs<R, C, MX> cur, nxt;
+  stream_issue<R, C, MX>(j, t_begin - j.item0, cur);
+  for (int u = threadIdx.x; u < j.k / 8; u += kThreads)
+    *reinterpret_cast<uint4*>(xs + u * 8) = ld_global_u4(j.x, (size_t)u * 16);
+  __syncthreads();
+
+  for (int t = t_begin; t < t_end; ++t) {
+    const bool more = t + 1 < t_end;
+    GemvJob jnext = j;
+    int jn_next = jn, boundary_next = boundary;
+    if (more) {
+      if (t + 1 >= boundary) {   // the run crosses into the next job
+        jn_next = jn + 1;
+        load_job_row(jobs, jn_next, jnext);
+        boundary_next = next_item0(jobs, jn_next, njobs);
+      }
+      stream_issue<R, C, MX>(jnext, t + 1 - jnext.item0, nxt);
+    }
+
+    const int row0 = (t - j.item0) * kRows + wave * R;
+    const int nch = j.k / 16;
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int ch = lane + kWave * c;
+      if (ch < nch) {
+        const uint4 x0 = *reinterpret_cast<const uint4*>(xs + ch * 16);
+        const uint4 x1 = *reinterpret_cast<const uint4*>(xs + ch * 16 + 8);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const uint4 d = cur.w[r][c];
+          const bf16x2 w[8] = {cvt_lo(d.x), cvt_hi(d.x), cvt_lo(d.y), cvt_hi(d.y),
+                               cvt_lo(d.z), cvt_hi(d.z), cvt_lo(d.w), cvt_hi(d.w)};
+          const float sc = MX ? cur.s[r][c] : cur.s[0][c];
+          acc[r] = __builtin_fmaf(sc, dot16(w, x0, x1), acc[r]);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float v = wave_sum(acc[r]);
+      if (lane == 0 && row0 + r < j.n)
+        st_global<uint16_t>(j.y, (size_t)(row0 + r) * 2, (uint16_t)f32_to_bf16_rne(v));
+    }
+    if (!more) break;
+    if (jn_next != jn) {   // restage x for the next job
+      __syncthreads();
+      for (int u = threadIdx.x; u < jnext.k / 8; u += kThreads)
+        *reinterpret_cast<uint4*>(xs + u * 8) = ld_global_u4(jnext.x, (size_t)u * 16);
+      __syncthreads();
+    }
+    j = jnext;
+    jn = jn_next;
+    boundary = boundary_next;
+    cur = nxt;
   }
 }
 
@@ -289,8 +449,8 @@ __device__ __forceinline__ void mfma_load(const GemvJob& j, int row, bool row_ok
       wv[q][h] = make_uint4(0, 0, 0, 0);
       ws[q][h] = 0.0f;
       if (row_ok && koff < len) {
-        wv[q][h] = *reinterpret_cast<const uint4*>(j.codes + (size_t)row * j.k + seg0 + koff);
-        if (MX) ws[q][h] = mx_scale(e8[(size_t)row * groups + (seg0 + koff) / kGroup]);
+        wv[q][h] = ld_stream_u4(j.codes, (size_t)row * j.k + seg0 + koff);
+        if (MX) ws[q][h] = mx_scale(ld_global<uint8_t>(e8, (size_t)row * groups + (seg0 + koff) / kGroup));
       }
     }
   }
@@ -370,7 +530,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv_mfma(GemvJob arg, const GemvJ
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[t] = part[t];
       } else {
-        const float bs = srow[(seg0 + kb * kTile) / kTile];
+        const float bs = ld_global<float>(srow, (size_t)((seg0 + kb * kTile) / kTile) * 4);
 #pragma unroll
         for (int t = 0; t < MT; ++t)
 #pragma unroll
@@ -405,7 +565,8 @@ __global__ __launch_bounds__(kThreads) void k_gemv_mfma(GemvJob arg, const GemvJ
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int r = row0 + 4 * g + jj;
-        if (r < j.n && mcol < m_rows) j.y[(size_t)mcol * j.n + r] = (uint16_t)f32_to_bf16_rne(acc[t][jj]);
+        if (r < j.n && mcol < m_rows)
+          st_global<uint16_t>(j.y, ((size_t)mcol * j.n + r) * 2, (uint16_t)f32_to_bf16_rne(acc[t][jj]));
       }
     }
   }
@@ -442,7 +603,7 @@ hipError_t dispatch_valu(int m, const GemvJob& job, const GemvJob* table, int nj
                          hipStream_t s) {
   if (G) {
     switch (m) {
-      case 1: return run_valu<1, 8, 3, MX, G>(job, table, njobs, blocks, s);
+      case 1: return run_valu<1, 4, 3, MX, G>(job, table, njobs, blocks, s);
       case 2: return run_valu<2, 4, 2, MX, G>(job, table, njobs, blocks, s);
       case 3: return run_valu<3, 4, 2, MX, G>(job, table, njobs, blocks, s);
       case 4: return run_valu<4, 4, 2, MX, G>(job, table, njobs, blocks, s);
@@ -481,7 +642,7 @@ hipError_t dispatch_mfma(int m, const GemvJob& job, const GemvJob* table, int nj
 
 int gemv_rows_per_block(int route, int m, bool grouped) {
   if (route == 1) {
-    if (grouped) return kWaves * (m == 1 ? 8 : 4);
+    if (grouped) return kWaves * 4;
     return kWaves * (m == 1 ? 1 : 2);
   }
   return grouped ? 64 : 16;
@@ -495,6 +656,36 @@ hipError_t launch_gemv(const GemvJob& job, int m, bool mx, int route, hipStream_
               : dispatch_valu<false, false>(m, job, nullptr, 1, blocks, stream);
   return mx ? dispatch_mfma<true, false>(m, job, nullptr, 1, blocks, stream)
             : dispatch_mfma<false, false>(m, job, nullptr, 1, blocks, stream);
+}
+
+// Streaming kernel of grouped M = 1 VALU plans: (R, C) and its K limit.
+constexpr int kStreamR = 4, kStreamC = 3;
+
+int gemv_stream_max_k() { return 1024 * kStreamC; }
+int gemv_stream_rows() { return kWaves * kStreamR; }
+
+hipError_t gemv_stream_slots(bool mx, int* slots) {
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess)
+    e = mx ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                 &per_cu, k_gemv_valu_stream<kStreamR, kStreamC, true>, kThreads, 0)
+           : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                 &per_cu, k_gemv_valu_stream<kStreamR, kStreamC, false>, kThreads, 0);
+  *slots = cus * (per_cu > 0 ? per_cu : 1);
+  return e;
+}
+
+hipError_t launch_gemv_stream(const GemvJob* table, int njobs, int64_t blocks, int64_t tiles,
+                              int tiles_per_block, bool mx, hipStream_t stream) {
+  if (mx)
+    hipLaunchKernelGGL((k_gemv_valu_stream<kStreamR, kStreamC, true>), dim3((unsigned)blocks),
+                       dim3(kThreads), 0, stream, table, njobs, (int)tiles, tiles_per_block);
+  else
+    hipLaunchKernelGGL((k_gemv_valu_stream<kStreamR, kStreamC, false>), dim3((unsigned)blocks),
+                       dim3(kThreads), 0, stream, table, njobs, (int)tiles, tiles_per_block);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemv_grouped(const GemvJob* table, int njobs, int64_t blocks, int m, bool mx,

@@ -33,4 +33,12 @@ hipError_t launch_gemv(const GemvJob& job, int m, bool mx, int route, hipStream_
 hipError_t launch_gemv_grouped(const GemvJob* device_table, int njobs, int64_t blocks, int m,
                                bool mx, int route, hipStream_t stream);
 
+// Streaming grouped kernel (VALU, m = 1, every K <= gemv_stream_max_k()):
+// tiles of gemv_stream_rows() rows, a contiguous run of tiles per workgroup.
+int gemv_stream_max_k();
+int gemv_stream_rows();
+hipError_t gemv_stream_slots(bool mx, int* slots);   // resident workgroups on the device
+hipError_t launch_gemv_stream(const GemvJob* device_table, int njobs, int64_t blocks,
+                              int64_t tiles, int tiles_per_block, bool mx, hipStream_t stream);
+
 }  // namespace fp8w

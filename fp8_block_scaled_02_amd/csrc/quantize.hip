@@ -71,7 +71,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_block_vec(const uint16_t* __
   for (int i = 0; i < 8; ++i) {
     const int row = row0 + 16 * i;
     v[i] = make_uint4(0, 0, 0, 0);
-    if (col_ok && row < n) v[i] = *reinterpret_cast<const uint4*>(w + (size_t)row * k + col);
+    if (col_ok && row < n) v[i] = ld_stream_u4(w, ((size_t)row * k + col) * 2);
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_block_vec(const uint16_t* __
       uint2 out;
       out.x = encode4_div(v[i].x, v[i].y, scale);
       out.y = encode4_div(v[i].z, v[i].w, scale);
-      *reinterpret_cast<uint2*>(codes + (size_t)row * k + col) = out;
+      st_stream_u2(codes, (size_t)row * k + col, out);
     }
   }
 }
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_mx_vec(const uint16_t* __res
   const size_t t = (size_t)blockIdx.x * kThreads + threadIdx.x;
   const bool ok = t < threads_total;
   uint4 v = make_uint4(0, 0, 0, 0);
-  if (ok) v = *reinterpret_cast<const uint4*>(w + 8 * t);
+  if (ok) v = ld_stream_u4(w, 16 * t);
   uint32_t amax = abs_max_pair(v.x, 0);
   amax = abs_max_pair(v.y, amax);
   amax = abs_max_pair(v.z, amax);
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_mx_vec(const uint16_t* __res
   uint2 out;
   out.x = encode4_mul(v.x, v.y, mul);
   out.y = encode4_mul(v.z, v.w, mul);
-  *reinterpret_cast<uint2*>(codes + 8 * t) = out;
+  st_stream_u2(codes, 8 * t, out);
 }
 
 // MX, any shape: one thread per (row, group), 2-byte loads.

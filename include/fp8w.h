@@ -175,12 +175,16 @@ typedef struct fp8w_gemv_desc {
 
 /* What fp8w_grouped_plan_init fills in; pass it to fp8w_gemv_grouped. */
 typedef struct fp8w_grouped_plan {
-  const void* table; /* the caller's device table buffer          */
-  int32_t count;     /* GEMVs in the group                        */
-  int32_t m;         /* activation rows, shared by the group      */
-  int32_t format;    /* fp8w_format                               */
-  int32_t route;     /* fp8w_route resolved for m (VALU or MFMA)  */
-  int64_t blocks;    /* workgroups of one launch                  */
+  const void* table;       /* the caller's device table buffer            */
+  int32_t count;           /* GEMVs in the group                          */
+  int32_t m;               /* activation rows, shared by the group        */
+  int32_t format;          /* fp8w_format                                 */
+  int32_t route;           /* fp8w_route resolved for m (VALU or MFMA)    */
+  int64_t blocks;          /* workgroups of one launch                    */
+  int64_t tiles;           /* row tiles of all GEMVs together             */
+  int32_t tiles_per_block; /* 0: one tile per workgroup; else a contiguous
+                              run of tiles per workgroup (streaming kernel) */
+  int32_t reserved;
 } fp8w_grouped_plan;
 
 /* Bytes of device memory a table for `count` GEMVs needs (0 if count < 1). */

@@ -119,9 +119,15 @@ def test_grouped_argument_errors(F):
     into_table = (F.GemvDesc * 1)(F.GemvDesc(A, B, C, T + 16, 16, 16))
     assert init(into_table, 1, 1, F.FORMAT_BLOCK, 0, T, ctypes.byref(plan)) == F.ERR_OVERLAP
     assert L.fp8w_gemv_grouped(None, None) == F.ERR_NULL
-    bad = F.GroupedPlanC(T, 1, 1, 0, 1, 0)        # zero blocks: not from plan_init
+    bad = F.GroupedPlanC(T, 1, 1, 0, 1, 0, 0, 0, 0)     # zero blocks: not from plan_init
     assert L.fp8w_gemv_grouped(ctypes.byref(bad), None) == F.ERR_SHAPE
-    bad = F.GroupedPlanC(T, 1, 9, 0, 1, 4)        # VALU route with m = 9
+    bad = F.GroupedPlanC(T, 1, 9, 0, 1, 4, 4, 0, 0)     # VALU route with m = 9
+    assert L.fp8w_gemv_grouped(ctypes.byref(bad), None) == F.ERR_SHAPE
+    bad = F.GroupedPlanC(T, 1, 1, 0, 1, 4, 100, 3, 0)   # runs do not cover the tiles
+    assert L.fp8w_gemv_grouped(ctypes.byref(bad), None) == F.ERR_SHAPE
+    bad = F.GroupedPlanC(T, 1, 2, 0, 1, 4, 100, 25, 0)  # streaming kernel is m = 1 only
+    assert L.fp8w_gemv_grouped(ctypes.byref(bad), None) == F.ERR_SHAPE
+    bad = F.GroupedPlanC(T, 1, 2, 0, 1, 4, 5, 0, 0)     # one tile per block: tiles == blocks
     assert L.fp8w_gemv_grouped(ctypes.byref(bad), None) == F.ERR_SHAPE
 
 

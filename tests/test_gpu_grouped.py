@@ -119,3 +119,31 @@ def test_grouped_and_single_calls_replay_in_a_graph(fp8w, oracle_mod):
         _sync()
         for a, b in zip(plan.ys + ys_single, eager_g + eager_s):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"replay {rep}"
+
+
+@pytest.mark.parametrize("fmt", ["block", "mx"])
+@pytest.mark.parametrize("case", ["projection_like", "many_small_jobs"])
+def test_grouped_streaming_kernel_matches_oracle(fp8w, oracle_mod, fmt, case):
+    """m = 1 with every K <= 3072 takes the streaming kernel (runs of tiles
+    per workgroup that cross job boundaries)."""
+    rng = np.random.default_rng(40)
+    if case == "projection_like":
+        shapes = [(300, 1008), (130, 272), (8192, 2560), (257, 2560), (64, 16), (2560, 3072), (17, 3072)]
+    else:
+        shapes = [(int(rng.integers(1, 300)), int(rng.integers(1, 193)) * 16) for _ in range(60)]
+    jobs = []
+    for i, (n, k) in enumerate(shapes):
+        bits = W.gaussian_weight(41, i, n, k, outlier_rows=fmt == "block", heavy_tail=fmt == "mx")
+        c, s = oracle_mod.quantize_block(bits) if fmt == "block" else oracle_mod.quantize_mx(bits)
+        jobs.append((n, k, c, s))
+    xs_h = [W.activation(42, 1, k) for (_, k, _, _) in jobs]
+    plan = fp8w.fp8w_grouped_plan_init([to_dev_bf16(x) for x in xs_h],
+                                       [to_dev(c) for (_, _, c, _) in jobs],
+                                       [to_dev(s) for (_, _, _, s) in jobs], fmt=fmt)
+    assert plan.plan.tiles_per_block > 0 and plan.plan.blocks * plan.plan.tiles_per_block >= plan.plan.tiles
+    ys = fp8w.fp8w_gemv_grouped(plan)
+    _sync()
+    ref = oracle_mod.gemv_block_f64 if fmt == "block" else oracle_mod.gemv_mx_f64
+    for (n, k, c, s), x, y in zip(jobs, xs_h, ys):
+        y_ref, bound = ref(x, c, s)
+        assert_within_bound(bf16_to_f64(y), y_ref, bound, f"stream {fmt} [{n}x{k}]")

@@ -9,8 +9,10 @@ distinct weights exceed the 256 MB Infinity Cache, so every pass streams the
 codes from HBM.  Weights are synthetic N(0, 0.02) bf16, quantized on the GPU
 by fp8w_quantize_block before timing; activations are N(0, 1) bf16.
 
-Timed with HIP events on the launching stream, the calls of a pass captured
-in a HIP graph (the decode path is graph-captured on the pages).  Prints ONE
+A step is one grouped launch (fp8w_gemv_grouped) computing the 96 GEMVs,
+timed with HIP events on the launching stream; the same pass as 96 single
+GEMV launches (captured in a HIP graph, as the pages' decode path is) is
+reported next to it.  Prints ONE
 JSON line; the other workloads (M = 8 / 16, the quantizers, lm_head, the
 dense layer, MXFP8) are reported under "rows".
 
@@ -30,6 +32,27 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM = 8.0e12          # MI355X HBM3E, bytes/s
+
+# HBM bytes per launch of the grouped M=1 streaming GEMV on the projection
+# set, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled by a 2 GiB device
+# copy (read factor 1.9999, write factor 1.0).  Valid only for the kernel
+# sources they were taken with (sha256 of gemv.hip + device.hpp); any change
+# to those sources reports traffic as null until the counters are retaken.
+COUNTED_TRAFFIC = {
+    "sources_sha256": "3a885f44b59b87918e77cad5bbd45996e9e0ec3983ff8a66b45144b8820c16e9",
+    "bytes_per_launch": 1339.1e6,
+}
+
+
+def counted_traffic():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gemv.hip", "device.hpp"):
+        with open(os.path.join(ROOT, "fp8_block_scaled_02_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != COUNTED_TRAFFIC["sources_sha256"]:
+        return None
+    return COUNTED_TRAFFIC["bytes_per_launch"]
 TILE, GROUP = 128, 32
 ALL_ROWS = ("proj", "quant", "lm_head", "dense", "mx", "single")
 
@@ -41,6 +64,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--rows", default=",".join(ALL_ROWS))
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--ms", default="1,8,16", help="M values of the projection-set rows")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="also run one device copy of this many MiB (counter calibration)")
     return p.parse_args()
@@ -241,7 +265,7 @@ def bench_proj(torch, fp8w, lean, timer, W, args, state, log):
     """The projection pass at M = 1, 8, 16: one grouped launch per pass, and
     96 single-GEMV launches per pass (both captured in a HIP graph)."""
     wl, bf, codes, scales = state
-    ms = (1, 8, 16)
+    ms = tuple(int(v) for v in args.ms.split(","))
     xs = activations(torch, W, 2, ms, (2560, 3072))
     rows, head = {}, None
     for m in ms:
@@ -249,11 +273,12 @@ def bench_proj(torch, fp8w, lean, timer, W, args, state, log):
         calls = [(xs[(m, c.shape[1])], c, s, y) for c, s, y in zip(codes, scales, ys)]
         nbytes = sum(gemv_bytes_block(m, c.shape[0], c.shape[1]) for c in codes)
         plan = fp8w.fp8w_grouped_plan_init([x for x, _, _, _ in calls], codes, scales, ys)
-        g = graph_of(torch, lean.grouped(plan))
-        per, total = timer.run(g.replay, args.steps, args.warmup)
+        # one kernel per pass: launched directly (a one-kernel graph replay
+        # adds 8-20 us of launch overhead per replay on ROCm)
+        per, total = timer.run(lean.grouped(plan), args.steps, args.warmup)
         row = {"grouped": dict(summarize(per, len(calls), nbytes), launches_per_pass=1,
-                               ms_per_pass=round(statistics.median(per), 4))}
-        del g
+                               ms_per_pass=round(statistics.median(per), 4),
+                               kernel="streaming" if plan.plan.tiles_per_block > 0 else "one tile per workgroup")}
         g = graph_of(torch, lean.gemv_block(calls))
         per_c, _ = timer.run(g.replay, args.steps, args.warmup)
         row["per_call"] = dict(summarize(per_c, len(calls), nbytes), launches_per_pass=len(calls),
@@ -321,11 +346,10 @@ def bench_dense(torch, fp8w, lean, timer, W, args, log):
         del g
         plan = fp8w.fp8w_grouped_plan_init([c[0] for c in calls], [c[1] for c in calls],
                                            [c[2] for c in calls], [c[3] for c in calls])
-        g = graph_of(torch, lean.grouped(plan))
-        per_g, _ = timer.run(g.replay, args.steps, args.warmup)
+        per_g, _ = timer.run(lean.grouped(plan), args.steps, args.warmup)
         row["grouped"] = summarize(per_g, len(calls), nbytes)
         out[f"m{m}"] = row
-        del g, plan
+        del plan
     log(f"dense layer: {out}")
     return {"dense_layer_h4096_i12288": out}
 
@@ -351,11 +375,10 @@ def bench_mx(torch, fp8w, lean, timer, W, args, log):
             del g
             plan = fp8w.fp8w_grouped_plan_init([c[0] for c in calls], [c[1] for c in calls],
                                                [c[2] for c in calls], [c[3] for c in calls], fmt="mx")
-            g = graph_of(torch, lean.grouped(plan))
-            per_g, _ = timer.run(g.replay, max(10, args.steps // 2), args.warmup)
+            per_g, _ = timer.run(lean.grouped(plan), max(10, args.steps // 2), args.warmup)
             row["grouped"] = summarize(per_g, len(calls), nb)
             out[f"gemv_mx_{key}_m{m}"] = row
-            del g, plan
+            del plan
         del copies
     log(f"mx: {out}")
     return {"mxfp8": out}
@@ -492,10 +515,11 @@ def main():
                    "shapes": "12x[6656x2560] + 36x[8192x2560] + 48x[2560x3072]",
                    "bytes_per_step": headline["bytes"],
                    "execution": "the 96 independent GEMVs of a pass in one grouped launch "
-                                "(fp8w_gemv_grouped), HIP graph replay, HIP events"},
+                                "(fp8w_gemv_grouped) per step, HIP events on the launch stream"},
         "roofline": {"bound": "hbm", "achieved": round(value, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                     "frac": round(value * 1e9 / PEAK_HBM, 4), "traffic": None,
-                     "kernel": "k_gemv_valu<M=1, R=8, C=3, block, grouped>",
+                     "frac": round(value * 1e9 / PEAK_HBM, 4), "traffic": counted_traffic(),
+                     "traffic_unit": "bytes per launch",
+                     "kernel": "k_gemv_valu_stream<R=4, C=3, block> (grouped, m=1)",
                      "avg_launch_us": round(ms_per_step * 1e3, 3),
                      "bytes_per_launch": headline["bytes"]},
         "cpu_baseline": cpu,

@@ -113,28 +113,37 @@ class Timer:
         self.torch.cuda._sleep(int(self.cycles_per_ms * ms))
 
     def run(self, fn, reps, warmup, hold_ms=0.0):
-        """Per-rep ms (event pair around each call of fn) and total ms.
+        """(per-rep ms, total ms).  The total brackets `reps` back-to-back
+        calls of fn with one event pair and nothing between them; a second
+        run puts an event pair around each call for the distribution.
 
         hold_ms > 0 queues a spin kernel first, for sequences whose host-side
         enqueue is slower than their GPU time (un-graphed launches); graph
-        replays are cheap to enqueue and run right after their warmup."""
+        replays and single grouped launches are cheap to enqueue."""
         t = self.torch
-        starts = [t.cuda.Event(enable_timing=True) for _ in range(reps)]
-        ends = [t.cuda.Event(enable_timing=True) for _ in range(reps)]
-        t0, t1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        ev = lambda: t.cuda.Event(enable_timing=True)
+        for _ in range(warmup):
+            fn()
+        t0, t1 = ev(), ev()
         if hold_ms > 0:
             t.cuda.synchronize()
             self.hold(hold_ms)
-        for _ in range(warmup):
-            fn()
         t0.record()
+        for _ in range(reps):
+            fn()
+        t1.record()
+        t.cuda.synchronize()
+        total = t0.elapsed_time(t1)
+        starts = [ev() for _ in range(reps)]
+        ends = [ev() for _ in range(reps)]
+        if hold_ms > 0:
+            self.hold(hold_ms)
         for i in range(reps):
             starts[i].record()
             fn()
             ends[i].record()
-        t1.record()
         t.cuda.synchronize()
-        return [s.elapsed_time(e) for s, e in zip(starts, ends)], t0.elapsed_time(t1)
+        return [s.elapsed_time(e) for s, e in zip(starts, ends)], total
 
 
 def graph_of(torch, fn):
@@ -284,7 +293,7 @@ def bench_proj(torch, fp8w, lean, timer, W, args, state, log):
         row["per_call"] = dict(summarize(per_c, len(calls), nbytes), launches_per_pass=len(calls),
                                ms_per_pass=round(statistics.median(per_c), 4))
         del g
-        row.update({"bytes_per_pass": nbytes, "route": "valu" if m <= 8 else "mfma"})
+        row.update({"bytes_per_pass": nbytes, "route": "valu" if plan.route == fp8w.ROUTE_VALU else "mfma"})
         if m == 1:
             head = {"per": per, "total_ms": total, "bytes": nbytes, "calls": len(calls), "row": row}
         rows[f"m{m}"] = row
@@ -342,7 +351,7 @@ def bench_dense(torch, fp8w, lean, timer, W, args, log):
         nbytes = sum(gemv_bytes_block(m, c.shape[0], c.shape[1]) for (_, c, _, _) in calls)
         g = graph_of(torch, lean.gemv_block(calls))
         per, _ = timer.run(g.replay, args.steps, args.warmup)
-        row = {"per_call": summarize(per, len(calls), nbytes), "route": "valu" if m <= 8 else "mfma"}
+        row = {"per_call": summarize(per, len(calls), nbytes), "route": "valu" if m <= 2 else "mfma"}
         del g
         plan = fp8w.fp8w_grouped_plan_init([c[0] for c in calls], [c[1] for c in calls],
                                            [c[2] for c in calls], [c[3] for c in calls])

@@ -2,9 +2,10 @@
 //
 // y[m][n] = bf16( sum_k x[m][k] * dec(code[n][k]) * scale(n, k) ), fp32
 // accumulation, for 1 <= M <= 32.  The fp8 weight stream dominates the
-// traffic, so every kernel reads each code byte once with 16-byte loads,
-// converts e4m3 -> bf16 in registers (exact: 4 significant bits) and keeps x
-// in LDS.  Two kernel families, split on M as the fused W8A16 GEMM of "feat:
+// traffic, so every kernel reads each code byte once with 16-byte loads and
+// converts e4m3 -> bf16 in registers (exact: 4 significant bits); x (at most
+// 32 rows) is re-read from LDS or from L2.  Two kernel families, split on M
+// as the fused W8A16 GEMM of "feat:
 // add FP8 blockwise weight quantization and FP8(E4M3) KV cache support"
 // (Summary; Notes for Reviewers) splits its SIMT and tensor-core routes:
 //
@@ -15,10 +16,14 @@
 //    x^T padded to 16 or 32 columns.
 //
 // Each call is a few microseconds of HBM traffic, so latency decides the
-// time: every kernel issues a K segment's weight loads first (non-temporal:
-// each code byte is read once), then stages x
-// (and the block-scale row) in LDS while those loads are in flight.  Segments
-// are sized so that the common K (up to a few thousand) is one segment.
+// time: every kernel issues its weight loads first (non-temporal: each code
+// byte is read once).  The VALU kernels and the grouped MFMA kernel then
+// stage a K segment of x (and the block-scale row) in LDS while those loads
+// are in flight; segments are sized so that the common K (up to a few
+// thousand) is one segment.  The single-call MFMA kernel keeps no x in LDS:
+// each wave walks its 128-column blocks with a register pipeline two blocks
+// deep, loading codes, x fragments and the scale of block q+2 before the
+// MFMAs of block q, so no barrier ever waits for a staging pass.
 //
 // A launch covers either one GEMV (the job travels as a kernel argument) or
 // a group of independent GEMVs (a job table in device memory; workgroup b
@@ -572,14 +577,157 @@ __global__ __launch_bounds__(kThreads) void k_gemv_mfma(GemvJob arg, const GemvJ
   }
 }
 
+// ------------------------------------------------------ MFMA, direct x --
+//
+// Single calls.  Same tile, lane and D layouts as above; the 4 waves of a
+// workgroup are 4/KW tiles of 16 rows, KW waves splitting K by 128-column
+// blocks (wave kw takes blocks kw, kw + KW, ...).  Each block's registers --
+// two 16-byte code chunks per lane, the x^T fragments of the same K
+// positions read from global memory (x is small and stays in L2), and the
+// block scale or the chunks' MX scales -- are requested D blocks ahead.
+template <int MT, bool MX>
+struct DirectRegs {
+  uint4 w[2];
+  uint4 xb[MT][2][2];   // [m tile][chunk][first / last 8 K positions]
+  float s[2];           // block: s[0] is the block scale; MX: one per chunk
+};
+
+template <int MT, int KW, int D, bool MX>
+__global__ __launch_bounds__(kThreads) void k_gemv_mfma_direct(GemvJob j, int m_rows) {
+  constexpr int kTiles = kWaves / KW;
+  __shared__ float red[KW > 1 ? kWaves * MT * 4 * kWave : 1];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int kw = wave % KW, tile = wave / KW;
+  const int i = lane & 15, g = lane >> 4;
+  const int row0 = (blockIdx.x * kTiles + tile) * 16;
+  const int row = row0 + i;
+  const bool row_ok = row < j.n;
+  const int nkb = (j.k + kTile - 1) / kTile;
+  const int groups = (j.k + kGroup - 1) / kGroup;
+  const int nq = row0 < j.n ? (nkb - kw + KW - 1) / KW : 0;   // this wave's column blocks
+  const float* __restrict__ srow =
+      MX ? nullptr
+         : static_cast<const float*>(j.scales) + (size_t)(min(row0, j.n - 1) / kTile) * nkb;
+  const uint8_t* __restrict__ e8 = static_cast<const uint8_t*>(j.scales);
+
+  auto issue = [&](int q, DirectRegs<MT, MX>& r) {
+    const int kb = kw + KW * q;
+    const bool live = q < nq;
+    r.s[0] = r.s[1] = 0.0f;
+    if (!MX && live) r.s[0] = ld_global<float>(srow, (size_t)kb * 4);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int kx = kb * kTile + h * 64 + 16 * g;
+      const bool in = live && kx < j.k;
+      r.w[h] = make_uint4(0, 0, 0, 0);
+      if (in && row_ok) {
+        r.w[h] = ld_stream_u4(j.codes, (size_t)row * j.k + kx);
+        if (MX) r.s[h] = mx_scale(ld_global<uint8_t>(e8, (size_t)row * groups + kx / kGroup));
+      }
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const int m = 16 * t + i;
+        r.xb[t][h][0] = r.xb[t][h][1] = make_uint4(0, 0, 0, 0);
+        if (in && m < m_rows) {
+          r.xb[t][h][0] = ld_global_u4(j.x, ((size_t)m * j.k + kx) * 2);
+          r.xb[t][h][1] = ld_global_u4(j.x, ((size_t)m * j.k + kx + 8) * 2);
+        }
+      }
+    }
+  };
+
+  f32x4 acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  DirectRegs<MT, MX> slot[D];
+#pragma unroll
+  for (int s = 0; s < D; ++s) issue(s, slot[s]);
+  for (int q0 = 0; q0 < nq; q0 += D) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      if (q0 + s < nq) {
+        f32x4 part[MT];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) part[t] = MX ? acc[t] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint4 d = slot[s].w[h];
+          bf16x2 a0, a1, a2, a3, b0, b1, b2, b3;
+          if (MX) {
+            const float sc = slot[s].s[h];
+            a0 = cvt_scaled<false>(d.x, sc), a1 = cvt_scaled<true>(d.x, sc);
+            a2 = cvt_scaled<false>(d.y, sc), a3 = cvt_scaled<true>(d.y, sc);
+            b0 = cvt_scaled<false>(d.z, sc), b1 = cvt_scaled<true>(d.z, sc);
+            b2 = cvt_scaled<false>(d.w, sc), b3 = cvt_scaled<true>(d.w, sc);
+          } else {
+            a0 = cvt_lo(d.x), a1 = cvt_hi(d.x), a2 = cvt_lo(d.y), a3 = cvt_hi(d.y);
+            b0 = cvt_lo(d.z), b1 = cvt_hi(d.z), b2 = cvt_lo(d.w), b3 = cvt_hi(d.w);
+          }
+          const bf16x8 A0 = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+          const bf16x8 A1 = {b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
+#pragma unroll
+          for (int t = 0; t < MT; ++t) {
+            part[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                A0, __builtin_bit_cast(bf16x8, slot[s].xb[t][h][0]), part[t], 0, 0, 0);
+            part[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                A1, __builtin_bit_cast(bf16x8, slot[s].xb[t][h][1]), part[t], 0, 0, 0);
+          }
+        }
+        if (MX) {
+#pragma unroll
+          for (int t = 0; t < MT; ++t) acc[t] = part[t];
+        } else {
+          const float bs = slot[s].s[0];
+#pragma unroll
+          for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) acc[t][jj] = __builtin_fmaf(bs, part[t][jj], acc[t][jj]);
+        }
+      }
+      issue(q0 + s + D, slot[s]);
+    }
+  }
+
+  if (KW > 1) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) red[((wave * MT + t) * 4 + jj) * kWave + lane] = acc[t][jj];
+    __syncthreads();
+    if (kw == 0) {
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          float v = acc[t][jj];
+          for (int w2 = 1; w2 < KW; ++w2) v += red[(((wave + w2) * MT + t) * 4 + jj) * kWave + lane];
+          acc[t][jj] = v;
+        }
+    }
+  }
+  if (kw == 0) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const int mcol = 16 * t + i;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int r = row0 + 4 * g + jj;
+        if (r < j.n && mcol < m_rows)
+          st_global<uint16_t>(j.y, ((size_t)mcol * j.n + r) * 2, (uint16_t)f32_to_bf16_rne(acc[t][jj]));
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------ dispatch --
 //
 // One compiled variant per (route, M, single/grouped), any N and K:
 //   VALU single call: R = 1 row per wave (4 rows per workgroup: the most
 //     workgroups for small N); grouped: more rows per wave (fewer, larger
 //     workgroups once many GEMVs share the launch).
-//   MFMA single call: the 4 waves of a 16-row tile split K; grouped: each
-//     wave owns a 16-row tile.
+//   MFMA single call: direct-x kernel, the 4 waves of a 16-row tile split
+//     K; grouped: LDS-staged kernel, each wave owns a 16-row tile.
 
 template <int M, int R, int C, bool MX, bool G>
 hipError_t run_valu(const GemvJob& job, const GemvJob* table, int njobs, int64_t blocks,
@@ -634,8 +782,11 @@ hipError_t dispatch_mfma(int m, const GemvJob& job, const GemvJob* table, int nj
     if (m <= 16) return run_mfma<1, 1, 4, MX, G>(job, table, njobs, blocks, m, s);
     return run_mfma<2, 1, 2, MX, G>(job, table, njobs, blocks, m, s);
   }
-  if (m <= 16) return run_mfma<1, 4, 2, MX, G>(job, table, njobs, blocks, m, s);
-  return run_mfma<2, 4, 1, MX, G>(job, table, njobs, blocks, m, s);
+  if (m <= 16)
+    hipLaunchKernelGGL((k_gemv_mfma_direct<1, 4, 2, MX>), dim3((unsigned)blocks), dim3(kThreads), 0, s, job, m);
+  else
+    hipLaunchKernelGGL((k_gemv_mfma_direct<2, 4, 2, MX>), dim3((unsigned)blocks), dim3(kThreads), 0, s, job, m);
+  return hipGetLastError();
 }
 
 }  // namespace

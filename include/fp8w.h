@@ -69,11 +69,12 @@ typedef enum fp8w_status {
   FP8W_ERR_HIP = 6          /* the HIP runtime rejected the launch              */
 } fp8w_status;
 
-/* GEMV kernel family.  AUTO picks VALU for m <= 8 and MFMA for m >= 9, the
- * split measured for the fused W8A16 GEMM in "feat: add FP8 blockwise weight
- * quantization ..." (Summary; Notes for Reviewers: SIMT for M <= 8,
- * tensor-core mma for 9 <= M <= 32).  VALU serves 1 <= m <= 8 only; MFMA
- * serves 1 <= m <= 32.  Every route meets the same error bound.          */
+/* GEMV kernel family.  The two routes follow the fused W8A16 GEMM of "feat:
+ * add FP8 blockwise weight quantization ..." (Summary; Notes for Reviewers:
+ * SIMT for M <= 8, tensor-core mma for 9 <= M <= 32): VALU serves
+ * 1 <= m <= 8 only; MFMA serves 1 <= m <= 32.  AUTO picks VALU for m <= 2
+ * and MFMA for m >= 3, the crossover measured on MI355X (gfx950 matrix cores
+ * win from 3 activation rows on).  Every route meets the same error bound. */
 typedef enum fp8w_route {
   FP8W_ROUTE_AUTO = 0,
   FP8W_ROUTE_VALU = 1,

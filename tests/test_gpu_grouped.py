@@ -43,7 +43,7 @@ def test_grouped_matches_oracle(fp8w, oracle_mod, fmt, m):
     plan = fp8w.fp8w_grouped_plan_init([to_dev_bf16(x) for x in xs_h],
                                        [to_dev(c) for (_, _, c, _) in jobs],
                                        [to_dev(s) for (_, _, _, s) in jobs], fmt=fmt)
-    assert plan.route == (fp8w.ROUTE_VALU if m <= 8 else fp8w.ROUTE_MFMA)
+    assert plan.route == (fp8w.ROUTE_VALU if m <= 2 else fp8w.ROUTE_MFMA)
     ys = fp8w.fp8w_gemv_grouped(plan)
     _sync()
     ref = oracle_mod.gemv_block_f64 if fmt == "block" else oracle_mod.gemv_mx_f64
@@ -52,19 +52,23 @@ def test_grouped_matches_oracle(fp8w, oracle_mod, fmt, m):
         assert_within_bound(bf16_to_f64(y), y_ref, bound, f"grouped {fmt} m={m} [{n}x{k}]")
 
 
-def test_grouped_mfma_route_at_small_m(fp8w, oracle_mod):
-    jobs = _jobs(oracle_mod, "block", 1)
-    for m in (1, 4, 8):
+@pytest.mark.parametrize("fmt", ["block", "mx"])
+@pytest.mark.parametrize("route,ms", [("mfma", (1, 2)), ("valu", (3, 4, 6, 8))])
+def test_grouped_explicit_route_where_auto_picks_the_other(fp8w, oracle_mod, fmt, route, ms):
+    jobs = _jobs(oracle_mod, fmt, 1)
+    r = {"valu": fp8w.ROUTE_VALU, "mfma": fp8w.ROUTE_MFMA}[route]
+    ref = oracle_mod.gemv_block_f64 if fmt == "block" else oracle_mod.gemv_mx_f64
+    for m in ms:
         xs_h = [W.activation(32, m, k) for (_, k, _, _) in jobs]
         plan = fp8w.fp8w_grouped_plan_init([to_dev_bf16(x) for x in xs_h],
                                            [to_dev(c) for (_, _, c, _) in jobs],
-                                           [to_dev(s) for (_, _, _, s) in jobs],
-                                           route=fp8w.ROUTE_MFMA)
+                                           [to_dev(s) for (_, _, _, s) in jobs], fmt=fmt, route=r)
+        assert plan.route == r
         ys = fp8w.fp8w_gemv_grouped(plan)
         _sync()
         for (n, k, c, s), x, y in zip(jobs, xs_h, ys):
-            y_ref, bound = oracle_mod.gemv_block_f64(x, c, s)
-            assert_within_bound(bf16_to_f64(y), y_ref, bound, f"grouped mfma m={m} [{n}x{k}]")
+            y_ref, bound = ref(x, c, s)
+            assert_within_bound(bf16_to_f64(y), y_ref, bound, f"grouped {route} {fmt} m={m} [{n}x{k}]")
 
 
 def test_grouped_rejects_overlapping_outputs(fp8w, oracle_mod):

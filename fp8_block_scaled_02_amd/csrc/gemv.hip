@@ -10,8 +10,8 @@
 // (Summary; Notes for Reviewers) splits its SIMT and tensor-core routes:
 //
 //  * VALU (M <= 8): v_dot2c_f32_bf16 products; the 64 lanes of a wave walk
-//    one row along K, and the wave's partial sums are folded with DPP row
-//    operations (no LDS round trips).
+//    one row along K, and the wave's partial sums are folded four at a time
+//    with lane-swap and DPP row operations (no LDS round trips).
 //  * MFMA (M <= 32): v_mfma_f32_16x16x32_bf16 on 16-row tiles of W against
 //    x^T padded to 16 or 32 columns.
 //
@@ -90,22 +90,52 @@ __device__ __forceinline__ float dot16(const bf16x2 (&w)[8], uint4 x0, uint4 x1)
   return p;
 }
 
-// Sum over the 64 lanes of a wave with DPP: pairs and quads (quad_perm),
-// 8 and 16 lanes (row half-mirror, row mirror), then the four rows folded
-// with row_bcast15 / row_bcast31 into lane 63, which is broadcast back.
-#define FP8W_DPP_ADD(v, ctrl, row_mask)                                                        \
+// Four wave-wide sums at once: returns, in every lane of 16-lane row q, the
+// sum over the 64 lanes of the q-th argument.  v_permlane32_swap folds the
+// upper half-wave onto the lower one for two values per instruction pair
+// (after it, lanes 0-31 carry a0 + ... and lanes 32-63 carry a2 + ...);
+// v_permlane16_swap then does the same between the 16-lane rows, leaving
+// value q in row q, summed over the four lanes {j, j+16, j+32, j+48}; four DPP
+// steps inside each row (quad_perm [1,0,3,2] and [2,3,0,1], row half mirror,
+// row mirror) finish the sums.  10 instructions for 4 values, against 7 per
+// value for a separate butterfly and readlane.
+#define FP8W_DPP_ADD(v, ctrl)                                                                   \
   (v) += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, (v)), \
-                                                               (ctrl), (row_mask), 0xF, false))
-__device__ __forceinline__ float wave_sum(float v) {
-  FP8W_DPP_ADD(v, 0xB1, 0xF);    // quad_perm [1,0,3,2]
-  FP8W_DPP_ADD(v, 0x4E, 0xF);    // quad_perm [2,3,0,1]
-  FP8W_DPP_ADD(v, 0x141, 0xF);   // row_half_mirror
-  FP8W_DPP_ADD(v, 0x140, 0xF);   // row_mirror
-  FP8W_DPP_ADD(v, 0x142, 0xA);   // row_bcast15 into rows 1 and 3
-  FP8W_DPP_ADD(v, 0x143, 0xC);   // row_bcast31 into rows 2 and 3
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+                                                               (ctrl), 0xF, 0xF, false))
+__device__ __forceinline__ float fold_halves(float a, float b, bool rows16) {
+  const auto r = rows16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false)
+                        : __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float wave_sum4(float a0, float a1, float a2, float a3) {
+  const float t02 = fold_halves(a0, a2, false);   // lanes 0-31: a0, lanes 32-63: a2
+  const float t13 = fold_halves(a1, a3, false);   // lanes 0-31: a1, lanes 32-63: a3
+  float v = fold_halves(t02, t13, true);          // row q: a_q
+  FP8W_DPP_ADD(v, 0xB1);    // quad_perm [1,0,3,2]
+  FP8W_DPP_ADD(v, 0x4E);    // quad_perm [2,3,0,1]
+  FP8W_DPP_ADD(v, 0x141);   // row_half_mirror
+  FP8W_DPP_ADD(v, 0x140);   // row_mirror
+  return v;
 }
 #undef FP8W_DPP_ADD
+
+// Wave sums of V values v[0..V) (any V): value f ends in every lane of row
+// f % 4 of the returned group f / 4.
+template <int V>
+struct WaveSums {
+  static constexpr int kGroups = (V + 3) / 4;
+  float g[kGroups];
+  __device__ __forceinline__ explicit WaveSums(const float (&v)[V]) {
+#pragma unroll
+    for (int q = 0; q < kGroups; ++q) {
+      const float a0 = v[4 * q];
+      const float a1 = 4 * q + 1 < V ? v[(4 * q + 1) % V] : 0.0f;
+      const float a2 = 4 * q + 2 < V ? v[(4 * q + 2) % V] : 0.0f;
+      const float a3 = 4 * q + 3 < V ? v[(4 * q + 3) % V] : 0.0f;
+      g[q] = wave_sum4(a0, a1, a2, a3);
+    }
+  }
+};
 
 // The job of this workgroup and the index of its tile within the job.
 template <bool GROUPED>
@@ -251,13 +281,19 @@ __global__ __launch_bounds__(kThreads) void k_gemv_valu(GemvJob arg, const GemvJ
     }
   }
 
+  float flat[R * M];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int row = row0 + r;
+  for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const float v = wave_sum(acc[r][m]);
-      if (lane == 0 && row < j.n) st_global<uint16_t>(j.y, ((size_t)m * j.n + row) * 2, (uint16_t)f32_to_bf16_rne(v));
+    for (int m = 0; m < M; ++m) flat[r * M + m] = acc[r][m];
+  const WaveSums<R * M> sums(flat);
+  if ((lane & 15) == 0) {
+#pragma unroll
+    for (int q = 0; q < WaveSums<R * M>::kGroups; ++q) {
+      const int f = 4 * q + (lane >> 4);   // value index r * M + m held by this row
+      const int r = f / M, m = f % M;
+      if (f < R * M && row0 + r < j.n)
+        st_global<uint16_t>(j.y, ((size_t)m * j.n + row0 + r) * 2, (uint16_t)f32_to_bf16_rne(sums.g[q]));
     }
   }
 }
@@ -394,11 +430,14 @@ __global__ __launch_bounds__(kThreads) void k_gemv_valu_stream(const GemvJob* __
         }
       }
     }
+    const WaveSums<R> sums(acc);
+    if ((lane & 15) == 0) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float v = wave_sum(acc[r]);
-      if (lane == 0 && row0 + r < j.n)
-        st_global<uint16_t>(j.y, (size_t)(row0 + r) * 2, (uint16_t)f32_to_bf16_rne(v));
+      for (int q = 0; q < WaveSums<R>::kGroups; ++q) {
+        const int r = 4 * q + (lane >> 4);
+        if (r < R && row0 + r < j.n)
+          st_global<uint16_t>(j.y, (size_t)(row0 + r) * 2, (uint16_t)f32_to_bf16_rne(sums.g[q]));
+      }
     }
     if (!more) break;
     if (jn_next != jn) {   // restage x for the next job

@@ -21,10 +21,11 @@ namespace {
 
 constexpr int64_t kMaxDim = 0x7FFFFFFF;   // kernels index rows and columns with int
 constexpr int kValuMaxM = 8;
-// AUTO route: VALU up to this m, MFMA above.  Measured on MI355X over the
-// 96-GEMV projection set: from m = 3 on, the MFMA kernels are faster both as
-// single calls and grouped.
+// AUTO route: VALU up to this m, MFMA above, measured on MI355X over the
+// 96-GEMV projection set.  Single calls: VALU is faster at m <= 2.  Grouped:
+// the streaming MFMA kernel is faster from m = 2 on (6.4 against 5.5 TB/s).
 constexpr int kAutoValuMaxM = 2;
+constexpr int kAutoValuMaxMGrouped = 1;
 
 bool aligned(const void* p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
 
@@ -73,10 +74,10 @@ fp8w_status check_gemv(const uint16_t* x, int64_t m, const uint8_t* codes, const
   return FP8W_OK;
 }
 
-int resolve_route(fp8w_route route, int64_t m) {
+int resolve_route(fp8w_route route, int64_t m, bool grouped) {
   if (route == FP8W_ROUTE_VALU) return 1;
   if (route == FP8W_ROUTE_MFMA) return 2;
-  return m <= kAutoValuMaxM ? 1 : 2;
+  return m <= (grouped ? kAutoValuMaxMGrouped : kAutoValuMaxM) ? 1 : 2;
 }
 
 }  // namespace
@@ -112,7 +113,7 @@ FP8W_API fp8w_status fp8w_gemv_block_route(const uint16_t* x, int64_t m, const u
       check_gemv(x, m, codes, scales, (uint64_t)block_count(n, k) * 4, n, k, y, route, true);
   if (st != FP8W_OK) return st;
   const fp8w::GemvJob job{x, codes, scales, y, (int32_t)n, (int32_t)k, 0, 0};
-  return from_hip(fp8w::launch_gemv(job, (int)m, false, resolve_route(route, m),
+  return from_hip(fp8w::launch_gemv(job, (int)m, false, resolve_route(route, m, false),
                                     static_cast<hipStream_t>(stream)));
 }
 
@@ -123,7 +124,7 @@ FP8W_API fp8w_status fp8w_gemv_mx_route(const uint16_t* x, int64_t m, const uint
       check_gemv(x, m, codes, e8m0, (uint64_t)mx_count(n, k), n, k, y, route, false);
   if (st != FP8W_OK) return st;
   const fp8w::GemvJob job{x, codes, e8m0, y, (int32_t)n, (int32_t)k, 0, 0};
-  return from_hip(fp8w::launch_gemv(job, (int)m, true, resolve_route(route, m),
+  return from_hip(fp8w::launch_gemv(job, (int)m, true, resolve_route(route, m, false),
                                     static_cast<hipStream_t>(stream)));
 }
 
@@ -170,14 +171,14 @@ FP8W_API fp8w_status fp8w_grouped_plan_init(const fp8w_gemv_desc* descs, int64_t
   ins.push_back({device_table, table_bytes});
   if (any_overlap(outs.data(), (int)outs.size(), ins.data(), (int)ins.size()))
     return FP8W_ERR_OVERLAP;
-  const int r = resolve_route(route, m);
+  const int r = resolve_route(route, m, true);
   int64_t max_k = 0;
   for (int64_t i = 0; i < count; ++i) max_k = descs[i].k > max_k ? descs[i].k : max_k;
-  // m = 1 on the VALU route with every K in one segment: the streaming
-  // kernel (contiguous runs of tiles per workgroup); otherwise one tile per
-  // workgroup.
-  const bool stream = r == 1 && m == 1 && max_k <= fp8w::gemv_stream_max_k();
-  const int rows = stream ? fp8w::gemv_stream_rows() : fp8w::gemv_rows_per_block(r, (int)m, true);
+  // Kernels: VALU at m = 1 with every K in one segment streams (contiguous
+  // runs of tiles per workgroup); other VALU plans take one tile per
+  // workgroup; MFMA plans always stream, x staged by K segments.
+  const bool valu_stream = r == 1 && m == 1 && max_k <= fp8w::gemv_stream_max_k();
+  const int rows = valu_stream ? fp8w::gemv_stream_rows() : fp8w::gemv_rows_per_block(r, (int)m, true);
   std::vector<fp8w::GemvJob> table((size_t)count);
   int64_t tiles = 0;
   for (int64_t i = 0; i < count; ++i) {
@@ -188,15 +189,23 @@ FP8W_API fp8w_status fp8w_grouped_plan_init(const fp8w_gemv_desc* descs, int64_t
     if (tiles > kMaxDim) return FP8W_ERR_SHAPE;
   }
   int64_t blocks = tiles;
-  int32_t per_block = 0;
-  if (stream) {
+  int32_t per_block = 0, seg_cols = 0;
+  if (valu_stream || r == 2) {
     int slots = 0;
-    if (fp8w::gemv_stream_slots(!block, &slots) != hipSuccess) return FP8W_ERR_HIP;
-    // about sixteen workgroups per resident slot (runs of ~3 tiles on the
-    // 48-layer projection set): the hardware dispatcher then balances the
-    // runs over the CUs, where long runs left a tail of late workgroups
-    // (measured on MI355X: 41-tile runs 6.1 TB/s, 3-tile runs 6.9 TB/s).
-    const int64_t want = (int64_t)16 * slots;
+    int64_t want = 0;
+    if (valu_stream) {
+      if (fp8w::gemv_stream_slots(!block, &slots) != hipSuccess) return FP8W_ERR_HIP;
+      // about sixteen workgroups per resident slot (runs of ~3 tiles on the
+      // 48-layer projection set): the hardware dispatcher then balances the
+      // runs over the CUs, where long runs left a tail of late workgroups
+      // (measured on MI355X: 41-tile runs 6.1 TB/s, 3-tile runs 6.9 TB/s).
+      want = (int64_t)16 * slots;
+    } else {
+      seg_cols = fp8w::gemv_mfma_stream_seg_cols((int)m, max_k);
+      if (fp8w::gemv_mfma_stream_slots((int)m, !block, seg_cols, &slots) != hipSuccess)
+        return FP8W_ERR_HIP;
+      want = (int64_t)8 * slots;
+    }
     per_block = (int32_t)((tiles + want - 1) / want);
     blocks = (tiles + per_block - 1) / per_block;
   }
@@ -204,7 +213,7 @@ FP8W_API fp8w_status fp8w_grouped_plan_init(const fp8w_gemv_desc* descs, int64_t
     return FP8W_ERR_HIP;
   *plan = fp8w_grouped_plan{device_table, (int32_t)count, (int32_t)m, (int32_t)format,
                             (int32_t)(r == 1 ? FP8W_ROUTE_VALU : FP8W_ROUTE_MFMA), blocks, tiles,
-                            per_block, 0};
+                            per_block, seg_cols};
   return FP8W_OK;
 }
 
@@ -220,16 +229,24 @@ FP8W_API fp8w_status fp8w_gemv_grouped(const fp8w_grouped_plan* plan, void* stre
   const bool mx = plan->format == FP8W_FORMAT_MX;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const fp8w::GemvJob* table = static_cast<const fp8w::GemvJob*>(plan->table);
-  if (plan->tiles_per_block > 0) {
-    if (plan->route != FP8W_ROUTE_VALU || plan->m != 1 ||
-        plan->blocks * (int64_t)plan->tiles_per_block < plan->tiles)
+  if (plan->tiles_per_block > 0 && plan->blocks * (int64_t)plan->tiles_per_block < plan->tiles)
+    return FP8W_ERR_SHAPE;
+  if (plan->route == FP8W_ROUTE_MFMA) {
+    const int seg = plan->seg_cols;
+    if (plan->tiles_per_block < 1 || seg < 256 || seg % 256 != 0 ||
+        fp8w::gemv_mfma_stream_lds(plan->m, seg) > fp8w::gemv_mfma_stream_lds_limit())
       return FP8W_ERR_SHAPE;
+    return from_hip(fp8w::launch_gemv_mfma_stream(table, plan->count, plan->blocks, plan->tiles,
+                                                  plan->tiles_per_block, plan->m, seg, mx, s));
+  }
+  if (plan->seg_cols != 0) return FP8W_ERR_SHAPE;
+  if (plan->tiles_per_block > 0) {
+    if (plan->m != 1) return FP8W_ERR_SHAPE;
     return from_hip(fp8w::launch_gemv_stream(table, plan->count, plan->blocks, plan->tiles,
                                              plan->tiles_per_block, mx, s));
   }
   if (plan->blocks != plan->tiles) return FP8W_ERR_SHAPE;
-  return from_hip(fp8w::launch_gemv_grouped(table, plan->count, plan->blocks, plan->m, mx,
-                                            plan->route == FP8W_ROUTE_VALU ? 1 : 2, s));
+  return from_hip(fp8w::launch_gemv_grouped(table, plan->count, plan->blocks, plan->m, mx, s));
 }
 
 // ------------------------------------------------------------- helpers --

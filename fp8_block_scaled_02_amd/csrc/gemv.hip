@@ -455,307 +455,364 @@ __global__ __launch_bounds__(kThreads) void k_gemv_valu_stream(const GemvJob* __
 
 // ------------------------------------------------------------------ MFMA --
 //
-// Workgroup = 4 waves on 4/KW tiles of 16 rows; KW waves split K by 128-
-// column blocks.  Lane l holds row i = l%16 of the tile and K-quarter
-// g = l/16: per 64-column chunk it loads codes [16g, 16g+16), whose first 8
-// feed one MFMA and last 8 a second one; the B operand (x^T) uses the same
-// K positions, so the two MFMAs sum exactly the chunk.  The D layout of the
-// 16x16 tile is D[4*(l/16) + j][l%16], j = 0..3.  A K segment holds CKB
-// column blocks per wave (KW*CKB*128 columns).
-template <int MT, int KW, int CKB>
-struct MfmaShape {
-  static constexpr int kTiles = kWaves / KW;
-  static constexpr int kRows = 16 * kTiles;
-  static constexpr int kMPad = 16 * MT;
-  static constexpr int kSeg = KW * CKB * kTile;
-  static constexpr int kLd = kSeg + 8;   // +16 B per row spreads B-operand reads over the banks
-  static constexpr int kLdsX = kMPad * kLd * 2;
-  static constexpr int kLdsRed = KW > 1 ? kWaves * MT * 4 * kWave * 4 : 0;
-  static constexpr int kLdsBytes = kLdsX > kLdsRed ? kLdsX : kLdsRed;
-  static_assert(kTile % kRows == 0 || kRows % kTile == 0, "tiles align with 128-row blocks");
-  static_assert(kLdsBytes <= 64 * 1024, "LDS budget");
+// bf16 v_mfma_f32_16x16x32_bf16 on 16-row tiles of W.  Lane l holds A row
+// i = l%16 and K-quarter g = l/16; the B operand (x^T) takes the same K
+// positions, and D[4*(l/16) + j][l%16] (j = 0..3) is y^T of the tile.
+//
+// Codes reach the A layout through a panel: a wave loads 16 rows x 256
+// bytes of its tile with four 16-byte loads per lane, each covering 4 rows x
+// 256 contiguous bytes (lane l: row 4q + l/16, bytes 16*(l%16)), writes the
+// panel to its own 4 KB of LDS and reads it back as A operands.  The A layout
+// loaded straight from memory would read 64 bytes from each of 16 rows per
+// instruction, which caps a pure read of the weight stream at about 5 TB/s
+// on MI355X against 6.9 TB/s for 256-byte row pieces.  Only the owning wave
+// touches its panel buffer, so no barrier is needed: one wave's LDS
+// operations complete in order.  The buffer is XOR-swizzled in 16-byte units
+// (unit c of panel row r at r*256 + 16*(c ^ r)), which keeps both the writes
+// and the A reads free of bank conflicts without padding.
+constexpr int kPanelCols = 256;                 // columns of a panel (two 128-column blocks)
+constexpr int kPanelBytes = 16 * kPanelCols;    // LDS bytes of one wave's panel buffer
+
+template <bool MX>
+struct Panel {
+  uint4 v[4];                // lane l: row 4q + l/16 of the tile, bytes 16*(l%16)
+  float s[MX ? 4 : 2];       // block: per 128-column block; MX: per (block, chunk) of the A layout
 };
 
-// Codes (and MX scale factors) of the wave's column blocks kb = kw + KW*q of
-// the K segment starting at seg0.
-template <int KW, int CKB, bool MX>
-__device__ __forceinline__ void mfma_load(const GemvJob& j, int row, bool row_ok, int seg0, int kw,
-                                          int groups, uint4 (&wv)[CKB][2], float (&ws)[CKB][2]) {
-  constexpr int kSeg = KW * CKB * kTile;
-  const int g = (threadIdx.x & (kWave - 1)) >> 4;
-  const int len = min(kSeg, j.k - seg0);
-  const uint8_t* __restrict__ e8 = static_cast<const uint8_t*>(j.scales);
+// Request panel p (columns [256p, 256p + 256)) of the 16-row tile at row0,
+// with its scales.  Rows >= n and columns >= k load zeros.
+template <bool MX>
+__device__ __forceinline__ void panel_issue(const GemvJob& j, int row0, int p, bool live, int nkb,
+                                            int groups, Panel<MX>& r) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int col = p * kPanelCols + 16 * (lane & 15);
 #pragma unroll
-  for (int q = 0; q < CKB; ++q) {
+  for (int q = 0; q < 4; ++q) {
+    const int row = row0 + 4 * q + (lane >> 4);
+    r.v[q] = make_uint4(0, 0, 0, 0);
+    if (live && row < j.n && col < j.k) r.v[q] = ld_stream_u4(j.codes, (size_t)row * j.k + col);
+  }
+  if (MX) {
+    const int row = row0 + (lane & 15);
+    const uint8_t* __restrict__ e8 = static_cast<const uint8_t*>(j.scales);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int koff = (kw + KW * q) * kTile + h * 64 + 16 * g;
-      wv[q][h] = make_uint4(0, 0, 0, 0);
-      ws[q][h] = 0.0f;
-      if (row_ok && koff < len) {
-        wv[q][h] = ld_stream_u4(j.codes, (size_t)row * j.k + seg0 + koff);
-        if (MX) ws[q][h] = mx_scale(ld_global<uint8_t>(e8, (size_t)row * groups + (seg0 + koff) / kGroup));
+    for (int c = 0; c < 4; ++c) {
+      const int kx = p * kPanelCols + 64 * c + 16 * (lane >> 4);   // block c/2, chunk c%2
+      r.s[c] = 0.0f;
+      if (live && row < j.n && kx < j.k)
+        r.s[c] = mx_scale(ld_global<uint8_t>(e8, (size_t)row * groups + kx / kGroup));
+    }
+  } else {
+    r.s[0] = r.s[1] = 0.0f;
+    if (live && row0 < j.n) {
+      const float* __restrict__ srow = static_cast<const float*>(j.scales) + (size_t)(row0 / kTile) * nkb;
+      r.s[0] = ld_global<float>(srow, (size_t)(2 * p) * 4);
+      if (2 * p + 1 < nkb) r.s[1] = ld_global<float>(srow, (size_t)(2 * p + 1) * 4);
+    }
+  }
+}
+
+// Panel registers -> LDS -> A operands: a[b][c] = row l%16, bytes
+// 128b + 64c + 16*(l/16) of the panel.
+__device__ __forceinline__ void panel_to_a(const uint4 (&v)[4], unsigned char* buf, uint4 (&a)[2][2]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int i = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = 4 * q + g;
+    *reinterpret_cast<uint4*>(buf + r * kPanelCols + 16 * (i ^ r)) = v[q];
+  }
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      a[b][c] = *reinterpret_cast<const uint4*>(buf + i * kPanelCols + 16 * ((8 * b + 4 * c + g) ^ i));
+}
+
+// 16 e4m3 codes -> the two bf16x8 A operands of one 64-column chunk (first
+// and last 8 K positions of each lane's 16), scaled by s for MX.
+template <bool MX>
+__device__ __forceinline__ void a_operands(uint4 d, float s, bf16x8& A0, bf16x8& A1) {
+  bf16x2 a0, a1, a2, a3, b0, b1, b2, b3;
+  if (MX) {
+    a0 = cvt_scaled<false>(d.x, s), a1 = cvt_scaled<true>(d.x, s);
+    a2 = cvt_scaled<false>(d.y, s), a3 = cvt_scaled<true>(d.y, s);
+    b0 = cvt_scaled<false>(d.z, s), b1 = cvt_scaled<true>(d.z, s);
+    b2 = cvt_scaled<false>(d.w, s), b3 = cvt_scaled<true>(d.w, s);
+  } else {
+    a0 = cvt_lo(d.x), a1 = cvt_hi(d.x), a2 = cvt_lo(d.y), a3 = cvt_hi(d.y);
+    b0 = cvt_lo(d.z), b1 = cvt_hi(d.z), b2 = cvt_lo(d.w), b3 = cvt_hi(d.w);
+  }
+  A0 = bf16x8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+  A1 = bf16x8{b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
+}
+
+// acc += the panel's products.  get_b(t, b, c, B0, B1) supplies the x^T
+// operands of m-tile t for block b, chunk c.  Block scales multiply each
+// 128-column block's partial sum; MX scales are already in the A operands.
+template <int MT, bool MX, typename GetB>
+__device__ __forceinline__ void panel_mfma(const uint4 (&a)[2][2], const float* s, GetB get_b,
+                                           f32x4 (&acc)[MT]) {
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    f32x4 part[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) part[t] = MX ? acc[t] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      bf16x8 A0, A1;
+      a_operands<MX>(a[b][c], MX ? s[2 * b + c] : 0.0f, A0, A1);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        uint4 B0, B1;
+        get_b(t, b, c, B0, B1);
+        part[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, __builtin_bit_cast(bf16x8, B0), part[t], 0, 0, 0);
+        part[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, __builtin_bit_cast(bf16x8, B1), part[t], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      if (MX) {
+        acc[t] = part[t];
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) acc[t][jj] = __builtin_fmaf(s[b], part[t][jj], acc[t][jj]);
       }
     }
   }
 }
 
-template <int MT, int KW, int CKB, bool MX, bool GROUPED>
-__global__ __launch_bounds__(kThreads) void k_gemv_mfma(GemvJob arg, const GemvJob* __restrict__ jobs,
-                                                        int njobs, int m_rows) {
-  using S = MfmaShape<MT, KW, CKB>;
-  __shared__ __align__(16) unsigned char smem[S::kLdsBytes];
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
-
-  GemvJob j;
-  int tile_group;
-  find_job<GROUPED>(arg, jobs, njobs, j, tile_group);
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int kw = wave % KW, tile = wave / KW;
+// y^T of a 16-row tile from the D layout; columns (activation rows) >= m_rows
+// and rows >= n are not written.
+template <int MT>
+__device__ __forceinline__ void store_tile(const GemvJob& j, int row0, int m_rows, const f32x4 (&acc)[MT]) {
+  const int lane = threadIdx.x & (kWave - 1);
   const int i = lane & 15, g = lane >> 4;
-  const int row0 = (tile_group * S::kTiles + tile) * 16;
-  const int row = row0 + i;
-  const bool row_ok = row < j.n;
-  const bool tile_live = row0 < j.n;   // a tile past the last row only joins the barriers
-  const int tiles_k = (j.k + kTile - 1) / kTile;
-  const int groups = (j.k + kGroup - 1) / kGroup;
-  const float* __restrict__ srow =
-      MX ? nullptr
-         : static_cast<const float*>(j.scales) + (size_t)(min(row0, j.n - 1) / kTile) * tiles_k;
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int mcol = 16 * t + i;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int r = row0 + 4 * g + jj;
+      if (r < j.n && mcol < m_rows)
+        st_global<uint16_t>(j.y, ((size_t)mcol * j.n + r) * 2, (uint16_t)f32_to_bf16_rne(acc[t][jj]));
+    }
+  }
+}
+
+// ------------------------------------------------------- MFMA streaming --
+//
+// Grouped launches.  A tile is 16*NW rows, one 16-row MFMA tile per wave;
+// each workgroup owns a contiguous run of tiles across job boundaries (as the
+// VALU streaming kernel) and walks them panel by panel, the panel D ahead
+// already requested.  x is staged in LDS by K segments of seg_cols columns
+// (a multiple of 256, sized on the host so that two workgroups fit on a CU):
+// restaged when the run enters a new job, and at every segment of a tile
+// when K spans more than one segment.
+template <int MT, int NW, int D, bool MX>
+__global__ __launch_bounds__(NW * kWave) void k_gemv_mfma_stream(const GemvJob* __restrict__ jobs,
+                                                                 int njobs, int total_tiles,
+                                                                 int tiles_per_block, int m_rows,
+                                                                 int seg_cols) {
+  constexpr int kRows = 16 * NW;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int t_begin = blockIdx.x * tiles_per_block;
+  const int t_end = min(total_tiles, t_begin + tiles_per_block);
+  if (t_begin >= t_end) return;   // whole workgroup: no barrier is skipped by part of it
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int i = lane & 15, g = lane >> 4;
+  unsigned char* pbuf = smem + wave * kPanelBytes;
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem + NW * kPanelBytes);
+  const int ldx = seg_cols + 8;   // +16 B per row spreads the B reads over the banks
+  const int seg_panels = seg_cols / kPanelCols;
+
+  int jn = 0;
+  {
+    int lo = 0, hi = njobs - 1;   // last job whose first tile is <= t_begin
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (ld_global<int32_t>(jobs, (size_t)mid * sizeof(GemvJob) + offsetof(GemvJob, item0)) <= t_begin)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    jn = lo;
+  }
+  // compute cursor: tile ct, panel cp of job cj
+  GemvJob cj;
+  load_job_row(jobs, jn, cj);
+  int c_bound = next_item0(jobs, jn, njobs);
+  int c_np = (cj.k + kPanelCols - 1) / kPanelCols;
+  int ct = t_begin, cp = 0;
+  // issue cursor: tile it, panel ip of job ij, D panels ahead
+  GemvJob ij = cj;
+  int ijn = jn, i_bound = c_bound, i_np = c_np, it = t_begin, ip = 0;
+
+  auto issue = [&](Panel<MX>& r) {
+    const bool live = it < t_end;
+    panel_issue<MX>(ij, (it - ij.item0) * kRows + 16 * wave, ip, live, (ij.k + kTile - 1) / kTile,
+                    (ij.k + kGroup - 1) / kGroup, r);
+    if (!live) return;
+    if (++ip == i_np) {
+      ip = 0;
+      if (++it < t_end && it >= i_bound) {
+        load_job_row(jobs, ++ijn, ij);
+        i_bound = next_item0(jobs, ijn, njobs);
+        i_np = (ij.k + kPanelCols - 1) / kPanelCols;
+      }
+    }
+  };
+  // x[:, seg0 : seg0 + seg_cols) of job j into LDS (columns < k only: the B
+  // reads never look past k)
+  auto stage = [&](const GemvJob& j, int seg0) {
+    const int units = min(seg_cols, j.k - seg0) / 8;
+    for (int u = threadIdx.x; u < m_rows * units; u += NW * kWave) {
+      const int r = u / units, c = (u - r * units) * 8;
+      *reinterpret_cast<uint4*>(xs + r * ldx + c) = ld_global_u4(j.x, ((size_t)r * j.k + seg0 + c) * 2);
+    }
+  };
+
+  Panel<MX> slot[D];
+#pragma unroll
+  for (int s = 0; s < D; ++s) issue(slot[s]);
+  stage(cj, 0);
+  __syncthreads();
 
   f32x4 acc[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-  for (int seg0 = 0; seg0 < j.k; seg0 += S::kSeg) {
-    const int len = min(S::kSeg, j.k - seg0);
-    const int nkb = (len + kTile - 1) / kTile;
-    uint4 cw[CKB][2];
-    float cs[CKB][2];
-    mfma_load<KW, CKB, MX>(j, row, row_ok, seg0, kw, groups, cw, cs);
-    if (seg0 > 0) __syncthreads();
-    stage_x(j.x, m_rows, S::kMPad, j.k, seg0, len, nkb * kTile, xs, S::kLd);
-    __syncthreads();
-
+  bool done = false;
+  while (!done) {
 #pragma unroll
-    for (int q = 0; q < CKB; ++q) {
-      const int kb = kw + KW * q;
-      if (!tile_live || kb >= nkb) break;
-      f32x4 part[MT];
+    for (int s = 0; s < D; ++s) {
+      if (done) break;
+      uint4 a[2][2];
+      panel_to_a(slot[s].v, pbuf, a);
+      float sc[MX ? 4 : 2];
 #pragma unroll
-      for (int t = 0; t < MT; ++t) part[t] = MX ? acc[t] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint4 d = cw[q][h];
-        const float s = cs[q][h];
-        bf16x2 a0, a1, a2, a3, b0, b1, b2, b3;
-        if (MX) {
-          a0 = cvt_scaled<false>(d.x, s), a1 = cvt_scaled<true>(d.x, s);
-          a2 = cvt_scaled<false>(d.y, s), a3 = cvt_scaled<true>(d.y, s);
-          b0 = cvt_scaled<false>(d.z, s), b1 = cvt_scaled<true>(d.z, s);
-          b2 = cvt_scaled<false>(d.w, s), b3 = cvt_scaled<true>(d.w, s);
-        } else {
-          a0 = cvt_lo(d.x), a1 = cvt_hi(d.x), a2 = cvt_lo(d.y), a3 = cvt_hi(d.y);
-          b0 = cvt_lo(d.z), b1 = cvt_hi(d.z), b2 = cvt_lo(d.w), b3 = cvt_hi(d.w);
+      for (int c = 0; c < (MX ? 4 : 2); ++c) sc[c] = slot[s].s[c];
+      issue(slot[s]);
+      const int kseg = (cp % seg_panels) * kPanelCols;   // panel start within the staged segment
+      const int kp = cp * kPanelCols;
+      panel_mfma<MT, MX>(a, sc, [&](int t, int b, int c, uint4& B0, uint4& B1) {
+        const int m = 16 * t + i;
+        const int kx = 128 * b + 64 * c + 16 * g;
+        B0 = B1 = make_uint4(0, 0, 0, 0);
+        if (m < m_rows && kp + kx < cj.k) {
+          B0 = *reinterpret_cast<const uint4*>(xs + m * ldx + kseg + kx);
+          B1 = *reinterpret_cast<const uint4*>(xs + m * ldx + kseg + kx + 8);
         }
-        const bf16x8 A0 = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
-        const bf16x8 A1 = {b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
-        const int kx = kb * kTile + h * 64 + 16 * g;
+      }, acc);
+      if (++cp == c_np) {   // tile done
+        store_tile<MT>(cj, (ct - cj.item0) * kRows + 16 * wave, m_rows, acc);
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-          const uint16_t* xr = xs + (16 * t + i) * S::kLd + kx;
-          const bf16x8 B0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(xr));
-          const bf16x8 B1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(xr + 8));
-          part[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B0, part[t], 0, 0, 0);
-          part[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B1, part[t], 0, 0, 0);
+        for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        cp = 0;
+        if (++ct >= t_end) {
+          done = true;
+        } else if (ct >= c_bound) {   // the run enters the next job
+          load_job_row(jobs, ++jn, cj);
+          c_bound = next_item0(jobs, jn, njobs);
+          c_np = (cj.k + kPanelCols - 1) / kPanelCols;
+          __syncthreads();
+          stage(cj, 0);
+          __syncthreads();
+        } else if (c_np > seg_panels) {   // next tile of a multi-segment job
+          __syncthreads();
+          stage(cj, 0);
+          __syncthreads();
         }
-      }
-      if (MX) {
-#pragma unroll
-        for (int t = 0; t < MT; ++t) acc[t] = part[t];
-      } else {
-        const float bs = ld_global<float>(srow, (size_t)((seg0 + kb * kTile) / kTile) * 4);
-#pragma unroll
-        for (int t = 0; t < MT; ++t)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) acc[t][jj] = __builtin_fmaf(bs, part[t][jj], acc[t][jj]);
-      }
-    }
-  }
-
-  if (KW > 1) {
-    __syncthreads();   // the x staging area is reused for the partial sums
-    float* red = reinterpret_cast<float*>(smem);
-#pragma unroll
-    for (int t = 0; t < MT; ++t)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) red[((wave * MT + t) * 4 + jj) * kWave + lane] = acc[t][jj];
-    __syncthreads();
-    if (kw == 0) {
-#pragma unroll
-      for (int t = 0; t < MT; ++t)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          float s = acc[t][jj];
-          for (int w2 = 1; w2 < KW; ++w2) s += red[(((wave + w2) * MT + t) * 4 + jj) * kWave + lane];
-          acc[t][jj] = s;
-        }
-    }
-  }
-  if (kw == 0) {
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const int mcol = 16 * t + i;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int r = row0 + 4 * g + jj;
-        if (r < j.n && mcol < m_rows)
-          st_global<uint16_t>(j.y, ((size_t)mcol * j.n + r) * 2, (uint16_t)f32_to_bf16_rne(acc[t][jj]));
+      } else if (cp % seg_panels == 0) {   // next segment of this tile
+        __syncthreads();
+        stage(cj, cp * kPanelCols);
+        __syncthreads();
       }
     }
   }
 }
 
-// ------------------------------------------------------ MFMA, direct x --
+// ----------------------------------------------------- MFMA, single call --
 //
-// Single calls.  Same tile, lane and D layouts as above; the 4 waves of a
-// workgroup are 4/KW tiles of 16 rows, KW waves splitting K by 128-column
-// blocks (wave kw takes blocks kw, kw + KW, ...).  Each block's registers --
-// two 16-byte code chunks per lane, the x^T fragments of the same K
-// positions read from global memory (x is small and stays in L2), and the
-// block scale or the chunks' MX scales -- are requested D blocks ahead.
+// One 16-row tile per workgroup; its 4 waves split the tile's panels (wave w
+// takes panels w, w + 4, ...) with a register pipeline two panels deep, and
+// read their x^T fragments straight from global memory (x is small and stays
+// in L2), so no barrier waits for a staging pass.  The waves' partial sums
+// meet in LDS at the end.
 template <int MT, bool MX>
-struct DirectRegs {
-  uint4 w[2];
-  uint4 xb[MT][2][2];   // [m tile][chunk][first / last 8 K positions]
-  float s[2];           // block: s[0] is the block scale; MX: one per chunk
+struct DirectSlot {
+  Panel<MX> p;
+  uint4 xb[MT][2][2][2];   // [m tile][block][chunk][first / last 8 K positions]
 };
 
-template <int MT, int KW, int D, bool MX>
+template <int MT, int D, bool MX>
 __global__ __launch_bounds__(kThreads) void k_gemv_mfma_direct(GemvJob j, int m_rows) {
-  constexpr int kTiles = kWaves / KW;
-  __shared__ float red[KW > 1 ? kWaves * MT * 4 * kWave : 1];
+  __shared__ __align__(16) unsigned char pb[kWaves * kPanelBytes];
+  __shared__ float red[kWaves * MT * 4 * kWave];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int kw = wave % KW, tile = wave / KW;
   const int i = lane & 15, g = lane >> 4;
-  const int row0 = (blockIdx.x * kTiles + tile) * 16;
-  const int row = row0 + i;
-  const bool row_ok = row < j.n;
+  const int row0 = blockIdx.x * 16;
+  const int np = (j.k + kPanelCols - 1) / kPanelCols;
   const int nkb = (j.k + kTile - 1) / kTile;
   const int groups = (j.k + kGroup - 1) / kGroup;
-  const int nq = row0 < j.n ? (nkb - kw + KW - 1) / KW : 0;   // this wave's column blocks
-  const float* __restrict__ srow =
-      MX ? nullptr
-         : static_cast<const float*>(j.scales) + (size_t)(min(row0, j.n - 1) / kTile) * nkb;
-  const uint8_t* __restrict__ e8 = static_cast<const uint8_t*>(j.scales);
+  const int nq = (np - wave + kWaves - 1) / kWaves;   // this wave's panels
 
-  auto issue = [&](int q, DirectRegs<MT, MX>& r) {
-    const int kb = kw + KW * q;
+  auto issue = [&](int q, DirectSlot<MT, MX>& r) {
+    const int p = wave + kWaves * q;
     const bool live = q < nq;
-    r.s[0] = r.s[1] = 0.0f;
-    if (!MX && live) r.s[0] = ld_global<float>(srow, (size_t)kb * 4);
+    panel_issue<MX>(j, row0, p, live, nkb, groups, r.p);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int kx = kb * kTile + h * 64 + 16 * g;
-      const bool in = live && kx < j.k;
-      r.w[h] = make_uint4(0, 0, 0, 0);
-      if (in && row_ok) {
-        r.w[h] = ld_stream_u4(j.codes, (size_t)row * j.k + kx);
-        if (MX) r.s[h] = mx_scale(ld_global<uint8_t>(e8, (size_t)row * groups + kx / kGroup));
-      }
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const int m = 16 * t + i;
-        r.xb[t][h][0] = r.xb[t][h][1] = make_uint4(0, 0, 0, 0);
-        if (in && m < m_rows) {
-          r.xb[t][h][0] = ld_global_u4(j.x, ((size_t)m * j.k + kx) * 2);
-          r.xb[t][h][1] = ld_global_u4(j.x, ((size_t)m * j.k + kx + 8) * 2);
+      for (int c = 0; c < 2; ++c) {
+        const int kx = p * kPanelCols + 128 * b + 64 * c + 16 * g;
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const int m = 16 * t + i;
+          r.xb[t][b][c][0] = r.xb[t][b][c][1] = make_uint4(0, 0, 0, 0);
+          if (live && m < m_rows && kx < j.k) {
+            r.xb[t][b][c][0] = ld_global_u4(j.x, ((size_t)m * j.k + kx) * 2);
+            r.xb[t][b][c][1] = ld_global_u4(j.x, ((size_t)m * j.k + kx + 8) * 2);
+          }
         }
       }
-    }
   };
 
   f32x4 acc[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  DirectRegs<MT, MX> slot[D];
+  DirectSlot<MT, MX> slot[D];
 #pragma unroll
   for (int s = 0; s < D; ++s) issue(s, slot[s]);
   for (int q0 = 0; q0 < nq; q0 += D) {
 #pragma unroll
     for (int s = 0; s < D; ++s) {
       if (q0 + s < nq) {
-        f32x4 part[MT];
-#pragma unroll
-        for (int t = 0; t < MT; ++t) part[t] = MX ? acc[t] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint4 d = slot[s].w[h];
-          bf16x2 a0, a1, a2, a3, b0, b1, b2, b3;
-          if (MX) {
-            const float sc = slot[s].s[h];
-            a0 = cvt_scaled<false>(d.x, sc), a1 = cvt_scaled<true>(d.x, sc);
-            a2 = cvt_scaled<false>(d.y, sc), a3 = cvt_scaled<true>(d.y, sc);
-            b0 = cvt_scaled<false>(d.z, sc), b1 = cvt_scaled<true>(d.z, sc);
-            b2 = cvt_scaled<false>(d.w, sc), b3 = cvt_scaled<true>(d.w, sc);
-          } else {
-            a0 = cvt_lo(d.x), a1 = cvt_hi(d.x), a2 = cvt_lo(d.y), a3 = cvt_hi(d.y);
-            b0 = cvt_lo(d.z), b1 = cvt_hi(d.z), b2 = cvt_lo(d.w), b3 = cvt_hi(d.w);
-          }
-          const bf16x8 A0 = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
-          const bf16x8 A1 = {b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
-#pragma unroll
-          for (int t = 0; t < MT; ++t) {
-            part[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                A0, __builtin_bit_cast(bf16x8, slot[s].xb[t][h][0]), part[t], 0, 0, 0);
-            part[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                A1, __builtin_bit_cast(bf16x8, slot[s].xb[t][h][1]), part[t], 0, 0, 0);
-          }
-        }
-        if (MX) {
-#pragma unroll
-          for (int t = 0; t < MT; ++t) acc[t] = part[t];
-        } else {
-          const float bs = slot[s].s[0];
-#pragma unroll
-          for (int t = 0; t < MT; ++t)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) acc[t][jj] = __builtin_fmaf(bs, part[t][jj], acc[t][jj]);
-        }
+        uint4 a[2][2];
+        panel_to_a(slot[s].p.v, pb + wave * kPanelBytes, a);
+        panel_mfma<MT, MX>(a, slot[s].p.s, [&](int t, int b, int c, uint4& B0, uint4& B1) {
+          B0 = slot[s].xb[t][b][c][0];
+          B1 = slot[s].xb[t][b][c][1];
+        }, acc);
       }
       issue(q0 + s + D, slot[s]);
     }
   }
 
-  if (KW > 1) {
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) red[((wave * MT + t) * 4 + jj) * kWave + lane] = acc[t][jj];
+  __syncthreads();
+  if (wave == 0) {
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) red[((wave * MT + t) * 4 + jj) * kWave + lane] = acc[t][jj];
-    __syncthreads();
-    if (kw == 0) {
-#pragma unroll
-      for (int t = 0; t < MT; ++t)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          float v = acc[t][jj];
-          for (int w2 = 1; w2 < KW; ++w2) v += red[(((wave + w2) * MT + t) * 4 + jj) * kWave + lane];
-          acc[t][jj] = v;
-        }
-    }
-  }
-  if (kw == 0) {
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const int mcol = 16 * t + i;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int r = row0 + 4 * g + jj;
-        if (r < j.n && mcol < m_rows)
-          st_global<uint16_t>(j.y, ((size_t)mcol * j.n + r) * 2, (uint16_t)f32_to_bf16_rne(acc[t][jj]));
-      }
-    }
+      for (int jj = 0; jj < 4; ++jj)
+        acc[t][jj] += red[((1 * MT + t) * 4 + jj) * kWave + lane] + red[((2 * MT + t) * 4 + jj) * kWave + lane] +
+                      red[((3 * MT + t) * 4 + jj) * kWave + lane];
+    store_tile<MT>(j, row0, m_rows, acc);
   }
 }
 
@@ -765,22 +822,14 @@ __global__ __launch_bounds__(kThreads) void k_gemv_mfma_direct(GemvJob j, int m_
 //   VALU single call: R = 1 row per wave (4 rows per workgroup: the most
 //     workgroups for small N); grouped: more rows per wave (fewer, larger
 //     workgroups once many GEMVs share the launch).
-//   MFMA single call: direct-x kernel, the 4 waves of a 16-row tile split
-//     K; grouped: LDS-staged kernel, each wave owns a 16-row tile.
+//   MFMA single call: k_gemv_mfma_direct, one 16-row tile per workgroup.
+//   MFMA grouped: k_gemv_mfma_stream, 8 waves, 128-row tiles.
 
 template <int M, int R, int C, bool MX, bool G>
 hipError_t run_valu(const GemvJob& job, const GemvJob* table, int njobs, int64_t blocks,
                     hipStream_t stream) {
   hipLaunchKernelGGL((k_gemv_valu<M, R, C, MX, G>), dim3((unsigned)blocks), dim3(kThreads), 0,
                      stream, job, table, njobs);
-  return hipGetLastError();
-}
-
-template <int MT, int KW, int CKB, bool MX, bool G>
-hipError_t run_mfma(const GemvJob& job, const GemvJob* table, int njobs, int64_t blocks, int m,
-                    hipStream_t stream) {
-  hipLaunchKernelGGL((k_gemv_mfma<MT, KW, CKB, MX, G>), dim3((unsigned)blocks), dim3(kThreads), 0,
-                     stream, job, table, njobs, m);
   return hipGetLastError();
 }
 
@@ -814,18 +863,32 @@ hipError_t dispatch_valu(int m, const GemvJob& job, const GemvJob* table, int nj
   return hipErrorInvalidValue;
 }
 
-template <bool MX, bool G>
-hipError_t dispatch_mfma(int m, const GemvJob& job, const GemvJob* table, int njobs, int64_t blocks,
-                         hipStream_t s) {
-  if (G) {
-    if (m <= 16) return run_mfma<1, 1, 4, MX, G>(job, table, njobs, blocks, m, s);
-    return run_mfma<2, 1, 2, MX, G>(job, table, njobs, blocks, m, s);
+// MFMA streaming kernel: waves per workgroup, pipeline depth per m tile
+// count, and the LDS each workgroup may take (two workgroups per CU).
+constexpr int kMfmaStreamWaves = 8;
+constexpr int kMfmaStreamLds = 80 * 1024;
+
+template <int MT, bool MX>
+constexpr auto mfma_stream_kernel() {
+  return &k_gemv_mfma_stream<MT, kMfmaStreamWaves, MT == 1 ? 3 : 2, MX>;
+}
+
+// The kernel needs more than the default 64 KB of dynamic LDS: raise the
+// limit once per device and variant.
+template <int MT, bool MX>
+hipError_t allow_mfma_stream_lds() {
+  static bool done[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (!done[dev]) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(mfma_stream_kernel<MT, MX>()),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kMfmaStreamLds);
+    if (e != hipSuccess) return e;
+    done[dev] = true;
   }
-  if (m <= 16)
-    hipLaunchKernelGGL((k_gemv_mfma_direct<1, 4, 2, MX>), dim3((unsigned)blocks), dim3(kThreads), 0, s, job, m);
-  else
-    hipLaunchKernelGGL((k_gemv_mfma_direct<2, 4, 2, MX>), dim3((unsigned)blocks), dim3(kThreads), 0, s, job, m);
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace
@@ -835,7 +898,7 @@ int gemv_rows_per_block(int route, int m, bool grouped) {
     if (grouped) return kWaves * 4;
     return kWaves * (m == 1 ? 1 : 2);
   }
-  return grouped ? 64 : 16;
+  return grouped ? 16 * kMfmaStreamWaves : 16;
 }
 
 hipError_t launch_gemv(const GemvJob& job, int m, bool mx, int route, hipStream_t stream) {
@@ -844,8 +907,15 @@ hipError_t launch_gemv(const GemvJob& job, int m, bool mx, int route, hipStream_
   if (route == 1)
     return mx ? dispatch_valu<true, false>(m, job, nullptr, 1, blocks, stream)
               : dispatch_valu<false, false>(m, job, nullptr, 1, blocks, stream);
-  return mx ? dispatch_mfma<true, false>(m, job, nullptr, 1, blocks, stream)
-            : dispatch_mfma<false, false>(m, job, nullptr, 1, blocks, stream);
+  const dim3 grid((unsigned)blocks), block(kThreads);
+  if (m <= 16) {
+    if (mx) hipLaunchKernelGGL((k_gemv_mfma_direct<1, 2, true>), grid, block, 0, stream, job, m);
+    else hipLaunchKernelGGL((k_gemv_mfma_direct<1, 2, false>), grid, block, 0, stream, job, m);
+  } else {
+    if (mx) hipLaunchKernelGGL((k_gemv_mfma_direct<2, 2, true>), grid, block, 0, stream, job, m);
+    else hipLaunchKernelGGL((k_gemv_mfma_direct<2, 2, false>), grid, block, 0, stream, job, m);
+  }
+  return hipGetLastError();
 }
 
 // Streaming kernel of grouped M = 1 VALU plans: (R, C) and its K limit.
@@ -879,13 +949,78 @@ hipError_t launch_gemv_stream(const GemvJob* table, int njobs, int64_t blocks, i
 }
 
 hipError_t launch_gemv_grouped(const GemvJob* table, int njobs, int64_t blocks, int m, bool mx,
-                               int route, hipStream_t stream) {
+                               hipStream_t stream) {
   const GemvJob none{};
-  if (route == 1)
-    return mx ? dispatch_valu<true, true>(m, none, table, njobs, blocks, stream)
-              : dispatch_valu<false, true>(m, none, table, njobs, blocks, stream);
-  return mx ? dispatch_mfma<true, true>(m, none, table, njobs, blocks, stream)
-            : dispatch_mfma<false, true>(m, none, table, njobs, blocks, stream);
+  return mx ? dispatch_valu<true, true>(m, none, table, njobs, blocks, stream)
+            : dispatch_valu<false, true>(m, none, table, njobs, blocks, stream);
+}
+
+int gemv_mfma_stream_seg_cols(int m, int64_t max_k) {
+  const int x_budget = kMfmaStreamLds - kMfmaStreamWaves * kPanelBytes;
+  const int cap = (x_budget / (2 * m) - 8) / kPanelCols * kPanelCols;
+  const int64_t kmax = (max_k + kPanelCols - 1) / kPanelCols * kPanelCols;
+  if (kmax <= cap) return (int)kmax;
+  const int64_t nseg = (kmax + cap - 1) / cap;
+  const int64_t per = (kmax + nseg - 1) / nseg;
+  return (int)((per + kPanelCols - 1) / kPanelCols * kPanelCols);
+}
+
+int gemv_mfma_stream_lds(int m, int seg_cols) {
+  return kMfmaStreamWaves * kPanelBytes + m * (seg_cols + 8) * 2;
+}
+
+int gemv_mfma_stream_lds_limit() { return kMfmaStreamLds; }
+
+hipError_t gemv_mfma_stream_slots(int m, bool mx, int seg_cols, int* slots) {
+  const size_t lds = (size_t)gemv_mfma_stream_lds(m, seg_cols);
+  const int threads = kMfmaStreamWaves * kWave;
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) {
+    if (m <= 16) {
+      e = mx ? allow_mfma_stream_lds<1, true>() : allow_mfma_stream_lds<1, false>();
+      if (e == hipSuccess)
+        e = mx ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_stream_kernel<1, true>(), threads, lds)
+               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_stream_kernel<1, false>(), threads, lds);
+    } else {
+      e = mx ? allow_mfma_stream_lds<2, true>() : allow_mfma_stream_lds<2, false>();
+      if (e == hipSuccess)
+        e = mx ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_stream_kernel<2, true>(), threads, lds)
+               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_stream_kernel<2, false>(), threads, lds);
+    }
+  }
+  *slots = cus * (per_cu > 0 ? per_cu : 1);
+  return e;
+}
+
+hipError_t launch_gemv_mfma_stream(const GemvJob* table, int njobs, int64_t blocks, int64_t tiles,
+                                   int tiles_per_block, int m, int seg_cols, bool mx,
+                                   hipStream_t stream) {
+  const size_t lds = (size_t)gemv_mfma_stream_lds(m, seg_cols);
+  const dim3 grid((unsigned)blocks), block(kMfmaStreamWaves * kWave);
+  constexpr int W = kMfmaStreamWaves;
+  hipError_t e;
+  if (m <= 16) {
+    e = mx ? allow_mfma_stream_lds<1, true>() : allow_mfma_stream_lds<1, false>();
+    if (e != hipSuccess) return e;
+    if (mx)
+      hipLaunchKernelGGL((k_gemv_mfma_stream<1, W, 3, true>), grid, block, lds, stream, table, njobs,
+                         (int)tiles, tiles_per_block, m, seg_cols);
+    else
+      hipLaunchKernelGGL((k_gemv_mfma_stream<1, W, 3, false>), grid, block, lds, stream, table, njobs,
+                         (int)tiles, tiles_per_block, m, seg_cols);
+  } else {
+    e = mx ? allow_mfma_stream_lds<2, true>() : allow_mfma_stream_lds<2, false>();
+    if (e != hipSuccess) return e;
+    if (mx)
+      hipLaunchKernelGGL((k_gemv_mfma_stream<2, W, 2, true>), grid, block, lds, stream, table, njobs,
+                         (int)tiles, tiles_per_block, m, seg_cols);
+    else
+      hipLaunchKernelGGL((k_gemv_mfma_stream<2, W, 2, false>), grid, block, lds, stream, table, njobs,
+                         (int)tiles, tiles_per_block, m, seg_cols);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace fp8w

@@ -30,15 +30,27 @@ hipError_t launch_quantize_mx(const uint16_t* w, int64_t n, int64_t k, uint8_t* 
 // route: 1 = VALU (m <= 8), 2 = MFMA (m <= 32).
 int gemv_rows_per_block(int route, int m, bool grouped);
 hipError_t launch_gemv(const GemvJob& job, int m, bool mx, int route, hipStream_t stream);
+// Grouped VALU launch, one tile of gemv_rows_per_block(1, m, true) rows per workgroup.
 hipError_t launch_gemv_grouped(const GemvJob* device_table, int njobs, int64_t blocks, int m,
-                               bool mx, int route, hipStream_t stream);
+                               bool mx, hipStream_t stream);
 
-// Streaming grouped kernel (VALU, m = 1, every K <= gemv_stream_max_k()):
+// Streaming grouped VALU kernel (m = 1, every K <= gemv_stream_max_k()):
 // tiles of gemv_stream_rows() rows, a contiguous run of tiles per workgroup.
 int gemv_stream_max_k();
 int gemv_stream_rows();
 hipError_t gemv_stream_slots(bool mx, int* slots);   // resident workgroups on the device
 hipError_t launch_gemv_stream(const GemvJob* device_table, int njobs, int64_t blocks,
                               int64_t tiles, int tiles_per_block, bool mx, hipStream_t stream);
+
+// Streaming grouped MFMA kernel (any m <= 32, any K): tiles of
+// gemv_rows_per_block(2, m, true) rows, x staged in LDS by K segments of
+// seg_cols columns (a multiple of 256 chosen by gemv_mfma_stream_seg_cols).
+int gemv_mfma_stream_seg_cols(int m, int64_t max_k);
+int gemv_mfma_stream_lds(int m, int seg_cols);      // LDS bytes per workgroup
+int gemv_mfma_stream_lds_limit();
+hipError_t gemv_mfma_stream_slots(int m, bool mx, int seg_cols, int* slots);
+hipError_t launch_gemv_mfma_stream(const GemvJob* device_table, int njobs, int64_t blocks,
+                                   int64_t tiles, int tiles_per_block, int m, int seg_cols,
+                                   bool mx, hipStream_t stream);
 
 }  // namespace fp8w

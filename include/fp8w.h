@@ -184,8 +184,9 @@ typedef struct fp8w_grouped_plan {
   int64_t blocks;          /* workgroups of one launch                    */
   int64_t tiles;           /* row tiles of all GEMVs together             */
   int32_t tiles_per_block; /* 0: one tile per workgroup; else a contiguous
-                              run of tiles per workgroup (streaming kernel) */
-  int32_t reserved;
+                              run of tiles per workgroup (streaming kernels) */
+  int32_t seg_cols;        /* MFMA route: K columns of x staged per pass
+                              (multiple of 256); 0 on the VALU route       */
 } fp8w_grouped_plan;
 
 /* Bytes of device memory a table for `count` GEMVs needs (0 if count < 1). */

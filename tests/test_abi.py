@@ -129,6 +129,16 @@ def test_grouped_argument_errors(F):
     assert L.fp8w_gemv_grouped(ctypes.byref(bad), None) == F.ERR_SHAPE
     bad = F.GroupedPlanC(T, 1, 2, 0, 1, 4, 5, 0, 0)     # one tile per block: tiles == blocks
     assert L.fp8w_gemv_grouped(ctypes.byref(bad), None) == F.ERR_SHAPE
+    bad = F.GroupedPlanC(T, 1, 1, 0, 1, 4, 4, 1, 256)   # VALU plans carry no x segment
+    assert L.fp8w_gemv_grouped(ctypes.byref(bad), None) == F.ERR_SHAPE
+    bad = F.GroupedPlanC(T, 1, 4, 0, 2, 4, 4, 0, 256)   # MFMA plans always stream
+    assert L.fp8w_gemv_grouped(ctypes.byref(bad), None) == F.ERR_SHAPE
+    bad = F.GroupedPlanC(T, 1, 4, 0, 2, 4, 4, 1, 0)     # MFMA: no x segment
+    assert L.fp8w_gemv_grouped(ctypes.byref(bad), None) == F.ERR_SHAPE
+    bad = F.GroupedPlanC(T, 1, 4, 0, 2, 4, 4, 1, 300)   # MFMA: segment not a multiple of 256
+    assert L.fp8w_gemv_grouped(ctypes.byref(bad), None) == F.ERR_SHAPE
+    bad = F.GroupedPlanC(T, 1, 32, 0, 2, 4, 4, 1, 4096)  # MFMA: x segment exceeds the LDS budget
+    assert L.fp8w_gemv_grouped(ctypes.byref(bad), None) == F.ERR_SHAPE
 
 
 def test_binding_refuses_cpu_tensors(F):

@@ -863,14 +863,16 @@ hipError_t dispatch_valu(int m, const GemvJob& job, const GemvJob* table, int nj
   return hipErrorInvalidValue;
 }
 
-// MFMA streaming kernel: waves per workgroup, pipeline depth per m tile
-// count, and the LDS each workgroup may take (two workgroups per CU).
+// MFMA streaming kernel: waves per workgroup (panel pipeline two deep) and
+// the LDS each workgroup may take (two workgroups per CU).  Measured on the
+// projection set: a deeper pipeline or 16-wave workgroups with twice the LDS
+// are no faster, and cost occupancy.
 constexpr int kMfmaStreamWaves = 8;
 constexpr int kMfmaStreamLds = 80 * 1024;
 
 template <int MT, bool MX>
 constexpr auto mfma_stream_kernel() {
-  return &k_gemv_mfma_stream<MT, kMfmaStreamWaves, MT == 1 ? 3 : 2, MX>;
+  return &k_gemv_mfma_stream<MT, kMfmaStreamWaves, 2, MX>;
 }
 
 // The kernel needs more than the default 64 KB of dynamic LDS: raise the
@@ -1005,10 +1007,10 @@ hipError_t launch_gemv_mfma_stream(const GemvJob* table, int njobs, int64_t bloc
     e = mx ? allow_mfma_stream_lds<1, true>() : allow_mfma_stream_lds<1, false>();
     if (e != hipSuccess) return e;
     if (mx)
-      hipLaunchKernelGGL((k_gemv_mfma_stream<1, W, 3, true>), grid, block, lds, stream, table, njobs,
+      hipLaunchKernelGGL((k_gemv_mfma_stream<1, W, 2, true>), grid, block, lds, stream, table, njobs,
                          (int)tiles, tiles_per_block, m, seg_cols);
     else
-      hipLaunchKernelGGL((k_gemv_mfma_stream<1, W, 3, false>), grid, block, lds, stream, table, njobs,
+      hipLaunchKernelGGL((k_gemv_mfma_stream<1, W, 2, false>), grid, block, lds, stream, table, njobs,
                          (int)tiles, tiles_per_block, m, seg_cols);
   } else {
     e = mx ? allow_mfma_stream_lds<2, true>() : allow_mfma_stream_lds<2, false>();

@@ -79,6 +79,10 @@ def _load():
             "oracle_quantize_mx": (ctypes.c_int, [P, I64, I64, P, P, I64]),
             "oracle_dequant_block": (ctypes.c_int, [P, P, I64, I64, P]),
             "oracle_dequant_mx": (ctypes.c_int, [P, P, I64, I64, P]),
+            "oracle_round_bf16": (ctypes.c_uint16, [ctypes.c_double]),
+            "oracle_round_bf16_array": (None, [P, I64, P]),
+            "oracle_dequant_block_bf16": (ctypes.c_int, [P, P, I64, I64, P]),
+            "oracle_dequant_mx_bf16": (ctypes.c_int, [P, P, I64, I64, P]),
             "oracle_gemv_block_f64": (ctypes.c_int, [P, I64, P, P, I64, I64, P, I64, P, P]),
             "oracle_gemv_mx_f64": (ctypes.c_int, [P, I64, P, P, I64, I64, P, I64, P, P]),
         }
@@ -204,6 +208,40 @@ def dequant_mx(codes: np.ndarray, e8m0: np.ndarray) -> np.ndarray:
         raise ValueError("e8m0 shape mismatch")
     out = np.empty((n, k), dtype=np.float64)
     _check(_load().oracle_dequant_mx(_ptr(c), _ptr(e), n, k, _ptr(out)), "dequant_mx")
+    return out
+
+
+def round_bf16(v) -> np.ndarray:
+    """bf16 bit patterns nearest to fp64 values (ties to even, IEEE overflow)."""
+    a = _as(np.asarray(v, dtype=np.float64), np.float64)
+    out = np.empty(a.shape, dtype=np.uint16)
+    _load().oracle_round_bf16_array(_ptr(a), a.size, _ptr(out))
+    return out
+
+
+def dequant_block_bf16(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """bf16 bits of fl32(dec(code) * scale), [n, k]."""
+    c = _as(codes, np.uint8)
+    s = _as(scales, np.float32)
+    n, k = c.shape
+    if s.shape != block_scale_shape(n, k):
+        raise ValueError("scale grid shape mismatch")
+    out = np.empty((n, k), dtype=np.uint16)
+    _check(_load().oracle_dequant_block_bf16(_ptr(c), _ptr(s), n, k, _ptr(out)),
+           "dequant_block_bf16")
+    return out
+
+
+def dequant_mx_bf16(codes: np.ndarray, e8m0: np.ndarray) -> np.ndarray:
+    """bf16 bits of dec(code) * 2^(E - 127), [n, k]."""
+    c = _as(codes, np.uint8)
+    e = _as(e8m0, np.uint8)
+    n, k = c.shape
+    if e.shape != mx_scale_shape(n, k):
+        raise ValueError("e8m0 shape mismatch")
+    out = np.empty((n, k), dtype=np.uint16)
+    _check(_load().oracle_dequant_mx_bf16(_ptr(c), _ptr(e), n, k, _ptr(out)),
+           "dequant_mx_bf16")
     return out
 
 

@@ -27,6 +27,9 @@
  *    exponent = ceil(log2(amax/448)), computed row-chunked so that the fp32
  *    transient stays near 32 MB ("Load-time MXFP8 requantization ..." issue,
  *    Proposed solution).
+ *  - dequantize to bf16: fp32 product of the decoded value and the scale,
+ *    rounded to bf16 (the dense-GEMM fallback of "feat: add FP8 blockwise
+ *    weight quantization ...", Summary, consumes bf16 weights).
  *  - GEMV reference: y = x . deq(W)^T with x bf16 [M,K] and W [N,K]; each
  *    product is exact in fp64 and the sum is taken in fp64 ("feat: add FP8
  *    blockwise weight quantization ...", Summary: fused W8A16 GEMM for
@@ -302,6 +305,86 @@ int oracle_dequant_mx(const uint8_t* codes, const uint8_t* e8m0, int64_t n,
     for (int64_t c = 0; c < k; ++c)
       out[r * k + c] = ldexp(oracle_e4m3_decode(codes[r * k + c]),
                              (int)e8m0[r * groups + c / MX_GROUP] - 127);
+  return ORACLE_OK;
+}
+
+/* ------------------------------------------------ dequantize to bf16 -- */
+
+/* bf16 nearest to v, ties to the even bit pattern; magnitudes at or above
+ * the midpoint between the largest finite bf16 and 2^128 become infinity
+ * (IEEE overflow under round-to-nearest).  A binary search over the 32,640
+ * non-negative finite bf16 patterns, which are ordered like their values;
+ * the two neighbours are compared in fp64, where every bf16 value and every
+ * fp32 input is exact. */
+uint16_t oracle_round_bf16(double v) {
+  if (isnan(v)) return 0x7FC0;
+  const uint16_t sign = signbit(v) ? 0x8000 : 0;
+  const double a = fabs(v);
+  const uint16_t kMaxFinite = 0x7F7F;
+  if (a >= (double)bf16_to_float(kMaxFinite)) {
+    const double top = ldexp(1.0, 128);   /* the value the next pattern would have */
+    const double lo = (double)bf16_to_float(kMaxFinite);
+    if (a - lo < top - a) return sign | kMaxFinite;
+    return sign | 0x7F80;                 /* at or past the midpoint: infinity */
+  }
+  uint16_t lo = 0, hi = kMaxFinite;       /* largest pattern with value <= a */
+  while (lo < hi) {
+    const uint16_t mid = (uint16_t)((lo + hi + 1) / 2);
+    if ((double)bf16_to_float(mid) <= a) lo = mid;
+    else hi = (uint16_t)(mid - 1);
+  }
+  const double below = (double)bf16_to_float(lo);
+  if (below == a) return sign | lo;
+  const double above = (double)bf16_to_float((uint16_t)(lo + 1));
+  const double d_lo = a - below, d_hi = above - a;
+  uint16_t pick;
+  if (d_lo < d_hi) pick = lo;
+  else if (d_hi < d_lo) pick = (uint16_t)(lo + 1);
+  else pick = (lo % 2 == 0) ? lo : (uint16_t)(lo + 1);
+  return sign | pick;
+}
+
+void oracle_round_bf16_array(const double* v, int64_t n, uint16_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_round_bf16(v[i]);
+}
+
+/* Dequantize to bf16 as a dequantize-then-dense-GEMM path consumes it: the
+ * decoded value times the scale, rounded to fp32 (one IEEE multiply; the
+ * fp64 product is exact, so converting it to float is that multiply), then
+ * rounded to bf16 ("feat: add FP8 blockwise weight quantization ...",
+ * Summary: larger M and prefill dequantize to bf16 for a dense GEMM; the
+ * round-trip check of "feat(quant): opt-in fp8-block QAT for the lm_head",
+ * Validation, pairs the quantizer with this dequantizer).  MX scales are
+ * powers of two, so there the fp32 product is exact and only the bf16
+ * rounding remains. */
+int oracle_dequant_block_bf16(const uint8_t* codes, const float* scales, int64_t n,
+                              int64_t k, uint16_t* out) {
+  if (!codes || !scales || !out || n < 1 || k < 1) return ORACLE_ERR_ARG;
+  const int64_t tiles_k = (k + TILE - 1) / TILE;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n; ++r)
+    for (int64_t c = 0; c < k; ++c) {
+      const double exact = oracle_e4m3_decode(codes[r * k + c]) *
+                           (double)scales[(r / TILE) * tiles_k + c / TILE];
+      const float p = (float)exact;
+      out[r * k + c] = oracle_round_bf16((double)p);
+    }
+  return ORACLE_OK;
+}
+
+int oracle_dequant_mx_bf16(const uint8_t* codes, const uint8_t* e8m0, int64_t n,
+                           int64_t k, uint16_t* out) {
+  if (!codes || !e8m0 || !out || n < 1 || k < 1) return ORACLE_ERR_ARG;
+  const int64_t groups = (k + MX_GROUP - 1) / MX_GROUP;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n; ++r)
+    for (int64_t c = 0; c < k; ++c) {
+      const double exact = ldexp(oracle_e4m3_decode(codes[r * k + c]),
+                                 (int)e8m0[r * groups + c / MX_GROUP] - 127);
+      const float p = (float)exact;
+      out[r * k + c] = oracle_round_bf16((double)p);
+    }
   return ORACLE_OK;
 }
 

@@ -15,6 +15,9 @@ Functions carry the names of the C entry points:
 * ``fp8w_gemv_mx(x, codes, e8m0) -> y``
 * ``fp8w_grouped_plan_init(xs, codes, scales) -> plan`` and
   ``fp8w_gemv_grouped(plan) -> ys``: many independent GEMVs in one launch
+* ``fp8w_dequantize_block(codes, scales) -> w`` / ``fp8w_dequantize_mx``: bf16 [n,k]
+* ``fp8w_gemm_block(x, codes, scales) -> y`` / ``fp8w_gemm_mx``: any m, through
+  dequantize + a dense bf16 GEMM (the large-M route)
 
 plus ``Fp8Weight``, a format-tagged weight whose GEMV asserts the format
 before dispatch (a scale buffer of the wrong format cannot be detected by a
@@ -45,6 +48,11 @@ SIGNATURES = {
     "fp8w_gemv_mx": (_I, [_P, _I64, _P, _P, _I64, _I64, _P, _P]),
     "fp8w_gemv_block_route": (_I, [_P, _I64, _P, _P, _I64, _I64, _P, _I, _P]),
     "fp8w_gemv_mx_route": (_I, [_P, _I64, _P, _P, _I64, _I64, _P, _I, _P]),
+    "fp8w_dequantize_block": (_I, [_P, _P, _I64, _I64, _P, _P]),
+    "fp8w_dequantize_mx": (_I, [_P, _P, _I64, _I64, _P, _P]),
+    "fp8w_gemm_workspace_bytes": (_I64, [_I64, _I64]),
+    "fp8w_gemm_block": (_I, [_P, _I64, _P, _P, _I64, _I64, _P, _P, _I64, _P]),
+    "fp8w_gemm_mx": (_I, [_P, _I64, _P, _P, _I64, _I64, _P, _P, _I64, _P]),
     "fp8w_grouped_table_bytes": (_I64, [_I64]),
     "fp8w_grouped_plan_init": (_I, [_P, _I64, _I64, _I, _I, _P, _P]),
     "fp8w_gemv_grouped": (_I, [_P, _P]),
@@ -215,6 +223,79 @@ def fp8w_gemv_mx(x, codes, e8m0, y=None, route=ROUTE_AUTO, stream=None):
     return _gemv("fp8w_gemv_mx", x, codes, e8m0, mx_scale_shape, torch.uint8, y, route, stream)
 
 
+# ------------------------------------------------------------- dequantize --
+
+def _dequantize(fn_name, codes, scale_t, scale_shape, scale_dtype, w, stream):
+    torch = _torch()
+    _require(codes, (torch.uint8,), "codes", 2)
+    _require(scale_t, (scale_dtype,), "scales", 2)
+    n, k = codes.shape
+    if tuple(scale_t.shape) != scale_shape(n, k):
+        raise ValueError(f"{fn_name}: scale grid {tuple(scale_t.shape)} != {scale_shape(n, k)}")
+    if w is None:
+        w = torch.empty((n, k), dtype=torch.bfloat16, device=codes.device)
+    _require(w, _bf16_like(torch), "w", 2)
+    if tuple(w.shape) != (n, k):
+        raise ValueError(f"{fn_name}: w must be [{n}, {k}]")
+    _check(getattr(lib(), fn_name)(codes.data_ptr(), scale_t.data_ptr(), n, k, w.data_ptr(),
+                                   _stream_handle(stream)), fn_name)
+    return w
+
+
+def fp8w_dequantize_block(codes, scales, w=None, stream=None):
+    """bf16 W [n,k] = fl32(dec(codes) * block scale), rounded to bf16."""
+    torch = _torch()
+    return _dequantize("fp8w_dequantize_block", codes, scales, block_scale_shape, torch.float32, w, stream)
+
+
+def fp8w_dequantize_mx(codes, e8m0, w=None, stream=None):
+    """bf16 W [n,k] = dec(codes) * 2^(e8m0 - 127), rounded to bf16."""
+    torch = _torch()
+    return _dequantize("fp8w_dequantize_mx", codes, e8m0, mx_scale_shape, torch.uint8, w, stream)
+
+
+# ------------------------------------------------------------------- GEMM --
+
+def _gemm(fn_name, x, codes, scale_t, scale_shape, scale_dtype, y, workspace, stream):
+    torch = _torch()
+    _require(x, _bf16_like(torch), "x", 2)
+    _require(codes, (torch.uint8,), "codes", 2)
+    _require(scale_t, (scale_dtype,), "scales", 2)
+    m, k = x.shape
+    n, k2 = codes.shape
+    if k != k2:
+        raise ValueError(f"{fn_name}: x has K={k}, codes have K={k2}")
+    if tuple(scale_t.shape) != scale_shape(n, k):
+        raise ValueError(f"{fn_name}: scale grid {tuple(scale_t.shape)} != {scale_shape(n, k)}")
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    _require(y, _bf16_like(torch), "y", 2)
+    if tuple(y.shape) != (m, n):
+        raise ValueError(f"{fn_name}: y must be [{m}, {n}]")
+    nbytes = int(lib().fp8w_gemm_workspace_bytes(n, k))
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    _require(workspace, (torch.uint8,), "workspace", 1)
+    _check(getattr(lib(), fn_name)(x.data_ptr(), m, codes.data_ptr(), scale_t.data_ptr(), n, k,
+                                   y.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                   _stream_handle(stream)), fn_name)
+    return y
+
+
+def fp8w_gemm_block(x, codes, scales, y=None, workspace=None, stream=None):
+    """y[m,n] = x[m,k] . deq(W)^T for any m: dequantize into ``workspace``
+    (u8, fp8w_gemm_workspace_bytes(n, k) bytes; allocated when None), then a
+    dense bf16 GEMM."""
+    torch = _torch()
+    return _gemm("fp8w_gemm_block", x, codes, scales, block_scale_shape, torch.float32, y,
+                 workspace, stream)
+
+
+def fp8w_gemm_mx(x, codes, e8m0, y=None, workspace=None, stream=None):
+    torch = _torch()
+    return _gemm("fp8w_gemm_mx", x, codes, e8m0, mx_scale_shape, torch.uint8, y, workspace, stream)
+
+
 # ---------------------------------------------------------------- grouped --
 
 class GroupedPlan:
@@ -313,3 +394,20 @@ class Fp8Weight:
         if self.fmt == BLOCK128:
             return fp8w_gemv_block(x, self.codes, self.scales, y, route, stream)
         return fp8w_gemv_mx(x, self.codes, self.scales, y, route, stream)
+
+    def dequantize(self, w=None, stream=None):
+        self.check_format()
+        if self.fmt == BLOCK128:
+            return fp8w_dequantize_block(self.codes, self.scales, w, stream)
+        return fp8w_dequantize_mx(self.codes, self.scales, w, stream)
+
+    def matmul(self, x, y=None, workspace=None, stream=None):
+        """y = x . deq(W)^T for any m: the fused GEMV for m <= 32 (the
+        blockwise page's decode routing, Summary), dequantize + dense GEMM
+        above."""
+        self.check_format()
+        if int(x.shape[0]) <= MAX_M:
+            return self.gemv(x, y, ROUTE_AUTO, stream)
+        if self.fmt == BLOCK128:
+            return fp8w_gemm_block(x, self.codes, self.scales, y, workspace, stream)
+        return fp8w_gemm_mx(x, self.codes, self.scales, y, workspace, stream)

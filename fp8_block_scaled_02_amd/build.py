@@ -3,8 +3,8 @@
     python -m fp8_block_scaled_02_amd.build
 
 The library is the HIP sources under ``csrc/`` linked into one shared object
-next to this file.  Only the ``fp8w_*`` symbols of ``include/fp8w.h`` are
-exported.  Packed-fp32 instructions are disabled for the whole build.
+next to this file, with rocBLAS for the dense GEMM of the large-M route.
+Only the ``fp8w_*`` symbols of ``include/fp8w.h`` are exported.  Packed-fp32 instructions are disabled for the whole build.
 """
 from __future__ import annotations
 
@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfp8w.so")
-SOURCES = ["quantize.hip", "gemv.hip", "api.cpp"]
+SOURCES = ["quantize.hip", "gemv.hip", "dequant.hip", "gemm.cpp", "api.cpp"]
 ARCH = "gfx950"
 
 FLAGS = [
@@ -58,7 +58,9 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(len(SOURCES)) as ex:
         objs = list(ex.map(compile_one, SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    rocm_lib = os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(cc))), "lib")
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp,
+           "-L", rocm_lib, "-lrocblas", "-Wl,-rpath," + rocm_lib]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)

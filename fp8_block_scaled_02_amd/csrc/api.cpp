@@ -140,6 +140,83 @@ FP8W_API fp8w_status fp8w_gemv_mx(const uint16_t* x, int64_t m, const uint8_t* c
   return fp8w_gemv_mx_route(x, m, codes, e8m0, n, k, y, FP8W_ROUTE_AUTO, stream);
 }
 
+// ---------------------------------------------------------- dequantize --
+
+namespace {
+
+fp8w_status check_dequant(const uint8_t* codes, const void* scales, uint64_t scale_bytes,
+                          int64_t n, int64_t k, const uint16_t* w, bool block) {
+  if (!codes || !scales || !w) return FP8W_ERR_NULL;
+  if (!dims_ok(n, k)) return FP8W_ERR_SHAPE;
+  if ((block && !aligned(scales, 4)) || !aligned(w, 2)) return FP8W_ERR_ALIGN;
+  const Span out[1] = {{w, (uint64_t)n * k * 2}};
+  const Span in[2] = {{codes, (uint64_t)n * k}, {scales, scale_bytes}};
+  if (any_overlap(out, 1, in, 2)) return FP8W_ERR_OVERLAP;
+  return FP8W_OK;
+}
+
+}  // namespace
+
+FP8W_API fp8w_status fp8w_dequantize_block(const uint8_t* codes, const float* scales, int64_t n,
+                                           int64_t k, uint16_t* w, void* stream) {
+  const fp8w_status st = check_dequant(codes, scales, (uint64_t)block_count(n, k) * 4, n, k, w, true);
+  if (st != FP8W_OK) return st;
+  return from_hip(fp8w::launch_dequantize_block(codes, scales, n, k, w, static_cast<hipStream_t>(stream)));
+}
+
+FP8W_API fp8w_status fp8w_dequantize_mx(const uint8_t* codes, const uint8_t* e8m0, int64_t n,
+                                        int64_t k, uint16_t* w, void* stream) {
+  const fp8w_status st = check_dequant(codes, e8m0, (uint64_t)mx_count(n, k), n, k, w, false);
+  if (st != FP8W_OK) return st;
+  return from_hip(fp8w::launch_dequantize_mx(codes, e8m0, n, k, w, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------- GEMM --
+
+namespace {
+
+fp8w_status check_gemm(const uint16_t* x, int64_t m, const uint8_t* codes, const void* scales,
+                       uint64_t scale_bytes, int64_t n, int64_t k, const uint16_t* y,
+                       const void* workspace, int64_t workspace_bytes, bool block) {
+  if (!x || !codes || !scales || !y || !workspace) return FP8W_ERR_NULL;
+  if (m < 1 || m > kMaxDim || !dims_ok(n, k)) return FP8W_ERR_SHAPE;
+  if (workspace_bytes < n * k * 2) return FP8W_ERR_SHAPE;
+  if (!aligned(x, 2) || !aligned(y, 2) || !aligned(workspace, 16) || (block && !aligned(scales, 4)))
+    return FP8W_ERR_ALIGN;
+  const Span out[2] = {{y, (uint64_t)m * n * 2}, {workspace, (uint64_t)n * k * 2}};
+  const Span in[3] = {{x, (uint64_t)m * k * 2}, {codes, (uint64_t)n * k}, {scales, scale_bytes}};
+  if (any_overlap(out, 2, in, 3)) return FP8W_ERR_OVERLAP;
+  return FP8W_OK;
+}
+
+}  // namespace
+
+FP8W_API int64_t fp8w_gemm_workspace_bytes(int64_t n, int64_t k) {
+  return (n < 1 || k < 1) ? 0 : n * k * 2;
+}
+
+FP8W_API fp8w_status fp8w_gemm_block(const uint16_t* x, int64_t m, const uint8_t* codes,
+                                     const float* scales, int64_t n, int64_t k, uint16_t* y,
+                                     void* workspace, int64_t workspace_bytes, void* stream) {
+  const fp8w_status st = check_gemm(x, m, codes, scales, (uint64_t)block_count(n, k) * 4, n, k, y,
+                                    workspace, workspace_bytes, true);
+  if (st != FP8W_OK) return st;
+  return from_hip(fp8w::launch_gemm_dequant(x, m, codes, scales, false, n, k, y,
+                                            static_cast<uint16_t*>(workspace),
+                                            static_cast<hipStream_t>(stream)));
+}
+
+FP8W_API fp8w_status fp8w_gemm_mx(const uint16_t* x, int64_t m, const uint8_t* codes,
+                                  const uint8_t* e8m0, int64_t n, int64_t k, uint16_t* y,
+                                  void* workspace, int64_t workspace_bytes, void* stream) {
+  const fp8w_status st = check_gemm(x, m, codes, e8m0, (uint64_t)mx_count(n, k), n, k, y, workspace,
+                                    workspace_bytes, false);
+  if (st != FP8W_OK) return st;
+  return from_hip(fp8w::launch_gemm_dequant(x, m, codes, e8m0, true, n, k, y,
+                                            static_cast<uint16_t*>(workspace),
+                                            static_cast<hipStream_t>(stream)));
+}
+
 // ------------------------------------------------------------- grouped --
 
 FP8W_API int64_t fp8w_grouped_table_bytes(int64_t count) {

@@ -27,6 +27,15 @@ hipError_t launch_quantize_block(const uint16_t* w, int64_t n, int64_t k, uint8_
 hipError_t launch_quantize_mx(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,
                               uint8_t* e8m0, hipStream_t stream);
 
+hipError_t launch_dequantize_block(const uint8_t* codes, const float* scales, int64_t n, int64_t k,
+                                   uint16_t* out, hipStream_t stream);
+hipError_t launch_dequantize_mx(const uint8_t* codes, const uint8_t* e8m0, int64_t n, int64_t k,
+                                uint16_t* out, hipStream_t stream);
+// Dequantize into w_bf16 [n, k], then y = x . w^T with rocBLAS.
+hipError_t launch_gemm_dequant(const uint16_t* x, int64_t m, const uint8_t* codes,
+                               const void* scales, bool mx, int64_t n, int64_t k, uint16_t* y,
+                               uint16_t* w_bf16, hipStream_t stream);
+
 // route: 1 = VALU (m <= 8), 2 = MFMA (m <= 32).
 int gemv_rows_per_block(int route, int m, bool grouped);
 hipError_t launch_gemv(const GemvJob& job, int m, bool mx, int route, hipStream_t stream);

@@ -2,10 +2,14 @@
  * fp8w.h -- C ABI of libfp8w: FP8 (OCP e4m3fn) weights for the decode path
  * on AMD Instinct MI355X (gfx950).
  *
- * Two operations, each in two scale formats:
+ * Operations, each in two scale formats:
  *
- *   quantize  bf16 W[n,k]  ->  e4m3fn codes[n,k] + a scale grid
- *   GEMV      y[m,n] = x[m,k] . deq(W)^T, bf16 in, bf16 out, fp32 accumulate
+ *   quantize    bf16 W[n,k]  ->  e4m3fn codes[n,k] + a scale grid
+ *   GEMV        y[m,n] = x[m,k] . deq(W)^T, bf16 in, bf16 out, fp32
+ *               accumulate, m <= 32 (single calls or grouped)
+ *   dequantize  codes + scales -> bf16 W[n,k]
+ *   GEMM        the same product for any m, through dequantize + a dense
+ *               bf16 GEMM (the large-M / prefill route)
  *
  * Scale formats:
  *   block : one fp32 scale per 128x128 tile, grid [ceil(n/128), ceil(k/128)]
@@ -33,7 +37,8 @@
  *
  * Memory and ownership: every tensor pointer is a DEVICE pointer on the
  * current HIP device.  The caller allocates and frees every buffer; the
- * library keeps no pointer after a call returns and never allocates.
+ * library keeps no pointer after a call returns and never allocates (the
+ * GEMM calls alone create one rocBLAS handle per device on first use).
  *
  * Execution: every call only enqueues work on `stream` (a hipStream_t;
  * NULL means the default stream) and returns without synchronizing.  Calls
@@ -145,6 +150,57 @@ fp8w_status fp8w_gemv_mx_route(const uint16_t* x, int64_t m,
                                const uint8_t* codes, const uint8_t* e8m0,
                                int64_t n, int64_t k, uint16_t* y,
                                fp8w_route route, void* stream);
+
+/* ---------------------------------------------------------- dequantize -- */
+
+/* Block dequantization: the inverse of fp8w_quantize_block.
+ *   codes  : u8   [n, k]                                      input
+ *   scales : f32  [ceil(n/128), ceil(k/128)] (4-byte aligned)  input
+ *   w      : bf16 [n, k]                                      output
+ * w[r][c] = bf16_rne( fl32( dec(codes[r][c]) * scales[r/128][c/128] ) ): one
+ * fp32 multiply, then rounding to nearest even bf16 (overflow gives inf).
+ * The dequantizer the lm_head QAT page pairs with its block quantizer ("feat
+ * (quant): opt-in fp8-block QAT for the lm_head", Changes), feeding the
+ * dense-GEMM route of "feat: add FP8 blockwise weight quantization ..."
+ * (Summary).  Any n, k >= 1; a 16-byte path when k % 16 == 0 and codes and w
+ * are 16-byte aligned.  NaN codes give NaN.
+ * Errors: NULL, SHAPE, ALIGN, OVERLAP, HIP. */
+fp8w_status fp8w_dequantize_block(const uint8_t* codes, const float* scales,
+                                  int64_t n, int64_t k, uint16_t* w, void* stream);
+
+/* MX dequantization: w[r][c] = bf16_rne( dec(codes[r][c]) *
+ * 2^(e8m0[r][c/32] - 127) ), the product exact in fp32 (a decoded code has
+ * 4 significant bits), so the result is the exact value wherever it is a
+ * normal bf16.
+ * Errors: NULL, SHAPE, OVERLAP, HIP. */
+fp8w_status fp8w_dequantize_mx(const uint8_t* codes, const uint8_t* e8m0,
+                               int64_t n, int64_t k, uint16_t* w, void* stream);
+
+/* ---------------------------------------------------------------- GEMM -- */
+
+/* The large-M route: y[m, n] = x[m, k] . deq(W)^T for any m >= 1, as
+ * "feat: add FP8 blockwise weight quantization ..." routes M > 32 and
+ * prefill (Summary): dequantize W into `workspace` (bf16 [n, k], as
+ * fp8w_dequantize_block / _mx write it), then one dense bf16 GEMM with fp32
+ * accumulation and a bf16 result (rocBLAS gemm_ex).
+ *   x         : bf16 [m, k]            input
+ *   y         : bf16 [m, n]            output
+ *   workspace : >= fp8w_gemm_workspace_bytes(n, k) bytes of device memory,
+ *               16-byte aligned; overwritten (holds deq(W) afterwards)
+ * Bound, with y_ref in fp64 from the exact dequantized weight:
+ * |y - y_ref| <= 2^-7 * sum_k |x[i][k]| |deq[j][k]| + 1e-6 (the bf16 weight
+ * adds at most 2^-8 of that sum).  The first call on a device creates the
+ * device's rocBLAS handle (rocBLAS allocates its own workspace then): make
+ * that call outside graph capture.  Calls on one device are serialized
+ * around its handle.  m, n, k <= 2^31 - 1.
+ * Errors: NULL, SHAPE (also: workspace too small), ALIGN, OVERLAP, HIP. */
+int64_t fp8w_gemm_workspace_bytes(int64_t n, int64_t k);
+fp8w_status fp8w_gemm_block(const uint16_t* x, int64_t m, const uint8_t* codes,
+                            const float* scales, int64_t n, int64_t k, uint16_t* y,
+                            void* workspace, int64_t workspace_bytes, void* stream);
+fp8w_status fp8w_gemm_mx(const uint16_t* x, int64_t m, const uint8_t* codes,
+                         const uint8_t* e8m0, int64_t n, int64_t k, uint16_t* y,
+                         void* workspace, int64_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------- grouped -- */
 

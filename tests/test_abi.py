@@ -103,6 +103,42 @@ def test_gemv_argument_errors(F):
     assert m(A, 1, B, C + 1, 16, 16, A + 16, F.ROUTE_AUTO, None) == F.ERR_OVERLAP
 
 
+def test_dequantize_argument_errors(F):
+    L = F.lib()
+    d = L.fp8w_dequantize_block
+    assert d(None, C, 4, 4, D, None) == F.ERR_NULL
+    assert d(B, C, 0, 4, D, None) == F.ERR_SHAPE
+    assert d(B, C, 4, 1 << 31, D, None) == F.ERR_SHAPE
+    assert d(B, C + 2, 4, 4, D, None) == F.ERR_ALIGN            # scale alignment
+    assert d(B, C, 4, 4, D + 1, None) == F.ERR_ALIGN            # bf16 output alignment
+    assert d(B, C, 64, 64, B + 32, None) == F.ERR_OVERLAP       # w over codes
+    assert d(B, C, 64, 64, C - 8, None) == F.ERR_OVERLAP        # w over scales
+    x = L.fp8w_dequantize_mx
+    assert x(B, None, 4, 4, D, None) == F.ERR_NULL
+    assert x(B, C + 1, 64, 64, C - 8, None) == F.ERR_OVERLAP    # e8m0 needs no alignment
+
+
+def test_gemm_argument_errors(F):
+    L = F.lib()
+    W = 0x20000000
+    assert L.fp8w_gemm_workspace_bytes(3, 5) == 30
+    assert L.fp8w_gemm_workspace_bytes(0, 5) == 0
+    g = L.fp8w_gemm_block
+    assert g(A, 64, B, C, 16, 16, D, None, 512, None) == F.ERR_NULL         # no workspace
+    assert g(A, 0, B, C, 16, 16, D, W, 512, None) == F.ERR_SHAPE
+    assert g(A, 1 << 31, B, C, 16, 16, D, W, 512, None) == F.ERR_SHAPE
+    assert g(A, 64, B, C, 16, 16, D, W, 511, None) == F.ERR_SHAPE          # workspace too small
+    assert g(A + 1, 64, B, C, 16, 16, D, W, 512, None) == F.ERR_ALIGN
+    assert g(A, 64, B, C, 16, 16, D, W + 8, 512, None) == F.ERR_ALIGN      # workspace 16-B alignment
+    assert g(A, 64, B, C + 2, 16, 16, D, W, 512, None) == F.ERR_ALIGN
+    assert g(A, 64, B, C, 16, 16, A + 64, W, 512, None) == F.ERR_OVERLAP   # y over x
+    assert g(A, 64, B, C, 16, 16, D, B, 512, None) == F.ERR_OVERLAP        # workspace over codes
+    assert g(A, 64, B, C, 16, 16, W + 256, W, 512, None) == F.ERR_OVERLAP  # y over workspace
+    m = L.fp8w_gemm_mx
+    assert m(A, 64, B, None, 16, 16, D, W, 512, None) == F.ERR_NULL
+    assert m(A, 64, B, C + 1, 16, 16, D, C, 512, None) == F.ERR_OVERLAP    # workspace over e8m0
+
+
 def test_grouped_argument_errors(F):
     L = F.lib()
     descs = (F.GemvDesc * 2)(F.GemvDesc(A, B, C, D, 16, 16), F.GemvDesc(A, B, C, D + 4096, 16, 16))

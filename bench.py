@@ -32,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM = 8.0e12          # MI355X HBM3E, bytes/s
+PEAK_BF16 = 2.5e15         # MI355X dense bf16 MFMA, flop/s
 
 # HBM bytes per launch of the grouped M=1 streaming GEMV on the projection
 # set, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled by a 2 GiB device
@@ -56,7 +57,7 @@ def counted_traffic():
         return None
     return COUNTED_TRAFFIC["bytes_per_launch"]
 TILE, GROUP = 128, 32
-ALL_ROWS = ("proj", "quant", "lm_head", "dense", "mx", "single")
+ALL_ROWS = ("proj", "quant", "lm_head", "dense", "mx", "single", "dequant", "gemm")
 
 
 def parse():
@@ -399,6 +400,102 @@ def bench_mx(torch, fp8w, lean, timer, W, args, log):
     return {"mxfp8": out}
 
 
+def dequant_bytes(n, k, mx):
+    return 3 * n * k + (n * (-(-k // GROUP)) if mx else 4 * (-(-n // TILE)) * (-(-k // TILE)))
+
+
+def bench_dequant(torch, fp8w, lean, timer, W, args, log):
+    """Dequantize to bf16: the dense layer's four weights x 6 copies (block),
+    and 16 copies of the MX [8192x2560] weight; one graph-captured pass of
+    every call, HBM-bound (1 B in, 2 B out per weight)."""
+    lib = fp8w.lib()
+    out = {}
+    layer = []
+    for w in W.WORKLOADS[4].weights:
+        c, s = fp8w.fp8w_quantize_block(upload_bf16(torch, w.bits(4)))
+        layer.append((c, s))
+    jobs = [(c if i == 0 else c.clone(), s if i == 0 else s.clone()) for i in range(6) for c, s in layer]
+    outs = [torch.empty(c.shape, dtype=torch.bfloat16, device="cuda") for c, _ in jobs]
+    args_c = [(c.data_ptr(), s.data_ptr(), c.shape[0], c.shape[1], o.data_ptr()) for (c, s), o in zip(jobs, outs)]
+    nbytes = sum(dequant_bytes(c.shape[0], c.shape[1], False) for c, _ in jobs)
+
+    def run_block():
+        st = lean.stream()
+        for a in args_c:
+            if lib.fp8w_dequantize_block(*a, st):
+                raise RuntimeError("fp8w_dequantize_block failed")
+    g = graph_of(torch, run_block)
+    per, _ = timer.run(g.replay, max(10, args.steps // 4), min(args.warmup, 20))
+    out["dequantize_block_dense_layer_x6"] = dict(summarize(per, len(jobs), nbytes), calls_per_pass=len(jobs))
+    del g, jobs, outs, layer
+    mw = W.WORKLOADS[5].weights[0]
+    c0, e0 = fp8w.fp8w_quantize_mx(upload_bf16(torch, mw.bits(5)))
+    mj = [(c0, e0)] + [(c0.clone(), e0.clone()) for _ in range(15)]
+    mo = [torch.empty(c0.shape, dtype=torch.bfloat16, device="cuda") for _ in mj]
+    margs = [(c.data_ptr(), e.data_ptr(), mw.n, mw.k, o.data_ptr()) for (c, e), o in zip(mj, mo)]
+
+    def run_mx():
+        st = lean.stream()
+        for a in margs:
+            if lib.fp8w_dequantize_mx(*a, st):
+                raise RuntimeError("fp8w_dequantize_mx failed")
+    g = graph_of(torch, run_mx)
+    per, _ = timer.run(g.replay, max(10, args.steps // 4), min(args.warmup, 20))
+    out[f"dequantize_mx_{mw.n}x{mw.k}_x16"] = dict(summarize(per, len(mj), 16 * dequant_bytes(mw.n, mw.k, True)),
+                                                    calls_per_pass=len(mj))
+    log(f"dequant: {out}")
+    return {"dequantize": out}
+
+
+def bench_gemm(torch, fp8w, lean, timer, W, args, log):
+    """The large-M route (dequantize + rocBLAS bf16 GEMM) on the dense layer's
+    four weights at prefill M; TFLOP/s against the bf16 MFMA peak.  Beside it,
+    for context, torch.matmul (hipBLASLt) on the already-dequantized bf16
+    weight: the GEMM alone."""
+    lib = fp8w.lib()
+    layer = []
+    for w in W.WORKLOADS[4].weights:
+        c, s = fp8w.fp8w_quantize_block(upload_bf16(torch, w.bits(4)))
+        layer.append((w, c, s))
+    ws = torch.empty(max(int(lib.fp8w_gemm_workspace_bytes(c.shape[0], c.shape[1])) for _, c, _ in layer),
+                     dtype=torch.uint8, device="cuda")
+    out = {}
+    for m in (128, 512, 2048):
+        xs = {k: upload_bf16(torch, W.activation(4, m, k)) for k in (4096, 12288)}
+        calls = [(xs[w.k], c, s, torch.empty((m, w.n), dtype=torch.bfloat16, device="cuda")) for w, c, s in layer]
+        flops = sum(2.0 * m * w.n * w.k for w, _, _ in layer)
+        cargs = [(x.data_ptr(), m, c.data_ptr(), s.data_ptr(), c.shape[0], c.shape[1], y.data_ptr(),
+                  ws.data_ptr(), ws.numel()) for x, c, s, y in calls]
+
+        def run():
+            st = lean.stream()
+            for a in cargs:
+                if lib.fp8w_gemm_block(*a, st):
+                    raise RuntimeError("fp8w_gemm_block failed")
+        run()
+        torch.cuda.synchronize()
+        per, _ = timer.run(run, 20, 3, hold_ms=5.0)
+        med = statistics.median(per)
+        row = {"ms_per_layer": round(med, 4), "TFLOPs": round(flops / (med * 1e-3) / 1e12, 1),
+               "pct_of_bf16_peak": round(100 * flops / (med * 1e-3) / PEAK_BF16, 1)}
+        deq = [fp8w.fp8w_dequantize_block(c, s) for _, c, s in layer]
+        mm = [(x, d) for (x, _, _, _), d in zip(calls, deq)]
+
+        def run_mm():
+            for x, d in mm:
+                torch.matmul(x, d.t())
+        run_mm()
+        torch.cuda.synchronize()
+        per_mm, _ = timer.run(run_mm, 20, 3, hold_ms=5.0)
+        med_mm = statistics.median(per_mm)
+        row["bf16_gemm_alone"] = {"ms_per_layer": round(med_mm, 4),
+                                  "TFLOPs": round(flops / (med_mm * 1e-3) / 1e12, 1)}
+        out[f"m{m}"] = row
+        del deq, mm, calls
+    log(f"gemm route: {out}")
+    return {"gemm_route_dense_layer": out}
+
+
 def bench_single(torch, fp8w, lean, timer, W, args, log):
     w = W.WORKLOADS[1].weights[0]
     bf = upload_bf16(torch, w.bits(1))
@@ -498,7 +595,7 @@ def main():
         del state
         torch.cuda.empty_cache()
     for name, fn in (("lm_head", bench_lm_head), ("dense", bench_dense), ("mx", bench_mx),
-                     ("single", bench_single)):
+                     ("single", bench_single), ("dequant", bench_dequant), ("gemm", bench_gemm)):
         if name in rows_wanted:
             rows.update(fn(torch, fp8w, lean, timer, W, args, log))
             torch.cuda.empty_cache()

@@ -83,6 +83,9 @@ def _load():
             "oracle_round_bf16_array": (None, [P, I64, P]),
             "oracle_dequant_block_bf16": (ctypes.c_int, [P, P, I64, I64, P]),
             "oracle_dequant_mx_bf16": (ctypes.c_int, [P, P, I64, I64, P]),
+            "oracle_quantize_act_tensor": (ctypes.c_int, [P, I64, I64, P, P]),
+            "oracle_gemv_w8a8_block_f64": (ctypes.c_int, [P, ctypes.c_float, I64, P, P, I64, I64, P, I64, P, P]),
+            "oracle_gemv_w8a8_mx_f64": (ctypes.c_int, [P, ctypes.c_float, I64, P, P, I64, I64, P, I64, P, P]),
             "oracle_gemv_block_f64": (ctypes.c_int, [P, I64, P, P, I64, I64, P, I64, P, P]),
             "oracle_gemv_mx_f64": (ctypes.c_int, [P, I64, P, P, I64, I64, P, I64, P, P]),
         }
@@ -279,6 +282,53 @@ def gemv_mx_f64(x_bf16, codes, e8m0, rows=None):
     if e.shape != mx_scale_shape(*np.shape(codes)):
         raise ValueError("e8m0 shape mismatch")
     return _gemv(_load().oracle_gemv_mx_f64, x_bf16, codes, e, rows)
+
+
+# ------------------------------------------------------------- W8A8 path --
+
+def quantize_act_tensor(x_bf16: np.ndarray):
+    """Per-tensor activation quantization: (codes u8 [m,k], scale float)."""
+    x = _as(x_bf16, np.uint16)
+    m, k = x.shape
+    codes = np.empty((m, k), dtype=np.uint8)
+    scale = np.empty(1, dtype=np.float32)
+    _check(_load().oracle_quantize_act_tensor(_ptr(x), m, k, _ptr(codes), _ptr(scale)),
+           "quantize_act_tensor")
+    return codes, float(scale[0])
+
+
+def _gemv_w8a8(fn, xc, xs, codes, scale_arr, rows):
+    xq = _as(xc, np.uint8)
+    c = _as(codes, np.uint8)
+    m, k = xq.shape
+    n, k2 = c.shape
+    if k != k2:
+        raise ValueError("x codes and weight codes disagree on K")
+    if rows is None:
+        rows_arr, nrows, rows_ptr = None, n, None
+    else:
+        rows_arr = _as(np.asarray(rows, dtype=np.int64), np.int64)
+        nrows, rows_ptr = rows_arr.size, _ptr(rows_arr)
+    y = np.empty((m, nrows), dtype=np.float64)
+    bound = np.empty((m, nrows), dtype=np.float64)
+    _check(fn(_ptr(xq), float(xs), m, _ptr(c), _ptr(scale_arr), n, k, rows_ptr, nrows,
+              _ptr(y), _ptr(bound)), "gemv_w8a8")
+    return y, bound
+
+
+def gemv_w8a8_block_f64(x_codes, x_scale, codes, scales, rows=None):
+    """fp64 y = (dec(x_codes) * x_scale) . deq(W)^T and its magnitude bound."""
+    s = _as(scales, np.float32)
+    if s.shape != block_scale_shape(*np.shape(codes)):
+        raise ValueError("scale grid shape mismatch")
+    return _gemv_w8a8(_load().oracle_gemv_w8a8_block_f64, x_codes, x_scale, codes, s, rows)
+
+
+def gemv_w8a8_mx_f64(x_codes, x_scale, codes, e8m0, rows=None):
+    e = _as(e8m0, np.uint8)
+    if e.shape != mx_scale_shape(*np.shape(codes)):
+        raise ValueError("e8m0 shape mismatch")
+    return _gemv_w8a8(_load().oracle_gemv_w8a8_mx_f64, x_codes, x_scale, codes, e, rows)
 
 
 def gemv_tolerance(bound: np.ndarray) -> np.ndarray:

@@ -388,6 +388,80 @@ int oracle_dequant_mx_bf16(const uint8_t* codes, const uint8_t* e8m0, int64_t n,
   return ORACLE_OK;
 }
 
+/* ------------------------------------------- activation quantization -- */
+
+/* Dynamic per-tensor activation quantization ("feat(qwen4_exp): load-time
+ * per-tensor FP8 dense projections", What this adds: a per-tensor
+ * activation scale from an amax pass, then the cast; its perf(fp8)
+ * follow-up computes the same amax block-parallel, bit for bit): one scale
+ * for the whole x [m, k], by the rule of the block quantizer applied to a
+ * single tile -- amax over every element, scale = fl32(amax / 448) (1.0 when
+ * amax == 0), code = enc(fl32(x / scale)). */
+int oracle_quantize_act_tensor(const uint16_t* x, int64_t m, int64_t k, uint8_t* codes,
+                               float* scale) {
+  if (!x || !codes || !scale || m < 1 || k < 1) return ORACLE_ERR_ARG;
+  const int64_t count = m * k;
+  if (!all_finite(x, count)) return ORACLE_ERR_NONFINITE;
+  float amax = 0.0f;
+  for (int64_t i = 0; i < count; ++i) {
+    const float a = fabsf(bf16_to_float(x[i]));
+    if (a > amax) amax = a;
+  }
+  const float s = amax > 0.0f ? (float)(amax / (float)E4M3_MAX) : 1.0f;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < count; ++i) codes[i] = oracle_e4m3_encode(bf16_to_float(x[i]) / s);
+  *scale = s;
+  return ORACLE_OK;
+}
+
+/* W8A8 GEMV reference on a quantized activation: y[i][j] = sum_k
+ * (dec(xc[i][k]) * xs) * deq[j][k] and bound[i][j] = sum_k |.| |.|, in fp64,
+ * for the requested weight rows (all when rows is NULL); deq as above. */
+static int gemv_xq_f64(const uint8_t* xc, float xs, int64_t m, const uint8_t* codes,
+                       const float* block_scales, const uint8_t* e8m0, int64_t n, int64_t k,
+                       const int64_t* rows, int64_t nrows, double* y, double* bound) {
+  if (!xc || !codes || !y || m < 1 || n < 1 || k < 1) return ORACLE_ERR_ARG;
+  if (!rows) nrows = n;
+  for (int64_t j = 0; rows && j < nrows; ++j)
+    if (rows[j] < 0 || rows[j] >= n) return ORACLE_ERR_ARG;
+  const int64_t tiles_k = (k + TILE - 1) / TILE;
+  const int64_t groups = (k + MX_GROUP - 1) / MX_GROUP;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t j = 0; j < nrows; ++j) {
+    const int64_t r = rows ? rows[j] : j;
+    for (int64_t i = 0; i < m; ++i) {
+      double acc = 0.0, mag = 0.0;
+      for (int64_t c = 0; c < k; ++c) {
+        double d = oracle_e4m3_decode(codes[r * k + c]);
+        if (block_scales)
+          d *= (double)block_scales[(r / TILE) * tiles_k + c / TILE];
+        else
+          d = ldexp(d, (int)e8m0[r * groups + c / MX_GROUP] - 127);
+        const double xv = oracle_e4m3_decode(xc[i * k + c]) * (double)xs;
+        acc += xv * d;
+        mag += fabs(xv) * fabs(d);
+      }
+      y[i * nrows + j] = acc;
+      if (bound) bound[i * nrows + j] = mag;
+    }
+  }
+  return ORACLE_OK;
+}
+
+int oracle_gemv_w8a8_block_f64(const uint8_t* xc, float xs, int64_t m, const uint8_t* codes,
+                               const float* scales, int64_t n, int64_t k, const int64_t* rows,
+                               int64_t nrows, double* y, double* bound) {
+  if (!scales) return ORACLE_ERR_ARG;
+  return gemv_xq_f64(xc, xs, m, codes, scales, NULL, n, k, rows, nrows, y, bound);
+}
+
+int oracle_gemv_w8a8_mx_f64(const uint8_t* xc, float xs, int64_t m, const uint8_t* codes,
+                            const uint8_t* e8m0, int64_t n, int64_t k, const int64_t* rows,
+                            int64_t nrows, double* y, double* bound) {
+  if (!e8m0) return ORACLE_ERR_ARG;
+  return gemv_xq_f64(xc, xs, m, codes, NULL, e8m0, n, k, rows, nrows, y, bound);
+}
+
 /* -------------------------------------------------------------- GEMV -- */
 
 /* For each requested weight row n (rows[j], or every row when rows is NULL)

@@ -18,6 +18,9 @@ Functions carry the names of the C entry points:
 * ``fp8w_dequantize_block(codes, scales) -> w`` / ``fp8w_dequantize_mx``: bf16 [n,k]
 * ``fp8w_gemm_block(x, codes, scales) -> y`` / ``fp8w_gemm_mx``: any m, through
   dequantize + a dense bf16 GEMM (the large-M route)
+* ``fp8w_quantize_act(x) -> (x_codes, x_scale)`` and
+  ``fp8w_gemv_block_w8a8(x_codes, x_scale, codes, scales) -> y`` / ``_mx_w8a8``:
+  the W8A8 route (per-tensor fp8 activation, fp8 x fp8 matrix cores)
 
 plus ``Fp8Weight``, a format-tagged weight whose GEMV asserts the format
 before dispatch (a scale buffer of the wrong format cannot be detected by a
@@ -53,6 +56,10 @@ SIGNATURES = {
     "fp8w_gemm_workspace_bytes": (_I64, [_I64, _I64]),
     "fp8w_gemm_block": (_I, [_P, _I64, _P, _P, _I64, _I64, _P, _P, _I64, _P]),
     "fp8w_gemm_mx": (_I, [_P, _I64, _P, _P, _I64, _I64, _P, _P, _I64, _P]),
+    "fp8w_quantize_act_workspace_bytes": (_I64, []),
+    "fp8w_quantize_act": (_I, [_P, _I64, _I64, _P, _P, _P, _I64, _P]),
+    "fp8w_gemv_block_w8a8": (_I, [_P, _P, _I64, _P, _P, _I64, _I64, _P, _P]),
+    "fp8w_gemv_mx_w8a8": (_I, [_P, _P, _I64, _P, _P, _I64, _I64, _P, _P]),
     "fp8w_grouped_table_bytes": (_I64, [_I64]),
     "fp8w_grouped_plan_init": (_I, [_P, _I64, _I64, _I, _I, _P, _P]),
     "fp8w_gemv_grouped": (_I, [_P, _P]),
@@ -294,6 +301,66 @@ def fp8w_gemm_block(x, codes, scales, y=None, workspace=None, stream=None):
 def fp8w_gemm_mx(x, codes, e8m0, y=None, workspace=None, stream=None):
     torch = _torch()
     return _gemm("fp8w_gemm_mx", x, codes, e8m0, mx_scale_shape, torch.uint8, y, workspace, stream)
+
+
+# ------------------------------------------------------------------- W8A8 --
+
+def fp8w_quantize_act(x, codes=None, scale=None, workspace=None, stream=None):
+    """Per-tensor activation quantization: bf16 x [m,k] -> (e4m3 codes u8
+    [m,k], fp32 scale [1] on the device)."""
+    torch = _torch()
+    _require(x, _bf16_like(torch), "x", 2)
+    m, k = x.shape
+    if codes is None:
+        codes = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(int(lib().fp8w_quantize_act_workspace_bytes()), dtype=torch.uint8,
+                                device=x.device)
+    _require(codes, (torch.uint8,), "codes", 2)
+    _require(scale, (torch.float32,), "scale", 1)
+    _require(workspace, (torch.uint8,), "workspace", 1)
+    if tuple(codes.shape) != (m, k) or scale.numel() != 1:
+        raise ValueError("fp8w_quantize_act: codes must be [m, k] and scale one element")
+    _check(lib().fp8w_quantize_act(x.data_ptr(), m, k, codes.data_ptr(), scale.data_ptr(),
+                                   workspace.data_ptr(), workspace.numel(), _stream_handle(stream)),
+           "fp8w_quantize_act")
+    return codes, scale
+
+
+def _gemv_w8a8(fn_name, x_codes, x_scale, codes, scale_t, scale_shape, scale_dtype, y, stream):
+    torch = _torch()
+    _require(x_codes, (torch.uint8,), "x_codes", 2)
+    _require(x_scale, (torch.float32,), "x_scale", 1)
+    _require(codes, (torch.uint8,), "codes", 2)
+    _require(scale_t, (scale_dtype,), "scales", 2)
+    m, k = x_codes.shape
+    n, k2 = codes.shape
+    if k != k2:
+        raise ValueError(f"{fn_name}: x has K={k}, codes have K={k2}")
+    if tuple(scale_t.shape) != scale_shape(n, k):
+        raise ValueError(f"{fn_name}: scale grid {tuple(scale_t.shape)} != {scale_shape(n, k)}")
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=codes.device)
+    _require(y, _bf16_like(torch), "y", 2)
+    _check(getattr(lib(), fn_name)(x_codes.data_ptr(), x_scale.data_ptr(), m, codes.data_ptr(),
+                                   scale_t.data_ptr(), n, k, y.data_ptr(), _stream_handle(stream)),
+           fn_name)
+    return y
+
+
+def fp8w_gemv_block_w8a8(x_codes, x_scale, codes, scales, y=None, stream=None):
+    """y = x_scale * dec(x_codes) . deq(W)^T with fp8 x fp8 matrix cores."""
+    torch = _torch()
+    return _gemv_w8a8("fp8w_gemv_block_w8a8", x_codes, x_scale, codes, scales, block_scale_shape,
+                      torch.float32, y, stream)
+
+
+def fp8w_gemv_mx_w8a8(x_codes, x_scale, codes, e8m0, y=None, stream=None):
+    torch = _torch()
+    return _gemv_w8a8("fp8w_gemv_mx_w8a8", x_codes, x_scale, codes, e8m0, mx_scale_shape,
+                      torch.uint8, y, stream)
 
 
 # ---------------------------------------------------------------- grouped --

@@ -217,6 +217,70 @@ FP8W_API fp8w_status fp8w_gemm_mx(const uint16_t* x, int64_t m, const uint8_t* c
                                             static_cast<hipStream_t>(stream)));
 }
 
+// ---------------------------------------------------------------- W8A8 --
+
+FP8W_API int64_t fp8w_quantize_act_workspace_bytes(void) {
+  return (int64_t)fp8w::act_quant_partials() * 4;
+}
+
+FP8W_API fp8w_status fp8w_quantize_act(const uint16_t* x, int64_t m, int64_t k, uint8_t* codes,
+                                       float* scale, void* workspace, int64_t workspace_bytes,
+                                       void* stream) {
+  if (!x || !codes || !scale) return FP8W_ERR_NULL;
+  if (m < 1 || k < 1 || m > kMaxDim || k > kMaxDim) return FP8W_ERR_SHAPE;
+  const int64_t count = m * k;
+  const bool needs_ws = count > 16384;
+  if (needs_ws && !workspace) return FP8W_ERR_NULL;
+  if (needs_ws && workspace_bytes < fp8w_quantize_act_workspace_bytes()) return FP8W_ERR_SHAPE;
+  if (!aligned(x, 2) || !aligned(scale, 4) || (needs_ws && !aligned(workspace, 4))) return FP8W_ERR_ALIGN;
+  const Span out[3] = {{codes, (uint64_t)count}, {scale, 4},
+                       {workspace, needs_ws ? (uint64_t)fp8w_quantize_act_workspace_bytes() : 0}};
+  const Span in[1] = {{x, (uint64_t)count * 2}};
+  if (any_overlap(out, 3, in, 1)) return FP8W_ERR_OVERLAP;
+  return from_hip(fp8w::launch_quantize_act(x, count, codes, scale, static_cast<uint32_t*>(workspace),
+                                            static_cast<hipStream_t>(stream)));
+}
+
+namespace {
+
+fp8w_status check_w8a8(const uint8_t* xc, const float* xs, int64_t m, const uint8_t* codes,
+                       const void* scales, uint64_t scale_bytes, int64_t n, int64_t k,
+                       const uint16_t* y, bool block) {
+  if (!xc || !xs || !codes || !scales || !y) return FP8W_ERR_NULL;
+  if (m < 1 || m > FP8W_MAX_M || !dims_ok(n, k) || k < 16) return FP8W_ERR_SHAPE;
+  if (k % 16 != 0 || !aligned(xc, 16) || !aligned(xs, 4) || !aligned(codes, 16) ||
+      (block && !aligned(scales, 4)) || !aligned(y, 2))
+    return FP8W_ERR_ALIGN;
+  const Span out[1] = {{y, (uint64_t)m * n * 2}};
+  const Span in[4] = {{xc, (uint64_t)m * k}, {xs, 4}, {codes, (uint64_t)n * k}, {scales, scale_bytes}};
+  if (any_overlap(out, 1, in, 4)) return FP8W_ERR_OVERLAP;
+  return FP8W_OK;
+}
+
+}  // namespace
+
+FP8W_API fp8w_status fp8w_gemv_block_w8a8(const uint8_t* x_codes, const float* x_scale, int64_t m,
+                                          const uint8_t* codes, const float* scales, int64_t n,
+                                          int64_t k, uint16_t* y, void* stream) {
+  const fp8w_status st = check_w8a8(x_codes, x_scale, m, codes, scales, (uint64_t)block_count(n, k) * 4,
+                                    n, k, y, true);
+  if (st != FP8W_OK) return st;
+  const fp8w::GemvJob job{reinterpret_cast<const uint16_t*>(x_codes), codes, scales, y, (int32_t)n,
+                          (int32_t)k, 0, 0};
+  return from_hip(fp8w::launch_gemv_w8a8(job, x_scale, (int)m, false, static_cast<hipStream_t>(stream)));
+}
+
+FP8W_API fp8w_status fp8w_gemv_mx_w8a8(const uint8_t* x_codes, const float* x_scale, int64_t m,
+                                       const uint8_t* codes, const uint8_t* e8m0, int64_t n, int64_t k,
+                                       uint16_t* y, void* stream) {
+  const fp8w_status st = check_w8a8(x_codes, x_scale, m, codes, e8m0, (uint64_t)mx_count(n, k), n, k, y,
+                                    false);
+  if (st != FP8W_OK) return st;
+  const fp8w::GemvJob job{reinterpret_cast<const uint16_t*>(x_codes), codes, e8m0, y, (int32_t)n,
+                          (int32_t)k, 0, 0};
+  return from_hip(fp8w::launch_gemv_w8a8(job, x_scale, (int)m, true, static_cast<hipStream_t>(stream)));
+}
+
 // ------------------------------------------------------------- grouped --
 
 FP8W_API int64_t fp8w_grouped_table_bytes(int64_t count) {

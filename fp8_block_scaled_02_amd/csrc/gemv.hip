@@ -816,6 +816,171 @@ __global__ __launch_bounds__(kThreads) void k_gemv_mfma_direct(GemvJob j, int m_
   }
 }
 
+// ------------------------------------------------------------------ W8A8 --
+//
+// The activation arrives quantized: e4m3fn codes xc[m, k] with one fp32
+// scale xs for the whole tensor (per-tensor dynamic activation quantization,
+// "feat(qwen4_exp): load-time per-tensor FP8 dense projections", What this
+// adds), and y = xs * sum_kb scale_w(kb) * sum_{k in kb} dec(xc) dec(code).
+// fp8 x fp8 products go straight to v_mfma_scale_f32_16x16x128_f8f6f4: one
+// instruction per 16-row tile and 128-column block, no decode.  Its K layout
+// (measured on MI355X): byte p of lane (i, g) is K position 16g + p for
+// p < 16 and 64 + 16g + (p - 16) for p >= 16, so a lane's operand is the two
+// 16-byte pieces at 16g and 64 + 16g -- exactly a[b][0] and a[b][1] of the
+// panel transpose.  The instruction's per-lane e8m0 scale applies to row i
+// and the 32-column group 4b + g of that block -- the MX layout -- so MX weights
+// pass their scale bytes to the instruction; block weights pass 2^0 and
+// scale each block's partial sum.  Its products are exact; its internal
+// accumulation is a little coarser than fp32 (about 2^-14 of sum |p|
+// measured), far inside the GEMV bound.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+constexpr int kE8m0One = 127;
+
+template <bool MX>
+struct Panel8 {
+  uint4 v[4];     // as Panel: lane l holds row 4q + l/16, bytes 16*(l%16)
+  float s[2];     // block: scale of each 128-column block
+  int e[2];       // MX: e8m0 byte of row l%16, group 4*(block) + l/16
+};
+
+template <bool MX>
+__device__ __forceinline__ void panel8_issue(const GemvJob& j, int row0, int p, bool live, int nkb,
+                                             int groups, Panel8<MX>& r) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int col = p * kPanelCols + 16 * (lane & 15);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = row0 + 4 * q + (lane >> 4);
+    r.v[q] = make_uint4(0, 0, 0, 0);
+    if (live && row < j.n && col < j.k) r.v[q] = ld_stream_u4(j.codes, (size_t)row * j.k + col);
+  }
+  r.s[0] = r.s[1] = 0.0f;
+  r.e[0] = r.e[1] = kE8m0One;
+  if (MX) {
+    const int row = row0 + (lane & 15);
+    const uint8_t* __restrict__ e8 = static_cast<const uint8_t*>(j.scales);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int grp = 4 * (2 * p + b) + (lane >> 4);
+      if (live && row < j.n && grp < groups) r.e[b] = ld_global<uint8_t>(e8, (size_t)row * groups + grp);
+    }
+  } else if (live && row0 < j.n) {
+    const float* __restrict__ srow = static_cast<const float*>(j.scales) + (size_t)(row0 / kTile) * nkb;
+    r.s[0] = ld_global<float>(srow, (size_t)(2 * p) * 4);
+    if (2 * p + 1 < nkb) r.s[1] = ld_global<float>(srow, (size_t)(2 * p + 1) * 4);
+  }
+}
+
+__device__ __forceinline__ i32x8 join8(uint4 lo, uint4 hi) {
+  return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+// acc += the panel's products; get_b(t, b, B_lo, B_hi) supplies the x codes
+// of m-tile t for block b (the pieces at 16g and 64 + 16g).
+template <int MT, bool MX, typename GetB>
+__device__ __forceinline__ void panel8_mfma(const uint4 (&a)[2][2], const Panel8<MX>& p, GetB get_b,
+                                            f32x4 (&acc)[MT]) {
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const i32x8 A = join8(a[b][0], a[b][1]);
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      uint4 lo, hi;
+      get_b(t, b, lo, hi);
+      const i32x8 B = join8(lo, hi);
+      if (MX) {
+        acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, acc[t], 0, 0, 0, p.e[b], 0, kE8m0One);
+      } else {
+        const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            A, B, f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, kE8m0One, 0, kE8m0One);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) acc[t][jj] = __builtin_fmaf(p.s[b], part[jj], acc[t][jj]);
+      }
+    }
+  }
+}
+
+// Single call: one 16-row tile per workgroup, the 4 waves split its panels
+// (as k_gemv_mfma_direct); x codes from global memory.  xc is [m, k] e4m3,
+// xs a device pointer to the activation scale.
+template <int MT, bool MX>
+struct Direct8Slot {
+  Panel8<MX> p;
+  uint4 xb[MT][2][2];   // [m tile][block][piece at 16g / at 64 + 16g]
+};
+
+template <int MT, int D, bool MX>
+__global__ __launch_bounds__(kThreads) void k_gemv_w8a8_direct(GemvJob j, const float* __restrict__ xs,
+                                                               int m_rows) {
+  __shared__ __align__(16) unsigned char pb[kWaves * kPanelBytes];
+  __shared__ float red[kWaves * MT * 4 * kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int i = lane & 15, g = lane >> 4;
+  const int row0 = blockIdx.x * 16;
+  const int np = (j.k + kPanelCols - 1) / kPanelCols;
+  const int nkb = (j.k + kTile - 1) / kTile;
+  const int groups = (j.k + kGroup - 1) / kGroup;
+  const int nq = (np - wave + kWaves - 1) / kWaves;
+  const uint8_t* __restrict__ xc = reinterpret_cast<const uint8_t*>(j.x);
+
+  auto issue = [&](int q, Direct8Slot<MT, MX>& r) {
+    const int p = wave + kWaves * q;
+    const bool live = q < nq;
+    panel8_issue<MX>(j, row0, p, live, nkb, groups, r.p);
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kx = p * kPanelCols + 128 * b + 64 * h + 16 * g;
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const int m = 16 * t + i;
+          r.xb[t][b][h] = make_uint4(0, 0, 0, 0);
+          if (live && m < m_rows && kx < j.k) r.xb[t][b][h] = ld_global_u4(xc, (size_t)m * j.k + kx);
+        }
+      }
+  };
+
+  f32x4 acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  Direct8Slot<MT, MX> slot[D];
+#pragma unroll
+  for (int s = 0; s < D; ++s) issue(s, slot[s]);
+  for (int q0 = 0; q0 < nq; q0 += D) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      if (q0 + s < nq) {
+        uint4 a[2][2];
+        panel_to_a(slot[s].p.v, pb + wave * kPanelBytes, a);
+        panel8_mfma<MT, MX>(a, slot[s].p, [&](int t, int b, uint4& lo, uint4& hi) {
+          lo = slot[s].xb[t][b][0];
+          hi = slot[s].xb[t][b][1];
+        }, acc);
+      }
+      issue(q0 + s + D, slot[s]);
+    }
+  }
+
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) red[((wave * MT + t) * 4 + jj) * kWave + lane] = acc[t][jj];
+  __syncthreads();
+  if (wave == 0) {
+    const float x_scale = ld_global<float>(xs, 0);
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        acc[t][jj] = x_scale * (acc[t][jj] + red[((1 * MT + t) * 4 + jj) * kWave + lane] +
+                                red[((2 * MT + t) * 4 + jj) * kWave + lane] +
+                                red[((3 * MT + t) * 4 + jj) * kWave + lane]);
+    store_tile<MT>(j, row0, m_rows, acc);
+  }
+}
+
 // ------------------------------------------------------------ dispatch --
 //
 // One compiled variant per (route, M, single/grouped), any N and K:
@@ -994,6 +1159,19 @@ hipError_t gemv_mfma_stream_slots(int m, bool mx, int seg_cols, int* slots) {
   }
   *slots = cus * (per_cu > 0 ? per_cu : 1);
   return e;
+}
+
+hipError_t launch_gemv_w8a8(const GemvJob& job, const float* x_scale, int m, bool mx,
+                            hipStream_t stream) {
+  const dim3 grid((unsigned)((job.n + 15) / 16)), block(kThreads);
+  if (m <= 16) {
+    if (mx) hipLaunchKernelGGL((k_gemv_w8a8_direct<1, 2, true>), grid, block, 0, stream, job, x_scale, m);
+    else hipLaunchKernelGGL((k_gemv_w8a8_direct<1, 2, false>), grid, block, 0, stream, job, x_scale, m);
+  } else {
+    if (mx) hipLaunchKernelGGL((k_gemv_w8a8_direct<2, 2, true>), grid, block, 0, stream, job, x_scale, m);
+    else hipLaunchKernelGGL((k_gemv_w8a8_direct<2, 2, false>), grid, block, 0, stream, job, x_scale, m);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_gemv_mfma_stream(const GemvJob* table, int njobs, int64_t blocks, int64_t tiles,

@@ -36,6 +36,16 @@ hipError_t launch_gemm_dequant(const uint16_t* x, int64_t m, const uint8_t* code
                                const void* scales, bool mx, int64_t n, int64_t k, uint16_t* y,
                                uint16_t* w_bf16, hipStream_t stream);
 
+// W8A8 GEMV: job.x points at e4m3 activation codes [m, k]; x_scale is a
+// device pointer to the activation's fp32 scale.
+hipError_t launch_gemv_w8a8(const GemvJob& job, const float* x_scale, int m, bool mx,
+                            hipStream_t stream);
+// Per-tensor activation quantization; workspace holds act_quant_partials()
+// uint32 partial maxima.
+int act_quant_partials();
+hipError_t launch_quantize_act(const uint16_t* x, int64_t count, uint8_t* codes, float* scale,
+                               uint32_t* workspace, hipStream_t stream);
+
 // route: 1 = VALU (m <= 8), 2 = MFMA (m <= 32).
 int gemv_rows_per_block(int route, int m, bool grouped);
 hipError_t launch_gemv(const GemvJob& job, int m, bool mx, int route, hipStream_t stream);

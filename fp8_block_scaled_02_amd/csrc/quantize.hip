@@ -181,7 +181,111 @@ __global__ __launch_bounds__(kThreads) void k_quant_mx_any(const uint16_t* __res
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// ------------------------------------------------ activation (per tensor) --
+//
+// Dynamic per-tensor quantization of an activation x [m, k] ("feat(qwen4_exp):
+// load-time per-tensor FP8 dense projections", What this adds and its
+// perf(fp8) follow-up): one scale fl32(amax/448) for the whole tensor (1.0
+// when amax == 0) and codes enc(fl32(x/scale)).  Up to kActSmall elements
+// one workgroup does the amax pass and the cast in one launch; above that a
+// grid-strided pass writes one partial amax per workgroup (at most
+// kActPartials, their count a runtime argument) and the cast pass reduces
+// the partials in every workgroup.  The maximum is exact in any order, so
+// both paths give the same bits.
+constexpr int64_t kActSmall = 16384;
+constexpr int kActPartials = 256;
+constexpr int kActVec = 8;   // elements per 16-byte load
+
+// |x| maximum (as bf16 magnitude bits) over elements [i0 + stride*j ...) of
+// this thread, vectorized when `vec`.
+__device__ __forceinline__ uint32_t act_amax_range(const uint16_t* __restrict__ x, int64_t count,
+                                                   bool vec, int64_t first, int64_t stride) {
+  uint32_t amax = 0;
+  if (vec) {
+    for (int64_t i = first * kActVec; i < count; i += stride * kActVec) {
+      const uint4 v = ld_global_u4(x, (size_t)i * 2);
+      amax = abs_max_pair(v.x, amax);
+      amax = abs_max_pair(v.y, amax);
+      amax = abs_max_pair(v.z, amax);
+      amax = abs_max_pair(v.w, amax);
+    }
+  } else {
+    for (int64_t i = first; i < count; i += stride) {
+      const uint32_t a = ld_global<uint16_t>(x, (size_t)i * 2) & 0x7FFFu;
+      amax = a > amax ? a : amax;
+    }
+  }
+  return amax;
+}
+
+__device__ __forceinline__ void act_cast_range(const uint16_t* __restrict__ x, int64_t count, bool vec,
+                                               int64_t first, int64_t stride, float scale,
+                                               uint8_t* __restrict__ codes) {
+  if (vec) {
+    for (int64_t i = first * kActVec; i < count; i += stride * kActVec) {
+      const uint4 v = ld_global_u4(x, (size_t)i * 2);
+      st_global<u32x2>(codes, (size_t)i, u32x2{encode4_div(v.x, v.y, scale), encode4_div(v.z, v.w, scale)});
+    }
+  } else {
+    for (int64_t i = first; i < count; i += stride) {
+      const uint32_t b = ld_global<uint16_t>(x, (size_t)i * 2);
+      codes[i] = (uint8_t)e4m3_encode(bf16_lo(b) / scale);
+    }
+  }
+}
+
+__device__ __forceinline__ float act_scale(uint32_t amax_bits) {
+  const float amax = bf16_lo(amax_bits);
+  return amax > 0.0f ? amax / 448.0f : 1.0f;
+}
+
+__global__ __launch_bounds__(kThreads) void k_act_quant_small(const uint16_t* __restrict__ x, int64_t count,
+                                                              bool vec, uint8_t* __restrict__ codes,
+                                                              float* __restrict__ scale_out) {
+  const uint32_t amax = block_max_u32(act_amax_range(x, count, vec, threadIdx.x, kThreads));
+  const float scale = act_scale(amax);
+  act_cast_range(x, count, vec, threadIdx.x, kThreads, scale, codes);
+  if (threadIdx.x == 0) *scale_out = scale;
+}
+
+__global__ __launch_bounds__(kThreads) void k_act_amax_partial(const uint16_t* __restrict__ x, int64_t count,
+                                                               bool vec, uint32_t* __restrict__ partial) {
+  const uint32_t amax = block_max_u32(act_amax_range(
+      x, count, vec, (int64_t)blockIdx.x * kThreads + threadIdx.x, (int64_t)gridDim.x * kThreads));
+  if (threadIdx.x == 0) st_global<uint32_t>(partial, (size_t)blockIdx.x * 4, amax);
+}
+
+__global__ __launch_bounds__(kThreads) void k_act_quant_cast(const uint16_t* __restrict__ x, int64_t count,
+                                                             bool vec, const uint32_t* __restrict__ partial,
+                                                             int partials, uint8_t* __restrict__ codes,
+                                                             float* __restrict__ scale_out) {
+  const uint32_t p = (int)threadIdx.x < partials ? ld_global<uint32_t>(partial, (size_t)threadIdx.x * 4) : 0u;
+  const float scale = act_scale(block_max_u32(p));
+  act_cast_range(x, count, vec, (int64_t)blockIdx.x * kThreads + threadIdx.x, (int64_t)gridDim.x * kThreads,
+                 scale, codes);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = scale;
+}
+
 }  // namespace
+
+int act_quant_partials() { return kActPartials; }
+
+hipError_t launch_quantize_act(const uint16_t* x, int64_t count, uint8_t* codes, float* scale,
+                               uint32_t* workspace, hipStream_t stream) {
+  const bool vec = count % kActVec == 0 && aligned(x, 16) && aligned(codes, 8);
+  if (count <= kActSmall) {
+    hipLaunchKernelGGL(k_act_quant_small, dim3(1), dim3(kThreads), 0, stream, x, count, vec, codes, scale);
+    return hipGetLastError();
+  }
+  const int64_t want = (count + kActSmall - 1) / kActSmall;
+  const int partials = (int)(want < kActPartials ? want : kActPartials);
+  hipLaunchKernelGGL(k_act_amax_partial, dim3(partials), dim3(kThreads), 0, stream, x, count, vec, workspace);
+  const int64_t per_block = (int64_t)kThreads * kActVec * 4;
+  const int64_t cast_blocks = (count + per_block - 1) / per_block;
+  hipLaunchKernelGGL(k_act_quant_cast, dim3((unsigned)(cast_blocks < 65535 ? cast_blocks : 65535)),
+                     dim3(kThreads), 0, stream, x, count, vec, workspace, partials, codes, scale);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_block(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,
                                  float* scales, hipStream_t stream) {

@@ -8,6 +8,8 @@
  *   GEMV        y[m,n] = x[m,k] . deq(W)^T, bf16 in, bf16 out, fp32
  *               accumulate, m <= 32 (single calls or grouped)
  *   dequantize  codes + scales -> bf16 W[n,k]
+ *   W8A8        per-tensor activation quantization, and the GEMV on fp8
+ *               activations (fp8 x fp8 matrix-core products)
  *   GEMM        the same product for any m, through dequantize + a dense
  *               bf16 GEMM (the large-M / prefill route)
  *
@@ -201,6 +203,46 @@ fp8w_status fp8w_gemm_block(const uint16_t* x, int64_t m, const uint8_t* codes,
 fp8w_status fp8w_gemm_mx(const uint16_t* x, int64_t m, const uint8_t* codes,
                          const uint8_t* e8m0, int64_t n, int64_t k, uint16_t* y,
                          void* workspace, int64_t workspace_bytes, void* stream);
+
+/* --------------------------------------------------------------- W8A8 -- */
+
+/* Dynamic per-tensor activation quantization ("feat(qwen4_exp): load-time
+ * per-tensor FP8 dense projections", What this adds: an amax pass, then the
+ * cast; its perf(fp8) follow-up splits the amax block-parallel above 16384
+ * elements with the same result).  One scale for the whole x [m, k]:
+ * scale = amax/448 in fp32 (1.0 if amax == 0), codes = enc(x/scale) in
+ * fp32 -- the block quantizer's rule on a single tile covering the tensor.
+ *   x         : bf16 [m, k]                                  input
+ *   codes     : u8 [m, k]                                    output
+ *   scale     : f32 [1] (4-byte aligned)                     output
+ *   workspace : >= fp8w_quantize_act_workspace_bytes() bytes, 4-byte
+ *               aligned, when m * k > 16384 (partial maxima); may be NULL
+ *               otherwise
+ * Up to 16384 elements: one launch; above: two, the second reducing the
+ * partials itself.  Both paths give the same bits.
+ * Errors: NULL, SHAPE (also: workspace too small), ALIGN, OVERLAP, HIP. */
+int64_t fp8w_quantize_act_workspace_bytes(void);
+fp8w_status fp8w_quantize_act(const uint16_t* x, int64_t m, int64_t k, uint8_t* codes,
+                              float* scale, void* workspace, int64_t workspace_bytes,
+                              void* stream);
+
+/* W8A8 GEMV on a quantized activation:
+ *   y[i][j] = bf16_rne( x_scale * sum_k dec(x_codes[i][k]) * deq[j][k] )
+ * with fp8 x fp8 matrix-core products, block scales applied per 128-column
+ * block (MX scales inside the instruction), fp32 accumulation.
+ *   x_codes : u8 [m, k], 16-byte aligned      input (fp8w_quantize_act)
+ *   x_scale : f32 [1] on the device, 4-B aligned  input (read on the device)
+ *   codes, scales / e8m0, n, k, y : as fp8w_gemv_block / fp8w_gemv_mx
+ * Bound against the fp64 product of the same quantized operands:
+ * |y - y_ref| <= 2^-7 * sum_k |x_scale dec(x_codes)| |deq| + 1e-6.
+ * Requires 1 <= m <= 32, k >= 16, k % 16 == 0.
+ * Errors: NULL, SHAPE, ALIGN, OVERLAP, HIP. */
+fp8w_status fp8w_gemv_block_w8a8(const uint8_t* x_codes, const float* x_scale, int64_t m,
+                                 const uint8_t* codes, const float* scales, int64_t n,
+                                 int64_t k, uint16_t* y, void* stream);
+fp8w_status fp8w_gemv_mx_w8a8(const uint8_t* x_codes, const float* x_scale, int64_t m,
+                              const uint8_t* codes, const uint8_t* e8m0, int64_t n, int64_t k,
+                              uint16_t* y, void* stream);
 
 /* ------------------------------------------------------------- grouped -- */
 

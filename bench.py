@@ -57,7 +57,7 @@ def counted_traffic():
         return None
     return COUNTED_TRAFFIC["bytes_per_launch"]
 TILE, GROUP = 128, 32
-ALL_ROWS = ("proj", "quant", "lm_head", "dense", "mx", "single", "dequant", "gemm")
+ALL_ROWS = ("proj", "quant", "lm_head", "dense", "mx", "single", "dequant", "gemm", "w8a8")
 
 
 def parse():
@@ -496,6 +496,53 @@ def bench_gemm(torch, fp8w, lean, timer, W, args, log):
     return {"gemm_route_dense_layer": out}
 
 
+def bench_w8a8(torch, fp8w, lean, timer, W, args, state, log):
+    """The W8A8 route on the projection set at M = 1, 8, 16: 96 single
+    fp8w_gemv_block_w8a8 calls per pass (graph-captured), the activations
+    quantized outside the timed region as the pages' raw W8A8 rows are; the
+    per-tensor activation quantization timed on its own."""
+    wl, bf, codes, scales = state
+    lib = fp8w.lib()
+    out = {}
+    ws = torch.empty(int(lib.fp8w_quantize_act_workspace_bytes()), dtype=torch.uint8, device="cuda")
+    for m in (1, 8, 16):
+        xq = {}
+        for k in (2560, 3072):
+            x = upload_bf16(torch, W.activation(2, m, k))
+            xq[k] = fp8w.fp8w_quantize_act(x, workspace=ws)
+        ys = [torch.empty((m, c.shape[0]), dtype=torch.bfloat16, device="cuda") for c in codes]
+        cargs = [(xq[c.shape[1]][0].data_ptr(), xq[c.shape[1]][1].data_ptr(), m, c.data_ptr(), s.data_ptr(),
+                  c.shape[0], c.shape[1], y.data_ptr()) for c, s, y in zip(codes, scales, ys)]
+        nbytes = sum(gemv_bytes_block(m, c.shape[0], c.shape[1]) - m * c.shape[1] for c in codes)  # fp8 x
+
+        def run():
+            st = lean.stream()
+            for a in cargs:
+                if lib.fp8w_gemv_block_w8a8(*a, st):
+                    raise RuntimeError("fp8w_gemv_block_w8a8 failed")
+        g = graph_of(torch, run)
+        per, _ = timer.run(g.replay, max(10, args.steps // 4), min(args.warmup, 20))
+        out[f"m{m}"] = dict(summarize(per, len(cargs), nbytes), ms_per_pass=round(statistics.median(per), 4),
+                            launches_per_pass=len(cargs))
+        del g
+    for m, k in ((1, 2560), (16, 3072), (32, 12288)):
+        x = upload_bf16(torch, W.activation(2, m, k))
+        c = torch.empty((m, k), dtype=torch.uint8, device="cuda")
+        sc = torch.empty(1, dtype=torch.float32, device="cuda")
+        a = (x.data_ptr(), m, k, c.data_ptr(), sc.data_ptr(), ws.data_ptr(), ws.numel())
+
+        def q():
+            if lib.fp8w_quantize_act(*a, lean.stream()):
+                raise RuntimeError("fp8w_quantize_act failed")
+        g = graph_of(torch, lambda: [q() for _ in range(32)])
+        per, _ = timer.run(g.replay, 20, 3)
+        out[f"quantize_act_{m}x{k}_us"] = round(1e3 * statistics.median(per) / 32, 3)
+    out["pages_per_pass_ms_context"] = {"raw torch._scaled_mm per-tensor, RTX 6000 Ada": [1.94, 1.93, 1.92],
+                                        "per-tensor W8A8 wrapper": [3.62, 3.59, 3.58]}
+    log(f"w8a8: {out}")
+    return {"w8a8_projection_set": out}
+
+
 def bench_single(torch, fp8w, lean, timer, W, args, log):
     w = W.WORKLOADS[1].weights[0]
     bf = upload_bf16(torch, w.bits(1))
@@ -585,10 +632,12 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         log(f"calibration copy of {args.calibrate_copy_mib} MiB done")
-    if "proj" in rows_wanted or "quant" in rows_wanted:
+    if "proj" in rows_wanted or "quant" in rows_wanted or "w8a8" in rows_wanted:
         state = projection_set(torch, fp8w, W, log)
         if "quant" in rows_wanted:
             rows.update(bench_quant(torch, fp8w, lean, timer, W, args, state, log))
+        if "w8a8" in rows_wanted:
+            rows.update(bench_w8a8(torch, fp8w, lean, timer, W, args, state, log))
         if "proj" in rows_wanted:
             proj, headline = bench_proj(torch, fp8w, lean, timer, W, args, state, log)
             rows["projection_set"] = proj

@@ -188,9 +188,9 @@ inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintp
 // perf(fp8) follow-up): one scale fl32(amax/448) for the whole tensor (1.0
 // when amax == 0) and codes enc(fl32(x/scale)).  Up to kActSmall elements
 // one workgroup does the amax pass and the cast in one launch; above that a
-// grid-strided pass writes one partial amax per workgroup (at most
-// kActPartials, their count a runtime argument) and the cast pass reduces
-// the partials in every workgroup.  The maximum is exact in any order, so
+// grid-strided pass writes one partial amax per workgroup (about one 16-byte
+// vector per thread, at most kActPartials workgroups, their count a runtime
+// argument) and the cast pass reduces the partials in every workgroup.  The maximum is exact in any order, so
 // both paths give the same bits.
 constexpr int64_t kActSmall = 16384;
 constexpr int kActPartials = 256;
@@ -239,12 +239,38 @@ __device__ __forceinline__ float act_scale(uint32_t amax_bits) {
   return amax > 0.0f ? amax / 448.0f : 1.0f;
 }
 
+// One workgroup, count <= kActSmall.  Vector path: thread t holds vectors
+// t + 256*j (j < 8) in registers between the amax and the cast, so x is read
+// once; the scalar path (odd count or alignment) reads it twice.
 __global__ __launch_bounds__(kThreads) void k_act_quant_small(const uint16_t* __restrict__ x, int64_t count,
                                                               bool vec, uint8_t* __restrict__ codes,
                                                               float* __restrict__ scale_out) {
-  const uint32_t amax = block_max_u32(act_amax_range(x, count, vec, threadIdx.x, kThreads));
+  constexpr int kPer = (int)(kActSmall / kActVec / kThreads);   // 8 vectors per thread
+  if (vec) {
+    uint4 v[kPer];
+    uint32_t amax = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int64_t e = ((int64_t)j * kThreads + threadIdx.x) * kActVec;
+      v[j] = e < count ? ld_global_u4(x, (size_t)e * 2) : make_uint4(0, 0, 0, 0);
+      amax = abs_max_pair(v[j].x, amax);
+      amax = abs_max_pair(v[j].y, amax);
+      amax = abs_max_pair(v[j].z, amax);
+      amax = abs_max_pair(v[j].w, amax);
+    }
+    const float scale = act_scale(block_max_u32(amax));
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int64_t e = ((int64_t)j * kThreads + threadIdx.x) * kActVec;
+      if (e < count)
+        st_global<u32x2>(codes, (size_t)e, u32x2{encode4_div(v[j].x, v[j].y, scale), encode4_div(v[j].z, v[j].w, scale)});
+    }
+    if (threadIdx.x == 0) *scale_out = scale;
+    return;
+  }
+  const uint32_t amax = block_max_u32(act_amax_range(x, count, false, threadIdx.x, kThreads));
   const float scale = act_scale(amax);
-  act_cast_range(x, count, vec, threadIdx.x, kThreads, scale, codes);
+  act_cast_range(x, count, false, threadIdx.x, kThreads, scale, codes);
   if (threadIdx.x == 0) *scale_out = scale;
 }
 
@@ -277,10 +303,11 @@ hipError_t launch_quantize_act(const uint16_t* x, int64_t count, uint8_t* codes,
     hipLaunchKernelGGL(k_act_quant_small, dim3(1), dim3(kThreads), 0, stream, x, count, vec, codes, scale);
     return hipGetLastError();
   }
-  const int64_t want = (count + kActSmall - 1) / kActSmall;
+  // about one 16-byte vector per thread per pass: the passes are latency-bound
+  const int64_t want = (count + kThreads * kActVec - 1) / (kThreads * kActVec);
   const int partials = (int)(want < kActPartials ? want : kActPartials);
   hipLaunchKernelGGL(k_act_amax_partial, dim3(partials), dim3(kThreads), 0, stream, x, count, vec, workspace);
-  const int64_t per_block = (int64_t)kThreads * kActVec * 4;
+  const int64_t per_block = (int64_t)kThreads * kActVec;
   const int64_t cast_blocks = (count + per_block - 1) / per_block;
   hipLaunchKernelGGL(k_act_quant_cast, dim3((unsigned)(cast_blocks < 65535 ? cast_blocks : 65535)),
                      dim3(kThreads), 0, stream, x, count, vec, workspace, partials, codes, scale);

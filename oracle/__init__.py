@@ -84,6 +84,10 @@ def _load():
             "oracle_dequant_block_bf16": (ctypes.c_int, [P, P, I64, I64, P]),
             "oracle_dequant_mx_bf16": (ctypes.c_int, [P, P, I64, I64, P]),
             "oracle_quantize_act_tensor": (ctypes.c_int, [P, I64, I64, P, P]),
+            "oracle_quantize_block_bf16": (ctypes.c_int, [P, I64, I64, P, P]),
+            "oracle_quantize_row": (ctypes.c_int, [P, I64, I64, P, P]),
+            "oracle_dequant_format_bf16": (ctypes.c_int, [P, P, ctypes.c_int, I64, I64, P]),
+            "oracle_gemv_format_f64": (ctypes.c_int, [P, I64, P, P, ctypes.c_int, I64, I64, P, I64, P, P]),
             "oracle_gemv_w8a8_block_f64": (ctypes.c_int, [P, ctypes.c_float, I64, P, P, I64, I64, P, I64, P, P]),
             "oracle_gemv_w8a8_mx_f64": (ctypes.c_int, [P, ctypes.c_float, I64, P, P, I64, I64, P, I64, P, P]),
             "oracle_gemv_block_f64": (ctypes.c_int, [P, I64, P, P, I64, I64, P, I64, P, P]),
@@ -282,6 +286,93 @@ def gemv_mx_f64(x_bf16, codes, e8m0, rows=None):
     if e.shape != mx_scale_shape(*np.shape(codes)):
         raise ValueError("e8m0 shape mismatch")
     return _gemv(_load().oracle_gemv_mx_f64, x_bf16, codes, e, rows)
+
+
+# ---------------------------------------------------- other scale formats --
+
+FORMATS = {"block": 0, "mx": 1, "block_bf16": 2, "row": 3, "tensor": 4}
+
+
+def scale_shape(fmt: str, n: int, k: int):
+    return {"block": block_scale_shape(n, k), "mx": mx_scale_shape(n, k),
+            "block_bf16": block_scale_shape(n, k), "row": (n,), "tensor": (1,)}[fmt]
+
+
+def scale_dtype(fmt: str):
+    return {"block": np.float32, "mx": np.uint8, "block_bf16": np.uint16, "row": np.float32,
+            "tensor": np.float32}[fmt]
+
+
+def quantize_block_bf16(w_bf16: np.ndarray):
+    """(codes u8 [n,k], bf16 scale bits u16 [ceil(n/128), ceil(k/128)])."""
+    w = _as(w_bf16, np.uint16)
+    n, k = w.shape
+    codes = np.empty((n, k), dtype=np.uint8)
+    scales = np.empty(block_scale_shape(n, k), dtype=np.uint16)
+    _check(_load().oracle_quantize_block_bf16(_ptr(w), n, k, _ptr(codes), _ptr(scales)),
+           "quantize_block_bf16")
+    return codes, scales
+
+
+def quantize_row(w_bf16: np.ndarray):
+    """(codes u8 [n,k], fp32 scales [n])."""
+    w = _as(w_bf16, np.uint16)
+    n, k = w.shape
+    codes = np.empty((n, k), dtype=np.uint8)
+    scales = np.empty((n,), dtype=np.float32)
+    _check(_load().oracle_quantize_row(_ptr(w), n, k, _ptr(codes), _ptr(scales)), "quantize_row")
+    return codes, scales
+
+
+def quantize_format(w_bf16: np.ndarray, fmt: str):
+    """Quantize in any format: (codes, scales as the format stores them)."""
+    if fmt == "block":
+        return quantize_block(w_bf16)
+    if fmt == "mx":
+        return quantize_mx(w_bf16)
+    if fmt == "block_bf16":
+        return quantize_block_bf16(w_bf16)
+    if fmt == "row":
+        return quantize_row(w_bf16)
+    codes, scale = quantize_act_tensor(w_bf16)
+    return codes, np.array([scale], dtype=np.float32)
+
+
+def _format_scales(fmt, codes, scales):
+    s = _as(scales, scale_dtype(fmt))
+    if s.shape != scale_shape(fmt, *np.shape(codes)):
+        raise ValueError(f"{fmt}: scale shape {s.shape} != {scale_shape(fmt, *np.shape(codes))}")
+    return s
+
+
+def dequant_format_bf16(codes, scales, fmt: str) -> np.ndarray:
+    c = _as(codes, np.uint8)
+    s = _format_scales(fmt, c, scales)
+    n, k = c.shape
+    out = np.empty((n, k), dtype=np.uint16)
+    _check(_load().oracle_dequant_format_bf16(_ptr(c), _ptr(s), FORMATS[fmt], n, k, _ptr(out)),
+           "dequant_format_bf16")
+    return out
+
+
+def gemv_format_f64(x_bf16, codes, scales, fmt: str, rows=None):
+    x = _as(x_bf16, np.uint16)
+    c = _as(codes, np.uint8)
+    s = _format_scales(fmt, c, scales)
+    m, k = x.shape
+    n, k2 = c.shape
+    if k != k2:
+        raise ValueError("x and codes disagree on K")
+    if rows is None:
+        rows_arr, nrows, rows_ptr = None, n, None
+    else:
+        rows_arr = _as(np.asarray(rows, dtype=np.int64), np.int64)
+        nrows, rows_ptr = rows_arr.size, _ptr(rows_arr)
+    y = np.empty((m, nrows), dtype=np.float64)
+    bound = np.empty((m, nrows), dtype=np.float64)
+    _check(_load().oracle_gemv_format_f64(_ptr(x), m, _ptr(c), _ptr(s), FORMATS[fmt], n, k, rows_ptr,
+                                          nrows, _ptr(y), _ptr(bound)), "gemv_format")
+    return y, bound
 
 
 # ------------------------------------------------------------- W8A8 path --

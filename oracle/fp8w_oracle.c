@@ -280,6 +280,133 @@ int oracle_quantize_mx(const uint16_t* w, int64_t n, int64_t k,
   return ORACLE_OK;
 }
 
+/* ------------------------------------------------ other scale formats -- */
+
+/* Scale formats, numbered as the library's fp8w_format. */
+#define FMT_BLOCK 0      /* fp32 per 128x128 tile                 */
+#define FMT_MX 1         /* e8m0 per row and 32 columns           */
+#define FMT_BLOCK_BF16 2 /* bf16 per 128x128 tile                 */
+#define FMT_ROW 3        /* fp32 per row                          */
+#define FMT_TENSOR 4     /* one fp32 for the whole tensor         */
+
+uint16_t oracle_round_bf16(double v);
+
+/* Block quantization with a bf16 scale per 128x128 tile ("feat(quant):
+ * opt-in fp8-block QAT for the lm_head", How it works: fp8 plus a bf16
+ * 128-block scale).  The fp32 scale amax/448 is rounded to the nearest bf16
+ * (ties to even; 1.0 for an all-zero tile) and the codes divide by that
+ * stored scale, so that dequantizing with it inverts them; a scale rounded
+ * down can put amax/scale just above 448, which saturates. */
+int oracle_quantize_block_bf16(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,
+                               uint16_t* scales) {
+  if (!w || !codes || !scales || n < 1 || k < 1) return ORACLE_ERR_ARG;
+  if (!all_finite(w, n * k)) return ORACLE_ERR_NONFINITE;
+  const int64_t tiles_n = (n + TILE - 1) / TILE;
+  const int64_t tiles_k = (k + TILE - 1) / TILE;
+#pragma omp parallel for collapse(2) schedule(dynamic, 4)
+  for (int64_t ti = 0; ti < tiles_n; ++ti) {
+    for (int64_t tj = 0; tj < tiles_k; ++tj) {
+      const int64_t r0 = ti * TILE, r1 = (r0 + TILE < n) ? r0 + TILE : n;
+      const int64_t c0 = tj * TILE, c1 = (c0 + TILE < k) ? c0 + TILE : k;
+      float amax = 0.0f;
+      for (int64_t r = r0; r < r1; ++r)
+        for (int64_t c = c0; c < c1; ++c) {
+          const float a = fabsf(bf16_to_float(w[r * k + c]));
+          if (a > amax) amax = a;
+        }
+      const uint16_t sb = amax > 0.0f ? oracle_round_bf16((double)(amax / 448.0f)) : 0x3F80;
+      const float scale = bf16_to_float(sb);
+      scales[ti * tiles_k + tj] = sb;
+      for (int64_t r = r0; r < r1; ++r)
+        for (int64_t c = c0; c < c1; ++c)
+          codes[r * k + c] = oracle_e4m3_encode(bf16_to_float(w[r * k + c]) / scale);
+    }
+  }
+  return ORACLE_OK;
+}
+
+/* Per-row quantization ("quantize_fp8_bs.rs", Atlas weight_map: the per-ROW
+ * BF16 -> FP8 quantizer of the DFlash head; "feat(qwen4_exp): load-time
+ * per-tensor FP8 dense projections", Why: the per-row W8A16 route): the
+ * block rule with a 1 x k tile -- scale[r] = amax(row r)/448 in fp32 (1.0
+ * for an all-zero row), code = enc(w/scale[r]). */
+int oracle_quantize_row(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes, float* scales) {
+  if (!w || !codes || !scales || n < 1 || k < 1) return ORACLE_ERR_ARG;
+  if (!all_finite(w, n * k)) return ORACLE_ERR_NONFINITE;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n; ++r) {
+    float amax = 0.0f;
+    for (int64_t c = 0; c < k; ++c) {
+      const float a = fabsf(bf16_to_float(w[r * k + c]));
+      if (a > amax) amax = a;
+    }
+    const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+    scales[r] = scale;
+    for (int64_t c = 0; c < k; ++c) codes[r * k + c] = oracle_e4m3_encode(bf16_to_float(w[r * k + c]) / scale);
+  }
+  return ORACLE_OK;
+}
+
+/* The scale that multiplies dec(code[r][c]) in each format. */
+static double format_scale(int format, const void* scales, int64_t k, int64_t r, int64_t c) {
+  switch (format) {
+    case FMT_BLOCK:
+      return (double)((const float*)scales)[(r / TILE) * ((k + TILE - 1) / TILE) + c / TILE];
+    case FMT_MX:
+      return ldexp(1.0, (int)((const uint8_t*)scales)[r * ((k + MX_GROUP - 1) / MX_GROUP) + c / MX_GROUP] - 127);
+    case FMT_BLOCK_BF16:
+      return (double)bf16_to_float(((const uint16_t*)scales)[(r / TILE) * ((k + TILE - 1) / TILE) + c / TILE]);
+    case FMT_ROW:
+      return (double)((const float*)scales)[r];
+    case FMT_TENSOR:
+      return (double)((const float*)scales)[0];
+  }
+  return NAN;
+}
+
+static int format_ok(int format) { return format >= FMT_BLOCK && format <= FMT_TENSOR; }
+
+/* Dequantize to bf16 in any format: bf16_rne(fl32(dec(code) * scale)). */
+int oracle_dequant_format_bf16(const uint8_t* codes, const void* scales, int format, int64_t n,
+                               int64_t k, uint16_t* out) {
+  if (!codes || !scales || !out || n < 1 || k < 1 || !format_ok(format)) return ORACLE_ERR_ARG;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n; ++r)
+    for (int64_t c = 0; c < k; ++c) {
+      const float p = (float)(oracle_e4m3_decode(codes[r * k + c]) * format_scale(format, scales, k, r, c));
+      out[r * k + c] = oracle_round_bf16((double)p);
+    }
+  return ORACLE_OK;
+}
+
+/* GEMV reference in any format, fp64: y[i][j] = sum_k x[i][k] * deq[r][k]
+ * with deq = dec(code) * scale (the scale as format_scale gives it). */
+int oracle_gemv_format_f64(const uint16_t* x, int64_t m, const uint8_t* codes, const void* scales,
+                           int format, int64_t n, int64_t k, const int64_t* rows, int64_t nrows,
+                           double* y, double* bound) {
+  if (!x || !codes || !scales || !y || m < 1 || n < 1 || k < 1 || !format_ok(format))
+    return ORACLE_ERR_ARG;
+  if (!rows) nrows = n;
+  for (int64_t j = 0; rows && j < nrows; ++j)
+    if (rows[j] < 0 || rows[j] >= n) return ORACLE_ERR_ARG;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t j = 0; j < nrows; ++j) {
+    const int64_t r = rows ? rows[j] : j;
+    for (int64_t i = 0; i < m; ++i) {
+      double acc = 0.0, mag = 0.0;
+      for (int64_t c = 0; c < k; ++c) {
+        const double d = oracle_e4m3_decode(codes[r * k + c]) * format_scale(format, scales, k, r, c);
+        const double xv = (double)bf16_to_float(x[i * k + c]);
+        acc += xv * d;
+        mag += fabs(xv) * fabs(d);
+      }
+      y[i * nrows + j] = acc;
+      if (bound) bound[i * nrows + j] = mag;
+    }
+  }
+  return ORACLE_OK;
+}
+
 /* -------------------------------------------------------- dequantize -- */
 
 /* deq[n][k] = dec(code) * scale[n/128][k/128], exact in fp64 (4 + 24 bits). */

@@ -45,6 +45,12 @@ MX_GROUP = 32
 # name -> (restype, argtypes); the exported C ABI, mirrored from include/fp8w.h
 _P, _I64, _I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
 SIGNATURES = {
+    "fp8w_scale_bytes": (_I64, [_I, _I64, _I64]),
+    "fp8w_quantize": (_I, [_P, _I64, _I64, _I, _P, _P, _P, _I64, _P]),
+    "fp8w_dequantize": (_I, [_P, _P, _I, _I64, _I64, _P, _P]),
+    "fp8w_gemv": (_I, [_P, _I64, _P, _P, _I, _I64, _I64, _P, _I, _P]),
+    "fp8w_gemm": (_I, [_P, _I64, _P, _P, _I, _I64, _I64, _P, _P, _I64, _P]),
+    "fp8w_gemv_w8a8": (_I, [_P, _P, _I64, _P, _P, _I, _I64, _I64, _P, _P]),
     "fp8w_quantize_block": (_I, [_P, _I64, _I64, _P, _P, _P]),
     "fp8w_quantize_mx": (_I, [_P, _I64, _I64, _P, _P, _P]),
     "fp8w_gemv_block": (_I, [_P, _I64, _P, _P, _I64, _I64, _P, _P]),
@@ -69,7 +75,9 @@ SIGNATURES = {
     "fp8w_version": (_I, []),
 }
 
-FORMAT_BLOCK, FORMAT_MX = 0, 1
+FORMAT_BLOCK, FORMAT_MX, FORMAT_BLOCK_BF16, FORMAT_ROW, FORMAT_TENSOR = 0, 1, 2, 3, 4
+FORMAT_IDS = {"block": FORMAT_BLOCK, "mx": FORMAT_MX, "block_bf16": FORMAT_BLOCK_BF16,
+              "row": FORMAT_ROW, "tensor": FORMAT_TENSOR}
 
 
 class GemvDesc(ctypes.Structure):
@@ -155,7 +163,116 @@ def mx_scale_shape(n: int, k: int):
     return (n, (k + MX_GROUP - 1) // MX_GROUP)
 
 
+def scale_shape(fmt: str, n: int, k: int):
+    """Shape of the scale buffer of an [n, k] weight in format ``fmt``."""
+    return {"block": block_scale_shape(n, k), "mx": mx_scale_shape(n, k),
+            "block_bf16": block_scale_shape(n, k), "row": (n,), "tensor": (1,)}[fmt]
+
+
+def _scale_dtype(torch, fmt: str):
+    return {"block": torch.float32, "mx": torch.uint8, "block_bf16": torch.bfloat16,
+            "row": torch.float32, "tensor": torch.float32}[fmt]
+
+
+def _format_id(fmt: str) -> int:
+    if fmt not in FORMAT_IDS:
+        raise ValueError(f"unknown scale format {fmt!r}")
+    return FORMAT_IDS[fmt]
+
+
+def _check_scales(torch, fmt, scales, n, k, what):
+    _require(scales, (_scale_dtype(torch, fmt),), "scales", len(scale_shape(fmt, n, k)))
+    if tuple(scales.shape) != scale_shape(fmt, n, k):
+        raise ValueError(f"{what}: {fmt} scales must be {scale_shape(fmt, n, k)}, got {tuple(scales.shape)}")
+
+
 # --------------------------------------------------------------- quantize --
+
+def fp8w_quantize(w, fmt: str = "block", codes=None, scales=None, workspace=None, stream=None):
+    """bf16 W [n,k] -> (e4m3 codes u8 [n,k], scales in format ``fmt``)."""
+    torch = _torch()
+    _require(w, _bf16_like(torch), "w", 2)
+    n, k = w.shape
+    fid = _format_id(fmt)
+    if codes is None:
+        codes = torch.empty((n, k), dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty(scale_shape(fmt, n, k), dtype=_scale_dtype(torch, fmt), device=w.device)
+    if workspace is None and fmt == "tensor":
+        workspace = torch.empty(int(lib().fp8w_quantize_act_workspace_bytes()), dtype=torch.uint8,
+                                device=w.device)
+    _require(codes, (torch.uint8,), "codes", 2)
+    _check_scales(torch, fmt, scales, n, k, "fp8w_quantize")
+    ws_ptr, ws_n = (workspace.data_ptr(), workspace.numel()) if workspace is not None else (None, 0)
+    _check(lib().fp8w_quantize(w.data_ptr(), n, k, fid, codes.data_ptr(), scales.data_ptr(), ws_ptr,
+                               ws_n, _stream_handle(stream)), "fp8w_quantize")
+    return codes, scales
+
+
+def fp8w_dequantize(codes, scales, fmt: str = "block", w=None, stream=None):
+    torch = _torch()
+    _require(codes, (torch.uint8,), "codes", 2)
+    n, k = codes.shape
+    _check_scales(torch, fmt, scales, n, k, "fp8w_dequantize")
+    if w is None:
+        w = torch.empty((n, k), dtype=torch.bfloat16, device=codes.device)
+    _require(w, _bf16_like(torch), "w", 2)
+    _check(lib().fp8w_dequantize(codes.data_ptr(), scales.data_ptr(), _format_id(fmt), n, k,
+                                 w.data_ptr(), _stream_handle(stream)), "fp8w_dequantize")
+    return w
+
+
+def fp8w_gemv(x, codes, scales, fmt: str = "block", y=None, route=0, stream=None):
+    torch = _torch()
+    _require(x, _bf16_like(torch), "x", 2)
+    _require(codes, (torch.uint8,), "codes", 2)
+    m, k = x.shape
+    n = codes.shape[0]
+    _check_scales(torch, fmt, scales, n, k, "fp8w_gemv")
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    _require(y, _bf16_like(torch), "y", 2)
+    _check(lib().fp8w_gemv(x.data_ptr(), m, codes.data_ptr(), scales.data_ptr(), _format_id(fmt), n,
+                           k, y.data_ptr(), int(route), _stream_handle(stream)), "fp8w_gemv")
+    return y
+
+
+def fp8w_gemm(x, codes, scales, fmt: str = "block", y=None, workspace=None, stream=None):
+    torch = _torch()
+    _require(x, _bf16_like(torch), "x", 2)
+    _require(codes, (torch.uint8,), "codes", 2)
+    m, k = x.shape
+    n = codes.shape[0]
+    _check_scales(torch, fmt, scales, n, k, "fp8w_gemm")
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(int(lib().fp8w_gemm_workspace_bytes(n, k)), dtype=torch.uint8,
+                                device=x.device)
+    _require(y, _bf16_like(torch), "y", 2)
+    _check(lib().fp8w_gemm(x.data_ptr(), m, codes.data_ptr(), scales.data_ptr(), _format_id(fmt), n, k,
+                           y.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream_handle(stream)),
+           "fp8w_gemm")
+    return y
+
+
+def fp8w_gemv_w8a8(x_codes, x_scale, codes, scales, fmt: str = "block", y=None, stream=None):
+    torch = _torch()
+    _require(x_codes, (torch.uint8,), "x_codes", 2)
+    _require(x_scale, (torch.float32,), "x_scale", 1)
+    _require(codes, (torch.uint8,), "codes", 2)
+    m, k = x_codes.shape
+    n = codes.shape[0]
+    _check_scales(torch, fmt, scales, n, k, "fp8w_gemv_w8a8")
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=codes.device)
+    _require(y, _bf16_like(torch), "y", 2)
+    _check(lib().fp8w_gemv_w8a8(x_codes.data_ptr(), x_scale.data_ptr(), m, codes.data_ptr(),
+                                scales.data_ptr(), _format_id(fmt), n, k, y.data_ptr(),
+                                _stream_handle(stream)), "fp8w_gemv_w8a8")
+    return y
+
+
 
 def fp8w_quantize_block(w, codes=None, scales=None, stream=None):
     """bf16 W [n,k] -> (e4m3fn codes u8 [n,k], fp32 scales [ceil(n/128), ceil(k/128)])."""
@@ -377,9 +494,8 @@ class GroupedPlan:
         torch = _torch()
         if not (len(xs) == len(codes) == len(scales)) or not xs:
             raise ValueError("xs, codes and scales must be non-empty lists of equal length")
-        fmt_id = {"block": FORMAT_BLOCK, "mx": FORMAT_MX}[fmt]
-        sdt, sshape = ((torch.float32, block_scale_shape) if fmt_id == FORMAT_BLOCK
-                       else (torch.uint8, mx_scale_shape))
+        fmt_id = _format_id(fmt)
+        sdt, sshape = _scale_dtype(torch, fmt), (lambda n, k: scale_shape(fmt, n, k))
         m = int(xs[0].shape[0])
         if ys is None:
             ys = [torch.empty((m, int(c.shape[0])), dtype=torch.bfloat16, device=c.device) for c in codes]
@@ -387,7 +503,7 @@ class GroupedPlan:
         for i, (x, c, s, y) in enumerate(zip(xs, codes, scales, ys)):
             _require(x, _bf16_like(torch), "x", 2)
             _require(c, (torch.uint8,), "codes", 2)
-            _require(s, (sdt,), "scales", 2)
+            _require(s, (sdt,), "scales", len(sshape(1, 16)))
             _require(y, _bf16_like(torch), "y", 2)
             n, k = c.shape
             if x.shape[0] != m or x.shape[1] != k or tuple(s.shape) != sshape(n, k) \
@@ -426,12 +542,16 @@ def fp8w_gemv_grouped(plan: GroupedPlan, stream=None):
 
 # ----------------------------------------------------------- tagged weight --
 
-BLOCK128, MX32 = "block128", "mx32"
+BLOCK128, MX32, BLOCK128_BF16, ROW, TENSOR = "block128", "mx32", "block128_bf16", "row", "tensor"
+_FMT_OF = {BLOCK128: "block", MX32: "mx", BLOCK128_BF16: "block_bf16", ROW: "row", TENSOR: "tensor"}
 
 
 @dataclass
 class Fp8Weight:
-    """Quantized weight with its scale format fixed at construction."""
+    """Quantized weight with its scale format fixed at construction.
+
+    ``fmt`` is one of block128 (fp32 per 128x128 tile), mx32 (e8m0 per 32
+    along K), block128_bf16, row (fp32 per row) and tensor (one fp32)."""
     codes: object
     scales: object
     n: int
@@ -440,33 +560,32 @@ class Fp8Weight:
 
     @classmethod
     def quantize(cls, w, fmt: str = BLOCK128, stream=None) -> "Fp8Weight":
-        if fmt == BLOCK128:
-            c, s = fp8w_quantize_block(w, stream=stream)
-        elif fmt == MX32:
-            c, s = fp8w_quantize_mx(w, stream=stream)
-        else:
+        if fmt not in _FMT_OF:
             raise ValueError(f"unknown scale format {fmt!r}")
+        c, s = fp8w_quantize(w, _FMT_OF[fmt], stream=stream)
         return cls(c, s, int(w.shape[0]), int(w.shape[1]), fmt)
+
+    @property
+    def format(self) -> str:
+        """The C ABI's name of the scale format."""
+        return _FMT_OF[self.fmt]
 
     def check_format(self) -> None:
         """The single place that decides which scale layout a weight carries."""
         torch = _torch()
-        want = ((torch.float32, block_scale_shape(self.n, self.k)) if self.fmt == BLOCK128 else
-                (torch.uint8, mx_scale_shape(self.n, self.k)) if self.fmt == MX32 else None)
-        if want is None or self.scales.dtype != want[0] or tuple(self.scales.shape) != want[1]:
+        if self.fmt not in _FMT_OF:
+            raise ValueError(f"Fp8Weight: unknown format {self.fmt!r}")
+        f = _FMT_OF[self.fmt]
+        if self.scales.dtype != _scale_dtype(torch, f) or tuple(self.scales.shape) != scale_shape(f, self.n, self.k):
             raise ValueError(f"Fp8Weight: scales do not match format {self.fmt!r}")
 
     def gemv(self, x, y=None, route=ROUTE_AUTO, stream=None):
         self.check_format()
-        if self.fmt == BLOCK128:
-            return fp8w_gemv_block(x, self.codes, self.scales, y, route, stream)
-        return fp8w_gemv_mx(x, self.codes, self.scales, y, route, stream)
+        return fp8w_gemv(x, self.codes, self.scales, self.format, y, route, stream)
 
     def dequantize(self, w=None, stream=None):
         self.check_format()
-        if self.fmt == BLOCK128:
-            return fp8w_dequantize_block(self.codes, self.scales, w, stream)
-        return fp8w_dequantize_mx(self.codes, self.scales, w, stream)
+        return fp8w_dequantize(self.codes, self.scales, self.format, w, stream)
 
     def matmul(self, x, y=None, workspace=None, stream=None):
         """y = x . deq(W)^T for any m: the fused GEMV for m <= 32 (the
@@ -475,6 +594,8 @@ class Fp8Weight:
         self.check_format()
         if int(x.shape[0]) <= MAX_M:
             return self.gemv(x, y, ROUTE_AUTO, stream)
-        if self.fmt == BLOCK128:
-            return fp8w_gemm_block(x, self.codes, self.scales, y, workspace, stream)
-        return fp8w_gemm_mx(x, self.codes, self.scales, y, workspace, stream)
+        return fp8w_gemm(x, self.codes, self.scales, self.format, y, workspace, stream)
+
+    def gemv_w8a8(self, x_codes, x_scale, y=None, stream=None):
+        self.check_format()
+        return fp8w_gemv_w8a8(x_codes, x_scale, self.codes, self.scales, self.format, y, stream)

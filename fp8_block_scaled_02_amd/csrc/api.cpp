@@ -55,24 +55,46 @@ bool dims_ok(int64_t n, int64_t k) { return n >= 1 && k >= 1 && n <= kMaxDim && 
 int64_t block_count(int64_t n, int64_t k) { return ((n + 127) / 128) * ((k + 127) / 128); }
 int64_t mx_count(int64_t n, int64_t k) { return n * ((k + 31) / 32); }
 
+bool format_ok(int f) { return f >= FP8W_FORMAT_BLOCK && f <= FP8W_FORMAT_TENSOR; }
+
+// Bytes of the scale buffer of an [n, k] weight in `format`.
+uint64_t scale_bytes(int format, int64_t n, int64_t k) {
+  switch (format) {
+    case FP8W_FORMAT_BLOCK: return (uint64_t)block_count(n, k) * 4;
+    case FP8W_FORMAT_MX: return (uint64_t)mx_count(n, k);
+    case FP8W_FORMAT_BLOCK_BF16: return (uint64_t)block_count(n, k) * 2;
+    case FP8W_FORMAT_ROW: return (uint64_t)n * 4;
+    case FP8W_FORMAT_TENSOR: return 4;
+  }
+  return 0;
+}
+
+// Alignment the scale buffer of `format` needs (its element size).
+uintptr_t scale_align(int format) {
+  return format == FP8W_FORMAT_MX ? 1 : format == FP8W_FORMAT_BLOCK_BF16 ? 2 : 4;
+}
+
 fp8w_status from_hip(hipError_t e) { return e == hipSuccess ? FP8W_OK : FP8W_ERR_HIP; }
 
 fp8w_status check_gemv(const uint16_t* x, int64_t m, const uint8_t* codes, const void* scales,
-                       uint64_t scale_bytes, int64_t n, int64_t k, uint16_t* y, fp8w_route route,
-                       bool block) {
+                       int format, int64_t n, int64_t k, uint16_t* y, fp8w_route route) {
   if (!x || !codes || !scales || !y) return FP8W_ERR_NULL;
+  if (!format_ok(format)) return FP8W_ERR_UNSUPPORTED;
   if (m < 1 || m > FP8W_MAX_M || !dims_ok(n, k) || k < 16) return FP8W_ERR_SHAPE;
-  if (k % 16 != 0 || !aligned(x, 16) || !aligned(codes, 16) || (block && !aligned(scales, 4)) ||
+  if (k % 16 != 0 || !aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, scale_align(format)) ||
       !aligned(y, 2))
     return FP8W_ERR_ALIGN;
   if (route != FP8W_ROUTE_AUTO && route != FP8W_ROUTE_VALU && route != FP8W_ROUTE_MFMA)
     return FP8W_ERR_UNSUPPORTED;
   if (route == FP8W_ROUTE_VALU && m > kValuMaxM) return FP8W_ERR_UNSUPPORTED;
   const Span out[1] = {{y, (uint64_t)m * n * 2}};
-  const Span in[3] = {{x, (uint64_t)m * k * 2}, {codes, (uint64_t)n * k}, {scales, scale_bytes}};
+  const Span in[3] = {{x, (uint64_t)m * k * 2}, {codes, (uint64_t)n * k}, {scales, scale_bytes(format, n, k)}};
   if (any_overlap(out, 1, in, 3)) return FP8W_ERR_OVERLAP;
   return FP8W_OK;
 }
+
+fp8w_status gemv_any(const uint16_t* x, int64_t m, const uint8_t* codes, const void* scales, int format,
+                     int64_t n, int64_t k, uint16_t* y, fp8w_route route, void* stream);
 
 int resolve_route(fp8w_route route, int64_t m, bool grouped) {
   if (route == FP8W_ROUTE_VALU) return 1;
@@ -82,139 +104,151 @@ int resolve_route(fp8w_route route, int64_t m, bool grouped) {
 
 }  // namespace
 
+FP8W_API int64_t fp8w_scale_bytes(fp8w_format format, int64_t n, int64_t k) {
+  return (!format_ok(format) || n < 1 || k < 1) ? 0 : (int64_t)scale_bytes(format, n, k);
+}
+
+FP8W_API fp8w_status fp8w_quantize(const uint16_t* w, int64_t n, int64_t k, fp8w_format format,
+                                   uint8_t* codes, void* scales, void* workspace,
+                                   int64_t workspace_bytes, void* stream) {
+  if (!w || !codes || !scales) return FP8W_ERR_NULL;
+  if (!format_ok(format)) return FP8W_ERR_UNSUPPORTED;
+  if (!dims_ok(n, k)) return FP8W_ERR_SHAPE;
+  const bool needs_ws = format == FP8W_FORMAT_TENSOR && n * k > 16384;
+  if (needs_ws && !workspace) return FP8W_ERR_NULL;
+  if (needs_ws && workspace_bytes < fp8w_quantize_act_workspace_bytes()) return FP8W_ERR_SHAPE;
+  if (!aligned(w, 2) || !aligned(scales, scale_align(format)) || (needs_ws && !aligned(workspace, 4)))
+    return FP8W_ERR_ALIGN;
+  const Span out[3] = {{codes, (uint64_t)n * k}, {scales, scale_bytes(format, n, k)},
+                       {workspace, needs_ws ? (uint64_t)fp8w_quantize_act_workspace_bytes() : 0}};
+  const Span in[1] = {{w, (uint64_t)n * k * 2}};
+  if (any_overlap(out, 3, in, 1)) return FP8W_ERR_OVERLAP;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (format) {
+    case FP8W_FORMAT_BLOCK:
+      return from_hip(fp8w::launch_quantize_block(w, n, k, codes, static_cast<float*>(scales), s));
+    case FP8W_FORMAT_MX:
+      return from_hip(fp8w::launch_quantize_mx(w, n, k, codes, static_cast<uint8_t*>(scales), s));
+    case FP8W_FORMAT_BLOCK_BF16:
+      return from_hip(fp8w::launch_quantize_block_bf16(w, n, k, codes, static_cast<uint16_t*>(scales), s));
+    case FP8W_FORMAT_ROW:
+      return from_hip(fp8w::launch_quantize_row(w, n, k, codes, static_cast<float*>(scales), s));
+    default:
+      return from_hip(fp8w::launch_quantize_act(w, n * k, codes, static_cast<float*>(scales),
+                                                static_cast<uint32_t*>(workspace), s));
+  }
+}
+
 FP8W_API fp8w_status fp8w_quantize_block(const uint16_t* w, int64_t n, int64_t k,
                                          uint8_t* codes, float* scales, void* stream) {
-  if (!w || !codes || !scales) return FP8W_ERR_NULL;
-  if (!dims_ok(n, k)) return FP8W_ERR_SHAPE;
-  if (!aligned(w, 2) || !aligned(scales, 4)) return FP8W_ERR_ALIGN;
-  const Span out[2] = {{codes, (uint64_t)n * k}, {scales, (uint64_t)block_count(n, k) * 4}};
-  const Span in[1] = {{w, (uint64_t)n * k * 2}};
-  if (any_overlap(out, 2, in, 1)) return FP8W_ERR_OVERLAP;
-  return from_hip(fp8w::launch_quantize_block(w, n, k, codes, scales,
-                                              static_cast<hipStream_t>(stream)));
+  return fp8w_quantize(w, n, k, FP8W_FORMAT_BLOCK, codes, scales, nullptr, 0, stream);
 }
 
 FP8W_API fp8w_status fp8w_quantize_mx(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,
                                       uint8_t* e8m0, void* stream) {
-  if (!w || !codes || !e8m0) return FP8W_ERR_NULL;
-  if (!dims_ok(n, k)) return FP8W_ERR_SHAPE;
-  if (!aligned(w, 2)) return FP8W_ERR_ALIGN;
-  const Span out[2] = {{codes, (uint64_t)n * k}, {e8m0, (uint64_t)mx_count(n, k)}};
-  const Span in[1] = {{w, (uint64_t)n * k * 2}};
-  if (any_overlap(out, 2, in, 1)) return FP8W_ERR_OVERLAP;
-  return from_hip(
-      fp8w::launch_quantize_mx(w, n, k, codes, e8m0, static_cast<hipStream_t>(stream)));
+  return fp8w_quantize(w, n, k, FP8W_FORMAT_MX, codes, e8m0, nullptr, 0, stream);
+}
+
+namespace {
+
+fp8w_status gemv_any(const uint16_t* x, int64_t m, const uint8_t* codes, const void* scales, int format,
+                     int64_t n, int64_t k, uint16_t* y, fp8w_route route, void* stream) {
+  const fp8w_status st = check_gemv(x, m, codes, scales, format, n, k, y, route);
+  if (st != FP8W_OK) return st;
+  const fp8w::GemvJob job{x, codes, scales, y, (int32_t)n, (int32_t)k, 0, format};
+  return from_hip(fp8w::launch_gemv(job, (int)m, format == FP8W_FORMAT_MX, resolve_route(route, m, false),
+                                    static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+FP8W_API fp8w_status fp8w_gemv(const uint16_t* x, int64_t m, const uint8_t* codes, const void* scales,
+                               fp8w_format format, int64_t n, int64_t k, uint16_t* y, fp8w_route route,
+                               void* stream) {
+  return gemv_any(x, m, codes, scales, format, n, k, y, route, stream);
 }
 
 FP8W_API fp8w_status fp8w_gemv_block_route(const uint16_t* x, int64_t m, const uint8_t* codes,
                                            const float* scales, int64_t n, int64_t k,
                                            uint16_t* y, fp8w_route route, void* stream) {
-  const fp8w_status st =
-      check_gemv(x, m, codes, scales, (uint64_t)block_count(n, k) * 4, n, k, y, route, true);
-  if (st != FP8W_OK) return st;
-  const fp8w::GemvJob job{x, codes, scales, y, (int32_t)n, (int32_t)k, 0, 0};
-  return from_hip(fp8w::launch_gemv(job, (int)m, false, resolve_route(route, m, false),
-                                    static_cast<hipStream_t>(stream)));
+  return gemv_any(x, m, codes, scales, FP8W_FORMAT_BLOCK, n, k, y, route, stream);
 }
 
 FP8W_API fp8w_status fp8w_gemv_mx_route(const uint16_t* x, int64_t m, const uint8_t* codes,
                                         const uint8_t* e8m0, int64_t n, int64_t k, uint16_t* y,
                                         fp8w_route route, void* stream) {
-  const fp8w_status st =
-      check_gemv(x, m, codes, e8m0, (uint64_t)mx_count(n, k), n, k, y, route, false);
-  if (st != FP8W_OK) return st;
-  const fp8w::GemvJob job{x, codes, e8m0, y, (int32_t)n, (int32_t)k, 0, 0};
-  return from_hip(fp8w::launch_gemv(job, (int)m, true, resolve_route(route, m, false),
-                                    static_cast<hipStream_t>(stream)));
+  return gemv_any(x, m, codes, e8m0, FP8W_FORMAT_MX, n, k, y, route, stream);
 }
 
 FP8W_API fp8w_status fp8w_gemv_block(const uint16_t* x, int64_t m, const uint8_t* codes,
                                      const float* scales, int64_t n, int64_t k, uint16_t* y,
                                      void* stream) {
-  return fp8w_gemv_block_route(x, m, codes, scales, n, k, y, FP8W_ROUTE_AUTO, stream);
+  return gemv_any(x, m, codes, scales, FP8W_FORMAT_BLOCK, n, k, y, FP8W_ROUTE_AUTO, stream);
 }
 
 FP8W_API fp8w_status fp8w_gemv_mx(const uint16_t* x, int64_t m, const uint8_t* codes,
                                   const uint8_t* e8m0, int64_t n, int64_t k, uint16_t* y,
                                   void* stream) {
-  return fp8w_gemv_mx_route(x, m, codes, e8m0, n, k, y, FP8W_ROUTE_AUTO, stream);
+  return gemv_any(x, m, codes, e8m0, FP8W_FORMAT_MX, n, k, y, FP8W_ROUTE_AUTO, stream);
 }
 
 // ---------------------------------------------------------- dequantize --
 
-namespace {
-
-fp8w_status check_dequant(const uint8_t* codes, const void* scales, uint64_t scale_bytes,
-                          int64_t n, int64_t k, const uint16_t* w, bool block) {
+FP8W_API fp8w_status fp8w_dequantize(const uint8_t* codes, const void* scales, fp8w_format format,
+                                     int64_t n, int64_t k, uint16_t* w, void* stream) {
   if (!codes || !scales || !w) return FP8W_ERR_NULL;
+  if (!format_ok(format)) return FP8W_ERR_UNSUPPORTED;
   if (!dims_ok(n, k)) return FP8W_ERR_SHAPE;
-  if ((block && !aligned(scales, 4)) || !aligned(w, 2)) return FP8W_ERR_ALIGN;
+  if (!aligned(scales, scale_align(format)) || !aligned(w, 2)) return FP8W_ERR_ALIGN;
   const Span out[1] = {{w, (uint64_t)n * k * 2}};
-  const Span in[2] = {{codes, (uint64_t)n * k}, {scales, scale_bytes}};
+  const Span in[2] = {{codes, (uint64_t)n * k}, {scales, scale_bytes(format, n, k)}};
   if (any_overlap(out, 1, in, 2)) return FP8W_ERR_OVERLAP;
-  return FP8W_OK;
+  return from_hip(fp8w::launch_dequantize_format(codes, scales, format, n, k, w, static_cast<hipStream_t>(stream)));
 }
-
-}  // namespace
 
 FP8W_API fp8w_status fp8w_dequantize_block(const uint8_t* codes, const float* scales, int64_t n,
                                            int64_t k, uint16_t* w, void* stream) {
-  const fp8w_status st = check_dequant(codes, scales, (uint64_t)block_count(n, k) * 4, n, k, w, true);
-  if (st != FP8W_OK) return st;
-  return from_hip(fp8w::launch_dequantize_block(codes, scales, n, k, w, static_cast<hipStream_t>(stream)));
+  return fp8w_dequantize(codes, scales, FP8W_FORMAT_BLOCK, n, k, w, stream);
 }
 
 FP8W_API fp8w_status fp8w_dequantize_mx(const uint8_t* codes, const uint8_t* e8m0, int64_t n,
                                         int64_t k, uint16_t* w, void* stream) {
-  const fp8w_status st = check_dequant(codes, e8m0, (uint64_t)mx_count(n, k), n, k, w, false);
-  if (st != FP8W_OK) return st;
-  return from_hip(fp8w::launch_dequantize_mx(codes, e8m0, n, k, w, static_cast<hipStream_t>(stream)));
+  return fp8w_dequantize(codes, e8m0, FP8W_FORMAT_MX, n, k, w, stream);
 }
 
 // ---------------------------------------------------------------- GEMM --
-
-namespace {
-
-fp8w_status check_gemm(const uint16_t* x, int64_t m, const uint8_t* codes, const void* scales,
-                       uint64_t scale_bytes, int64_t n, int64_t k, const uint16_t* y,
-                       const void* workspace, int64_t workspace_bytes, bool block) {
-  if (!x || !codes || !scales || !y || !workspace) return FP8W_ERR_NULL;
-  if (m < 1 || m > kMaxDim || !dims_ok(n, k)) return FP8W_ERR_SHAPE;
-  if (workspace_bytes < n * k * 2) return FP8W_ERR_SHAPE;
-  if (!aligned(x, 2) || !aligned(y, 2) || !aligned(workspace, 16) || (block && !aligned(scales, 4)))
-    return FP8W_ERR_ALIGN;
-  const Span out[2] = {{y, (uint64_t)m * n * 2}, {workspace, (uint64_t)n * k * 2}};
-  const Span in[3] = {{x, (uint64_t)m * k * 2}, {codes, (uint64_t)n * k}, {scales, scale_bytes}};
-  if (any_overlap(out, 2, in, 3)) return FP8W_ERR_OVERLAP;
-  return FP8W_OK;
-}
-
-}  // namespace
 
 FP8W_API int64_t fp8w_gemm_workspace_bytes(int64_t n, int64_t k) {
   return (n < 1 || k < 1) ? 0 : n * k * 2;
 }
 
+FP8W_API fp8w_status fp8w_gemm(const uint16_t* x, int64_t m, const uint8_t* codes, const void* scales,
+                               fp8w_format format, int64_t n, int64_t k, uint16_t* y, void* workspace,
+                               int64_t workspace_bytes, void* stream) {
+  if (!x || !codes || !scales || !y || !workspace) return FP8W_ERR_NULL;
+  if (!format_ok(format)) return FP8W_ERR_UNSUPPORTED;
+  if (m < 1 || m > kMaxDim || !dims_ok(n, k)) return FP8W_ERR_SHAPE;
+  if (workspace_bytes < n * k * 2) return FP8W_ERR_SHAPE;
+  if (!aligned(x, 2) || !aligned(y, 2) || !aligned(workspace, 16) || !aligned(scales, scale_align(format)))
+    return FP8W_ERR_ALIGN;
+  const Span out[2] = {{y, (uint64_t)m * n * 2}, {workspace, (uint64_t)n * k * 2}};
+  const Span in[3] = {{x, (uint64_t)m * k * 2}, {codes, (uint64_t)n * k}, {scales, scale_bytes(format, n, k)}};
+  if (any_overlap(out, 2, in, 3)) return FP8W_ERR_OVERLAP;
+  return from_hip(fp8w::launch_gemm_dequant(x, m, codes, scales, format, n, k, y,
+                                            static_cast<uint16_t*>(workspace),
+                                            static_cast<hipStream_t>(stream)));
+}
+
 FP8W_API fp8w_status fp8w_gemm_block(const uint16_t* x, int64_t m, const uint8_t* codes,
                                      const float* scales, int64_t n, int64_t k, uint16_t* y,
                                      void* workspace, int64_t workspace_bytes, void* stream) {
-  const fp8w_status st = check_gemm(x, m, codes, scales, (uint64_t)block_count(n, k) * 4, n, k, y,
-                                    workspace, workspace_bytes, true);
-  if (st != FP8W_OK) return st;
-  return from_hip(fp8w::launch_gemm_dequant(x, m, codes, scales, false, n, k, y,
-                                            static_cast<uint16_t*>(workspace),
-                                            static_cast<hipStream_t>(stream)));
+  return fp8w_gemm(x, m, codes, scales, FP8W_FORMAT_BLOCK, n, k, y, workspace, workspace_bytes, stream);
 }
 
 FP8W_API fp8w_status fp8w_gemm_mx(const uint16_t* x, int64_t m, const uint8_t* codes,
                                   const uint8_t* e8m0, int64_t n, int64_t k, uint16_t* y,
                                   void* workspace, int64_t workspace_bytes, void* stream) {
-  const fp8w_status st = check_gemm(x, m, codes, e8m0, (uint64_t)mx_count(n, k), n, k, y, workspace,
-                                    workspace_bytes, false);
-  if (st != FP8W_OK) return st;
-  return from_hip(fp8w::launch_gemm_dequant(x, m, codes, e8m0, true, n, k, y,
-                                            static_cast<uint16_t*>(workspace),
-                                            static_cast<hipStream_t>(stream)));
+  return fp8w_gemm(x, m, codes, e8m0, FP8W_FORMAT_MX, n, k, y, workspace, workspace_bytes, stream);
 }
 
 // ---------------------------------------------------------------- W8A8 --
@@ -241,44 +275,35 @@ FP8W_API fp8w_status fp8w_quantize_act(const uint16_t* x, int64_t m, int64_t k, 
                                             static_cast<hipStream_t>(stream)));
 }
 
-namespace {
-
-fp8w_status check_w8a8(const uint8_t* xc, const float* xs, int64_t m, const uint8_t* codes,
-                       const void* scales, uint64_t scale_bytes, int64_t n, int64_t k,
-                       const uint16_t* y, bool block) {
-  if (!xc || !xs || !codes || !scales || !y) return FP8W_ERR_NULL;
+FP8W_API fp8w_status fp8w_gemv_w8a8(const uint8_t* x_codes, const float* x_scale, int64_t m,
+                                    const uint8_t* codes, const void* scales, fp8w_format format,
+                                    int64_t n, int64_t k, uint16_t* y, void* stream) {
+  if (!x_codes || !x_scale || !codes || !scales || !y) return FP8W_ERR_NULL;
+  if (!format_ok(format)) return FP8W_ERR_UNSUPPORTED;
   if (m < 1 || m > FP8W_MAX_M || !dims_ok(n, k) || k < 16) return FP8W_ERR_SHAPE;
-  if (k % 16 != 0 || !aligned(xc, 16) || !aligned(xs, 4) || !aligned(codes, 16) ||
-      (block && !aligned(scales, 4)) || !aligned(y, 2))
+  if (k % 16 != 0 || !aligned(x_codes, 16) || !aligned(x_scale, 4) || !aligned(codes, 16) ||
+      !aligned(scales, scale_align(format)) || !aligned(y, 2))
     return FP8W_ERR_ALIGN;
   const Span out[1] = {{y, (uint64_t)m * n * 2}};
-  const Span in[4] = {{xc, (uint64_t)m * k}, {xs, 4}, {codes, (uint64_t)n * k}, {scales, scale_bytes}};
+  const Span in[4] = {{x_codes, (uint64_t)m * k}, {x_scale, 4}, {codes, (uint64_t)n * k},
+                      {scales, scale_bytes(format, n, k)}};
   if (any_overlap(out, 1, in, 4)) return FP8W_ERR_OVERLAP;
-  return FP8W_OK;
+  const fp8w::GemvJob job{reinterpret_cast<const uint16_t*>(x_codes), codes, scales, y, (int32_t)n,
+                          (int32_t)k, 0, format};
+  return from_hip(fp8w::launch_gemv_w8a8(job, x_scale, (int)m, format == FP8W_FORMAT_MX,
+                                         static_cast<hipStream_t>(stream)));
 }
-
-}  // namespace
 
 FP8W_API fp8w_status fp8w_gemv_block_w8a8(const uint8_t* x_codes, const float* x_scale, int64_t m,
                                           const uint8_t* codes, const float* scales, int64_t n,
                                           int64_t k, uint16_t* y, void* stream) {
-  const fp8w_status st = check_w8a8(x_codes, x_scale, m, codes, scales, (uint64_t)block_count(n, k) * 4,
-                                    n, k, y, true);
-  if (st != FP8W_OK) return st;
-  const fp8w::GemvJob job{reinterpret_cast<const uint16_t*>(x_codes), codes, scales, y, (int32_t)n,
-                          (int32_t)k, 0, 0};
-  return from_hip(fp8w::launch_gemv_w8a8(job, x_scale, (int)m, false, static_cast<hipStream_t>(stream)));
+  return fp8w_gemv_w8a8(x_codes, x_scale, m, codes, scales, FP8W_FORMAT_BLOCK, n, k, y, stream);
 }
 
 FP8W_API fp8w_status fp8w_gemv_mx_w8a8(const uint8_t* x_codes, const float* x_scale, int64_t m,
                                        const uint8_t* codes, const uint8_t* e8m0, int64_t n, int64_t k,
                                        uint16_t* y, void* stream) {
-  const fp8w_status st = check_w8a8(x_codes, x_scale, m, codes, e8m0, (uint64_t)mx_count(n, k), n, k, y,
-                                    false);
-  if (st != FP8W_OK) return st;
-  const fp8w::GemvJob job{reinterpret_cast<const uint16_t*>(x_codes), codes, e8m0, y, (int32_t)n,
-                          (int32_t)k, 0, 0};
-  return from_hip(fp8w::launch_gemv_w8a8(job, x_scale, (int)m, true, static_cast<hipStream_t>(stream)));
+  return fp8w_gemv_w8a8(x_codes, x_scale, m, codes, e8m0, FP8W_FORMAT_MX, n, k, y, stream);
 }
 
 // ------------------------------------------------------------- grouped --
@@ -292,16 +317,16 @@ FP8W_API fp8w_status fp8w_grouped_plan_init(const fp8w_gemv_desc* descs, int64_t
                                             void* device_table, fp8w_grouped_plan* plan) {
   if (!descs || !device_table || !plan) return FP8W_ERR_NULL;
   if (count < 1 || count > kMaxDim) return FP8W_ERR_SHAPE;
-  if (format != FP8W_FORMAT_BLOCK && format != FP8W_FORMAT_MX) return FP8W_ERR_UNSUPPORTED;
+  if (!format_ok(format)) return FP8W_ERR_UNSUPPORTED;
   if (!aligned(device_table, 16)) return FP8W_ERR_ALIGN;
-  const bool block = format == FP8W_FORMAT_BLOCK;
+  const bool mx = format == FP8W_FORMAT_MX;
   std::vector<Span> ins, outs;
   ins.reserve(3 * count);
   outs.reserve(count);
   for (int64_t i = 0; i < count; ++i) {
     const fp8w_gemv_desc& d = descs[i];
-    const uint64_t sb = block ? (uint64_t)block_count(d.n, d.k) * 4 : (uint64_t)mx_count(d.n, d.k);
-    const fp8w_status st = check_gemv(d.x, m, d.codes, d.scales, sb, d.n, d.k, d.y, route, block);
+    const uint64_t sb = scale_bytes(format, d.n, d.k);
+    const fp8w_status st = check_gemv(d.x, m, d.codes, d.scales, format, d.n, d.k, d.y, route);
     if (st != FP8W_OK) return st;
     ins.push_back({d.x, (uint64_t)m * d.k * 2});
     ins.push_back({d.codes, (uint64_t)d.n * d.k});
@@ -325,7 +350,7 @@ FP8W_API fp8w_status fp8w_grouped_plan_init(const fp8w_gemv_desc* descs, int64_t
   for (int64_t i = 0; i < count; ++i) {
     const fp8w_gemv_desc& d = descs[i];
     table[i] = fp8w::GemvJob{d.x, d.codes, d.scales, d.y, (int32_t)d.n, (int32_t)d.k,
-                             (int32_t)tiles, 0};
+                             (int32_t)tiles, (int32_t)format};
     tiles += (d.n + rows - 1) / rows;
     if (tiles > kMaxDim) return FP8W_ERR_SHAPE;
   }
@@ -335,7 +360,7 @@ FP8W_API fp8w_status fp8w_grouped_plan_init(const fp8w_gemv_desc* descs, int64_t
     int slots = 0;
     int64_t want = 0;
     if (valu_stream) {
-      if (fp8w::gemv_stream_slots(!block, &slots) != hipSuccess) return FP8W_ERR_HIP;
+      if (fp8w::gemv_stream_slots(mx, &slots) != hipSuccess) return FP8W_ERR_HIP;
       // about sixteen workgroups per resident slot (runs of ~3 tiles on the
       // 48-layer projection set): the hardware dispatcher then balances the
       // runs over the CUs, where long runs left a tail of late workgroups
@@ -343,7 +368,7 @@ FP8W_API fp8w_status fp8w_grouped_plan_init(const fp8w_gemv_desc* descs, int64_t
       want = (int64_t)16 * slots;
     } else {
       seg_cols = fp8w::gemv_mfma_stream_seg_cols((int)m, max_k);
-      if (fp8w::gemv_mfma_stream_slots((int)m, !block, seg_cols, &slots) != hipSuccess)
+      if (fp8w::gemv_mfma_stream_slots((int)m, mx, seg_cols, &slots) != hipSuccess)
         return FP8W_ERR_HIP;
       want = (int64_t)8 * slots;
     }
@@ -365,7 +390,7 @@ FP8W_API fp8w_status fp8w_gemv_grouped(const fp8w_grouped_plan* plan, void* stre
   if (plan->count < 1 || plan->m < 1 || plan->m > FP8W_MAX_M || !route_ok || plan->blocks < 1 ||
       plan->blocks > kMaxDim || plan->tiles < plan->blocks || plan->tiles > kMaxDim ||
       plan->tiles_per_block < 0 ||
-      (plan->format != FP8W_FORMAT_BLOCK && plan->format != FP8W_FORMAT_MX))
+      !format_ok(plan->format))
     return FP8W_ERR_SHAPE;
   const bool mx = plan->format == FP8W_FORMAT_MX;
   const hipStream_t s = static_cast<hipStream_t>(stream);

@@ -52,10 +52,9 @@ hipError_t blas_gemm(const uint16_t* x, int m, const uint16_t* w, int n, int k, 
 }  // namespace
 
 hipError_t launch_gemm_dequant(const uint16_t* x, int64_t m, const uint8_t* codes,
-                               const void* scales, bool mx, int64_t n, int64_t k, uint16_t* y,
+                               const void* scales, int format, int64_t n, int64_t k, uint16_t* y,
                                uint16_t* w_bf16, hipStream_t stream) {
-  hipError_t e = mx ? launch_dequantize_mx(codes, static_cast<const uint8_t*>(scales), n, k, w_bf16, stream)
-                    : launch_dequantize_block(codes, static_cast<const float*>(scales), n, k, w_bf16, stream);
+  hipError_t e = launch_dequantize_format(codes, scales, format, n, k, w_bf16, stream);
   if (e != hipSuccess) return e;
   return blas_gemm(x, (int)m, w_bf16, (int)n, (int)k, y, stream);
 }

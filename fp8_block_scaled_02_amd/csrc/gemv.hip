@@ -76,6 +76,22 @@ __device__ __forceinline__ bf16x2 cvt_scaled(uint32_t d, float s) {
 
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t d) { return __builtin_bit_cast(bf16x2, d); }
 
+// Non-MX scale formats.  The scale of 128-column block kb for the 128-row
+// block holding row0 (fp32 or bf16 grid), or 1 when the format scales whole
+// rows or the whole weight -- those multiply each output once, at the end.
+// The format is uniform across a launch, so the branches cost nothing.
+__device__ __forceinline__ float block_scale(const GemvJob& j, int row0, int kb, int nkb) {
+  const size_t at = (size_t)(row0 / kTile) * nkb + kb;
+  if (j.format == kFmtBlock) return ld_global<float>(j.scales, at * 4);
+  if (j.format == kFmtBlockBf16) return bf16_lo(ld_global<uint16_t>(j.scales, at * 2));
+  return 1.0f;
+}
+__device__ __forceinline__ float output_scale(const GemvJob& j, int row) {
+  if (j.format == kFmtRow) return ld_global<float>(j.scales, (size_t)row * 4);
+  if (j.format == kFmtTensor) return ld_global<float>(j.scales, 0);
+  return 1.0f;
+}
+
 // sum_j x[j] * dec(code[j]) over one 16-byte chunk (16 codes, 16 bf16 x).
 __device__ __forceinline__ float dot16(const bf16x2 (&w)[8], uint4 x0, uint4 x1) {
   float p = 0.0f;
@@ -163,6 +179,7 @@ __device__ __forceinline__ void find_job(const GemvJob& arg, const GemvJob* __re
   job.n = ld_global<int32_t>(jobs, row + offsetof(GemvJob, n));
   job.k = ld_global<int32_t>(jobs, row + offsetof(GemvJob, k));
   job.item0 = ld_global<int32_t>(jobs, row + offsetof(GemvJob, item0));
+  job.format = ld_global<int32_t>(jobs, row + offsetof(GemvJob, format));
   tile = b - job.item0;
 }
 
@@ -234,9 +251,6 @@ __global__ __launch_bounds__(kThreads) void k_gemv_valu(GemvJob arg, const GemvJ
   const int row0 = tile * S::kRows + wave * R;
   const int tiles_k = (j.k + kTile - 1) / kTile;
   const int groups = (j.k + kGroup - 1) / kGroup;
-  const float* __restrict__ srow =
-      MX ? nullptr
-         : static_cast<const float*>(j.scales) + (size_t)(tile * S::kRows / kTile) * tiles_k;
 
   float acc[R][M];
 #pragma unroll
@@ -254,7 +268,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv_valu(GemvJob arg, const GemvJ
     stage_x(j.x, M, M, j.k, seg0, len, len, xs, S::kSeg);
     if (!MX) {
       const int nkb = (len + kTile - 1) / kTile;
-      if ((int)threadIdx.x < nkb) ss[threadIdx.x] = ld_global<float>(srow, (size_t)(seg0 / kTile + threadIdx.x) * 4);
+      if ((int)threadIdx.x < nkb) ss[threadIdx.x] = block_scale(j, tile * S::kRows, seg0 / kTile + threadIdx.x, tiles_k);
     }
     __syncthreads();
 
@@ -293,7 +307,8 @@ __global__ __launch_bounds__(kThreads) void k_gemv_valu(GemvJob arg, const GemvJ
       const int f = 4 * q + (lane >> 4);   // value index r * M + m held by this row
       const int r = f / M, m = f % M;
       if (f < R * M && row0 + r < j.n)
-        st_global<uint16_t>(j.y, ((size_t)m * j.n + row0 + r) * 2, (uint16_t)f32_to_bf16_rne(sums.g[q]));
+        st_global<uint16_t>(j.y, ((size_t)m * j.n + row0 + r) * 2,
+                            (uint16_t)f32_to_bf16_rne(sums.g[q] * output_scale(j, row0 + r)));
     }
   }
 }
@@ -320,6 +335,7 @@ __device__ __forceinline__ void load_job_row(const GemvJob* __restrict__ jobs, i
   job.n = ld_global<int32_t>(jobs, row + offsetof(GemvJob, n));
   job.k = ld_global<int32_t>(jobs, row + offsetof(GemvJob, k));
   job.item0 = ld_global<int32_t>(jobs, row + offsetof(GemvJob, item0));
+  job.format = ld_global<int32_t>(jobs, row + offsetof(GemvJob, format));
 }
 
 __device__ __forceinline__ int next_item0(const GemvJob* __restrict__ jobs, int jn, int njobs) {
@@ -336,8 +352,6 @@ __device__ __forceinline__ void stream_issue(const GemvJob& j, int tile, TileReg
   const int nch = j.k / 16;
   const int tiles_k = (j.k + kTile - 1) / kTile;
   const int groups = (j.k + kGroup - 1) / kGroup;
-  const float* __restrict__ srow =
-      MX ? nullptr : static_cast<const float*>(j.scales) + (size_t)(tile * kRows / kTile) * tiles_k;
   const uint8_t* __restrict__ e8 = static_cast<const uint8_t*>(j.scales);
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -357,7 +371,7 @@ __device__ __forceinline__ void stream_issue(const GemvJob& j, int tile, TileReg
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       const int ch = lane + kWave * c;
-      t.s[0][c] = ch < nch ? ld_global<float>(srow, (size_t)(ch >> 3) * 4) : 0.0f;
+      t.s[0][c] = ch < nch ? block_scale(j, tile * kRows, ch >> 3, tiles_k) : 0.0f;
     }
   }
 }
@@ -436,7 +450,8 @@ __global__ __launch_bounds__(kThreads) void k_gemv_valu_stream(const GemvJob* __
       for (int q = 0; q < WaveSums<R>::kGroups; ++q) {
         const int r = 4 * q + (lane >> 4);
         if (r < R && row0 + r < j.n)
-          st_global<uint16_t>(j.y, (size_t)(row0 + r) * 2, (uint16_t)f32_to_bf16_rne(sums.g[q]));
+          st_global<uint16_t>(j.y, (size_t)(row0 + r) * 2,
+                              (uint16_t)f32_to_bf16_rne(sums.g[q] * output_scale(j, row0 + r)));
       }
     }
     if (!more) break;
@@ -505,9 +520,8 @@ __device__ __forceinline__ void panel_issue(const GemvJob& j, int row0, int p, b
   } else {
     r.s[0] = r.s[1] = 0.0f;
     if (live && row0 < j.n) {
-      const float* __restrict__ srow = static_cast<const float*>(j.scales) + (size_t)(row0 / kTile) * nkb;
-      r.s[0] = ld_global<float>(srow, (size_t)(2 * p) * 4);
-      if (2 * p + 1 < nkb) r.s[1] = ld_global<float>(srow, (size_t)(2 * p + 1) * 4);
+      r.s[0] = block_scale(j, row0, 2 * p, nkb);
+      if (2 * p + 1 < nkb) r.s[1] = block_scale(j, row0, 2 * p + 1, nkb);
     }
   }
 }
@@ -585,17 +599,20 @@ __device__ __forceinline__ void panel_mfma(const uint4 (&a)[2][2], const float* 
 // y^T of a 16-row tile from the D layout; columns (activation rows) >= m_rows
 // and rows >= n are not written.
 template <int MT>
-__device__ __forceinline__ void store_tile(const GemvJob& j, int row0, int m_rows, const f32x4 (&acc)[MT]) {
+__device__ __forceinline__ void store_tile(const GemvJob& j, int row0, int m_rows, const f32x4 (&acc)[MT],
+                                           float factor = 1.0f) {
   const int lane = threadIdx.x & (kWave - 1);
   const int i = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const int mcol = 16 * t + i;
+  for (int jj = 0; jj < 4; ++jj) {
+    const int r = row0 + 4 * g + jj;
+    if (r >= j.n) continue;
+    const float os = factor * output_scale(j, r);
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int r = row0 + 4 * g + jj;
-      if (r < j.n && mcol < m_rows)
-        st_global<uint16_t>(j.y, ((size_t)mcol * j.n + r) * 2, (uint16_t)f32_to_bf16_rne(acc[t][jj]));
+    for (int t = 0; t < MT; ++t) {
+      const int mcol = 16 * t + i;
+      if (mcol < m_rows)
+        st_global<uint16_t>(j.y, ((size_t)mcol * j.n + r) * 2, (uint16_t)f32_to_bf16_rne(acc[t][jj] * os));
     }
   }
 }
@@ -865,9 +882,8 @@ __device__ __forceinline__ void panel8_issue(const GemvJob& j, int row0, int p, 
       if (live && row < j.n && grp < groups) r.e[b] = ld_global<uint8_t>(e8, (size_t)row * groups + grp);
     }
   } else if (live && row0 < j.n) {
-    const float* __restrict__ srow = static_cast<const float*>(j.scales) + (size_t)(row0 / kTile) * nkb;
-    r.s[0] = ld_global<float>(srow, (size_t)(2 * p) * 4);
-    if (2 * p + 1 < nkb) r.s[1] = ld_global<float>(srow, (size_t)(2 * p + 1) * 4);
+    r.s[0] = block_scale(j, row0, 2 * p, nkb);
+    if (2 * p + 1 < nkb) r.s[1] = block_scale(j, row0, 2 * p + 1, nkb);
   }
 }
 
@@ -969,15 +985,13 @@ __global__ __launch_bounds__(kThreads) void k_gemv_w8a8_direct(GemvJob j, const 
     for (int jj = 0; jj < 4; ++jj) red[((wave * MT + t) * 4 + jj) * kWave + lane] = acc[t][jj];
   __syncthreads();
   if (wave == 0) {
-    const float x_scale = ld_global<float>(xs, 0);
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
-        acc[t][jj] = x_scale * (acc[t][jj] + red[((1 * MT + t) * 4 + jj) * kWave + lane] +
-                                red[((2 * MT + t) * 4 + jj) * kWave + lane] +
-                                red[((3 * MT + t) * 4 + jj) * kWave + lane]);
-    store_tile<MT>(j, row0, m_rows, acc);
+        acc[t][jj] += red[((1 * MT + t) * 4 + jj) * kWave + lane] + red[((2 * MT + t) * 4 + jj) * kWave + lane] +
+                      red[((3 * MT + t) * 4 + jj) * kWave + lane];
+    store_tile<MT>(j, row0, m_rows, acc, ld_global<float>(xs, 0));
   }
 }
 

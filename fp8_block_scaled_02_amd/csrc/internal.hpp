@@ -9,16 +9,23 @@
 
 namespace fp8w {
 
+// Weight scale formats (the values of fp8w_format).
+constexpr int kFmtBlock = 0;       // fp32 per 128x128 tile
+constexpr int kFmtMx = 1;          // e8m0 per row and 32 columns
+constexpr int kFmtBlockBf16 = 2;   // bf16 per 128x128 tile
+constexpr int kFmtRow = 3;         // fp32 per row
+constexpr int kFmtTensor = 4;      // one fp32 for the whole weight
+
 // One GEMV y[m, n] = x[m, k] . deq(codes)^T.  The same layout is the row of
 // a grouped launch's device table (fp8w_grouped_plan_init writes it).
 struct GemvJob {
-  const uint16_t* x;        // bf16 [m, k]
+  const uint16_t* x;        // bf16 [m, k] (W8A8: e4m3 codes [m, k])
   const uint8_t* codes;     // e4m3fn [n, k]
-  const void* scales;       // fp32 [ceil(n/128), ceil(k/128)] or e8m0 [n, ceil(k/32)]
+  const void* scales;       // in `format`: block grid, e8m0 grid, bf16 grid, [n] or [1]
   uint16_t* y;              // bf16 [m, n]
   int32_t n, k;             // validated to fit int32 on the host
   int32_t item0;            // first workgroup of this job in a grouped launch
-  int32_t reserved;
+  int32_t format;           // kFmt*; kFmtMx jobs run the MX kernel variants
 };
 static_assert(sizeof(GemvJob) == 48, "device table row");
 
@@ -27,13 +34,19 @@ hipError_t launch_quantize_block(const uint16_t* w, int64_t n, int64_t k, uint8_
 hipError_t launch_quantize_mx(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,
                               uint8_t* e8m0, hipStream_t stream);
 
+hipError_t launch_quantize_block_bf16(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,
+                                      uint16_t* scales, hipStream_t stream);
+hipError_t launch_quantize_row(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes, float* scales,
+                               hipStream_t stream);
+hipError_t launch_dequantize_format(const uint8_t* codes, const void* scales, int format, int64_t n,
+                                    int64_t k, uint16_t* out, hipStream_t stream);
 hipError_t launch_dequantize_block(const uint8_t* codes, const float* scales, int64_t n, int64_t k,
                                    uint16_t* out, hipStream_t stream);
 hipError_t launch_dequantize_mx(const uint8_t* codes, const uint8_t* e8m0, int64_t n, int64_t k,
                                 uint16_t* out, hipStream_t stream);
 // Dequantize into w_bf16 [n, k], then y = x . w^T with rocBLAS.
 hipError_t launch_gemm_dequant(const uint16_t* x, int64_t m, const uint8_t* codes,
-                               const void* scales, bool mx, int64_t n, int64_t k, uint16_t* y,
+                               const void* scales, int format, int64_t n, int64_t k, uint16_t* y,
                                uint16_t* w_bf16, hipStream_t stream);
 
 // W8A8 GEMV: job.x points at e4m3 activation codes [m, k]; x_scale is a

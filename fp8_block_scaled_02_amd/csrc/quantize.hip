@@ -51,15 +51,35 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v) {
   return r;
 }
 
+// The tile's scale amax/448 (1.0 for an all-zero tile), stored by thread 0
+// as fp32, or rounded to the nearest bf16 (at least the smallest positive
+// bf16, 2^-133) and stored as bf16 -- then the codes divide by that rounded
+// scale ("feat(quant): opt-in fp8-block QAT for the lm_head", How it works:
+// a bf16 128-block scale).
+template <bool BF16S>
+__device__ __forceinline__ float tile_scale(float amax_f, void* scales) {
+  float scale = amax_f > 0.0f ? amax_f / 448.0f : 1.0f;
+  if (BF16S) {
+    uint32_t bits = f32_to_bf16_rne(scale);
+    if (bits == 0) bits = 1;
+    scale = bf16_lo(bits);
+    if (threadIdx.x == 0) st_global<uint16_t>(scales, (size_t)blockIdx.x * 2, (uint16_t)bits);
+  } else if (threadIdx.x == 0) {
+    st_global<float>(scales, (size_t)blockIdx.x * 4, scale);
+  }
+  return scale;
+}
+
 // One 256-thread block per 128x128 tile; flat block index b -> tile
 // (b / tiles_k, b % tiles_k).  Vector path: k % 8 == 0, w 16-B aligned and
 // codes 8-B aligned.  Thread t owns columns 8*(t%16) .. +7 of rows
 // t/16 + 16*i (i = 0..7): each row of the tile is read as 16 x 16 B and
 // written as 16 x 8 B, and the tile stays in registers between the amax and
 // the encode pass (the bf16 source is read from HBM once).
+template <bool BF16S>
 __global__ __launch_bounds__(kThreads) void k_quant_block_vec(const uint16_t* __restrict__ w,
                                                               uint8_t* __restrict__ codes,
-                                                              float* __restrict__ scales, int n,
+                                                              void* __restrict__ scales, int n,
                                                               int k, int tiles_k) {
   const int ti = blockIdx.x / tiles_k, tj = blockIdx.x % tiles_k;
   const int col = tj * kTile + (threadIdx.x & 15) * 8;
@@ -82,8 +102,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_block_vec(const uint16_t* __
   }
   amax = block_max_u32(amax);
   const float amax_f = __uint_as_float(amax << 16);
-  const float scale = amax_f > 0.0f ? amax_f / 448.0f : 1.0f;
-  if (threadIdx.x == 0) scales[blockIdx.x] = scale;
+  const float scale = tile_scale<BF16S>(amax_f, scales);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int row = row0 + 16 * i;
@@ -98,9 +117,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_block_vec(const uint16_t* __
 
 // Any shape and alignment: element e = t + 256*j (j = 0..63) of the tile,
 // row e/128, column e%128, 2-byte loads and 1-byte stores.
+template <bool BF16S>
 __global__ __launch_bounds__(kThreads) void k_quant_block_any(const uint16_t* __restrict__ w,
                                                               uint8_t* __restrict__ codes,
-                                                              float* __restrict__ scales, int n,
+                                                              void* __restrict__ scales, int n,
                                                               int k, int tiles_k) {
   const int ti = blockIdx.x / tiles_k, tj = blockIdx.x % tiles_k;
   uint16_t v[64];
@@ -116,8 +136,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_block_any(const uint16_t* __
   }
   amax = block_max_u32(amax);
   const float amax_f = __uint_as_float(amax << 16);
-  const float scale = amax_f > 0.0f ? amax_f / 448.0f : 1.0f;
-  if (threadIdx.x == 0) scales[blockIdx.x] = scale;
+  const float scale = tile_scale<BF16S>(amax_f, scales);
 #pragma unroll
   for (int j = 0; j < 64; ++j) {
     const int e = threadIdx.x + kThreads * j;
@@ -180,6 +199,50 @@ __global__ __launch_bounds__(kThreads) void k_quant_mx_any(const uint16_t* __res
 }
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// ------------------------------------------------------------ per row --
+//
+// One wave per row, 4 rows per workgroup: scale[r] = amax(row r)/448 (1.0
+// for an all-zero row), codes enc(w/scale[r]).  The row is read twice (amax,
+// then encode); the second read mostly hits L2.  Vector path when k % 8 == 0
+// and w / codes are 16- / 8-byte aligned.
+__global__ __launch_bounds__(kThreads) void k_quant_row(const uint16_t* __restrict__ w,
+                                                        uint8_t* __restrict__ codes,
+                                                        float* __restrict__ scales, int n, int k,
+                                                        bool vec) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int row = blockIdx.x * (kThreads / kWave) + (int)(threadIdx.x / kWave);
+  if (row >= n) return;   // a whole wave; this kernel has no workgroup barrier
+  const size_t base = (size_t)row * k;
+  uint32_t amax = 0;
+  if (vec) {
+    for (int c = lane * 8; c < k; c += kWave * 8) {
+      const uint4 v = ld_global_u4(w, (base + c) * 2);
+      amax = abs_max_pair(v.x, amax);
+      amax = abs_max_pair(v.y, amax);
+      amax = abs_max_pair(v.z, amax);
+      amax = abs_max_pair(v.w, amax);
+    }
+  } else {
+    for (int c = lane; c < k; c += kWave) {
+      const uint32_t a = ld_global<uint16_t>(w, (base + c) * 2) & 0x7FFFu;
+      amax = a > amax ? a : amax;
+    }
+  }
+  amax = group_max_u32<kWave>(amax);
+  const float amax_f = __uint_as_float(amax << 16);
+  const float scale = amax_f > 0.0f ? amax_f / 448.0f : 1.0f;
+  if (lane == 0) scales[row] = scale;
+  if (vec) {
+    for (int c = lane * 8; c < k; c += kWave * 8) {
+      const uint4 v = ld_global_u4(w, (base + c) * 2);
+      st_global<u32x2>(codes, base + c, u32x2{encode4_div(v.x, v.y, scale), encode4_div(v.z, v.w, scale)});
+    }
+  } else {
+    for (int c = lane; c < k; c += kWave)
+      codes[base + c] = (uint8_t)e4m3_encode(bf16_lo(ld_global<uint16_t>(w, (base + c) * 2)) / scale);
+  }
+}
 
 // ------------------------------------------------ activation (per tensor) --
 //
@@ -314,16 +377,36 @@ hipError_t launch_quantize_act(const uint16_t* x, int64_t count, uint8_t* codes,
   return hipGetLastError();
 }
 
-hipError_t launch_quantize_block(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,
-                                 float* scales, hipStream_t stream) {
+template <bool BF16S>
+hipError_t quantize_block_tiles(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes, void* scales,
+                                hipStream_t stream) {
   const int64_t tiles_n = (n + kTile - 1) / kTile, tiles_k = (k + kTile - 1) / kTile;
   const dim3 grid((unsigned)(tiles_n * tiles_k)), block(kThreads);
   if (k % 8 == 0 && aligned(w, 16) && aligned(codes, 8))
-    hipLaunchKernelGGL(k_quant_block_vec, grid, block, 0, stream, w, codes, scales, (int)n, (int)k,
+    hipLaunchKernelGGL((k_quant_block_vec<BF16S>), grid, block, 0, stream, w, codes, scales, (int)n, (int)k,
                        (int)tiles_k);
   else
-    hipLaunchKernelGGL(k_quant_block_any, grid, block, 0, stream, w, codes, scales, (int)n, (int)k,
+    hipLaunchKernelGGL((k_quant_block_any<BF16S>), grid, block, 0, stream, w, codes, scales, (int)n, (int)k,
                        (int)tiles_k);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_block(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,
+                                 float* scales, hipStream_t stream) {
+  return quantize_block_tiles<false>(w, n, k, codes, scales, stream);
+}
+
+hipError_t launch_quantize_block_bf16(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,
+                                      uint16_t* scales, hipStream_t stream) {
+  return quantize_block_tiles<true>(w, n, k, codes, scales, stream);
+}
+
+hipError_t launch_quantize_row(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes, float* scales,
+                               hipStream_t stream) {
+  const bool vec = k % 8 == 0 && aligned(w, 16) && aligned(codes, 8);
+  const int rows_per_block = kThreads / kWave;
+  hipLaunchKernelGGL(k_quant_row, dim3((unsigned)((n + rows_per_block - 1) / rows_per_block)), dim3(kThreads),
+                     0, stream, w, codes, scales, (int)n, (int)k, vec);
   return hipGetLastError();
 }
 

@@ -88,6 +88,36 @@ typedef enum fp8w_route {
   FP8W_ROUTE_MFMA = 2
 } fp8w_route;
 
+/* Scale formats.  The calls named _block / _mx fix BLOCK / MX; the generic
+ * calls (fp8w_quantize, fp8w_dequantize, fp8w_gemv, fp8w_gemm,
+ * fp8w_gemv_w8a8, grouped plans) take any of them.  The other three are
+ * degenerate tilings of the same rule -- scale = amax/448 over the tile, 1.0
+ * for an all-zero tile, code = enc(w/scale):
+ *   BLOCK_BF16 : the 128x128 tile, scale stored as the nearest bf16 (at
+ *                least 2^-133) and the codes divided by that stored value
+ *                ("feat(quant): opt-in fp8-block QAT for the lm_head", How it
+ *                works: a bf16 128-block scale)
+ *   ROW        : a 1 x k tile, f32 [n] ("quantize_fp8_bs.rs", Atlas
+ *                weight_map: the per-ROW quantizer of the DFlash head; the
+ *                per-row W8A16 route of "feat(qwen4_exp): load-time
+ *                per-tensor FP8 dense projections", Why)
+ *   TENSOR     : one tile covering the weight, f32 [1] (the per-tensor
+ *                weights of the same page, What this adds)
+ * A scale buffer of the wrong format cannot be detected by a kernel
+ * ("quantize_fp8_bs.rs", module notes), so the format is always explicit. */
+typedef enum fp8w_format {
+  FP8W_FORMAT_BLOCK = 0,      /* f32 [ceil(n/128), ceil(k/128)]  */
+  FP8W_FORMAT_MX = 1,         /* u8 e8m0 [n, ceil(k/32)]          */
+  FP8W_FORMAT_BLOCK_BF16 = 2, /* bf16 [ceil(n/128), ceil(k/128)] */
+  FP8W_FORMAT_ROW = 3,        /* f32 [n]                          */
+  FP8W_FORMAT_TENSOR = 4      /* f32 [1]                          */
+} fp8w_format;
+
+/* Bytes of the scale buffer of an [n, k] weight in `format` (0 if the
+ * format or the shape is invalid).  Scale buffers are aligned to their
+ * element size (4, 1, 2, 4, 4 bytes). */
+int64_t fp8w_scale_bytes(fp8w_format format, int64_t n, int64_t k);
+
 /* Largest m (activation rows) served by the GEMV calls.  Larger batches are
  * prefill work, served elsewhere ("feat: add FP8 blockwise weight
  * quantization ...", Summary: M > 32 uses dequantize + dense GEMM). */
@@ -117,6 +147,15 @@ fp8w_status fp8w_quantize_block(const uint16_t* w, int64_t n, int64_t k,
  * Errors: NULL, SHAPE, OVERLAP, HIP. */
 fp8w_status fp8w_quantize_mx(const uint16_t* w, int64_t n, int64_t k,
                              uint8_t* codes, uint8_t* e8m0, void* stream);
+
+/* Quantization in any format, load time: codes [n, k] and the format's
+ * scale buffer.  TENSOR needs `workspace` (>= fp8w_quantize_act_workspace_bytes()
+ * bytes, 4-byte aligned) when n * k > 16384, as fp8w_quantize_act; the other
+ * formats ignore it (may be NULL).  Any n, k >= 1.
+ * Errors: NULL, SHAPE, ALIGN, UNSUPPORTED (format), OVERLAP, HIP. */
+fp8w_status fp8w_quantize(const uint16_t* w, int64_t n, int64_t k, fp8w_format format,
+                          uint8_t* codes, void* scales, void* workspace,
+                          int64_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------- GEMV -- */
 
@@ -244,6 +283,30 @@ fp8w_status fp8w_gemv_mx_w8a8(const uint8_t* x_codes, const float* x_scale, int6
                               const uint8_t* codes, const uint8_t* e8m0, int64_t n, int64_t k,
                               uint16_t* y, void* stream);
 
+/* ----------------------------------------------------- generic formats -- */
+
+/* GEMV in any format, with the same contract and bound as fp8w_gemv_block
+ * (block scales multiply each 128-column block's partial sum; row and
+ * tensor scales multiply each output).  fp8w_gemv_block / _mx and the _route
+ * calls are this call with the format fixed. */
+fp8w_status fp8w_gemv(const uint16_t* x, int64_t m, const uint8_t* codes, const void* scales,
+                      fp8w_format format, int64_t n, int64_t k, uint16_t* y, fp8w_route route,
+                      void* stream);
+
+/* Dequantization in any format: bf16_rne(fl32(dec(code) * scale)). */
+fp8w_status fp8w_dequantize(const uint8_t* codes, const void* scales, fp8w_format format,
+                            int64_t n, int64_t k, uint16_t* w, void* stream);
+
+/* The large-M route in any format (contract of fp8w_gemm_block). */
+fp8w_status fp8w_gemm(const uint16_t* x, int64_t m, const uint8_t* codes, const void* scales,
+                      fp8w_format format, int64_t n, int64_t k, uint16_t* y, void* workspace,
+                      int64_t workspace_bytes, void* stream);
+
+/* The W8A8 GEMV in any format (contract of fp8w_gemv_block_w8a8). */
+fp8w_status fp8w_gemv_w8a8(const uint8_t* x_codes, const float* x_scale, int64_t m,
+                           const uint8_t* codes, const void* scales, fp8w_format format,
+                           int64_t n, int64_t k, uint16_t* y, void* stream);
+
 /* ------------------------------------------------------------- grouped -- */
 
 /* A group of independent GEMVs served by one kernel launch: the fixed cost
@@ -253,14 +316,9 @@ fp8w_status fp8w_gemv_mx_w8a8(const uint8_t* x_codes, const float* x_scale, int6
  * dense projections", Why; the grouped expert GEMM that reads [N/128,
  * K/128] fp32 block scales in "quantize_fp8_bs.rs", Atlas weight_map).  The
  * GEMVs of a group must not depend on one another (no y of one is the x of
- * another); all share m, the scale format and the route.  Each GEMV meets
- * the same error bound as the single call (the summation order may differ,
- * so the last bit of y may too). */
-
-typedef enum fp8w_format {
-  FP8W_FORMAT_BLOCK = 0, /* fp32 scales, one per 128x128 tile */
-  FP8W_FORMAT_MX = 1     /* e8m0 bytes, one per 32 elements along K */
-} fp8w_format;
+ * another); all share m, the scale format (any fp8w_format) and the route.
+ * Each GEMV meets the same error bound as the single call (the summation
+ * order may differ, so the last bit of y may too). */
 
 /* One GEMV of a group; the same layout rules as fp8w_gemv_block /
  * fp8w_gemv_mx.  scales is `const float*` (block) or `const uint8_t*` (mx). */

@@ -296,7 +296,9 @@ uint16_t oracle_round_bf16(double v);
  * 128-block scale).  The fp32 scale amax/448 is rounded to the nearest bf16
  * (ties to even; 1.0 for an all-zero tile) and the codes divide by that
  * stored scale, so that dequantizing with it inverts them; a scale rounded
- * down can put amax/scale just above 448, which saturates. */
+ * down can put amax/scale just above 448, which saturates.  A scale that
+ * would round to zero (amax below 448 * 2^-134) is the smallest positive
+ * bf16, 2^-133, instead. */
 int oracle_quantize_block_bf16(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,
                                uint16_t* scales) {
   if (!w || !codes || !scales || n < 1 || k < 1) return ORACLE_ERR_ARG;
@@ -314,7 +316,8 @@ int oracle_quantize_block_bf16(const uint16_t* w, int64_t n, int64_t k, uint8_t*
           const float a = fabsf(bf16_to_float(w[r * k + c]));
           if (a > amax) amax = a;
         }
-      const uint16_t sb = amax > 0.0f ? oracle_round_bf16((double)(amax / 448.0f)) : 0x3F80;
+      uint16_t sb = amax > 0.0f ? oracle_round_bf16((double)(amax / 448.0f)) : 0x3F80;
+      if (sb == 0) sb = 1;   /* amax/448 below half the smallest bf16: keep the scale positive */
       const float scale = bf16_to_float(sb);
       scales[ti * tiles_k + tj] = sb;
       for (int64_t r = r0; r < r1; ++r)

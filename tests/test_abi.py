@@ -139,6 +139,30 @@ def test_gemm_argument_errors(F):
     assert m(A, 64, B, C + 1, 16, 16, D, C, 512, None) == F.ERR_OVERLAP    # workspace over e8m0
 
 
+def test_generic_format_calls_argument_errors(F):
+    L = F.lib()
+    assert [L.fp8w_scale_bytes(f, 129, 257) for f in range(5)] == [24, 129 * 9, 12, 129 * 4, 4]
+    assert L.fp8w_scale_bytes(5, 4, 4) == 0 and L.fp8w_scale_bytes(0, 0, 4) == 0
+    q = L.fp8w_quantize
+    assert q(A, 4, 4, 7, B, C, None, 0, None) == F.ERR_UNSUPPORTED                 # unknown format
+    assert q(A, 256, 256, F.FORMAT_TENSOR, B, C, None, 0, None) == F.ERR_NULL      # tensor needs workspace
+    assert q(A, 256, 256, F.FORMAT_TENSOR, B, C, D, 16, None) == F.ERR_SHAPE       # workspace too small
+    assert q(A, 4, 4, F.FORMAT_BLOCK_BF16, B, C + 1, None, 0, None) == F.ERR_ALIGN # bf16 scales: 2 B
+    assert q(A, 4, 4, F.FORMAT_ROW, B, C + 2, None, 0, None) == F.ERR_ALIGN        # f32 scales: 4 B
+    assert q(A, 64, 64, F.FORMAT_ROW, B, B + 32, None, 0, None) == F.ERR_OVERLAP   # scales over codes
+    g = L.fp8w_gemv
+    assert g(A, 1, B, C, 9, 16, 16, D, 0, None) == F.ERR_UNSUPPORTED
+    assert g(A, 1, B, C + 1, F.FORMAT_BLOCK_BF16, 16, 16, D, 0, None) == F.ERR_ALIGN
+    assert g(A, 1, B, C, F.FORMAT_TENSOR, 16, 16, C, 0, None) == F.ERR_OVERLAP     # y over the scale
+    d = L.fp8w_dequantize
+    assert d(B, C, 6, 4, 4, D, None) == F.ERR_UNSUPPORTED
+    assert d(B, C, F.FORMAT_ROW, 64, 64, C - 16, None) == F.ERR_OVERLAP
+    w = L.fp8w_gemv_w8a8
+    assert w(A, C, 1, B, D, F.FORMAT_ROW, 16, 16, None, None) == F.ERR_NULL
+    assert w(A, C, 1, B, D + 2, F.FORMAT_ROW, 16, 16, 0x3000000, None) == F.ERR_ALIGN
+    assert L.fp8w_gemm(A, 64, B, C, 11, 16, 16, D, 0x20000000, 512, None) == F.ERR_UNSUPPORTED
+
+
 def test_grouped_argument_errors(F):
     L = F.lib()
     descs = (F.GemvDesc * 2)(F.GemvDesc(A, B, C, D, 16, 16), F.GemvDesc(A, B, C, D + 4096, 16, 16))
@@ -147,7 +171,7 @@ def test_grouped_argument_errors(F):
     init = L.fp8w_grouped_plan_init
     assert init(None, 2, 1, F.FORMAT_BLOCK, 0, T, ctypes.byref(plan)) == F.ERR_NULL
     assert init(descs, 0, 1, F.FORMAT_BLOCK, 0, T, ctypes.byref(plan)) == F.ERR_SHAPE
-    assert init(descs, 2, 1, 5, 0, T, ctypes.byref(plan)) == F.ERR_UNSUPPORTED
+    assert init(descs, 2, 1, 5, 0, T, ctypes.byref(plan)) == F.ERR_UNSUPPORTED    # formats 0..4
     assert init(descs, 2, 1, F.FORMAT_BLOCK, 0, T + 8, ctypes.byref(plan)) == F.ERR_ALIGN
     assert init(descs, 2, 40, F.FORMAT_BLOCK, 0, T, ctypes.byref(plan)) == F.ERR_SHAPE
     clash = (F.GemvDesc * 2)(F.GemvDesc(A, B, C, D, 16, 16), F.GemvDesc(A, B, C, D + 8, 16, 16))

@@ -36,13 +36,13 @@ PEAK_BF16 = 2.5e15         # MI355X dense bf16 MFMA, flop/s
 
 # HBM bytes per launch of the grouped M=1 streaming GEMV on the projection
 # set, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled by a 2 GiB device
-# copy (read factor 1.99993, write factor 1.0): 1339.36 MB read + 1.00 MB
+# copy (read factor 1.99993, write factor 1.0): 1339.37 MB read + 1.00 MB
 # written.  Valid only for the sources they were taken with (sha256 of the
 # kernel, launch-plan and helper sources); any change to those reports
 # traffic as null until the counters are retaken.
 COUNTED_TRAFFIC = {
-    "sources_sha256": "7c561162be08be3a7876c308dd13e896b5be83a1c70b651c377881dacb6f6ac0",
-    "bytes_per_launch": 1340.35e6,
+    "sources_sha256": "9c2cb404627cb48b03bed0cb7494cffd4448db2505b81e88849cee74c9b9b183",
+    "bytes_per_launch": 1340.37e6,
 }
 TRAFFIC_SOURCES = ('gemv.hip', 'device.hpp', 'internal.hpp', 'api.cpp')
 
@@ -57,7 +57,7 @@ def counted_traffic():
         return None
     return COUNTED_TRAFFIC["bytes_per_launch"]
 TILE, GROUP = 128, 32
-ALL_ROWS = ("proj", "quant", "lm_head", "dense", "mx", "single", "dequant", "gemm", "w8a8")
+ALL_ROWS = ("proj", "quant", "lm_head", "dense", "mx", "single", "dequant", "gemm", "w8a8", "row")
 
 
 def parse():
@@ -543,6 +543,42 @@ def bench_w8a8(torch, fp8w, lean, timer, W, args, state, log):
     return {"w8a8_projection_set": out}
 
 
+def bench_row_format(torch, fp8w, lean, timer, W, args, state, log):
+    """The projection set quantized with one fp32 scale per row (the pages'
+    per-row W8A16 route), GEMV at M = 1, 8, 16: one grouped launch per pass,
+    and 96 single fp8w_gemv calls (graph-captured)."""
+    wl, bf, _, _ = state
+    lib = fp8w.lib()
+    qs = [fp8w.fp8w_quantize(w, "row") for w in bf]
+    codes = [c for c, _ in qs]
+    scales = [s for _, s in qs]
+    out = {}
+    for m in (1, 8, 16):
+        xs = {k: upload_bf16(torch, W.activation(2, m, k)) for k in (2560, 3072)}
+        ys = [torch.empty((m, c.shape[0]), dtype=torch.bfloat16, device="cuda") for c in codes]
+        nbytes = sum(c.shape[0] * c.shape[1] + 4 * c.shape[0] + 2 * m * c.shape[1] + 2 * m * c.shape[0]
+                     for c in codes)
+        plan = fp8w.fp8w_grouped_plan_init([xs[c.shape[1]] for c in codes], codes, scales, ys, fmt="row")
+        per, _ = timer.run(lean.grouped(plan), max(10, args.steps // 2), args.warmup)
+        row = {"grouped": dict(summarize(per, len(codes), nbytes), ms_per_pass=round(statistics.median(per), 4))}
+        cargs = [(xs[c.shape[1]].data_ptr(), m, c.data_ptr(), s.data_ptr(), fp8w.FORMAT_ROW, c.shape[0],
+                  c.shape[1], y.data_ptr(), 0) for c, s, y in zip(codes, scales, ys)]
+
+        def run():
+            st = lean.stream()
+            for a in cargs:
+                if lib.fp8w_gemv(*a, st):
+                    raise RuntimeError("fp8w_gemv failed")
+        g = graph_of(torch, run)
+        per_c, _ = timer.run(g.replay, max(10, args.steps // 4), min(args.warmup, 20))
+        row["per_call"] = dict(summarize(per_c, len(codes), nbytes), ms_per_pass=round(statistics.median(per_c), 4))
+        del g, plan
+        out[f"m{m}"] = row
+    out["pages_per_pass_ms_context"] = {"FreeToken per-row W8A16, RTX 6000 Ada": [3.70, 3.07, 3.06]}
+    log(f"row format: {out}")
+    return {"row_scale_projection_set": out}
+
+
 def bench_single(torch, fp8w, lean, timer, W, args, log):
     w = W.WORKLOADS[1].weights[0]
     bf = upload_bf16(torch, w.bits(1))
@@ -632,12 +668,14 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         log(f"calibration copy of {args.calibrate_copy_mib} MiB done")
-    if "proj" in rows_wanted or "quant" in rows_wanted or "w8a8" in rows_wanted:
+    if any(r in rows_wanted for r in ("proj", "quant", "w8a8", "row")):
         state = projection_set(torch, fp8w, W, log)
         if "quant" in rows_wanted:
             rows.update(bench_quant(torch, fp8w, lean, timer, W, args, state, log))
         if "w8a8" in rows_wanted:
             rows.update(bench_w8a8(torch, fp8w, lean, timer, W, args, state, log))
+        if "row" in rows_wanted:
+            rows.update(bench_row_format(torch, fp8w, lean, timer, W, args, state, log))
         if "proj" in rows_wanted:
             proj, headline = bench_proj(torch, fp8w, lean, timer, W, args, state, log)
             rows["projection_set"] = proj

@@ -49,20 +49,51 @@ def _tiles_for(amax_bits):
     return np.concatenate([owner[:, None].astype(np.uint16), body], axis=1)
 
 
+def _misaligned_bf16(bits):
+    """Device copy of bf16 bits whose data pointer is only 2-byte aligned,
+    which sends the quantizer down its any-shape path."""
+    import torch
+    n, k = bits.shape
+    buf = torch.empty(n * k + 1, dtype=torch.bfloat16, device="cuda")
+    buf[1:].copy_(to_dev_bf16(bits).reshape(-1))
+    return buf[1:].view(n, k)
+
+
+@pytest.mark.parametrize("path", ["vector", "any"])
 @pytest.mark.parametrize("part", range(4))
-def test_block_quantizer_every_w_amax_pair(fp8w, oracle_mod, part):
+def test_block_quantizer_every_w_amax_pair(fp8w, oracle_mod, part, path):
     """All positive finite bf16 amax values (subnormals included) split in 4
-    parts; each part is one [128*T, 128] weight, one tile column."""
+    parts; each part is one [128*T, 128] weight, one tile column, through
+    the 16-byte kernel and through the any-shape kernel."""
     amax_all = np.arange(1, 0x7F80, dtype=np.int64)
     amax = amax_all[part::4]
     tiles = _tiles_for(amax)
     t = tiles.shape[0]
     bits = tiles.reshape(t, TILE, TILE).reshape(t * TILE, TILE)
-    codes, scales = fp8w.fp8w_quantize_block(to_dev_bf16(bits))
+    w = to_dev_bf16(bits) if path == "vector" else _misaligned_bf16(bits)
+    codes, scales = fp8w.fp8w_quantize_block(w)
     _sync()
     rc, rs = oracle_mod.quantize_block(bits)
     gs = scales.cpu().numpy()
     assert np.array_equal(gs.view(np.uint32), rs.view(np.uint32))
+    gc = codes.cpu().numpy()
+    bad = np.flatnonzero((gc != rc).any(axis=1))
+    assert bad.size == 0, f"first mismatching row {bad[:5]}"
+
+
+@pytest.mark.parametrize("part", range(4))
+def test_block_bf16_scale_quantizer_every_w_amax_pair(fp8w, oracle_mod, part):
+    """The same pairs with the scale stored as bf16: the codes divide by the
+    rounded scale, a different set of divisors."""
+    import torch
+    amax = np.arange(1, 0x7F80, dtype=np.int64)[part::4]
+    tiles = _tiles_for(amax)
+    t = tiles.shape[0]
+    bits = tiles.reshape(t, TILE, TILE).reshape(t * TILE, TILE)
+    codes, scales = fp8w.fp8w_quantize(to_dev_bf16(bits), "block_bf16")
+    _sync()
+    rc, rs = oracle_mod.quantize_block_bf16(bits)
+    assert np.array_equal(scales.view(torch.int16).cpu().numpy().view(np.uint16), rs)
     gc = codes.cpu().numpy()
     bad = np.flatnonzero((gc != rc).any(axis=1))
     assert bad.size == 0, f"first mismatching row {bad[:5]}"

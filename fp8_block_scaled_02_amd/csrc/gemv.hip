@@ -344,6 +344,44 @@ __device__ __forceinline__ int next_item0(const GemvJob* __restrict__ jobs, int 
              : 0x7FFFFFFF;
 }
 
+// Where a streaming kernel finds its GEMVs: the device table `jobs` of
+// `njobs` jobs (grouped launches, ONE = false), or the single job `one`
+// passed by value with item0 = 0 (single calls, ONE = true: no table, no
+// search).  The table stays a __restrict__ kernel parameter, so its rows
+// are read with scalar loads that no pending weight load has to wait for.
+struct JobList {
+  const GemvJob* __restrict__ table;
+  int count;
+  const GemvJob& one;
+};
+
+// Index of the job that holds tile t (the last one whose first tile is <= t).
+template <bool ONE>
+__device__ __forceinline__ int job_of_tile(const JobList& l, int t) {
+  if (ONE) return 0;
+  int lo = 0, hi = l.count - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (ld_global<int32_t>(l.table, (size_t)mid * sizeof(GemvJob) + offsetof(GemvJob, item0)) <= t)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+template <bool ONE>
+__device__ __forceinline__ void load_job(const JobList& l, int jn, GemvJob& j) {
+  if (ONE) j = l.one;
+  else load_job_row(l.table, jn, j);
+}
+
+// First tile after job jn.
+template <bool ONE>
+__device__ __forceinline__ int job_end(const JobList& l, int jn) {
+  return ONE ? 0x7FFFFFFF : next_item0(l.table, jn, l.count);
+}
+
 template <int R, int C, bool MX>
 __device__ __forceinline__ void stream_issue(const GemvJob& j, int tile, TileRegs<R, C, MX>& t) {
   constexpr int kRows = kWaves * R;
@@ -376,10 +414,11 @@ __device__ __forceinline__ void stream_issue(const GemvJob& j, int tile, TileReg
   }
 }
 
-template <int R, int C, bool MX>
-__global__ __launch_bounds__(kThreads) void k_gemv_valu_stream(const GemvJob* __restrict__ jobs,
-                                                               int njobs, int total_tiles,
+template <int R, int C, bool MX, bool ONE>
+__global__ __launch_bounds__(kThreads) void k_gemv_valu_stream(const GemvJob* __restrict__ table,
+                                                               int njobs, GemvJob one, int total_tiles,
                                                                int tiles_per_block) {
+  const JobList jobs{table, njobs, one};
   constexpr int kRows = kWaves * R, kSeg = 1024 * C;
   static_assert(kTile % kRows == 0, "a tile must stay inside one 128-row block");
   __shared__ __align__(16) uint16_t xs[kSeg];
@@ -388,21 +427,10 @@ __global__ __launch_bounds__(kThreads) void k_gemv_valu_stream(const GemvJob* __
   if (t_begin >= t_end) return;   // whole workgroup: no barrier is skipped by part of it
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
 
-  int jn = 0;
-  {
-    int lo = 0, hi = njobs - 1;   // last job whose first tile is <= t_begin
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (ld_global<int32_t>(jobs, (size_t)mid * sizeof(GemvJob) + offsetof(GemvJob, item0)) <= t_begin)
-        lo = mid;
-      else
-        hi = mid - 1;
-    }
-    jn = lo;
-  }
+  int jn = job_of_tile<ONE>(jobs, t_begin);
   GemvJob j;
-  load_job_row(jobs, jn, j);
-  int boundary = next_item0(jobs, jn, njobs);
+  load_job<ONE>(jobs, jn, j);
+  int boundary = job_end<ONE>(jobs, jn);
 
   TileRegs<R, C, MX> cur, nxt;
   stream_issue<R, C, MX>(j, t_begin - j.item0, cur);
@@ -417,8 +445,8 @@ __global__ __launch_bounds__(kThreads) void k_gemv_valu_stream(const GemvJob* __
     if (more) {
       if (t + 1 >= boundary) {   // the run crosses into the next job
         jn_next = jn + 1;
-        load_job_row(jobs, jn_next, jnext);
-        boundary_next = next_item0(jobs, jn_next, njobs);
+        load_job<ONE>(jobs, jn_next, jnext);
+        boundary_next = job_end<ONE>(jobs, jn_next);
       }
       stream_issue<R, C, MX>(jnext, t + 1 - jnext.item0, nxt);
     }
@@ -626,11 +654,12 @@ __device__ __forceinline__ void store_tile(const GemvJob& j, int row0, int m_row
 // (a multiple of 256, sized on the host so that two workgroups fit on a CU):
 // restaged when the run enters a new job, and at every segment of a tile
 // when K spans more than one segment.
-template <int MT, int NW, int D, bool MX>
-__global__ __launch_bounds__(NW * kWave) void k_gemv_mfma_stream(const GemvJob* __restrict__ jobs,
-                                                                 int njobs, int total_tiles,
+template <int MT, int NW, int D, bool MX, bool ONE>
+__global__ __launch_bounds__(NW * kWave) void k_gemv_mfma_stream(const GemvJob* __restrict__ table,
+                                                                 int njobs, GemvJob one, int total_tiles,
                                                                  int tiles_per_block, int m_rows,
                                                                  int seg_cols) {
+  const JobList jobs{table, njobs, one};
   constexpr int kRows = 16 * NW;
   extern __shared__ __align__(16) unsigned char smem[];
   const int t_begin = blockIdx.x * tiles_per_block;
@@ -644,22 +673,11 @@ __global__ __launch_bounds__(NW * kWave) void k_gemv_mfma_stream(const GemvJob* 
   const int ldx = seg_cols + 8;   // +16 B per row spreads the B reads over the banks
   const int seg_panels = seg_cols / kPanelCols;
 
-  int jn = 0;
-  {
-    int lo = 0, hi = njobs - 1;   // last job whose first tile is <= t_begin
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (ld_global<int32_t>(jobs, (size_t)mid * sizeof(GemvJob) + offsetof(GemvJob, item0)) <= t_begin)
-        lo = mid;
-      else
-        hi = mid - 1;
-    }
-    jn = lo;
-  }
+  int jn = job_of_tile<ONE>(jobs, t_begin);
   // compute cursor: tile ct, panel cp of job cj
   GemvJob cj;
-  load_job_row(jobs, jn, cj);
-  int c_bound = next_item0(jobs, jn, njobs);
+  load_job<ONE>(jobs, jn, cj);
+  int c_bound = job_end<ONE>(jobs, jn);
   int c_np = (cj.k + kPanelCols - 1) / kPanelCols;
   int ct = t_begin, cp = 0;
   // issue cursor: tile it, panel ip of job ij, D panels ahead
@@ -674,8 +692,8 @@ __global__ __launch_bounds__(NW * kWave) void k_gemv_mfma_stream(const GemvJob* 
     if (++ip == i_np) {
       ip = 0;
       if (++it < t_end && it >= i_bound) {
-        load_job_row(jobs, ++ijn, ij);
-        i_bound = next_item0(jobs, ijn, njobs);
+        load_job<ONE>(jobs, ++ijn, ij);
+        i_bound = job_end<ONE>(jobs, ijn);
         i_np = (ij.k + kPanelCols - 1) / kPanelCols;
       }
     }
@@ -729,8 +747,8 @@ __global__ __launch_bounds__(NW * kWave) void k_gemv_mfma_stream(const GemvJob* 
         if (++ct >= t_end) {
           done = true;
         } else if (ct >= c_bound) {   // the run enters the next job
-          load_job_row(jobs, ++jn, cj);
-          c_bound = next_item0(jobs, jn, njobs);
+          load_job<ONE>(jobs, ++jn, cj);
+          c_bound = job_end<ONE>(jobs, jn);
           c_np = (cj.k + kPanelCols - 1) / kPanelCols;
           __syncthreads();
           stage(cj, 0);
@@ -1012,11 +1030,14 @@ hipError_t run_valu(const GemvJob& job, const GemvJob* table, int njobs, int64_t
   return hipGetLastError();
 }
 
-// (rows per wave R, 16-byte chunks per lane per segment C) of the VALU route
+// (rows per wave R, 16-byte chunks per lane per segment C) of the VALU
+// route.  WIDE (grouped launches, and single calls with many rows): 4 rows
+// per wave, fewer and larger workgroups; otherwise 1 or 2 rows per wave, the
+// most workgroups for small N.
 template <bool MX, bool G>
-hipError_t dispatch_valu(int m, const GemvJob& job, const GemvJob* table, int njobs, int64_t blocks,
-                         hipStream_t s) {
-  if (G) {
+hipError_t dispatch_valu(int m, bool wide, const GemvJob& job, const GemvJob* table, int njobs,
+                         int64_t blocks, hipStream_t s) {
+  if (wide) {
     switch (m) {
       case 1: return run_valu<1, 4, 3, MX, G>(job, table, njobs, blocks, s);
       case 2: return run_valu<2, 4, 2, MX, G>(job, table, njobs, blocks, s);
@@ -1049,14 +1070,17 @@ hipError_t dispatch_valu(int m, const GemvJob& job, const GemvJob* table, int nj
 constexpr int kMfmaStreamWaves = 8;
 constexpr int kMfmaStreamLds = 80 * 1024;
 
-template <int MT, bool MX>
+// Streaming kernel of M = 1 VALU launches: (R, C) and its K limit.
+constexpr int kStreamR = 4, kStreamC = 3;
+
+template <int MT, bool MX, bool ONE>
 constexpr auto mfma_stream_kernel() {
-  return &k_gemv_mfma_stream<MT, kMfmaStreamWaves, 2, MX>;
+  return &k_gemv_mfma_stream<MT, kMfmaStreamWaves, 2, MX, ONE>;
 }
 
 // The kernel needs more than the default 64 KB of dynamic LDS: raise the
 // limit once per device and variant.
-template <int MT, bool MX>
+template <int MT, bool MX, bool ONE>
 hipError_t allow_mfma_stream_lds() {
   static bool done[64] = {};
   int dev = 0;
@@ -1064,13 +1088,54 @@ hipError_t allow_mfma_stream_lds() {
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
   if (!done[dev]) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(mfma_stream_kernel<MT, MX>()),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(mfma_stream_kernel<MT, MX, ONE>()),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kMfmaStreamLds);
     if (e != hipSuccess) return e;
     done[dev] = true;
   }
   return hipSuccess;
 }
+
+// Launch arguments of a streaming kernel: a job table, or one job.
+struct StreamJobs {
+  const GemvJob* table;
+  int count;
+  GemvJob one;
+};
+
+template <bool MX, bool ONE>
+hipError_t run_valu_stream(const StreamJobs& l, int64_t blocks, int64_t tiles, int tiles_per_block,
+                           hipStream_t stream) {
+  hipLaunchKernelGGL((k_gemv_valu_stream<kStreamR, kStreamC, MX, ONE>), dim3((unsigned)blocks),
+                     dim3(kThreads), 0, stream, l.table, l.count, l.one, (int)tiles, tiles_per_block);
+  return hipGetLastError();
+}
+
+template <int MT, bool MX, bool ONE>
+hipError_t run_mfma_stream(const StreamJobs& l, int64_t blocks, int64_t tiles, int tiles_per_block, int m,
+                           int seg_cols, hipStream_t stream);
+
+template <bool ONE>
+hipError_t dispatch_mfma_stream(const StreamJobs& l, int64_t blocks, int64_t tiles, int tiles_per_block,
+                                int m, int seg_cols, bool mx, hipStream_t s) {
+  if (m <= 16)
+    return mx ? run_mfma_stream<1, true, ONE>(l, blocks, tiles, tiles_per_block, m, seg_cols, s)
+              : run_mfma_stream<1, false, ONE>(l, blocks, tiles, tiles_per_block, m, seg_cols, s);
+  return mx ? run_mfma_stream<2, true, ONE>(l, blocks, tiles, tiles_per_block, m, seg_cols, s)
+            : run_mfma_stream<2, false, ONE>(l, blocks, tiles, tiles_per_block, m, seg_cols, s);
+}
+
+// Single calls with many rows take the wide VALU tiles (the streaming
+// kernel at m = 1, K <= 3072) and the streaming MFMA kernel (one job passed
+// by value, one 128-row tile per workgroup, x staged once per tile in LDS):
+// their larger tiles keep more weight bytes in flight per wave, and once
+// the launch has enough tiles to fill the chip that wins.  Crossovers
+// measured on MI355X over N = 4096..65536, K = 2048..4096: VALU from N =
+// 16384 (1.05-1.2x at K <= 3072, even at K = 4096); MFMA from N = 32768
+// (1.1-2.5x, the gain growing with m), and from N = 16384 when m > 16.
+constexpr int64_t kSingleWideMinRowsValu = 16384;
+
+bool single_call_streams_mfma(int64_t n, int m) { return n >= 32768 || (n >= 16384 && m > 16); }
 
 }  // namespace
 
@@ -1082,59 +1147,8 @@ int gemv_rows_per_block(int route, int m, bool grouped) {
   return grouped ? 16 * kMfmaStreamWaves : 16;
 }
 
-hipError_t launch_gemv(const GemvJob& job, int m, bool mx, int route, hipStream_t stream) {
-  const int rows = gemv_rows_per_block(route, m, false);
-  const int64_t blocks = (job.n + rows - 1) / rows;
-  if (route == 1)
-    return mx ? dispatch_valu<true, false>(m, job, nullptr, 1, blocks, stream)
-              : dispatch_valu<false, false>(m, job, nullptr, 1, blocks, stream);
-  const dim3 grid((unsigned)blocks), block(kThreads);
-  if (m <= 16) {
-    if (mx) hipLaunchKernelGGL((k_gemv_mfma_direct<1, 2, true>), grid, block, 0, stream, job, m);
-    else hipLaunchKernelGGL((k_gemv_mfma_direct<1, 2, false>), grid, block, 0, stream, job, m);
-  } else {
-    if (mx) hipLaunchKernelGGL((k_gemv_mfma_direct<2, 2, true>), grid, block, 0, stream, job, m);
-    else hipLaunchKernelGGL((k_gemv_mfma_direct<2, 2, false>), grid, block, 0, stream, job, m);
-  }
-  return hipGetLastError();
-}
-
-// Streaming kernel of grouped M = 1 VALU plans: (R, C) and its K limit.
-constexpr int kStreamR = 4, kStreamC = 3;
-
 int gemv_stream_max_k() { return 1024 * kStreamC; }
 int gemv_stream_rows() { return kWaves * kStreamR; }
-
-hipError_t gemv_stream_slots(bool mx, int* slots) {
-  int dev = 0, cus = 0, per_cu = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e == hipSuccess)
-    e = mx ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                 &per_cu, k_gemv_valu_stream<kStreamR, kStreamC, true>, kThreads, 0)
-           : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                 &per_cu, k_gemv_valu_stream<kStreamR, kStreamC, false>, kThreads, 0);
-  *slots = cus * (per_cu > 0 ? per_cu : 1);
-  return e;
-}
-
-hipError_t launch_gemv_stream(const GemvJob* table, int njobs, int64_t blocks, int64_t tiles,
-                              int tiles_per_block, bool mx, hipStream_t stream) {
-  if (mx)
-    hipLaunchKernelGGL((k_gemv_valu_stream<kStreamR, kStreamC, true>), dim3((unsigned)blocks),
-                       dim3(kThreads), 0, stream, table, njobs, (int)tiles, tiles_per_block);
-  else
-    hipLaunchKernelGGL((k_gemv_valu_stream<kStreamR, kStreamC, false>), dim3((unsigned)blocks),
-                       dim3(kThreads), 0, stream, table, njobs, (int)tiles, tiles_per_block);
-  return hipGetLastError();
-}
-
-hipError_t launch_gemv_grouped(const GemvJob* table, int njobs, int64_t blocks, int m, bool mx,
-                               hipStream_t stream) {
-  const GemvJob none{};
-  return mx ? dispatch_valu<true, true>(m, none, table, njobs, blocks, stream)
-            : dispatch_valu<false, true>(m, none, table, njobs, blocks, stream);
-}
 
 int gemv_mfma_stream_seg_cols(int m, int64_t max_k) {
   const int x_budget = kMfmaStreamLds - kMfmaStreamWaves * kPanelBytes;
@@ -1152,6 +1166,84 @@ int gemv_mfma_stream_lds(int m, int seg_cols) {
 
 int gemv_mfma_stream_lds_limit() { return kMfmaStreamLds; }
 
+namespace {
+
+template <int MT, bool MX, bool ONE>
+hipError_t run_mfma_stream(const StreamJobs& l, int64_t blocks, int64_t tiles, int tiles_per_block, int m,
+                           int seg_cols, hipStream_t stream) {
+  const hipError_t e = allow_mfma_stream_lds<MT, MX, ONE>();
+  if (e != hipSuccess) return e;
+  const size_t lds = (size_t)gemv_mfma_stream_lds(m, seg_cols);
+  hipLaunchKernelGGL((k_gemv_mfma_stream<MT, kMfmaStreamWaves, 2, MX, ONE>), dim3((unsigned)blocks),
+                     dim3(kMfmaStreamWaves * kWave), lds, stream, l.table, l.count, l.one, (int)tiles,
+                     tiles_per_block, m, seg_cols);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemv(const GemvJob& job, int m, bool mx, int route, hipStream_t stream) {
+  if (route == 1) {
+    const bool wide = job.n >= kSingleWideMinRowsValu;
+    if (wide && m == 1 && job.k <= gemv_stream_max_k()) {
+      StreamJobs l{nullptr, 1, job};
+      l.one.item0 = 0;
+      const int64_t tiles = (job.n + gemv_stream_rows() - 1) / gemv_stream_rows();
+      return mx ? run_valu_stream<true, true>(l, tiles, tiles, 1, stream)
+                : run_valu_stream<false, true>(l, tiles, tiles, 1, stream);
+    }
+    const int rows = wide ? gemv_rows_per_block(route, m, true) : gemv_rows_per_block(route, m, false);
+    const int64_t blocks = (job.n + rows - 1) / rows;
+    return mx ? dispatch_valu<true, false>(m, wide, job, nullptr, 1, blocks, stream)
+              : dispatch_valu<false, false>(m, wide, job, nullptr, 1, blocks, stream);
+  }
+  if (single_call_streams_mfma(job.n, m)) {
+    StreamJobs l{nullptr, 1, job};
+    l.one.item0 = 0;
+    const int rows = gemv_rows_per_block(route, m, true);
+    const int64_t tiles = (job.n + rows - 1) / rows;
+    return dispatch_mfma_stream<true>(l, tiles, tiles, 1, m, gemv_mfma_stream_seg_cols(m, job.k), mx,
+                                      stream);
+  }
+  const int64_t blocks = (job.n + 15) / 16;
+  const dim3 grid((unsigned)blocks), block(kThreads);
+  if (m <= 16) {
+    if (mx) hipLaunchKernelGGL((k_gemv_mfma_direct<1, 2, true>), grid, block, 0, stream, job, m);
+    else hipLaunchKernelGGL((k_gemv_mfma_direct<1, 2, false>), grid, block, 0, stream, job, m);
+  } else {
+    if (mx) hipLaunchKernelGGL((k_gemv_mfma_direct<2, 2, true>), grid, block, 0, stream, job, m);
+    else hipLaunchKernelGGL((k_gemv_mfma_direct<2, 2, false>), grid, block, 0, stream, job, m);
+  }
+  return hipGetLastError();
+}
+
+hipError_t gemv_stream_slots(bool mx, int* slots) {
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess)
+    e = mx ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                 &per_cu, k_gemv_valu_stream<kStreamR, kStreamC, true, false>, kThreads, 0)
+           : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                 &per_cu, k_gemv_valu_stream<kStreamR, kStreamC, false, false>, kThreads, 0);
+  *slots = cus * (per_cu > 0 ? per_cu : 1);
+  return e;
+}
+
+hipError_t launch_gemv_stream(const GemvJob* table, int njobs, int64_t blocks, int64_t tiles,
+                              int tiles_per_block, bool mx, hipStream_t stream) {
+  const StreamJobs l{table, njobs, GemvJob{}};
+  return mx ? run_valu_stream<true, false>(l, blocks, tiles, tiles_per_block, stream)
+            : run_valu_stream<false, false>(l, blocks, tiles, tiles_per_block, stream);
+}
+
+hipError_t launch_gemv_grouped(const GemvJob* table, int njobs, int64_t blocks, int m, bool mx,
+                               hipStream_t stream) {
+  const GemvJob none{};
+  return mx ? dispatch_valu<true, true>(m, true, none, table, njobs, blocks, stream)
+            : dispatch_valu<false, true>(m, true, none, table, njobs, blocks, stream);
+}
+
 hipError_t gemv_mfma_stream_slots(int m, bool mx, int seg_cols, int* slots) {
   const size_t lds = (size_t)gemv_mfma_stream_lds(m, seg_cols);
   const int threads = kMfmaStreamWaves * kWave;
@@ -1160,15 +1252,19 @@ hipError_t gemv_mfma_stream_slots(int m, bool mx, int seg_cols, int* slots) {
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess) {
     if (m <= 16) {
-      e = mx ? allow_mfma_stream_lds<1, true>() : allow_mfma_stream_lds<1, false>();
+      e = mx ? allow_mfma_stream_lds<1, true, false>() : allow_mfma_stream_lds<1, false, false>();
       if (e == hipSuccess)
-        e = mx ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_stream_kernel<1, true>(), threads, lds)
-               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_stream_kernel<1, false>(), threads, lds);
+        e = mx ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_stream_kernel<1, true, false>(),
+                                                              threads, lds)
+               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_stream_kernel<1, false, false>(),
+                                                              threads, lds);
     } else {
-      e = mx ? allow_mfma_stream_lds<2, true>() : allow_mfma_stream_lds<2, false>();
+      e = mx ? allow_mfma_stream_lds<2, true, false>() : allow_mfma_stream_lds<2, false, false>();
       if (e == hipSuccess)
-        e = mx ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_stream_kernel<2, true>(), threads, lds)
-               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_stream_kernel<2, false>(), threads, lds);
+        e = mx ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_stream_kernel<2, true, false>(),
+                                                              threads, lds)
+               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_stream_kernel<2, false, false>(),
+                                                              threads, lds);
     }
   }
   *slots = cus * (per_cu > 0 ? per_cu : 1);
@@ -1191,30 +1287,8 @@ hipError_t launch_gemv_w8a8(const GemvJob& job, const float* x_scale, int m, boo
 hipError_t launch_gemv_mfma_stream(const GemvJob* table, int njobs, int64_t blocks, int64_t tiles,
                                    int tiles_per_block, int m, int seg_cols, bool mx,
                                    hipStream_t stream) {
-  const size_t lds = (size_t)gemv_mfma_stream_lds(m, seg_cols);
-  const dim3 grid((unsigned)blocks), block(kMfmaStreamWaves * kWave);
-  constexpr int W = kMfmaStreamWaves;
-  hipError_t e;
-  if (m <= 16) {
-    e = mx ? allow_mfma_stream_lds<1, true>() : allow_mfma_stream_lds<1, false>();
-    if (e != hipSuccess) return e;
-    if (mx)
-      hipLaunchKernelGGL((k_gemv_mfma_stream<1, W, 2, true>), grid, block, lds, stream, table, njobs,
-                         (int)tiles, tiles_per_block, m, seg_cols);
-    else
-      hipLaunchKernelGGL((k_gemv_mfma_stream<1, W, 2, false>), grid, block, lds, stream, table, njobs,
-                         (int)tiles, tiles_per_block, m, seg_cols);
-  } else {
-    e = mx ? allow_mfma_stream_lds<2, true>() : allow_mfma_stream_lds<2, false>();
-    if (e != hipSuccess) return e;
-    if (mx)
-      hipLaunchKernelGGL((k_gemv_mfma_stream<2, W, 2, true>), grid, block, lds, stream, table, njobs,
-                         (int)tiles, tiles_per_block, m, seg_cols);
-    else
-      hipLaunchKernelGGL((k_gemv_mfma_stream<2, W, 2, false>), grid, block, lds, stream, table, njobs,
-                         (int)tiles, tiles_per_block, m, seg_cols);
-  }
-  return hipGetLastError();
+  const StreamJobs l{table, njobs, GemvJob{}};
+  return dispatch_mfma_stream<false>(l, blocks, tiles, tiles_per_block, m, seg_cols, mx, stream);
 }
 
 }  // namespace fp8w

@@ -1,0 +1,123 @@
+"""GPU parity of single GEMV calls on weights with many rows, which run on
+the wide VALU tiles (the streaming kernel at m = 1 with K <= 3072, one job
+passed by value) and on the streaming MFMA kernel with one job.
+
+Ragged N (not a multiple of 16 or 128) and ragged K (not a multiple of the
+256-column panel), every scale format, the AUTO route and both forced
+routes.  Codes and scales are seeded random inputs (finite codes, scales of
+the format's kind), so the oracle only runs the GEMV, on sampled rows that
+include both ends of the weight and the tile boundaries.
+"""
+import numpy as np
+import pytest
+
+from fp8_block_scaled_02_amd import workloads as W
+from gpu_util import assert_within_bound, bf16_to_f64, to_dev, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+FORMATS = ("block", "mx", "block_bf16", "row", "tensor")
+
+
+@pytest.fixture(scope="module")
+def fp8w():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    import fp8_block_scaled_02_amd as F
+    F.lib()
+    return F
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def _codes(rng, n, k):
+    c = rng.integers(0, 256, size=(n, k), dtype=np.uint8)
+    c[(c & 0x7F) == 0x7F] -= 1   # no NaN codes: 0x7F -> 0x7E, 0xFF -> 0xFE
+    return c
+
+
+def _scales(oracle_mod, rng, fmt, n, k):
+    shape = oracle_mod.scale_shape(fmt, n, k)
+    if fmt == "mx":
+        return rng.integers(117, 131, size=shape, dtype=np.uint8)
+    v = np.ldexp(rng.uniform(1.0, 2.0, size=shape), rng.integers(-12, -2, size=shape)).astype(np.float32)
+    if fmt == "block_bf16":
+        return (v.view(np.uint32) >> 16).astype(np.uint16)
+    return v
+
+
+def _dev_scales(fmt, s):
+    import torch
+    t = to_dev(np.ascontiguousarray(s))
+    return t.view(torch.bfloat16) if fmt == "block_bf16" else t
+
+
+def _rows(n, rng):
+    edges = {0, 1, 15, 16, 127, 128, n - 2, n - 1, n // 16 * 16 - 1, n // 16 * 16,
+             n // 128 * 128 - 1, n // 128 * 128}
+    rows = {r for r in edges if 0 <= r < n}
+    rows.update(int(r) for r in rng.choice(n, size=40, replace=False))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+@pytest.fixture(scope="module")
+def weights(fp8w, oracle_mod):
+    """One ragged weight per (n, k) and format, on the device and the host."""
+    cache = {}
+
+    def get(n, k, fmt):
+        key = (n, k, fmt)
+        if key not in cache:
+            rng = np.random.default_rng([n, k, FORMATS.index(fmt)])
+            c = _codes(rng, n, k)
+            s = _scales(oracle_mod, rng, fmt, n, k)
+            cache.clear()   # keep one weight alive at a time
+            cache[key] = (c, s, to_dev(c), _dev_scales(fmt, s))
+        return cache[key]
+    return get
+
+
+def _check(fp8w, oracle_mod, weights, n, k, m, fmt, route):
+    c, s, dc, ds = weights(n, k, fmt)
+    x = W.activation(90, m, k)
+    y = fp8w.fp8w_gemv(to_dev_bf16(x), dc, ds, fmt, route=route)
+    _sync()
+    rows = _rows(n, np.random.default_rng([n, m, route]))
+    y_ref, bound = oracle_mod.gemv_format_f64(x, c, s, fmt, rows=rows)
+    assert_within_bound(bf16_to_f64(y)[:, rows], y_ref, bound, f"n={n} k={k} m={m} {fmt} route={route}")
+
+
+# VALU: m = 1 with K <= 3072 takes the streaming kernel, one job by value
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_valu_stream_single_job(fp8w, oracle_mod, weights, fmt):
+    _check(fp8w, oracle_mod, weights, 16405, 2064, 1, fmt, 0)
+
+
+# VALU wide tiles without streaming: K above the streaming limit, m = 2
+# (AUTO) and forced VALU up to m = 8
+@pytest.mark.parametrize("fmt", ("block", "mx", "row"))
+@pytest.mark.parametrize("m,k", [(1, 4112), (2, 2064), (3, 1040), (8, 4112)])
+def test_valu_wide_single_call(fp8w, oracle_mod, weights, fmt, m, k):
+    import fp8_block_scaled_02_amd as F
+    _check(fp8w, oracle_mod, weights, 16405, k, m, fmt, F.ROUTE_VALU if m > 2 else 0)
+
+
+# MFMA: the streaming kernel with one job from 32768 rows, and from 16384
+# rows when m > 16; m = 16 at 16405 rows stays on the single-call kernel
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("n,m", [(32813, 3), (32813, 9), (32813, 16), (32813, 17), (32813, 32),
+                                 (16405, 16), (16405, 17), (16405, 32)])
+def test_mfma_stream_single_job(fp8w, oracle_mod, weights, fmt, n, m):
+    _check(fp8w, oracle_mod, weights, n, 1040, m, fmt, 0)
+
+
+# forced MFMA at m = 1 and 2 on the streaming kernel, K over several
+# LDS segments at m = 32 (K = 4112 at 2 bytes x 32 rows)
+@pytest.mark.parametrize("fmt", ("block", "mx"))
+@pytest.mark.parametrize("m,k", [(1, 2064), (2, 1040), (32, 4112)])
+def test_mfma_stream_single_job_forced(fp8w, oracle_mod, weights, fmt, m, k):
+    import fp8_block_scaled_02_amd as F
+    _check(fp8w, oracle_mod, weights, 32813, k, m, fmt, F.ROUTE_MFMA)

@@ -323,8 +323,34 @@ __global__ __launch_bounds__(kThreads) void k_gemv_valu(GemvJob arg, const GemvJ
 template <int R, int C, bool MX>
 struct TileRegs {
   uint4 w[R][C];
-  float s[R][C];   // MX: per row and chunk; block: row 0 holds the chunk scales
+  float s[C];         // block: the scale of each chunk's 128-column block
+  uint32_t e[2];      // MX: the wave's R rows of exponent bytes, 4 per lane (two halves)
 };
+
+// MX exponents of a wave's R rows: rows row0..row0+R-1 are contiguous in the
+// [n, groups] array, R * groups <= 512 bytes, read as dwords (lane l: bytes
+// 4l and 256 + 4l of the span) instead of one byte load per row and chunk.
+// row0 is a multiple of R = 4, so with a 4-byte aligned base every dword is
+// aligned; the last dword of a job is assembled from bytes when it would
+// reach past row n-1.
+__device__ __forceinline__ void mx_span_issue(const GemvJob& j, int row0, int rows, int groups,
+                                              uint32_t (&e)[2]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint8_t* __restrict__ e8 = static_cast<const uint8_t*>(j.scales);
+  const int valid = max(0, min(j.n - row0, rows)) * groups;   // bytes of the span inside the array
+  const size_t base = (size_t)row0 * groups;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int off = 4 * (lane + kWave * h);
+    uint32_t v = 0;
+    if (off + 4 <= valid) {
+      v = ld_global<uint32_t>(e8, base + off);
+    } else if (off < valid) {
+      for (int b = 0; b < valid - off; ++b) v |= (uint32_t)ld_global<uint8_t>(e8, base + off + b) << (8 * b);
+    }
+    e[h] = v;
+  }
+}
 
 __device__ __forceinline__ void load_job_row(const GemvJob* __restrict__ jobs, int jn, GemvJob& job) {
   const size_t row = (size_t)jn * sizeof(GemvJob);
@@ -390,7 +416,6 @@ __device__ __forceinline__ void stream_issue(const GemvJob& j, int tile, TileReg
   const int nch = j.k / 16;
   const int tiles_k = (j.k + kTile - 1) / kTile;
   const int groups = (j.k + kGroup - 1) / kGroup;
-  const uint8_t* __restrict__ e8 = static_cast<const uint8_t*>(j.scales);
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int row = row0 + r;
@@ -398,18 +423,16 @@ __device__ __forceinline__ void stream_issue(const GemvJob& j, int tile, TileReg
     for (int c = 0; c < C; ++c) {
       const int ch = lane + kWave * c;
       t.w[r][c] = make_uint4(0, 0, 0, 0);
-      t.s[r][c] = 0.0f;
-      if (ch < nch && row < j.n) {
-        t.w[r][c] = ld_stream_u4(j.codes, (size_t)row * j.k + ch * 16);
-        if (MX) t.s[r][c] = mx_scale(ld_global<uint8_t>(e8, (size_t)row * groups + ch / 2));
-      }
+      if (ch < nch && row < j.n) t.w[r][c] = ld_stream_u4(j.codes, (size_t)row * j.k + ch * 16);
     }
   }
-  if (!MX) {
+  if (MX) {
+    mx_span_issue(j, row0, R, groups, t.e);
+  } else {
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       const int ch = lane + kWave * c;
-      t.s[0][c] = ch < nch ? block_scale(j, tile * kRows, ch >> 3, tiles_k) : 0.0f;
+      t.s[c] = ch < nch ? block_scale(j, tile * kRows, ch >> 3, tiles_k) : 0.0f;
     }
   }
 }
@@ -421,7 +444,9 @@ __global__ __launch_bounds__(kThreads) void k_gemv_valu_stream(const GemvJob* __
   const JobList jobs{table, njobs, one};
   constexpr int kRows = kWaves * R, kSeg = 1024 * C;
   static_assert(kTile % kRows == 0, "a tile must stay inside one 128-row block");
+  static_assert(!MX || (R == 4 && kSeg / kGroup * R <= 2 * 4 * kWave), "MX exponent span: two dwords per lane");
   __shared__ __align__(16) uint16_t xs[kSeg];
+  __shared__ __align__(16) uint32_t ex[MX ? kWaves * 2 * kWave : 1];   // each wave's exponent span
   const int t_begin = blockIdx.x * tiles_per_block;
   const int t_end = min(total_tiles, t_begin + tiles_per_block);
   if (t_begin >= t_end) return;   // whole workgroup: no barrier is skipped by part of it
@@ -453,6 +478,15 @@ __global__ __launch_bounds__(kThreads) void k_gemv_valu_stream(const GemvJob* __
 
     const int row0 = (t - j.item0) * kRows + wave * R;
     const int nch = j.k / 16;
+    const int groups = (j.k + kGroup - 1) / kGroup;
+    // MX: this wave's exponent span through its own LDS slice (one wave's
+    // LDS operations complete in order, so no barrier)
+    uint32_t* exw = ex + (MX ? wave * 2 * kWave : 0);
+    if (MX) {
+      exw[lane] = cur.e[0];
+      exw[kWave + lane] = cur.e[1];
+    }
+    const uint8_t* exb = reinterpret_cast<const uint8_t*>(exw);
     float acc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = 0.0f;
@@ -467,7 +501,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv_valu_stream(const GemvJob* __
           const uint4 d = cur.w[r][c];
           const bf16x2 w[8] = {cvt_lo(d.x), cvt_hi(d.x), cvt_lo(d.y), cvt_hi(d.y),
                                cvt_lo(d.z), cvt_hi(d.z), cvt_lo(d.w), cvt_hi(d.w)};
-          const float sc = MX ? cur.s[r][c] : cur.s[0][c];
+          const float sc = MX ? mx_scale(exb[r * groups + ch / 2]) : cur.s[c];
           acc[r] = __builtin_fmaf(sc, dot16(w, x0, x1), acc[r]);
         }
       }
@@ -536,14 +570,29 @@ __device__ __forceinline__ void panel_issue(const GemvJob& j, int row0, int p, b
     if (live && row < j.n && col < j.k) r.v[q] = ld_stream_u4(j.codes, (size_t)row * j.k + col);
   }
   if (MX) {
+    // Lane l needs the exponents of groups 8p + 2c + (l/16)/2, c = 0..3, of
+    // row l%16: all inside the row's 8 bytes for this panel.  When every row
+    // starts 8-byte aligned (groups % 8 == 0, aligned base) one 8-byte load
+    // brings them; otherwise one byte load per chunk.
     const int row = row0 + (lane & 15);
     const uint8_t* __restrict__ e8 = static_cast<const uint8_t*>(j.scales);
+    if ((groups & 7) == 0 && (reinterpret_cast<uintptr_t>(e8) & 7) == 0) {
+      u32x2 w = {0u, 0u};
+      if (live && row < j.n && p * kPanelCols < j.k) w = ld_global<u32x2>(e8, (size_t)row * groups + 8 * p);
+      const int sh = 8 * ((lane >> 5) & 1);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int kx = p * kPanelCols + 64 * c + 16 * (lane >> 4);   // block c/2, chunk c%2
-      r.s[c] = 0.0f;
-      if (live && row < j.n && kx < j.k)
-        r.s[c] = mx_scale(ld_global<uint8_t>(e8, (size_t)row * groups + kx / kGroup));
+      for (int c = 0; c < 4; ++c)
+        r.s[c] = (live && row < j.n && p * kPanelCols < j.k)
+                     ? mx_scale((uint8_t)(((c < 2 ? w.x : w.y) >> (16 * (c & 1) + sh)) & 0xFF))
+                     : 0.0f;
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int kx = p * kPanelCols + 64 * c + 16 * (lane >> 4);   // block c/2, chunk c%2
+        r.s[c] = 0.0f;
+        if (live && row < j.n && kx < j.k)
+          r.s[c] = mx_scale(ld_global<uint8_t>(e8, (size_t)row * groups + kx / kGroup));
+      }
     }
   } else {
     r.s[0] = r.s[1] = 0.0f;
@@ -1185,7 +1234,8 @@ hipError_t run_mfma_stream(const StreamJobs& l, int64_t blocks, int64_t tiles, i
 hipError_t launch_gemv(const GemvJob& job, int m, bool mx, int route, hipStream_t stream) {
   if (route == 1) {
     const bool wide = job.n >= kSingleWideMinRowsValu;
-    if (wide && m == 1 && job.k <= gemv_stream_max_k()) {
+    if (wide && m == 1 && job.k <= gemv_stream_max_k() &&
+        (!mx || reinterpret_cast<uintptr_t>(job.scales) % 4 == 0)) {
       StreamJobs l{nullptr, 1, job};
       l.one.item0 = 0;
       const int64_t tiles = (job.n + gemv_stream_rows() - 1) / gemv_stream_rows();

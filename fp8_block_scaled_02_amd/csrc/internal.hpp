@@ -66,7 +66,8 @@ hipError_t launch_gemv(const GemvJob& job, int m, bool mx, int route, hipStream_
 hipError_t launch_gemv_grouped(const GemvJob* device_table, int njobs, int64_t blocks, int m,
                                bool mx, hipStream_t stream);
 
-// Streaming grouped VALU kernel (m = 1, every K <= gemv_stream_max_k()):
+// Streaming grouped VALU kernel (m = 1, every K <= gemv_stream_max_k(), MX
+// exponent arrays 4-byte aligned):
 // tiles of gemv_stream_rows() rows, a contiguous run of tiles per workgroup.
 int gemv_stream_max_k();
 int gemv_stream_rows();

@@ -153,3 +153,41 @@ def test_grouped_streaming_kernel_matches_oracle(fp8w, oracle_mod, fmt, case):
     for (n, k, c, s), x, y in zip(jobs, xs_h, ys):
         y_ref, bound = ref(x, c, s)
         assert_within_bound(bf16_to_f64(y), y_ref, bound, f"stream {fmt} [{n}x{k}]")
+
+
+def _offset_dev(a: np.ndarray, off: int):
+    """Device copy of a uint8 array starting `off` bytes past an aligned
+    allocation (torch allocations are 256-byte aligned)."""
+    import torch
+    buf = torch.zeros(a.size + off, dtype=torch.uint8, device="cuda")
+    buf[off:].copy_(to_dev(np.ascontiguousarray(a).reshape(-1)))
+    return buf[off:].view(a.shape)
+
+
+@pytest.mark.parametrize("off", [0, 1, 4])
+@pytest.mark.parametrize("m", [1, 8, 17])
+def test_mx_exponent_alignment_paths(fp8w, oracle_mod, off, m):
+    """MX exponents at every alignment: the streaming VALU kernel reads them
+    as dwords only when 4-byte aligned; the MFMA panels read 8 bytes at once
+    only when 8-byte aligned with groups % 8 == 0 (K = 240 and 496 have
+    groups % 8 == 0 without K % 256 == 0).  Grouped plans and single calls."""
+    shapes = [(37, 240), (130, 496), (300, 2048), (61, 2064), (129, 1040), (7, 3056)]
+    jobs = []
+    for i, (n, k) in enumerate(shapes):
+        bits = W.gaussian_weight(43, i, n, k, heavy_tail=True)
+        c, e = oracle_mod.quantize_mx(bits)
+        jobs.append((n, k, c, e))
+    xs_h = [W.activation(44, m, k) for (_, k, _, _) in jobs]
+    xs = [to_dev_bf16(x) for x in xs_h]
+    codes = [to_dev(c) for (_, _, c, _) in jobs]
+    exps = [_offset_dev(e, off) for (_, _, _, e) in jobs]
+    plan = fp8w.fp8w_grouped_plan_init(xs, codes, exps, fmt="mx")
+    if m == 1:
+        assert (plan.plan.tiles_per_block > 0) == (off % 4 == 0)
+    ys = fp8w.fp8w_gemv_grouped(plan)
+    ys_single = [fp8w.fp8w_gemv_mx(x, c, e) for x, c, e in zip(xs, codes, exps)]
+    _sync()
+    for (n, k, c, e), x, yg, ysg in zip(jobs, xs_h, ys, ys_single):
+        y_ref, bound = oracle_mod.gemv_mx_f64(x, c, e)
+        assert_within_bound(bf16_to_f64(yg), y_ref, bound, f"grouped mx off={off} m={m} [{n}x{k}]")
+        assert_within_bound(bf16_to_f64(ysg), y_ref, bound, f"single mx off={off} m={m} [{n}x{k}]")

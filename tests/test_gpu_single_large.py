@@ -121,3 +121,20 @@ def test_mfma_stream_single_job(fp8w, oracle_mod, weights, fmt, n, m):
 def test_mfma_stream_single_job_forced(fp8w, oracle_mod, weights, fmt, m, k):
     import fp8_block_scaled_02_amd as F
     _check(fp8w, oracle_mod, weights, 32813, k, m, fmt, F.ROUTE_MFMA)
+
+
+# MX exponents at an odd address: the single call leaves the streaming
+# kernel (which reads them as aligned dwords) for the wide VALU tiles
+@pytest.mark.parametrize("m", [1, 17])
+def test_mx_single_call_misaligned_exponents(fp8w, oracle_mod, weights, m):
+    import torch
+    n, k = 16405, 2064
+    c, s, dc, ds = weights(n, k, "mx")
+    buf = torch.zeros(s.size + 1, dtype=torch.uint8, device="cuda")
+    buf[1:].copy_(ds.reshape(-1))
+    x = W.activation(91, m, k)
+    y = fp8w.fp8w_gemv(to_dev_bf16(x), dc, buf[1:].view(s.shape), "mx")
+    _sync()
+    rows = _rows(n, np.random.default_rng([n, m, 7]))
+    y_ref, bound = oracle_mod.gemv_format_f64(x, c, s, "mx", rows=rows)
+    assert_within_bound(bf16_to_f64(y)[:, rows], y_ref, bound, f"misaligned mx m={m}")

@@ -36,13 +36,13 @@ PEAK_BF16 = 2.5e15         # MI355X dense bf16 MFMA, flop/s
 
 # HBM bytes per launch of the grouped M=1 streaming GEMV on the projection
 # set, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled by a 2 GiB device
-# copy (read factor 1.99993, write factor 1.0): 1339.37 MB read + 1.00 MB
+# copy (read factor 1.99993, write factor 1.0): 1339.39 MB read + 1.00 MB
 # written.  Valid only for the sources they were taken with (sha256 of the
 # kernel, launch-plan and helper sources); any change to those reports
 # traffic as null until the counters are retaken.
 COUNTED_TRAFFIC = {
-    "sources_sha256": "9c2cb404627cb48b03bed0cb7494cffd4448db2505b81e88849cee74c9b9b183",
-    "bytes_per_launch": 1340.37e6,
+    "sources_sha256": "7a5d0641e1153027d457c94679f6032cf7489a4dd335b716c87dd66ba5d5d654",
+    "bytes_per_launch": 1340.39e6,
 }
 TRAFFIC_SOURCES = ('gemv.hip', 'device.hpp', 'internal.hpp', 'api.cpp')
 
@@ -72,9 +72,14 @@ def parse():
     p.add_argument("--rows", default=",".join(ALL_ROWS))
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--ms", default="1,8,16", help="M values of the projection-set rows")
+    p.add_argument("--route", default="auto", choices=("auto", "valu", "mfma"),
+                   help="route of the projection-set rows (auto: the library's choice per M)")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="also run one device copy of this many MiB (counter calibration)")
-    return p.parse_args()
+    a = p.parse_args()
+    if a.route == "valu" and any(int(v) > 8 for v in a.ms.split(",") if v):
+        p.error("--route valu serves m <= 8 only")
+    return a
 
 
 # ------------------------------------------------------------ byte counts --
@@ -284,24 +289,25 @@ def bench_proj(torch, fp8w, lean, timer, W, args, state, log):
     ms = tuple(int(v) for v in args.ms.split(","))
     xs = activations(torch, W, 2, ms, (2560, 3072))
     rows, head = {}, None
+    route = {"auto": fp8w.ROUTE_AUTO, "valu": fp8w.ROUTE_VALU, "mfma": fp8w.ROUTE_MFMA}[args.route]
     for m in ms:
         ys = [torch.empty((m, c.shape[0]), dtype=torch.bfloat16, device="cuda") for c in codes]
         calls = [(xs[(m, c.shape[1])], c, s, y) for c, s, y in zip(codes, scales, ys)]
         nbytes = sum(gemv_bytes_block(m, c.shape[0], c.shape[1]) for c in codes)
-        plan = fp8w.fp8w_grouped_plan_init([x for x, _, _, _ in calls], codes, scales, ys)
+        plan = fp8w.fp8w_grouped_plan_init([x for x, _, _, _ in calls], codes, scales, ys, route=route)
         # one kernel per pass: launched directly (a one-kernel graph replay
         # adds 8-20 us of launch overhead per replay on ROCm)
         per, total = timer.run(lean.grouped(plan), args.steps, args.warmup)
         row = {"grouped": dict(summarize(per, len(calls), nbytes), launches_per_pass=1,
                                ms_per_pass=round(statistics.median(per), 4),
                                kernel="streaming" if plan.plan.tiles_per_block > 0 else "one tile per workgroup")}
-        g = graph_of(torch, lean.gemv_block(calls))
+        g = graph_of(torch, lean.gemv_block(calls, route))
         per_c, _ = timer.run(g.replay, args.steps, args.warmup)
         row["per_call"] = dict(summarize(per_c, len(calls), nbytes), launches_per_pass=len(calls),
                                ms_per_pass=round(statistics.median(per_c), 4))
         del g
         row.update({"bytes_per_pass": nbytes, "route": "valu" if plan.route == fp8w.ROUTE_VALU else "mfma"})
-        if m == 1:
+        if m == 1 and route == fp8w.ROUTE_AUTO:
             head = {"per": per, "total_ms": total, "bytes": nbytes, "calls": len(calls), "row": row}
         rows[f"m{m}"] = row
         log(f"proj m={m}: {row}")
@@ -598,6 +604,32 @@ def bench_single(torch, fp8w, lean, timer, W, args, log):
     return {"single_1024x1024": out}
 
 
+# ------------------------------------------------------ HBM read ceiling --
+
+def read_ceiling(torch, fp8w, timer, log, gib=2, reps=100, warmup=150):
+    """GB/s of fp8w_read_ceiling over a `gib` GiB buffer: a kernel that only
+    reads HBM, with the GEMV's load pattern, in this session.  Warmed up for
+    ~45 ms like the GEMV (past the power-management transient: ten warm-up
+    reads leave the timed ones in its slow phase, 5 % low)."""
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    out = torch.empty(2048, dtype=torch.int32, device="cuda")
+    fn = fp8w.lib().fp8w_read_ceiling
+    a = (buf.data_ptr(), buf.numel(), out.data_ptr(), out.numel())
+    def launch():
+        rc = fn(*a, torch.cuda.current_stream().cuda_stream)
+        if rc:
+            raise RuntimeError(f"fp8w_read_ceiling failed: {rc}")
+    per, _ = timer.run(launch, reps, warmup)
+    med = statistics.median(per)
+    res = {"GBps": round(buf.numel() / (med * 1e-3) / 1e9, 1), "bytes": buf.numel(),
+           "ms_p50": round(med, 4), "kernel": "k_read_xor (16-byte non-temporal loads, XOR fold)"}
+    log(f"read ceiling: {res}")
+    del buf, out
+    torch.cuda.empty_cache()
+    return res
+
+
 # ------------------------------------------------------------ CPU baseline --
 
 def cpu_baseline(W, log, min_seconds=10.0, max_passes=40):
@@ -686,6 +718,7 @@ def main():
         if name in rows_wanted:
             rows.update(fn(torch, fp8w, lean, timer, W, args, log))
             torch.cuda.empty_cache()
+    ceiling = None if headline is None else read_ceiling(torch, fp8w, timer, log)
     cpu = None if args.no_cpu or headline is None else cpu_baseline(W, log)
 
     if headline is None:
@@ -725,7 +758,9 @@ def main():
                      "traffic_unit": "bytes per launch",
                      "kernel": "k_gemv_valu_stream<R=4, C=3, block> (grouped, m=1)",
                      "avg_launch_us": round(ms_per_step * 1e3, 3),
-                     "bytes_per_launch": headline["bytes"]},
+                     "bytes_per_launch": headline["bytes"],
+                     "read_ceiling_GBps": ceiling["GBps"],
+                     "frac_of_read_ceiling": round(value / ceiling["GBps"], 4)},
         "cpu_baseline": cpu,
         "rows": rows,
     }

@@ -66,6 +66,7 @@ SIGNATURES = {
     "fp8w_quantize_act": (_I, [_P, _I64, _I64, _P, _P, _P, _I64, _P]),
     "fp8w_gemv_block_w8a8": (_I, [_P, _P, _I64, _P, _P, _I64, _I64, _P, _P]),
     "fp8w_gemv_mx_w8a8": (_I, [_P, _P, _I64, _P, _P, _I64, _I64, _P, _P]),
+    "fp8w_read_ceiling": (_I, [_P, _I64, _P, _I64, _P]),
     "fp8w_grouped_table_bytes": (_I64, [_I64]),
     "fp8w_grouped_plan_init": (_I, [_P, _I64, _I64, _I, _I, _P, _P]),
     "fp8w_gemv_grouped": (_I, [_P, _P]),
@@ -421,6 +422,21 @@ def fp8w_gemm_mx(x, codes, e8m0, y=None, workspace=None, stream=None):
 
 
 # ------------------------------------------------------------------- W8A8 --
+
+def fp8w_read_ceiling(buf, out=None, stream=None):
+    """Read every byte of the contiguous GPU tensor ``buf`` once (measurement
+    aid: the practical HBM read ceiling); returns the per-workgroup XOR words
+    (2048 int32 by default), whose XOR is the XOR of the buffer's dwords."""
+    torch = _torch()
+    if not isinstance(buf, torch.Tensor) or buf.device.type != "cuda" or not buf.is_contiguous():
+        raise ValueError("fp8w_read_ceiling: buf must be a contiguous GPU tensor")
+    if out is None:
+        out = torch.empty(2048, dtype=torch.int32, device=buf.device)
+    _require(out, (torch.int32,), "out", 1)
+    _check(lib().fp8w_read_ceiling(buf.data_ptr(), buf.numel() * buf.element_size(), out.data_ptr(),
+                                   out.numel(), _stream_handle(stream)), "fp8w_read_ceiling")
+    return out
+
 
 def fp8w_quantize_act(x, codes=None, scale=None, workspace=None, stream=None):
     """Per-tensor activation quantization: bf16 x [m,k] -> (e4m3 codes u8

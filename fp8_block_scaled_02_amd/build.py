@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfp8w.so")
-SOURCES = ["quantize.hip", "gemv.hip", "dequant.hip", "gemm.cpp", "api.cpp"]
+SOURCES = ["quantize.hip", "gemv.hip", "dequant.hip", "read_ceiling.hip", "gemm.cpp", "api.cpp"]
 ARCH = "gfx950"
 
 FLAGS = [

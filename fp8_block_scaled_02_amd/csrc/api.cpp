@@ -428,6 +428,18 @@ FP8W_API int64_t fp8w_mx_scale_count(int64_t n, int64_t k) {
   return (n < 1 || k < 1) ? 0 : mx_count(n, k);
 }
 
+FP8W_API fp8w_status fp8w_read_ceiling(const void* buf, int64_t bytes, uint32_t* out, int64_t out_words,
+                                       void* stream) {
+  if (!buf || !out) return FP8W_ERR_NULL;
+  if (bytes < 16 || bytes % 16 != 0 || out_words < 1 || out_words > kMaxDim) return FP8W_ERR_SHAPE;
+  if (!aligned(buf, 16) || !aligned(out, 4)) return FP8W_ERR_ALIGN;
+  const Span o[1] = {{out, (uint64_t)out_words * 4}};
+  const Span in[1] = {{buf, (uint64_t)bytes}};
+  if (any_overlap(o, 1, in, 1)) return FP8W_ERR_OVERLAP;
+  const int64_t blocks = fp8w::read_ceiling_blocks(bytes, out_words);
+  return from_hip(fp8w::launch_read_ceiling(buf, bytes, out, blocks, static_cast<hipStream_t>(stream)));
+}
+
 FP8W_API const char* fp8w_status_string(fp8w_status status) {
   switch (status) {
     case FP8W_OK: return "FP8W_OK";

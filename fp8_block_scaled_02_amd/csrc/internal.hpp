@@ -86,4 +86,10 @@ hipError_t launch_gemv_mfma_stream(const GemvJob* device_table, int njobs, int64
                                    int64_t tiles, int tiles_per_block, int m, int seg_cols,
                                    bool mx, hipStream_t stream);
 
+// Read-only pass over `bytes` (a multiple of 16) of device memory, one
+// 32-bit XOR per workgroup into out[0 .. blocks).
+int64_t read_ceiling_blocks(int64_t bytes, int64_t max_blocks);
+hipError_t launch_read_ceiling(const void* buf, int64_t bytes, uint32_t* out, int64_t blocks,
+                               hipStream_t stream);
+
 }  // namespace fp8w

@@ -374,6 +374,19 @@ int64_t fp8w_block_scale_count(int64_t n, int64_t k);
 /* Number of e8m0 bytes for [n, k]: n * ceil(k/32); 0 if n < 1 or k < 1. */
 int64_t fp8w_mx_scale_count(int64_t n, int64_t k);
 
+/* Measurement aid, not part of the method: read `bytes` of device memory
+ * at `buf` once, as the GEMV reads its weight stream (16-byte non-temporal
+ * loads over a grid sized to the chip), and write one 32-bit XOR of the
+ * data per workgroup to `out`.  The rate of this call is the practical HBM
+ * read ceiling that the weight-streaming kernels are compared with, beside
+ * the published peak.  `out` holds `out_words` words (caller-owned device
+ * memory); the grid is min(out_words, ceil(bytes / 32768)) workgroups, and
+ * 2048 words fill MI355X.  Asynchronous, allocation-free.  Errors: NULL,
+ * SHAPE (bytes < 16, bytes % 16 != 0, out_words < 1), ALIGN (buf not
+ * 16-byte or out not 4-byte aligned), OVERLAP, HIP. */
+fp8w_status fp8w_read_ceiling(const void* buf, int64_t bytes, uint32_t* out, int64_t out_words,
+                              void* stream);
+
 /* Static, NUL-terminated name of a status code. */
 const char* fp8w_status_string(fp8w_status status);
 

@@ -118,6 +118,18 @@ def test_dequantize_argument_errors(F):
     assert x(B, C + 1, 64, 64, C - 8, None) == F.ERR_OVERLAP    # e8m0 needs no alignment
 
 
+def test_read_ceiling_argument_errors(F):
+    r = F.lib().fp8w_read_ceiling
+    assert r(None, 64, D, 4, None) == F.ERR_NULL
+    assert r(B, 64, None, 4, None) == F.ERR_NULL
+    assert r(B, 0, D, 4, None) == F.ERR_SHAPE
+    assert r(B, 40, D, 4, None) == F.ERR_SHAPE                 # not a multiple of 16
+    assert r(B, 64, D, 0, None) == F.ERR_SHAPE
+    assert r(B + 8, 64, D, 4, None) == F.ERR_ALIGN
+    assert r(B, 64, D + 2, 4, None) == F.ERR_ALIGN
+    assert r(B, 64, B + 32, 4, None) == F.ERR_OVERLAP
+
+
 def test_gemm_argument_errors(F):
     L = F.lib()
     W = 0x20000000

@@ -72,6 +72,9 @@ def parse():
     p.add_argument("--rows", default=",".join(ALL_ROWS))
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--ms", default="1,8,16", help="M values of the projection-set rows")
+    p.add_argument("--cpu-sweep", action="store_true",
+                   help="also time the oracle's quantizers and GEMV (M = 1, 8, 16) on one "
+                        "[8192x2560] weight, on 1 thread and on all host threads")
     p.add_argument("--route", default="auto", choices=("auto", "valu", "mfma"),
                    help="route of the projection-set rows (auto: the library's choice per M)")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -666,6 +669,47 @@ def cpu_baseline(W, log, min_seconds=10.0, max_passes=40):
     return res
 
 
+def cpu_sweep(W, log):
+    """The oracle on one [8192x2560] projection weight: block and MX
+    quantization and the fp64 GEMV at M = 1, 8, 16, each on one thread and on
+    all host threads, as GB/s of algorithmic bytes."""
+    import platform
+    import oracle
+    w = W.WORKLOADS[2].weights[12]
+    n, k = w.n, w.k
+    bits = w.bits(2)
+    all_threads = oracle.max_threads()
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    out = {"weight": [n, k], "host_threads": all_threads, "cpu": model or platform.processor(), "ops": {}}
+
+    def timed(fn, nbytes):
+        t = time.perf_counter()
+        r = fn()
+        dt = time.perf_counter() - t
+        return r, {"seconds": round(dt, 3), "GBps": round(nbytes / dt / 1e9, 3)}
+
+    try:
+        for threads in (1, all_threads):
+            oracle.set_threads(threads)
+            (c, s), a = timed(lambda: oracle.quantize_block(bits), quant_bytes_block(n, k))
+            _, b = timed(lambda: oracle.quantize_mx(bits), quant_bytes_mx(n, k))
+            out["ops"][f"quantize_block_t{threads}"] = a
+            out["ops"][f"quantize_mx_t{threads}"] = b
+            for m in (1, 8, 16):
+                x = W.activation(2, m, k)
+                _, g = timed(lambda: oracle.gemv_block_f64(x, c, s), gemv_bytes_block(m, n, k))
+                out["ops"][f"gemv_block_m{m}_t{threads}"] = g
+    finally:
+        oracle.set_threads(all_threads)
+    log(f"cpu sweep: {out}")
+    return out
+
+
 # -------------------------------------------------------------------- main --
 
 def main():
@@ -720,6 +764,8 @@ def main():
             torch.cuda.empty_cache()
     ceiling = None if headline is None else read_ceiling(torch, fp8w, timer, log)
     cpu = None if args.no_cpu or headline is None else cpu_baseline(W, log)
+    if args.cpu_sweep:
+        rows["oracle_cpu_sweep"] = cpu_sweep(W, log)
 
     if headline is None:
         print(json.dumps({"rows": rows}))

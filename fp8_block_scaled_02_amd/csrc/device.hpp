@@ -63,28 +63,23 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// e4m3fn encoder: round |q| to the nearest representable magnitude with ties
-// to even, saturate at 448, keep the sign bit.  Works on the fp32 bit
-// pattern: in the normal range (|q| >= 2^-6) the top three mantissa bits are
-// kept and the 20 dropped bits round to nearest even, the carry ripples into
-// the exponent, and the exponent is rebiased from 127 to 7; below 2^-6 the
-// e4m3 grid is uniform with step 2^-9, so the code is |q| * 512 rounded to
-// the nearest even integer (0..8, where 8 is the smallest normal, 2^-6).
-// Inputs must not be NaN.
-__device__ __forceinline__ uint32_t e4m3_encode(float q) {
-  const uint32_t u = __float_as_uint(q);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  uint32_t code;
-  if (a >= kF32Bits448) {
-    code = 0x7Eu;
-  } else if (a >= kF32BitsMinNormalE4M3) {
-    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
-    code = (r >> 20) - (120u << 3);
-  } else {
-    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-  }
-  return sign | code;
+// e4m3fn codes by the hardware conversion (v_cvt_pk_fp8_f32: round to
+// nearest even, OCP e4m3fn on gfx950, sign kept, -0 -> 0x80) after clamping
+// to [-448, 448], which is the saturation.  Measured on MI355X over every
+// non-NaN fp32 bit pattern, in both byte positions of the packed result: the
+// byte equals an integer RNE encoder of the bit pattern (top three mantissa
+// bits kept, 20 dropped bits rounded to nearest even, exponent rebiased; the
+// uniform 2^-9 grid below 2^-6) in every case.  Inputs must not be NaN.
+__device__ __forceinline__ float clamp448(float q) { return __builtin_fminf(__builtin_fmaxf(q, -448.0f), 448.0f); }
+
+// Four codes packed little-endian: a in bits 0-7, ..., d in bits 24-31.
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clamp448(c), clamp448(d), lo, true);
+}
+
+__device__ __forceinline__ uint32_t e4m3_code(float q) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clamp448(q), 0.0f, 0, false) & 0xFFu;
 }
 
 // MX exponent of a group from its amax (the fp32 bit pattern of a

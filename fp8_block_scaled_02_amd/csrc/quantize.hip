@@ -29,14 +29,12 @@ __device__ __forceinline__ uint32_t abs_max_pair(uint32_t d, uint32_t acc) {
 
 // Four codes of four packed bf16 (two dwords) divided by `scale`.
 __device__ __forceinline__ uint32_t encode4_div(uint32_t d0, uint32_t d1, float scale) {
-  return e4m3_encode(bf16_lo(d0) / scale) | (e4m3_encode(bf16_hi(d0) / scale) << 8) |
-         (e4m3_encode(bf16_lo(d1) / scale) << 16) | (e4m3_encode(bf16_hi(d1) / scale) << 24);
+  return e4m3_pack4(bf16_lo(d0) / scale, bf16_hi(d0) / scale, bf16_lo(d1) / scale, bf16_hi(d1) / scale);
 }
 
 // Four codes of four packed bf16 multiplied by a power of two.
 __device__ __forceinline__ uint32_t encode4_mul(uint32_t d0, uint32_t d1, float mul) {
-  return e4m3_encode(bf16_lo(d0) * mul) | (e4m3_encode(bf16_hi(d0) * mul) << 8) |
-         (e4m3_encode(bf16_lo(d1) * mul) << 16) | (e4m3_encode(bf16_hi(d1) * mul) << 24);
+  return e4m3_pack4(bf16_lo(d0) * mul, bf16_hi(d0) * mul, bf16_lo(d1) * mul, bf16_hi(d1) * mul);
 }
 
 // Block-wide max of a per-thread value (256 threads = 4 waves).
@@ -142,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_block_any(const uint16_t* __
     const int e = threadIdx.x + kThreads * j;
     const int row = ti * kTile + (e >> 7), col = tj * kTile + (e & 127);
     if (row < n && col < k)
-      codes[(size_t)row * k + col] = (uint8_t)e4m3_encode(__uint_as_float((uint32_t)v[j] << 16) / scale);
+      codes[(size_t)row * k + col] = (uint8_t)e4m3_code(__uint_as_float((uint32_t)v[j] << 16) / scale);
   }
 }
 
@@ -195,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_mx_any(const uint16_t* __res
   e8m0[t] = (uint8_t)(e + 127);
   const float mul = pow2_neg(e);
   for (int c = c0; c < c1; ++c)
-    codes[row * k + c] = (uint8_t)e4m3_encode(__uint_as_float((uint32_t)src[c] << 16) * mul);
+    codes[row * k + c] = (uint8_t)e4m3_code(__uint_as_float((uint32_t)src[c] << 16) * mul);
 }
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -240,7 +238,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_row(const uint16_t* __restri
     }
   } else {
     for (int c = lane; c < k; c += kWave)
-      codes[base + c] = (uint8_t)e4m3_encode(bf16_lo(ld_global<uint16_t>(w, (base + c) * 2)) / scale);
+      codes[base + c] = (uint8_t)e4m3_code(bf16_lo(ld_global<uint16_t>(w, (base + c) * 2)) / scale);
   }
 }
 
@@ -292,7 +290,7 @@ __device__ __forceinline__ void act_cast_range(const uint16_t* __restrict__ x, i
   } else {
     for (int64_t i = first; i < count; i += stride) {
       const uint32_t b = ld_global<uint16_t>(x, (size_t)i * 2);
-      codes[i] = (uint8_t)e4m3_encode(bf16_lo(b) / scale);
+      codes[i] = (uint8_t)e4m3_code(bf16_lo(b) / scale);
     }
   }
 }

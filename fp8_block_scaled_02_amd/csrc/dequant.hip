@@ -15,7 +15,7 @@ namespace fp8w {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kChunksPerThread = 4;   // 16-code chunks in flight per thread
+constexpr int kUnitsPerThread = 8;   // 8-code units in flight per thread
 
 __device__ __forceinline__ float pow2_e8m0(uint8_t e) {
   return __uint_as_float(e ? (uint32_t)e << 23 : 0x00400000u);   // 2^(e-127), exact
@@ -33,50 +33,55 @@ __device__ __forceinline__ float weight_scale(const void* scales, int format, in
   return ld_global<float>(scales, 0);
 }
 
-// Four codes of d times s -> four bf16 (two packed dwords).
-__device__ __forceinline__ uint2 dequant4(uint32_t d, float s) {
-  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(d, false);
-  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(d, true);
-  return make_uint2(f32_to_bf16_rne(lo.x * s) | (f32_to_bf16_rne(lo.y * s) << 16),
-                    f32_to_bf16_rne(hi.x * s) | (f32_to_bf16_rne(hi.y * s) << 16));
+// Eight codes (two dwords) times s -> eight bf16, rounded to nearest even
+// by the hardware conversion (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ u32x4 dequant8(u32x2 d, float s) {
+  u32x4 o;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(d[h], false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(d[h], true);
+    const bf16x2 a = {(__bf16)(lo.x * s), (__bf16)(lo.y * s)};
+    const bf16x2 b = {(__bf16)(hi.x * s), (__bf16)(hi.y * s)};
+    o[2 * h] = __builtin_bit_cast(uint32_t, a);
+    o[2 * h + 1] = __builtin_bit_cast(uint32_t, b);
+  }
+  return o;
 }
 
-// Vector path (k % 16 == 0, codes 16-B and out 16-B aligned): chunk c is
-// codes[c*16 .. c*16+15] of the flat [n, k] array; a chunk never straddles a
-// row, a 128-column block or a 32-column MX group.  Thread t of workgroup b
-// takes chunks (b*4 + u)*256 + t, u = 0..3: all loads first, then the
-// stores.
-template <bool MX>
+// Vector path (k % 8 == 0, codes 8-byte and out 16-byte aligned): unit u is
+// codes[8u .. 8u+7] of the flat [n, k] array, written as one 16-byte store
+// at out + 16u, so both the loads and the stores of a wave are contiguous.
+// A unit never straddles a row, a 128-column block or a 32-column MX group.
+// Thread t of workgroup b takes units (b*8 + i)*256 + t, i = 0..7: all
+// loads first, then the stores.  IDX is the index type of the row division
+// (32-bit when every unit index fits).
+template <bool MX, typename IDX>
 __global__ __launch_bounds__(kThreads) void k_dequant_vec(const uint8_t* __restrict__ codes,
                                                           const void* __restrict__ scales,
-                                                          uint16_t* __restrict__ out, int64_t chunks,
-                                                          int chunks_per_row, int scale_cols, int format) {
-  uint4 c[kChunksPerThread];
-  float s[kChunksPerThread];
+                                                          uint16_t* __restrict__ out, int64_t units,
+                                                          int units_per_row, int scale_cols, int format) {
+  u32x2 c[kUnitsPerThread];
+  float s[kUnitsPerThread];
 #pragma unroll
-  for (int u = 0; u < kChunksPerThread; ++u) {
-    const int64_t ch = ((int64_t)blockIdx.x * kChunksPerThread + u) * kThreads + threadIdx.x;
-    c[u] = make_uint4(0, 0, 0, 0);
-    s[u] = 0.0f;
-    if (ch < chunks) {
-      c[u] = ld_stream_u4(codes, (size_t)ch * 16);
-      const int64_t row = ch / chunks_per_row;
-      const int col = (int)(ch - row * chunks_per_row) * 16;
+  for (int i = 0; i < kUnitsPerThread; ++i) {
+    const int64_t u = ((int64_t)blockIdx.x * kUnitsPerThread + i) * kThreads + threadIdx.x;
+    c[i] = u32x2{0u, 0u};
+    s[i] = 0.0f;
+    if (u < units) {
+      c[i] = __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x2*)(codes + (size_t)u * 8));
+      const IDX row = (IDX)u / (IDX)units_per_row;
+      const int col = (int)((IDX)u - row * (IDX)units_per_row) * 8;
       if (MX)
-        s[u] = pow2_e8m0(ld_global<uint8_t>(scales, (size_t)row * scale_cols + col / kGroup));
+        s[i] = pow2_e8m0(ld_global<uint8_t>(scales, (size_t)row * scale_cols + col / kGroup));
       else
-        s[u] = weight_scale(scales, format, row, col, scale_cols);
+        s[i] = weight_scale(scales, format, (int64_t)row, col, scale_cols);
     }
   }
 #pragma unroll
-  for (int u = 0; u < kChunksPerThread; ++u) {
-    const int64_t ch = ((int64_t)blockIdx.x * kChunksPerThread + u) * kThreads + threadIdx.x;
-    if (ch < chunks) {
-      const uint2 a = dequant4(c[u].x, s[u]), b = dequant4(c[u].y, s[u]);
-      const uint2 d = dequant4(c[u].z, s[u]), e = dequant4(c[u].w, s[u]);
-      st_global<u32x4>(out, (size_t)ch * 32, u32x4{a.x, a.y, b.x, b.y});
-      st_global<u32x4>(out, (size_t)ch * 32 + 16, u32x4{d.x, d.y, e.x, e.y});
-    }
+  for (int i = 0; i < kUnitsPerThread; ++i) {
+    const int64_t u = ((int64_t)blockIdx.x * kUnitsPerThread + i) * kThreads + threadIdx.x;
+    if (u < units) st_global<u32x4>(out, (size_t)u * 16, dequant8(c[i], s[i]));
   }
 }
 
@@ -93,7 +98,7 @@ __global__ __launch_bounds__(kThreads) void k_dequant_any(const uint8_t* __restr
   const float s = MX ? pow2_e8m0(ld_global<uint8_t>(scales, (size_t)row * scale_cols + col / kGroup))
                      : weight_scale(scales, format, row, col, scale_cols);
   const f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8((uint32_t)codes[i], false);
-  out[i] = (uint16_t)f32_to_bf16_rne(v.x * s);
+  out[i] = __builtin_bit_cast(uint16_t, (__bf16)(v.x * s));
 }
 
 inline bool aligned_to(const void* p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
@@ -102,12 +107,17 @@ template <bool MX>
 hipError_t launch_dequant(const uint8_t* codes, const void* scales, int format, int64_t n, int64_t k,
                           uint16_t* out, hipStream_t stream) {
   const int scale_cols = (int)(MX ? (k + kGroup - 1) / kGroup : (k + kTile - 1) / kTile);
-  if (k % 16 == 0 && aligned_to(codes, 16) && aligned_to(out, 16)) {
-    const int64_t chunks = n * (k / 16);
-    const int64_t per_block = (int64_t)kThreads * kChunksPerThread;
-    const dim3 grid((unsigned)((chunks + per_block - 1) / per_block));
-    hipLaunchKernelGGL((k_dequant_vec<MX>), grid, dim3(kThreads), 0, stream, codes, scales, out, chunks,
-                       (int)(k / 16), scale_cols, format);
+  if (k % 8 == 0 && aligned_to(codes, 8) && aligned_to(out, 16)) {
+    const int64_t units = n * (k / 8);
+    const int64_t per_block = (int64_t)kThreads * kUnitsPerThread;
+    const dim3 grid((unsigned)((units + per_block - 1) / per_block));
+    // 32-bit row division when every unit index of the grid fits
+    if ((int64_t)grid.x * per_block <= 0xFFFFFFFFLL)
+      hipLaunchKernelGGL((k_dequant_vec<MX, uint32_t>), grid, dim3(kThreads), 0, stream, codes, scales, out,
+                         units, (int)(k / 8), scale_cols, format);
+    else
+      hipLaunchKernelGGL((k_dequant_vec<MX, int64_t>), grid, dim3(kThreads), 0, stream, codes, scales, out,
+                         units, (int)(k / 8), scale_cols, format);
   } else {
     const int64_t total = n * k;
     const dim3 grid((unsigned)((total + kThreads - 1) / kThreads));

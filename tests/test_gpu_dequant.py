@@ -67,6 +67,27 @@ def test_dequantize_matches_oracle_on_ragged_shapes(fp8w, oracle_mod, n, k, fmt)
 
 
 @pytest.mark.parametrize("fmt", ["block", "mx"])
+def test_dequantize_vector_path_on_8_byte_aligned_codes(fp8w, oracle_mod, fmt):
+    """Codes 8 bytes past an aligned allocation: the vector path's 8-byte
+    unit loads, with k % 16 == 8."""
+    import torch
+    n, k = 77, 1032
+    rng = np.random.default_rng(6)
+    codes = rng.choice(NON_NAN, size=(n, k)).astype(np.uint8)
+    buf = torch.empty(n * k + 8, dtype=torch.uint8, device="cuda")
+    buf[8:].copy_(torch.from_numpy(codes.reshape(-1)))
+    c = buf[8:].view(n, k)
+    if fmt == "block":
+        s = rng.uniform(1e-4, 1e-2, oracle_mod.block_scale_shape(n, k)).astype(np.float32)
+        got, want = fp8w.fp8w_dequantize_block(c, to_dev(s)), oracle_mod.dequant_block_bf16(codes, s)
+    else:
+        e = rng.integers(100, 130, oracle_mod.mx_scale_shape(n, k)).astype(np.uint8)
+        got, want = fp8w.fp8w_dequantize_mx(c, to_dev(e)), oracle_mod.dequant_mx_bf16(codes, e)
+    _sync()
+    assert np.array_equal(_bits(got), want)
+
+
+@pytest.mark.parametrize("fmt", ["block", "mx"])
 def test_dequantize_scalar_path_on_misaligned_codes(fp8w, oracle_mod, fmt):
     n, k = 256, 512                     # k % 16 == 0, but the codes pointer is odd
     rng = np.random.default_rng(5)

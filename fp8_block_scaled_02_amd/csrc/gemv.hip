@@ -41,6 +41,8 @@
 // weights must be finite in fp32 (|deq| < 2^128): only e8m0 bytes >= 247,
 // i.e. weights within 0.4 % of the bf16 maximum, can break that.
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 #include <stddef.h>
 
 #include "device.hpp"
@@ -209,17 +211,17 @@ template <int M, int R, int C>
 struct ValuShape {
   static constexpr int kRows = kWaves * R;
   static constexpr int kSeg = 1024 * C;
+  static constexpr int kSegGroups = kSeg / kGroup;   // MX exponents per row and segment
   static constexpr int kLdsX = M * kSeg * 2;
-  static constexpr int kLdsBytes = kLdsX + (kSeg / kTile) * 4;
+  static constexpr int kLdsScales = (kSeg / kTile) * 4;
+  static constexpr int kLdsBytes = kLdsX + (kLdsScales > kRows * kSegGroups ? kLdsScales : kRows * kSegGroups);
   static_assert(kTile % kRows == 0, "a workgroup must stay inside one 128-row block");
   static_assert(kLdsBytes <= 64 * 1024, "LDS budget");
 };
 
-template <int R, int C, bool MX>
-__device__ __forceinline__ void valu_load(const GemvJob& j, int row0, int seg0, int nch, int groups,
-                                          uint4 (&wv)[R][C], float (&ws)[R][C]) {
+template <int R, int C>
+__device__ __forceinline__ void valu_load(const GemvJob& j, int row0, int seg0, int nch, uint4 (&wv)[R][C]) {
   const int lane = threadIdx.x & (kWave - 1);
-  const uint8_t* __restrict__ e8 = static_cast<const uint8_t*>(j.scales);
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int row = row0 + r;
@@ -227,11 +229,32 @@ __device__ __forceinline__ void valu_load(const GemvJob& j, int row0, int seg0, 
     for (int c = 0; c < C; ++c) {
       const int ch = lane + kWave * c;
       wv[r][c] = make_uint4(0, 0, 0, 0);
-      ws[r][c] = 0.0f;
-      if (ch < nch && row < j.n) {
-        wv[r][c] = ld_stream_u4(j.codes, (size_t)row * j.k + seg0 + ch * 16);
-        if (MX) ws[r][c] = mx_scale(ld_global<uint8_t>(e8, (size_t)row * groups + (seg0 + ch * 16) / kGroup));
-      }
+      if (ch < nch && row < j.n) wv[r][c] = ld_stream_u4(j.codes, (size_t)row * j.k + seg0 + ch * 16);
+    }
+  }
+}
+
+// MX exponents of the workgroup's `rows` rows for the segment's `ng` groups
+// starting at group gs, into LDS rows of `ld` bytes (rows >= n read as 0).
+// When every row's exponents start 4-byte aligned (groups % 4 == 0, aligned
+// base; gs is a multiple of 4) they are read as dwords: each row's span then
+// ends on a dword inside the row.  Otherwise one byte per load.
+__device__ __forceinline__ void stage_exponents(const GemvJob& j, int row0, int rows, int groups, int gs, int ng,
+                                                unsigned char* ex, int ld) {
+  const uint8_t* __restrict__ e8 = static_cast<const uint8_t*>(j.scales);
+  if ((groups & 3) == 0 && (reinterpret_cast<uintptr_t>(e8) & 3) == 0) {
+    const int per_row = (ng + 3) / 4;
+    for (int u = threadIdx.x; u < rows * per_row; u += kThreads) {
+      const int r = u / per_row, d = u - r * per_row;
+      const int row = row0 + r;
+      const uint32_t v = row < j.n ? ld_global<uint32_t>(e8, (size_t)row * groups + gs + 4 * d) : 0u;
+      *reinterpret_cast<uint32_t*>(ex + r * ld + 4 * d) = v;
+    }
+  } else {
+    for (int u = threadIdx.x; u < rows * ng; u += kThreads) {
+      const int r = u / ng, g = u - r * ng;
+      const int row = row0 + r;
+      ex[r * ld + g] = row < j.n ? ld_global<uint8_t>(e8, (size_t)row * groups + gs + g) : (uint8_t)0;
     }
   }
 }
@@ -242,7 +265,8 @@ __global__ __launch_bounds__(kThreads) void k_gemv_valu(GemvJob arg, const GemvJ
   using S = ValuShape<M, R, C>;
   __shared__ __align__(16) unsigned char smem[S::kLdsBytes];
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
-  float* ss = reinterpret_cast<float*>(smem + S::kLdsX);
+  float* ss = reinterpret_cast<float*>(smem + S::kLdsX);            // block: the segment's block scales
+  unsigned char* ex = smem + S::kLdsX;                               // MX: [kRows][kSegGroups] exponents
 
   GemvJob j;
   int tile;
@@ -262,11 +286,13 @@ __global__ __launch_bounds__(kThreads) void k_gemv_valu(GemvJob arg, const GemvJ
     const int len = min(S::kSeg, j.k - seg0);
     const int nch = len / 16;
     uint4 cw[R][C];
-    float cs[R][C];
-    valu_load<R, C, MX>(j, row0, seg0, nch, groups, cw, cs);
+    valu_load<R, C>(j, row0, seg0, nch, cw);
     if (seg0 > 0) __syncthreads();   // the previous segment's LDS reads are done
     stage_x(j.x, M, M, j.k, seg0, len, len, xs, S::kSeg);
-    if (!MX) {
+    if (MX) {
+      stage_exponents(j, tile * S::kRows, S::kRows, groups, seg0 / kGroup, (len + kGroup - 1) / kGroup, ex,
+                      S::kSegGroups);
+    } else {
       const int nkb = (len + kTile - 1) / kTile;
       if ((int)threadIdx.x < nkb) ss[threadIdx.x] = block_scale(j, tile * S::kRows, seg0 / kTile + threadIdx.x, tiles_k);
     }
@@ -287,7 +313,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv_valu(GemvJob arg, const GemvJ
           const uint4 d = cw[r][c];
           const bf16x2 w[8] = {cvt_lo(d.x), cvt_hi(d.x), cvt_lo(d.y), cvt_hi(d.y),
                                cvt_lo(d.z), cvt_hi(d.z), cvt_lo(d.w), cvt_hi(d.w)};
-          const float s = MX ? cs[r][c] : bs;
+          const float s = MX ? mx_scale(ex[(wave * R + r) * S::kSegGroups + ch / 2]) : bs;
 #pragma unroll
           for (int m = 0; m < M; ++m) acc[r][m] = __builtin_fmaf(s, dot16(w, x0[m], x1[m]), acc[r][m]);
         }
@@ -1128,19 +1154,20 @@ constexpr auto mfma_stream_kernel() {
 }
 
 // The kernel needs more than the default 64 KB of dynamic LDS: raise the
-// limit once per device and variant.
+// limit once per device and variant.  Host threads may race here; setting
+// the attribute twice is harmless, so a relaxed flag suffices.
 template <int MT, bool MX, bool ONE>
 hipError_t allow_mfma_stream_lds() {
-  static bool done[64] = {};
+  static std::atomic<bool> done[64];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (!done[dev]) {
+  if (!done[dev].load(std::memory_order_relaxed)) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(mfma_stream_kernel<MT, MX, ONE>()),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kMfmaStreamLds);
     if (e != hipSuccess) return e;
-    done[dev] = true;
+    done[dev].store(true, std::memory_order_relaxed);
   }
   return hipSuccess;
 }

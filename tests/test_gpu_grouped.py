@@ -164,14 +164,18 @@ def _offset_dev(a: np.ndarray, off: int):
     return buf[off:].view(a.shape)
 
 
+@pytest.mark.parametrize("long_k", [False, True])
 @pytest.mark.parametrize("off", [0, 1, 4])
-@pytest.mark.parametrize("m", [1, 8, 17])
-def test_mx_exponent_alignment_paths(fp8w, oracle_mod, off, m):
-    """MX exponents at every alignment: the streaming VALU kernel reads them
-    as dwords only when 4-byte aligned; the MFMA panels read 8 bytes at once
-    only when 8-byte aligned with groups % 8 == 0 (K = 240 and 496 have
-    groups % 8 == 0 without K % 256 == 0).  Grouped plans and single calls."""
+@pytest.mark.parametrize("m", [1, 2, 8, 17])
+def test_mx_exponent_alignment_paths(fp8w, oracle_mod, off, m, long_k):
+    """MX exponents at every alignment: the streaming VALU kernel and the
+    per-call VALU kernel read them as dwords only when each row starts 4-byte
+    aligned; the MFMA panels read 8 bytes at once only when 8-byte aligned
+    with groups % 8 == 0 (K = 240 and 496 have groups % 8 == 0 without K %
+    256 == 0).  Grouped plans, single calls and forced-VALU single calls."""
     shapes = [(37, 240), (130, 496), (300, 2048), (61, 2064), (129, 1040), (7, 3056)]
+    if long_k:   # several K segments in the per-call VALU kernel; no streaming plan
+        shapes.append((19, 4240))
     jobs = []
     for i, (n, k) in enumerate(shapes):
         bits = W.gaussian_weight(43, i, n, k, heavy_tail=True)
@@ -182,12 +186,16 @@ def test_mx_exponent_alignment_paths(fp8w, oracle_mod, off, m):
     codes = [to_dev(c) for (_, _, c, _) in jobs]
     exps = [_offset_dev(e, off) for (_, _, _, e) in jobs]
     plan = fp8w.fp8w_grouped_plan_init(xs, codes, exps, fmt="mx")
-    if m == 1:
-        assert (plan.plan.tiles_per_block > 0) == (off % 4 == 0)
+    if m == 1:   # streaming only with aligned exponents and every K <= 3072
+        assert (plan.plan.tiles_per_block > 0) == (off % 4 == 0 and max(k for _, k in shapes) <= 3072)
     ys = fp8w.fp8w_gemv_grouped(plan)
     ys_single = [fp8w.fp8w_gemv_mx(x, c, e) for x, c, e in zip(xs, codes, exps)]
+    ys_valu = [fp8w.fp8w_gemv_mx(x, c, e, route=fp8w.ROUTE_VALU) if m <= 8 else None
+               for x, c, e in zip(xs, codes, exps)]
     _sync()
-    for (n, k, c, e), x, yg, ysg in zip(jobs, xs_h, ys, ys_single):
+    for (n, k, c, e), x, yg, ysg, ysv in zip(jobs, xs_h, ys, ys_single, ys_valu):
         y_ref, bound = oracle_mod.gemv_mx_f64(x, c, e)
         assert_within_bound(bf16_to_f64(yg), y_ref, bound, f"grouped mx off={off} m={m} [{n}x{k}]")
         assert_within_bound(bf16_to_f64(ysg), y_ref, bound, f"single mx off={off} m={m} [{n}x{k}]")
+        if ysv is not None:
+            assert_within_bound(bf16_to_f64(ysv), y_ref, bound, f"single valu mx off={off} m={m} [{n}x{k}]")

@@ -200,6 +200,22 @@ __device__ __forceinline__ void stage_x(const uint16_t* __restrict__ x, int rows
   }
 }
 
+// As stage_x for e4m3 activation codes x[0:rows, ...] (1 byte each), each
+// code widened to bf16 (exact) on the way into LDS.  len and seg0 are
+// multiples of 16 and x is 16-byte aligned, so every 8-code load is aligned.
+__device__ __forceinline__ void stage_x8(const uint8_t* __restrict__ x, int rows, int k, int seg0, int len,
+                                         uint16_t* xs, int ld) {
+  const int units = len / 8;
+  for (int u = threadIdx.x; u < rows * units; u += kThreads) {
+    const int r = u / units, c = (u - r * units) * 8;
+    const u32x2 v = ld_global<u32x2>(x, (size_t)r * k + seg0 + c);
+    const bf16x2 a = cvt_lo(v.x), b = cvt_hi(v.x), d = cvt_lo(v.y), e = cvt_hi(v.y);
+    *reinterpret_cast<u32x4*>(xs + r * ld + c) =
+        u32x4{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, d),
+              __builtin_bit_cast(uint32_t, e)};
+  }
+}
+
 // ------------------------------------------------------------------ VALU --
 //
 // Workgroup = 4 waves x R rows.  Wave w owns rows row0 + r (r < R); lane l
@@ -259,9 +275,12 @@ __device__ __forceinline__ void stage_exponents(const GemvJob& j, int row0, int 
   }
 }
 
-template <int M, int R, int C, bool MX, bool GROUPED>
+// X8: the activation is e4m3 codes (j.x points at bytes) with the fp32
+// tensor scale at *xscale (the W8A8 path at small m): the codes are widened
+// to bf16 while x is staged and the outputs are multiplied by the scale.
+template <int M, int R, int C, bool MX, bool GROUPED, bool X8 = false>
 __global__ __launch_bounds__(kThreads) void k_gemv_valu(GemvJob arg, const GemvJob* __restrict__ jobs,
-                                                        int njobs) {
+                                                        int njobs, const float* __restrict__ xscale = nullptr) {
   using S = ValuShape<M, R, C>;
   __shared__ __align__(16) unsigned char smem[S::kLdsBytes];
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
@@ -288,7 +307,8 @@ __global__ __launch_bounds__(kThreads) void k_gemv_valu(GemvJob arg, const GemvJ
     uint4 cw[R][C];
     valu_load<R, C>(j, row0, seg0, nch, cw);
     if (seg0 > 0) __syncthreads();   // the previous segment's LDS reads are done
-    stage_x(j.x, M, M, j.k, seg0, len, len, xs, S::kSeg);
+    if (X8) stage_x8(reinterpret_cast<const uint8_t*>(j.x), M, j.k, seg0, len, xs, S::kSeg);
+    else stage_x(j.x, M, M, j.k, seg0, len, len, xs, S::kSeg);
     if (MX) {
       stage_exponents(j, tile * S::kRows, S::kRows, groups, seg0 / kGroup, (len + kGroup - 1) / kGroup, ex,
                       S::kSegGroups);
@@ -327,14 +347,16 @@ __global__ __launch_bounds__(kThreads) void k_gemv_valu(GemvJob arg, const GemvJ
 #pragma unroll
     for (int m = 0; m < M; ++m) flat[r * M + m] = acc[r][m];
   const WaveSums<R * M> sums(flat);
+  const float xf = X8 ? ld_global<float>(xscale, 0) : 1.0f;
   if ((lane & 15) == 0) {
 #pragma unroll
     for (int q = 0; q < WaveSums<R * M>::kGroups; ++q) {
       const int f = 4 * q + (lane >> 4);   // value index r * M + m held by this row
       const int r = f / M, m = f % M;
-      if (f < R * M && row0 + r < j.n)
-        st_global<uint16_t>(j.y, ((size_t)m * j.n + row0 + r) * 2,
-                            (uint16_t)f32_to_bf16_rne(sums.g[q] * output_scale(j, row0 + r)));
+      if (f < R * M && row0 + r < j.n) {
+        const float v = sums.g[q] * output_scale(j, row0 + r);
+        st_global<uint16_t>(j.y, ((size_t)m * j.n + row0 + r) * 2, (uint16_t)f32_to_bf16_rne(X8 ? v * xf : v));
+      }
     }
   }
 }
@@ -1348,8 +1370,31 @@ hipError_t gemv_mfma_stream_slots(int m, bool mx, int seg_cols, int* slots) {
   return e;
 }
 
+namespace {
+
+template <int M, int R, int C, bool MX>
+hipError_t run_valu_x8(const GemvJob& job, const float* x_scale, hipStream_t stream) {
+  const int rows = kWaves * R;
+  hipLaunchKernelGGL((k_gemv_valu<M, R, C, MX, false, true>), dim3((unsigned)((job.n + rows - 1) / rows)),
+                     dim3(kThreads), 0, stream, job, nullptr, 1, x_scale);
+  return hipGetLastError();
+}
+
+template <bool MX>
+hipError_t dispatch_valu_x8(const GemvJob& job, const float* x_scale, int m, hipStream_t s) {
+  const bool wide = job.n >= kSingleWideMinRowsValu;
+  if (m == 1) return wide ? run_valu_x8<1, 4, 3, MX>(job, x_scale, s) : run_valu_x8<1, 1, 4, MX>(job, x_scale, s);
+  return wide ? run_valu_x8<2, 4, 2, MX>(job, x_scale, s) : run_valu_x8<2, 2, 4, MX>(job, x_scale, s);
+}
+
+}  // namespace
+
+// W8A8: m <= 2 on the VALU kernel with the codes widened while x is staged
+// (as the W8A16 route, which is faster than the MFMA kernel at these m);
+// larger m on the fp8 x fp8 MFMA.
 hipError_t launch_gemv_w8a8(const GemvJob& job, const float* x_scale, int m, bool mx,
                             hipStream_t stream) {
+  if (m <= 2) return mx ? dispatch_valu_x8<true>(job, x_scale, m, stream) : dispatch_valu_x8<false>(job, x_scale, m, stream);
   const dim3 grid((unsigned)((job.n + 15) / 16)), block(kThreads);
   if (m <= 16) {
     if (mx) hipLaunchKernelGGL((k_gemv_w8a8_direct<1, 2, true>), grid, block, 0, stream, job, x_scale, m);

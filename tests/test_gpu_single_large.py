@@ -138,3 +138,21 @@ def test_mx_single_call_misaligned_exponents(fp8w, oracle_mod, weights, m):
     rows = _rows(n, np.random.default_rng([n, m, 7]))
     y_ref, bound = oracle_mod.gemv_format_f64(x, c, s, "mx", rows=rows)
     assert_within_bound(bf16_to_f64(y)[:, rows], y_ref, bound, f"misaligned mx m={m}")
+
+
+# W8A8 at m <= 2 on many rows: the wide VALU tiles with the activation codes
+# widened to bf16 while x is staged.  dec(codes) is exact in bf16, so the
+# bf16 reference on the decoded codes, times the activation scale, applies.
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("m", [1, 2])
+def test_w8a8_small_m_many_rows(fp8w, oracle_mod, weights, fmt, m):
+    n, k = 16405, 2064
+    c, s, dc, ds = weights(n, k, fmt)
+    x = W.activation(92, m, k)
+    xc, xs = oracle_mod.quantize_act_tensor(x)
+    y = fp8w.fp8w_gemv_w8a8(to_dev(xc), to_dev(np.array([xs], np.float32)), dc, ds, fmt)
+    _sync()
+    rows = _rows(n, np.random.default_rng([n, m, 8]))
+    xb = (oracle_mod.e4m3_decode(xc).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    y_ref, bound = oracle_mod.gemv_format_f64(xb, c, s, fmt, rows=rows)
+    assert_within_bound(bf16_to_f64(y)[:, rows], xs * y_ref, xs * bound, f"w8a8 {fmt} m={m}")

@@ -239,3 +239,38 @@ def test_gemv_guard_bands_and_no_write_on_error(fp8w, oracle_mod):
                                     to_dev(scales).data_ptr(), n, k, yb2.data_ptr(), None)
     _sync()
     assert st == fp8w.ERR_SHAPE and (yb2 == 77.0).all()
+
+
+# ------------------------------------------------ minimal and long-K shapes --
+
+EDGE_GEMV = [(1, 16), (17, 16), (1, 65552), (3, 32784), (33, 4112)]
+
+
+@pytest.mark.parametrize("fmt", ["block", "mx"])
+@pytest.mark.parametrize("m", [1, 2, 8, 9, 16, 17, 32])
+def test_gemv_minimal_and_long_k_on_every_route(fp8w, oracle_mod, fmt, m):
+    """N = 1 and K = 16 (one 16-byte chunk, a tile and panel almost all
+    padding), and K up to 65552 (dozens of K segments on the VALU kernels,
+    many x segments on the streaming MFMA kernel): single calls on AUTO and
+    on both routes, and the same GEMVs as one grouped plan."""
+    routes = [fp8w.ROUTE_AUTO, fp8w.ROUTE_MFMA] + ([fp8w.ROUTE_VALU] if m <= 8 else [])
+    quant = oracle_mod.quantize_block if fmt == "block" else oracle_mod.quantize_mx
+    ref = oracle_mod.gemv_block_f64 if fmt == "block" else oracle_mod.gemv_mx_f64
+    jobs = []
+    for i, (n, k) in enumerate(EDGE_GEMV):
+        c, s = quant(W.gaussian_weight(17, i, n, k, outlier_rows=fmt == "block", heavy_tail=fmt == "mx"))
+        x = W.activation(17, m, k)
+        jobs.append((n, k, c, s, x, ref(x, c, s)))
+    dev = [(to_dev_bf16(x), to_dev(c), to_dev(s)) for (_, _, c, s, x, _) in jobs]
+    for r in routes:
+        for (n, k, _, _, _, (y_ref, bound)), (xd, cd, sd) in zip(jobs, dev):
+            y = fp8w.fp8w_gemv(xd, cd, sd, fmt, route=r)
+            _sync()
+            assert_within_bound(bf16_to_f64(y), y_ref, bound, f"{fmt} m={m} route={r} [{n}x{k}]")
+    for r in routes:
+        plan = fp8w.fp8w_grouped_plan_init([d[0] for d in dev], [d[1] for d in dev], [d[2] for d in dev],
+                                           fmt=fmt, route=r)
+        ys = fp8w.fp8w_gemv_grouped(plan)
+        _sync()
+        for (n, k, _, _, _, (y_ref, bound)), y in zip(jobs, ys):
+            assert_within_bound(bf16_to_f64(y), y_ref, bound, f"grouped {fmt} m={m} route={r} [{n}x{k}]")

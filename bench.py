@@ -36,13 +36,13 @@ PEAK_BF16 = 2.5e15         # MI355X dense bf16 MFMA, flop/s
 
 # HBM bytes per launch of the grouped M=1 streaming GEMV on the projection
 # set, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled by a 2 GiB device
-# copy (read factor 1.99993, write factor 1.0): 1339.37 MB read + 1.00 MB
+# copy (read factor 1.99993, write factor 1.0): 1339.38 MB read + 1.00 MB
 # written.  Valid only for the sources they were taken with (sha256 of the
 # kernel, launch-plan and helper sources); any change to those reports
 # traffic as null until the counters are retaken.
 COUNTED_TRAFFIC = {
-    "sources_sha256": "da5b6a14226877217c76c7c586c79bc27d9696c2a211ab9576df117a59b73ef6",
-    "bytes_per_launch": 1340.37e6,
+    "sources_sha256": "e5abc7c709f07861dcbc74010cf384a86e92eadec62f197566833a245f50324f",
+    "bytes_per_launch": 1340.38e6,
 }
 TRAFFIC_SOURCES = ('gemv.hip', 'device.hpp', 'internal.hpp', 'api.cpp')
 
@@ -89,6 +89,11 @@ def parse():
 
 def gemv_bytes_block(m, n, k):
     return n * k + 4 * (-(-n // TILE)) * (-(-k // TILE)) + 2 * m * k + 2 * m * n
+
+
+def w8a8_bytes_block(m, n, k):
+    """fp8 codes + block scales + fp8 activation codes and scale + bf16 y."""
+    return n * k + 4 * (-(-n // TILE)) * (-(-k // TILE)) + m * k + 4 + 2 * m * n
 
 
 def gemv_bytes_mx(m, n, k):
@@ -346,12 +351,28 @@ def bench_lm_head(torch, fp8w, lean, timer, W, args, log):
     out = {"quantize_block": dict(summarize(qper, 1, quant_bytes_block(n, k)), shape=[n, k])}
     del bf
     copies = [(c0, s0)] + [(c0.clone(), s0.clone()) for _ in range(3)]
+    lib = fp8w.lib()
     for m in wl.ms:
         x = upload_bf16(torch, W.activation(3, m, k))
         calls = [(x, c, s, torch.empty((m, n), dtype=torch.bfloat16, device="cuda")) for c, s in copies]
         g = graph_of(torch, lean.gemv_block(calls))
         per, _ = timer.run(g.replay, args.steps, args.warmup)
         out[f"gemv_m{m}"] = summarize(per, len(calls), len(calls) * gemv_bytes_block(m, n, k))
+        del g
+        # W8A8 on the same weights: activation quantized once, GEMV per call
+        xc, xs = fp8w.fp8w_quantize_act(x)
+        w8 = [(xc.data_ptr(), xs.data_ptr(), m, c.data_ptr(), s.data_ptr(), n, k, y.data_ptr())
+              for (_, c, s, y) in calls]
+
+        def run_w8():
+            st = torch.cuda.current_stream().cuda_stream
+            for a in w8:
+                rc = lib.fp8w_gemv_block_w8a8(*a, st)
+                if rc:
+                    raise RuntimeError(f"fp8w_gemv_block_w8a8 failed: {rc}")
+        g = graph_of(torch, run_w8)
+        per, _ = timer.run(g.replay, args.steps, args.warmup)
+        out[f"w8a8_gemv_m{m}"] = summarize(per, len(calls), len(calls) * w8a8_bytes_block(m, n, k))
         del g
     log(f"lm_head: {out}")
     return {"lm_head_151936x2048": out}

@@ -1110,6 +1110,75 @@ __global__ __launch_bounds__(kThreads) void k_gemv_w8a8_direct(GemvJob j, const 
   }
 }
 
+// Single calls on weights with many rows: one 128-row tile per workgroup, a
+// 16-row tile per wave over the whole K, the x codes staged once per tile in
+// LDS by K segments of seg_cols columns (rows of seg_cols + 16 bytes), so x
+// is read from L2 once per 128 rows instead of once per 16.
+template <int MT, bool MX>
+__global__ __launch_bounds__(8 * kWave) void k_gemv_w8a8_tiles(GemvJob j, const float* __restrict__ xs_scale,
+                                                               int m_rows, int seg_cols) {
+  constexpr int NW = 8, D = 2;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int i = lane & 15, g = lane >> 4;
+  unsigned char* pbuf = smem + wave * kPanelBytes;
+  unsigned char* xs = smem + NW * kPanelBytes;
+  const int ldx = seg_cols + 16;
+  const int seg_panels = seg_cols / kPanelCols;
+  const int row0 = blockIdx.x * (16 * NW) + 16 * wave;
+  const int np = (j.k + kPanelCols - 1) / kPanelCols;
+  const int nkb = (j.k + kTile - 1) / kTile;
+  const int groups = (j.k + kGroup - 1) / kGroup;
+  const uint8_t* __restrict__ xc = reinterpret_cast<const uint8_t*>(j.x);
+  // x codes [0, m_rows) x [seg0, seg0 + seg_cols) into LDS (columns < k only:
+  // the B reads never look past k)
+  auto stage = [&](int seg0) {
+    const int units = min(seg_cols, j.k - seg0) / 16;
+    for (int u = threadIdx.x; u < m_rows * units; u += NW * kWave) {
+      const int r = u / units, c = (u - r * units) * 16;
+      *reinterpret_cast<uint4*>(xs + r * ldx + c) = ld_global_u4(xc, (size_t)r * j.k + seg0 + c);
+    }
+  };
+
+  Panel8<MX> slot[D];
+#pragma unroll
+  for (int s = 0; s < D; ++s) panel8_issue<MX>(j, row0, s, s < np, nkb, groups, slot[s]);
+  stage(0);
+  __syncthreads();
+  f32x4 acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int p0 = 0; p0 < np; p0 += D) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      const int p = p0 + s;
+      if (p < np) {   // uniform over the workgroup
+        if (p > 0 && p % seg_panels == 0) {   // next K segment of x
+          __syncthreads();
+          stage(p * kPanelCols);
+          __syncthreads();
+        }
+        uint4 a[2][2];
+        panel_to_a(slot[s].v, pbuf, a);
+        Panel8<MX> cur;
+        cur.s[0] = slot[s].s[0], cur.s[1] = slot[s].s[1];
+        cur.e[0] = slot[s].e[0], cur.e[1] = slot[s].e[1];
+        panel8_issue<MX>(j, row0, p + D, p + D < np, nkb, groups, slot[s]);
+        const int kseg = (p % seg_panels) * kPanelCols, kp = p * kPanelCols;
+        panel8_mfma<MT, MX>(a, cur, [&](int t, int b, uint4& lo, uint4& hi) {
+          const int m = 16 * t + i;
+          const int kx = 128 * b + 16 * g;
+          lo = hi = make_uint4(0, 0, 0, 0);
+          if (m < m_rows && kp + kx < j.k) lo = *reinterpret_cast<const uint4*>(xs + m * ldx + kseg + kx);
+          if (m < m_rows && kp + kx + 64 < j.k) hi = *reinterpret_cast<const uint4*>(xs + m * ldx + kseg + kx + 64);
+        }, acc);
+      }
+    }
+  }
+  store_tile<MT>(j, row0, m_rows, acc, ld_global<float>(xs_scale, 0));
+}
+
 // ------------------------------------------------------------ dispatch --
 //
 // One compiled variant per (route, M, single/grouped), any N and K:
@@ -1387,14 +1456,53 @@ hipError_t dispatch_valu_x8(const GemvJob& job, const float* x_scale, int m, hip
   return wide ? run_valu_x8<2, 4, 2, MX>(job, x_scale, s) : run_valu_x8<2, 2, 4, MX>(job, x_scale, s);
 }
 
+// The 128-row W8A8 kernel's LDS: eight 4 KB panel buffers and the staged x
+// codes, within the same per-workgroup budget as the streaming MFMA kernel.
+int w8a8_tiles_seg_cols(int m, int64_t k) {
+  const int x_budget = kMfmaStreamLds - 8 * kPanelBytes;
+  const int cap = (x_budget / m - 16) / kPanelCols * kPanelCols;
+  const int64_t kmax = (k + kPanelCols - 1) / kPanelCols * kPanelCols;
+  if (kmax <= cap) return (int)kmax;
+  const int64_t nseg = (kmax + cap - 1) / cap;
+  const int64_t per = (kmax + nseg - 1) / nseg;
+  return (int)((per + kPanelCols - 1) / kPanelCols * kPanelCols);
+}
+
+template <int MT, bool MX>
+hipError_t run_w8a8_tiles(const GemvJob& job, const float* x_scale, int m, hipStream_t stream) {
+  static std::atomic<bool> done[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (!done[dev].load(std::memory_order_relaxed)) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_w8a8_tiles<MT, MX>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kMfmaStreamLds);
+    if (e != hipSuccess) return e;
+    done[dev].store(true, std::memory_order_relaxed);
+  }
+  const int seg = w8a8_tiles_seg_cols(m, job.k);
+  const size_t lds = (size_t)8 * kPanelBytes + (size_t)m * (seg + 16);
+  hipLaunchKernelGGL((k_gemv_w8a8_tiles<MT, MX>), dim3((unsigned)((job.n + 127) / 128)), dim3(8 * kWave), lds,
+                     stream, job, x_scale, m, seg);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 // W8A8: m <= 2 on the VALU kernel with the codes widened while x is staged
 // (as the W8A16 route, which is faster than the MFMA kernel at these m);
-// larger m on the fp8 x fp8 MFMA.
+// larger m on the fp8 x fp8 MFMA.  Above m = 8 on weights with many rows
+// (the W8A16 MFMA route's size rule), 128-row tiles with x staged in LDS:
+// lm_head [151936x2048] at m = 16 / 32 5.3 / 4.8 TB/s against 4.5 / 2.9 with
+// 16-row tiles; at m = 4 the 16-row tiles are ahead (6.1 against 5.8).
 hipError_t launch_gemv_w8a8(const GemvJob& job, const float* x_scale, int m, bool mx,
                             hipStream_t stream) {
   if (m <= 2) return mx ? dispatch_valu_x8<true>(job, x_scale, m, stream) : dispatch_valu_x8<false>(job, x_scale, m, stream);
+  if (m > 8 && single_call_streams_mfma(job.n, m)) {
+    if (m <= 16) return mx ? run_w8a8_tiles<1, true>(job, x_scale, m, stream) : run_w8a8_tiles<1, false>(job, x_scale, m, stream);
+    return mx ? run_w8a8_tiles<2, true>(job, x_scale, m, stream) : run_w8a8_tiles<2, false>(job, x_scale, m, stream);
+  }
   const dim3 grid((unsigned)((job.n + 15) / 16)), block(kThreads);
   if (m <= 16) {
     if (mx) hipLaunchKernelGGL((k_gemv_w8a8_direct<1, 2, true>), grid, block, 0, stream, job, x_scale, m);

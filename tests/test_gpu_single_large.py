@@ -156,3 +156,21 @@ def test_w8a8_small_m_many_rows(fp8w, oracle_mod, weights, fmt, m):
     xb = (oracle_mod.e4m3_decode(xc).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
     y_ref, bound = oracle_mod.gemv_format_f64(xb, c, s, fmt, rows=rows)
     assert_within_bound(bf16_to_f64(y)[:, rows], xs * y_ref, xs * bound, f"w8a8 {fmt} m={m}")
+
+
+# W8A8 from m = 9 on many rows: 128-row tiles with the x codes staged in LDS
+# (from 32768 rows, and from 16384 rows when m > 16); K = 4112 at m = 32 spans
+# several x segments.  m = 3 on many rows stays on the 16-row tiles.
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("n,m,k", [(32813, 3, 1040), (32813, 9, 2064), (32813, 16, 1040), (32813, 17, 1040),
+                                   (32813, 32, 4112), (16405, 17, 2064), (16405, 32, 1040)])
+def test_w8a8_tiles_many_rows(fp8w, oracle_mod, weights, fmt, n, m, k):
+    c, s, dc, ds = weights(n, k, fmt)
+    x = W.activation(93, m, k)
+    xc, xs = oracle_mod.quantize_act_tensor(x)
+    y = fp8w.fp8w_gemv_w8a8(to_dev(xc), to_dev(np.array([xs], np.float32)), dc, ds, fmt)
+    _sync()
+    rows = _rows(n, np.random.default_rng([n, m, 9]))
+    xb = (oracle_mod.e4m3_decode(xc).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    y_ref, bound = oracle_mod.gemv_format_f64(xb, c, s, fmt, rows=rows)
+    assert_within_bound(bf16_to_f64(y)[:, rows], xs * y_ref, xs * bound, f"w8a8 tiles {fmt} m={m} [{n}x{k}]")

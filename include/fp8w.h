@@ -2,7 +2,7 @@
  * fp8w.h -- C ABI of libfp8w: FP8 (OCP e4m3fn) weights for the decode path
  * on AMD Instinct MI355X (gfx950).
  *
- * Operations, each in two scale formats:
+ * Operations (each in every scale format below):
  *
  *   quantize    bf16 W[n,k]  ->  e4m3fn codes[n,k] + a scale grid
  *   GEMV        y[m,n] = x[m,k] . deq(W)^T, bf16 in, bf16 out, fp32
@@ -12,6 +12,8 @@
  *               activations (fp8 x fp8 matrix-core products)
  *   GEMM        the same product for any m, through dequantize + a dense
  *               bf16 GEMM (the large-M / prefill route)
+ * and a measurement aid: a read-only pass over device memory with the
+ * GEMV's loads (fp8w_read_ceiling).
  *
  * Scale formats:
  *   block : one fp32 scale per 128x128 tile, grid [ceil(n/128), ceil(k/128)]
@@ -80,8 +82,11 @@ typedef enum fp8w_status {
  * add FP8 blockwise weight quantization ..." (Summary; Notes for Reviewers:
  * SIMT for M <= 8, tensor-core mma for 9 <= M <= 32): VALU serves
  * 1 <= m <= 8 only; MFMA serves 1 <= m <= 32.  AUTO picks VALU for m <= 2
- * and MFMA for m >= 3, the crossover measured on MI355X (gfx950 matrix cores
- * win from 3 activation rows on).  Every route meets the same error bound. */
+ * in single calls and for m = 1 in grouped launches, MFMA above: the
+ * crossovers measured on MI355X (gfx950 matrix cores win from 3 activation
+ * rows on in single calls, from 2 in grouped launches).  Within a route the
+ * kernel also depends on n (weights with many rows take the streaming
+ * kernels), never on values.  Every route meets the same error bound. */
 typedef enum fp8w_route {
   FP8W_ROUTE_AUTO = 0,
   FP8W_ROUTE_VALU = 1,
@@ -267,8 +272,10 @@ fp8w_status fp8w_quantize_act(const uint16_t* x, int64_t m, int64_t k, uint8_t* 
 
 /* W8A8 GEMV on a quantized activation:
  *   y[i][j] = bf16_rne( x_scale * sum_k dec(x_codes[i][k]) * deq[j][k] )
- * with fp8 x fp8 matrix-core products, block scales applied per 128-column
- * block (MX scales inside the instruction), fp32 accumulation.
+ * with fp32 accumulation.  From m = 3 the products are fp8 x fp8 on the
+ * matrix cores, block scales applied per 128-column block (MX scales inside
+ * the instruction); at m <= 2 the activation codes are widened to bf16
+ * (exact) and the products run on the vector units.
  *   x_codes : u8 [m, k], 16-byte aligned      input (fp8w_quantize_act)
  *   x_scale : f32 [1] on the device, 4-B aligned  input (read on the device)
  *   codes, scales / e8m0, n, k, y : as fp8w_gemv_block / fp8w_gemv_mx
@@ -320,12 +327,13 @@ fp8w_status fp8w_gemv_w8a8(const uint8_t* x_codes, const float* x_scale, int64_t
  * Each GEMV meets the same error bound as the single call (the summation
  * order may differ, so the last bit of y may too). */
 
-/* One GEMV of a group; the same layout rules as fp8w_gemv_block /
- * fp8w_gemv_mx.  scales is `const float*` (block) or `const uint8_t*` (mx). */
+/* One GEMV of a group; the same layout rules as fp8w_gemv.  scales points
+ * at the group's format's scale buffer (f32 grid, e8m0 bytes, bf16 grid,
+ * f32 per row or one f32). */
 typedef struct fp8w_gemv_desc {
   const uint16_t* x;     /* bf16 [m, k], 16-byte aligned       */
   const uint8_t* codes;  /* e4m3fn [n, k], 16-byte aligned     */
-  const void* scales;    /* block: f32 grid (4-B aligned); mx: e8m0 bytes */
+  const void* scales;    /* the format's scale buffer, aligned to its element */
   uint16_t* y;           /* bf16 [m, n], output                */
   int64_t n, k;          /* n >= 1, k >= 16, k % 16 == 0       */
 } fp8w_gemv_desc;

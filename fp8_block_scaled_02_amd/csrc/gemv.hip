@@ -1,34 +1,41 @@
-// gemv.hip -- W8A16 decode GEMV / skinny GEMM for gfx950.
+// gemv.hip -- W8A16 (and W8A8) decode GEMV / skinny GEMM for gfx950.
 //
 // y[m][n] = bf16( sum_k x[m][k] * dec(code[n][k]) * scale(n, k) ), fp32
 // accumulation, for 1 <= M <= 32.  The fp8 weight stream dominates the
 // traffic, so every kernel reads each code byte once with 16-byte loads and
 // converts e4m3 -> bf16 in registers (exact: 4 significant bits); x (at most
 // 32 rows) is re-read from LDS or from L2.  Two kernel families, split on M
-// as the fused W8A16 GEMM of "feat:
-// add FP8 blockwise weight quantization and FP8(E4M3) KV cache support"
-// (Summary; Notes for Reviewers) splits its SIMT and tensor-core routes:
+// as the fused W8A16 GEMM of "feat: add FP8 blockwise weight quantization
+// and FP8(E4M3) KV cache support" (Summary; Notes for Reviewers) splits its
+// SIMT and tensor-core routes:
 //
 //  * VALU (M <= 8): v_dot2c_f32_bf16 products; the 64 lanes of a wave walk
-//    one row along K, and the wave's partial sums are folded four at a time
+//    rows along K, and the wave's partial sums are folded four at a time
 //    with lane-swap and DPP row operations (no LDS round trips).
+//    k_gemv_valu: one tile of rows per workgroup, K in segments staged
+//    with x in LDS.  k_gemv_valu_stream (M = 1, K <= 3072): a contiguous
+//    run of 16-row tiles per workgroup, the next tile's codes requested
+//    before the current one is computed.
 //  * MFMA (M <= 32): v_mfma_f32_16x16x32_bf16 on 16-row tiles of W against
-//    x^T padded to 16 or 32 columns.
+//    x^T padded to 16 or 32 columns.  Codes reach the A layout through a
+//    per-wave LDS transpose of 16-row x 256-byte panels.  k_gemv_mfma_direct
+//    (single calls): one 16-row tile per workgroup, its 4 waves splitting
+//    the panels, x fragments from L2.  k_gemv_mfma_stream: runs of 128-row
+//    tiles, one 16-row tile per wave, x staged in LDS by K segments.
+//  * W8A8: fp8 x fp8 v_mfma_scale_f32_16x16x128_f8f6f4 (k_gemv_w8a8_direct,
+//    and k_gemv_w8a8_tiles on weights with many rows), and k_gemv_valu with
+//    the activation codes widened to bf16 at M <= 2.
 //
 // Each call is a few microseconds of HBM traffic, so latency decides the
 // time: every kernel issues its weight loads first (non-temporal: each code
-// byte is read once).  The VALU kernels and the grouped MFMA kernel then
-// stage a K segment of x (and the block-scale row) in LDS while those loads
-// are in flight; segments are sized so that the common K (up to a few
-// thousand) is one segment.  The single-call MFMA kernel keeps no x in LDS:
-// each wave walks its 128-column blocks with a register pipeline two blocks
-// deep, loading codes, x fragments and the scale of block q+2 before the
-// MFMAs of block q, so no barrier ever waits for a staging pass.
+// byte is read once) and stages x while they are in flight.
 //
 // A launch covers either one GEMV (the job travels as a kernel argument) or
-// a group of independent GEMVs (a job table in device memory; workgroup b
-// finds its job by binary search on the jobs' first workgroup index), which
-// removes the fixed per-launch cost from a sequence of small GEMVs.
+// a group of independent GEMVs (a job table in device memory; a workgroup
+// finds its job by binary search on the jobs' first tile index), which
+// removes the fixed per-launch cost from a sequence of small GEMVs.  Single
+// calls on weights with many rows run the streaming kernels with their one
+// job passed by value.
 //
 // Block scales: one fp32 per 128x128 tile.  A 16-byte code chunk never
 // straddles a 128-column block and a workgroup's rows never straddle a
@@ -39,7 +46,8 @@
 // multiplies the decoded codes by it in fp32 (exact) and rounds to bf16 for
 // the A operand (exact while the product is a normal bf16).  Dequantized
 // weights must be finite in fp32 (|deq| < 2^128): only e8m0 bytes >= 247,
-// i.e. weights within 0.4 % of the bf16 maximum, can break that.
+// i.e. weights within 0.4 % of the bf16 maximum, can break that.  Row and
+// tensor scales multiply each output.
 #include <hip/hip_runtime.h>
 
 #include <atomic>

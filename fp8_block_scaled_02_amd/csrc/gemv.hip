@@ -76,12 +76,14 @@ __device__ __forceinline__ bf16x2 cvt_hi(uint32_t d) {
   return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, 1.0f, true);
 }
 
-// Two e4m3 codes -> fp32 (exact), times the MX scale (exact in fp32),
-// rounded to bf16.
+// Two e4m3 codes times the MX scale s = 2^(E-127), rounded to bf16, in one
+// instruction.  Measured on MI355X over every code and every e8m0 byte
+// 0..254: bit-identical to rounding fp32(code) * s (exact in fp32) to bf16;
+// byte 255, E8M0's NaN, gives NaN where that product would be infinite (a
+// non-finite weight, outside the contract either way).
 template <bool HI>
 __device__ __forceinline__ bf16x2 cvt_scaled(uint32_t d, float s) {
-  const f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8(d, HI);
-  return bf16x2{(__bf16)(v.x * s), (__bf16)(v.y * s)};
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, s, HI);
 }
 
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t d) { return __builtin_bit_cast(bf16x2, d); }

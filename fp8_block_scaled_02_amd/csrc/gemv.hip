@@ -195,6 +195,29 @@ __device__ __forceinline__ void find_job(const GemvJob& arg, const GemvJob* __re
   tile = b - job.item0;
 }
 
+// A workgroup-wide copy of `total` units into LDS: unit u is fetched by
+// load(u) and written by store(u, v).  Each thread issues the loads of up to
+// kBatch units before the first of their stores, so a staging pass waits on
+// memory once per batch rather than once per unit.  (Vector-memory waits
+// count in issue order, so a wait for one unit also waits for every weight
+// load a wave issued before it: a pass of one-unit round trips would drain
+// the weight stream once per unit.)
+template <int kBatch, int kStride, typename T, typename Load, typename Store>
+__device__ __forceinline__ void copy_batched(int total, Load load, Store store) {
+  for (int base = threadIdx.x; base < total; base += kBatch * kStride) {
+    T v[kBatch];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q)
+      if (base + q * kStride < total) v[q] = load(base + q * kStride);
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q)
+      if (base + q * kStride < total) store(base + q * kStride, v[q]);
+  }
+}
+
+// Units of the staging copies in flight per thread.
+constexpr int kStageBatch = 4;
+
 // Copy x[0:rows, seg0 : seg0+len] (len a multiple of 16) into LDS rows of
 // stride `ld` elements, covering columns [0, len_pad); columns >= len and
 // rows rows..rows_pad-1 are zero-filled, so padded products are exact zeros.
@@ -202,12 +225,16 @@ __device__ __forceinline__ void stage_x(const uint16_t* __restrict__ x, int rows
                                         int k, int seg0, int len, int len_pad, uint16_t* xs,
                                         int ld) {
   const int units = len_pad / 8;   // 16-byte units per row
-  for (int u = threadIdx.x; u < rows_pad * units; u += kThreads) {
-    const int r = u / units, c = (u % units) * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r < rows && c < len) v = ld_global_u4(x, ((size_t)r * k + seg0 + c) * 2);
-    *reinterpret_cast<uint4*>(xs + r * ld + c) = v;
-  }
+  copy_batched<kStageBatch, kThreads, uint4>(
+      rows_pad * units,
+      [&](int u) {
+        const int r = u / units, c = (u - r * units) * 8;
+        return (r < rows && c < len) ? ld_global_u4(x, ((size_t)r * k + seg0 + c) * 2) : make_uint4(0, 0, 0, 0);
+      },
+      [&](int u, uint4 v) {
+        const int r = u / units, c = (u - r * units) * 8;
+        *reinterpret_cast<uint4*>(xs + r * ld + c) = v;
+      });
 }
 
 // As stage_x for e4m3 activation codes x[0:rows, ...] (1 byte each), each
@@ -216,14 +243,26 @@ __device__ __forceinline__ void stage_x(const uint16_t* __restrict__ x, int rows
 __device__ __forceinline__ void stage_x8(const uint8_t* __restrict__ x, int rows, int k, int seg0, int len,
                                          uint16_t* xs, int ld) {
   const int units = len / 8;
-  for (int u = threadIdx.x; u < rows * units; u += kThreads) {
-    const int r = u / units, c = (u - r * units) * 8;
-    const u32x2 v = ld_global<u32x2>(x, (size_t)r * k + seg0 + c);
-    const bf16x2 a = cvt_lo(v.x), b = cvt_hi(v.x), d = cvt_lo(v.y), e = cvt_hi(v.y);
-    *reinterpret_cast<u32x4*>(xs + r * ld + c) =
-        u32x4{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, d),
-              __builtin_bit_cast(uint32_t, e)};
-  }
+  copy_batched<kStageBatch, kThreads, u32x2>(
+      rows * units,
+      [&](int u) {
+        const int r = u / units, c = (u - r * units) * 8;
+        return ld_global<u32x2>(x, (size_t)r * k + seg0 + c);
+      },
+      [&](int u, u32x2 v) {
+        const int r = u / units, c = (u - r * units) * 8;
+        const bf16x2 a = cvt_lo(v.x), b = cvt_hi(v.x), d = cvt_lo(v.y), e = cvt_hi(v.y);
+        *reinterpret_cast<u32x4*>(xs + r * ld + c) =
+            u32x4{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, d),
+                  __builtin_bit_cast(uint32_t, e)};
+      });
+}
+
+// x[0, 0:k] (one activation row, k a multiple of 8) into LDS.
+__device__ __forceinline__ void stage_row(const uint16_t* __restrict__ x, int k, uint16_t* xs) {
+  copy_batched<kStageBatch, kThreads, uint4>(
+      k / 8, [&](int u) { return ld_global_u4(x, (size_t)u * 16); },
+      [&](int u, uint4 v) { *reinterpret_cast<uint4*>(xs + u * 8) = v; });
 }
 
 // ------------------------------------------------------------------ VALU --
@@ -517,8 +556,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv_valu_stream(const GemvJob* __
 
   TileRegs<R, C, MX> cur, nxt;
   stream_issue<R, C, MX>(j, t_begin - j.item0, cur);
-  for (int u = threadIdx.x; u < j.k / 8; u += kThreads)
-    *reinterpret_cast<uint4*>(xs + u * 8) = ld_global_u4(j.x, (size_t)u * 16);
+  stage_row(j.x, j.k, xs);
   __syncthreads();
 
   for (int t = t_begin; t < t_end; ++t) {
@@ -577,8 +615,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv_valu_stream(const GemvJob* __
     if (!more) break;
     if (jn_next != jn) {   // restage x for the next job
       __syncthreads();
-      for (int u = threadIdx.x; u < jnext.k / 8; u += kThreads)
-        *reinterpret_cast<uint4*>(xs + u * 8) = ld_global_u4(jnext.x, (size_t)u * 16);
+      stage_row(jnext.x, jnext.k, xs);
       __syncthreads();
     }
     j = jnext;
@@ -809,10 +846,16 @@ __global__ __launch_bounds__(NW * kWave) void k_gemv_mfma_stream(const GemvJob* 
   // reads never look past k)
   auto stage = [&](const GemvJob& j, int seg0) {
     const int units = min(seg_cols, j.k - seg0) / 8;
-    for (int u = threadIdx.x; u < m_rows * units; u += NW * kWave) {
-      const int r = u / units, c = (u - r * units) * 8;
-      *reinterpret_cast<uint4*>(xs + r * ldx + c) = ld_global_u4(j.x, ((size_t)r * j.k + seg0 + c) * 2);
-    }
+    copy_batched<kStageBatch, NW * kWave, uint4>(
+        m_rows * units,
+        [&](int u) {
+          const int r = u / units, c = (u - r * units) * 8;
+          return ld_global_u4(j.x, ((size_t)r * j.k + seg0 + c) * 2);
+        },
+        [&](int u, uint4 v) {
+          const int r = u / units, c = (u - r * units) * 8;
+          *reinterpret_cast<uint4*>(xs + r * ldx + c) = v;
+        });
   };
 
   Panel<MX> slot[D];
@@ -1145,10 +1188,16 @@ __global__ __launch_bounds__(8 * kWave) void k_gemv_w8a8_tiles(GemvJob j, const 
   // the B reads never look past k)
   auto stage = [&](int seg0) {
     const int units = min(seg_cols, j.k - seg0) / 16;
-    for (int u = threadIdx.x; u < m_rows * units; u += NW * kWave) {
-      const int r = u / units, c = (u - r * units) * 16;
-      *reinterpret_cast<uint4*>(xs + r * ldx + c) = ld_global_u4(xc, (size_t)r * j.k + seg0 + c);
-    }
+    copy_batched<kStageBatch, NW * kWave, uint4>(
+        m_rows * units,
+        [&](int u) {
+          const int r = u / units, c = (u - r * units) * 16;
+          return ld_global_u4(xc, (size_t)r * j.k + seg0 + c);
+        },
+        [&](int u, uint4 v) {
+          const int r = u / units, c = (u - r * units) * 16;
+          *reinterpret_cast<uint4*>(xs + r * ldx + c) = v;
+        });
   };
 
   Panel8<MX> slot[D];

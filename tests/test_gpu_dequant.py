@@ -126,6 +126,22 @@ def test_dequantize_mx_every_code_times_every_scale_byte(fp8w, oracle_mod):
     assert np.array_equal(_bits(got), oracle_mod.dequant_mx_bf16(codes, e8m0))   # incl. overflow to inf
 
 
+@pytest.mark.parametrize("misaligned", [False, True])
+def test_dequantize_mx_exponent_positions(fp8w, oracle_mod, misaligned):
+    """Exponent rows of 80 bytes (k = 2560) whose bytes run through every
+    value 0..254 at each of the four byte positions of a dword, on an
+    aligned and on an odd exponent pointer: each group takes its own
+    exponent."""
+    n, k = 97, 2560
+    rng = np.random.default_rng(8)
+    codes = rng.choice(NON_NAN, size=(n, k)).astype(np.uint8)
+    e8m0 = (np.arange(n * (k // 32)) % 255).astype(np.uint8).reshape(n, k // 32)
+    e = _misaligned_u8(e8m0) if misaligned else to_dev(e8m0)
+    got = fp8w.fp8w_dequantize_mx(to_dev(codes), e)
+    _sync()
+    assert np.array_equal(_bits(got), oracle_mod.dequant_mx_bf16(codes, e8m0))
+
+
 @pytest.mark.parametrize("fmt", ["block", "mx"])
 def test_dequantize_nan_codes_give_nan(fp8w, fmt):
     import torch

@@ -417,6 +417,8 @@ __global__ __launch_bounds__(kThreads) void k_gemv_valu(GemvJob arg, const GemvJ
 // requests tile t+1's codes and scales before computing tile t, so the weight
 // stream never waits for a workgroup to start, look up its job or stage x.
 // x is restaged in LDS only when the run crosses into the next job.
+// Single calls at M = 1 on many rows use the same kernel with the job passed
+// by value and one tile per workgroup.
 template <int R, int C, bool MX>
 struct TileRegs {
   uint4 w[R][C];
@@ -560,7 +562,10 @@ __global__ __launch_bounds__(kThreads) void k_gemv_valu_stream(const GemvJob* __
   __syncthreads();
 
   for (int t = t_begin; t < t_end; ++t) {
-    const bool more = t + 1 < t_end;
+    // A single call (ONE) takes one tile per workgroup: no next tile is
+    // requested, and the kernel holds no registers for one (78 VGPRs
+    // against 133, so twice the waves per SIMD).
+    const bool more = !ONE && t + 1 < t_end;
     GemvJob jnext = j;
     int jn_next = jn, boundary_next = boundary;
     if (more) {
@@ -1332,6 +1337,7 @@ struct StreamJobs {
 template <bool MX, bool ONE>
 hipError_t run_valu_stream(const StreamJobs& l, int64_t blocks, int64_t tiles, int tiles_per_block,
                            hipStream_t stream) {
+  if (ONE && (tiles_per_block != 1 || blocks != tiles)) return hipErrorInvalidValue;   // one tile each
   hipLaunchKernelGGL((k_gemv_valu_stream<kStreamR, kStreamC, MX, ONE>), dim3((unsigned)blocks),
                      dim3(kThreads), 0, stream, l.table, l.count, l.one, (int)tiles, tiles_per_block);
   return hipGetLastError();

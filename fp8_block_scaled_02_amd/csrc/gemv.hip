@@ -19,9 +19,10 @@
 //  * MFMA (M <= 32): v_mfma_f32_16x16x32_bf16 on 16-row tiles of W against
 //    x^T padded to 16 or 32 columns.  Codes reach the A layout through a
 //    per-wave LDS transpose of 16-row x 256-byte panels.  k_gemv_mfma_direct
-//    (single calls): one 16-row tile per workgroup, its 4 waves splitting
-//    the panels, x fragments from L2.  k_gemv_mfma_stream: runs of 128-row
-//    tiles, one 16-row tile per wave, x staged in LDS by K segments.
+//    (single calls): one 16-row tile per workgroup, its 4 waves (8 when
+//    N <= 4096) splitting the panels, x fragments from L2.
+//    k_gemv_mfma_stream: runs of 128-row tiles, one 16-row tile per wave,
+//    x staged in LDS by K segments.
 //  * W8A8: fp8 x fp8 v_mfma_scale_f32_16x16x128_f8f6f4 (k_gemv_w8a8_direct,
 //    and k_gemv_w8a8_tiles on weights with many rows), and k_gemv_valu with
 //    the activation codes widened to bf16 at M <= 2.
@@ -924,21 +925,23 @@ __global__ __launch_bounds__(NW * kWave) void k_gemv_mfma_stream(const GemvJob* 
 
 // ----------------------------------------------------- MFMA, single call --
 //
-// One 16-row tile per workgroup; its 4 waves split the tile's panels (wave w
-// takes panels w, w + 4, ...) with a register pipeline two panels deep, and
-// read their x^T fragments straight from global memory (x is small and stays
-// in L2), so no barrier waits for a staging pass.  The waves' partial sums
-// meet in LDS at the end.
+// One 16-row tile per workgroup; its NW waves split the tile's panels (wave
+// w takes panels w, w + NW, ...) with a register pipeline two panels deep,
+// and read their x^T fragments straight from global memory (x is small and
+// stays in L2), so no barrier waits for a staging pass.  The waves' partial
+// sums meet in LDS at the end.  A call is latency-bound when its grid is
+// small: with one workgroup or less per CU (N <= 4096 on MI355X), 8 waves
+// per tile halve the panels each wave waits for in turn.
 template <int MT, bool MX>
 struct DirectSlot {
   Panel<MX> p;
   uint4 xb[MT][2][2][2];   // [m tile][block][chunk][first / last 8 K positions]
 };
 
-template <int MT, int D, bool MX>
-__global__ __launch_bounds__(kThreads) void k_gemv_mfma_direct(GemvJob j, int m_rows) {
-  __shared__ __align__(16) unsigned char pb[kWaves * kPanelBytes];
-  __shared__ float red[kWaves * MT * 4 * kWave];
+template <int MT, int D, bool MX, int NW>
+__global__ __launch_bounds__(NW * kWave) void k_gemv_mfma_direct(GemvJob j, int m_rows) {
+  __shared__ __align__(16) unsigned char pb[NW * kPanelBytes];
+  __shared__ float red[NW * MT * 4 * kWave];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int i = lane & 15, g = lane >> 4;
@@ -946,10 +949,10 @@ __global__ __launch_bounds__(kThreads) void k_gemv_mfma_direct(GemvJob j, int m_
   const int np = (j.k + kPanelCols - 1) / kPanelCols;
   const int nkb = (j.k + kTile - 1) / kTile;
   const int groups = (j.k + kGroup - 1) / kGroup;
-  const int nq = (np - wave + kWaves - 1) / kWaves;   // this wave's panels
+  const int nq = (np - wave + NW - 1) / NW;   // this wave's panels
 
   auto issue = [&](int q, DirectSlot<MT, MX>& r) {
-    const int p = wave + kWaves * q;
+    const int p = wave + NW * q;
     const bool live = q < nq;
     panel_issue<MX>(j, row0, p, live, nkb, groups, r.p);
 #pragma unroll
@@ -1000,8 +1003,8 @@ __global__ __launch_bounds__(kThreads) void k_gemv_mfma_direct(GemvJob j, int m_
     for (int t = 0; t < MT; ++t)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
-        acc[t][jj] += red[((1 * MT + t) * 4 + jj) * kWave + lane] + red[((2 * MT + t) * 4 + jj) * kWave + lane] +
-                      red[((3 * MT + t) * 4 + jj) * kWave + lane];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) acc[t][jj] += red[((w * MT + t) * 4 + jj) * kWave + lane];
     store_tile<MT>(j, row0, m_rows, acc);
   }
 }
@@ -1249,7 +1252,8 @@ __global__ __launch_bounds__(8 * kWave) void k_gemv_w8a8_tiles(GemvJob j, const 
 //   VALU single call: R = 1 row per wave (4 rows per workgroup: the most
 //     workgroups for small N); grouped: more rows per wave (fewer, larger
 //     workgroups once many GEMVs share the launch).
-//   MFMA single call: k_gemv_mfma_direct, one 16-row tile per workgroup.
+//   MFMA single call: k_gemv_mfma_direct, one 16-row tile per workgroup
+//     (4 waves; 8 on at most kDirect8MaxRows rows).
 //   MFMA grouped: k_gemv_mfma_stream, 8 waves, 128-row tiles.
 
 template <int M, int R, int C, bool MX, bool G>
@@ -1302,6 +1306,10 @@ constexpr int kMfmaStreamLds = 80 * 1024;
 
 // Streaming kernel of M = 1 VALU launches: (R, C) and its K limit.
 constexpr int kStreamR = 4, kStreamC = 3;
+
+// Single MFMA calls on at most this many rows (one 16-row workgroup or less
+// per CU) split each tile's panels over 8 waves instead of 4.
+constexpr int64_t kDirect8MaxRows = 4096;
 
 template <int MT, bool MX, bool ONE>
 constexpr auto mfma_stream_kernel() {
@@ -1439,13 +1447,24 @@ hipError_t launch_gemv(const GemvJob& job, int m, bool mx, int route, hipStream_
                                       stream);
   }
   const int64_t blocks = (job.n + 15) / 16;
+  if (job.n <= kDirect8MaxRows) {
+    const dim3 grid((unsigned)blocks), block(8 * kWave);
+    if (m <= 16) {
+      if (mx) hipLaunchKernelGGL((k_gemv_mfma_direct<1, 2, true, 8>), grid, block, 0, stream, job, m);
+      else hipLaunchKernelGGL((k_gemv_mfma_direct<1, 2, false, 8>), grid, block, 0, stream, job, m);
+    } else {
+      if (mx) hipLaunchKernelGGL((k_gemv_mfma_direct<2, 2, true, 8>), grid, block, 0, stream, job, m);
+      else hipLaunchKernelGGL((k_gemv_mfma_direct<2, 2, false, 8>), grid, block, 0, stream, job, m);
+    }
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)blocks), block(kThreads);
   if (m <= 16) {
-    if (mx) hipLaunchKernelGGL((k_gemv_mfma_direct<1, 2, true>), grid, block, 0, stream, job, m);
-    else hipLaunchKernelGGL((k_gemv_mfma_direct<1, 2, false>), grid, block, 0, stream, job, m);
+    if (mx) hipLaunchKernelGGL((k_gemv_mfma_direct<1, 2, true, kWaves>), grid, block, 0, stream, job, m);
+    else hipLaunchKernelGGL((k_gemv_mfma_direct<1, 2, false, kWaves>), grid, block, 0, stream, job, m);
   } else {
-    if (mx) hipLaunchKernelGGL((k_gemv_mfma_direct<2, 2, true>), grid, block, 0, stream, job, m);
-    else hipLaunchKernelGGL((k_gemv_mfma_direct<2, 2, false>), grid, block, 0, stream, job, m);
+    if (mx) hipLaunchKernelGGL((k_gemv_mfma_direct<2, 2, true, kWaves>), grid, block, 0, stream, job, m);
+    else hipLaunchKernelGGL((k_gemv_mfma_direct<2, 2, false, kWaves>), grid, block, 0, stream, job, m);
   }
   return hipGetLastError();
 }

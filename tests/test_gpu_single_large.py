@@ -1,6 +1,7 @@
 """GPU parity of single GEMV calls on weights with many rows, which run on
 the wide VALU tiles (the streaming kernel at m = 1 with K <= 3072, one job
-passed by value) and on the streaming MFMA kernel with one job.
+passed by value) and on the streaming MFMA kernel with one job, and of the
+single-call MFMA kernel on either side of its 4- / 8-wave split.
 
 Ragged N (not a multiple of 16 or 128) and ragged K (not a multiple of the
 256-column panel), every scale format, the AUTO route and both forced
@@ -174,3 +175,12 @@ def test_w8a8_tiles_many_rows(fp8w, oracle_mod, weights, fmt, n, m, k):
     xb = (oracle_mod.e4m3_decode(xc).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
     y_ref, bound = oracle_mod.gemv_format_f64(xb, c, s, fmt, rows=rows)
     assert_within_bound(bf16_to_f64(y)[:, rows], xs * y_ref, xs * bound, f"w8a8 tiles {fmt} m={m} [{n}x{k}]")
+
+
+# MFMA single calls on either side of the 8-wave split: N <= 4096 rows take
+# 8 waves per 16-row tile, more rows take 4; m over both MFMA tile widths
+@pytest.mark.parametrize("fmt", ("block", "mx"))
+@pytest.mark.parametrize("n", [4096, 4112])
+@pytest.mark.parametrize("m", [3, 16, 17, 32])
+def test_mfma_direct_wave_split(fp8w, oracle_mod, weights, fmt, n, m):
+    _check(fp8w, oracle_mod, weights, n, 2320, m, fmt, 0)

@@ -1101,11 +1101,11 @@ struct Direct8Slot {
   uint4 xb[MT][2][2];   // [m tile][block][piece at 16g / at 64 + 16g]
 };
 
-template <int MT, int D, bool MX>
-__global__ __launch_bounds__(kThreads) void k_gemv_w8a8_direct(GemvJob j, const float* __restrict__ xs,
-                                                               int m_rows) {
-  __shared__ __align__(16) unsigned char pb[kWaves * kPanelBytes];
-  __shared__ float red[kWaves * MT * 4 * kWave];
+template <int MT, int D, bool MX, int NW>
+__global__ __launch_bounds__(NW * kWave) void k_gemv_w8a8_direct(GemvJob j, const float* __restrict__ xs,
+                                                                 int m_rows) {
+  __shared__ __align__(16) unsigned char pb[NW * kPanelBytes];
+  __shared__ float red[NW * MT * 4 * kWave];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int i = lane & 15, g = lane >> 4;
@@ -1113,11 +1113,11 @@ __global__ __launch_bounds__(kThreads) void k_gemv_w8a8_direct(GemvJob j, const 
   const int np = (j.k + kPanelCols - 1) / kPanelCols;
   const int nkb = (j.k + kTile - 1) / kTile;
   const int groups = (j.k + kGroup - 1) / kGroup;
-  const int nq = (np - wave + kWaves - 1) / kWaves;
+  const int nq = (np - wave + NW - 1) / NW;
   const uint8_t* __restrict__ xc = reinterpret_cast<const uint8_t*>(j.x);
 
   auto issue = [&](int q, Direct8Slot<MT, MX>& r) {
-    const int p = wave + kWaves * q;
+    const int p = wave + NW * q;
     const bool live = q < nq;
     panel8_issue<MX>(j, row0, p, live, nkb, groups, r.p);
 #pragma unroll
@@ -1165,8 +1165,8 @@ __global__ __launch_bounds__(kThreads) void k_gemv_w8a8_direct(GemvJob j, const 
     for (int t = 0; t < MT; ++t)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
-        acc[t][jj] += red[((1 * MT + t) * 4 + jj) * kWave + lane] + red[((2 * MT + t) * 4 + jj) * kWave + lane] +
-                      red[((3 * MT + t) * 4 + jj) * kWave + lane];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) acc[t][jj] += red[((w * MT + t) * 4 + jj) * kWave + lane];
     store_tile<MT>(j, row0, m_rows, acc, ld_global<float>(xs, 0));
   }
 }
@@ -1587,13 +1587,25 @@ hipError_t launch_gemv_w8a8(const GemvJob& job, const float* x_scale, int m, boo
     if (m <= 16) return mx ? run_w8a8_tiles<1, true>(job, x_scale, m, stream) : run_w8a8_tiles<1, false>(job, x_scale, m, stream);
     return mx ? run_w8a8_tiles<2, true>(job, x_scale, m, stream) : run_w8a8_tiles<2, false>(job, x_scale, m, stream);
   }
-  const dim3 grid((unsigned)((job.n + 15) / 16)), block(kThreads);
+  const dim3 grid((unsigned)((job.n + 15) / 16));
+  if (job.n <= kDirect8MaxRows) {   // as the bf16 single call: 8 waves per tile on few rows
+    const dim3 block(8 * kWave);
+    if (m <= 16) {
+      if (mx) hipLaunchKernelGGL((k_gemv_w8a8_direct<1, 2, true, 8>), grid, block, 0, stream, job, x_scale, m);
+      else hipLaunchKernelGGL((k_gemv_w8a8_direct<1, 2, false, 8>), grid, block, 0, stream, job, x_scale, m);
+    } else {
+      if (mx) hipLaunchKernelGGL((k_gemv_w8a8_direct<2, 2, true, 8>), grid, block, 0, stream, job, x_scale, m);
+      else hipLaunchKernelGGL((k_gemv_w8a8_direct<2, 2, false, 8>), grid, block, 0, stream, job, x_scale, m);
+    }
+    return hipGetLastError();
+  }
+  const dim3 block(kThreads);
   if (m <= 16) {
-    if (mx) hipLaunchKernelGGL((k_gemv_w8a8_direct<1, 2, true>), grid, block, 0, stream, job, x_scale, m);
-    else hipLaunchKernelGGL((k_gemv_w8a8_direct<1, 2, false>), grid, block, 0, stream, job, x_scale, m);
+    if (mx) hipLaunchKernelGGL((k_gemv_w8a8_direct<1, 2, true, kWaves>), grid, block, 0, stream, job, x_scale, m);
+    else hipLaunchKernelGGL((k_gemv_w8a8_direct<1, 2, false, kWaves>), grid, block, 0, stream, job, x_scale, m);
   } else {
-    if (mx) hipLaunchKernelGGL((k_gemv_w8a8_direct<2, 2, true>), grid, block, 0, stream, job, x_scale, m);
-    else hipLaunchKernelGGL((k_gemv_w8a8_direct<2, 2, false>), grid, block, 0, stream, job, x_scale, m);
+    if (mx) hipLaunchKernelGGL((k_gemv_w8a8_direct<2, 2, true, kWaves>), grid, block, 0, stream, job, x_scale, m);
+    else hipLaunchKernelGGL((k_gemv_w8a8_direct<2, 2, false, kWaves>), grid, block, 0, stream, job, x_scale, m);
   }
   return hipGetLastError();
 }

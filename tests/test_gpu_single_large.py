@@ -184,3 +184,21 @@ def test_w8a8_tiles_many_rows(fp8w, oracle_mod, weights, fmt, n, m, k):
 @pytest.mark.parametrize("m", [3, 16, 17, 32])
 def test_mfma_direct_wave_split(fp8w, oracle_mod, weights, fmt, n, m):
     _check(fp8w, oracle_mod, weights, n, 2320, m, fmt, 0)
+
+
+# W8A8 single calls on either side of the same split (m >= 3 on fewer rows
+# than the 128-row W8A8 tiles take)
+@pytest.mark.parametrize("fmt", ("block", "mx"))
+@pytest.mark.parametrize("n", [4096, 4112])
+@pytest.mark.parametrize("m", [3, 16, 17, 32])
+def test_w8a8_direct_wave_split(fp8w, oracle_mod, weights, fmt, n, m):
+    k = 2320
+    c, s, dc, ds = weights(n, k, fmt)
+    x = W.activation(94, m, k)
+    xc, xs = oracle_mod.quantize_act_tensor(x)
+    y = fp8w.fp8w_gemv_w8a8(to_dev(xc), to_dev(np.array([xs], np.float32)), dc, ds, fmt)
+    _sync()
+    rows = _rows(n, np.random.default_rng([n, m, 10]))
+    xb = (oracle_mod.e4m3_decode(xc).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    y_ref, bound = oracle_mod.gemv_format_f64(xb, c, s, fmt, rows=rows)
+    assert_within_bound(bf16_to_f64(y)[:, rows], xs * y_ref, xs * bound, f"w8a8 direct {fmt} m={m} [{n}x{k}]")

@@ -359,6 +359,16 @@ FP8W_API fp8w_status fp8w_grouped_plan_init(const fp8w_gemv_desc* descs, int64_t
   }
   int64_t blocks = tiles;
   int32_t per_block = 0, seg_cols = 0;
+  if (r == 1 && m == 1 && !valu_stream) {
+    // wide tiles at m = 1: 4096-column K segments when, summed over the
+    // group's rows, they take fewer segment rounds than 3072-column ones
+    int64_t rounds3 = 0, rounds4 = 0;
+    for (int64_t i = 0; i < count; ++i) {
+      rounds3 += descs[i].n * fp8w::gemv_wide_seg_rounds(descs[i].k, 3072);
+      rounds4 += descs[i].n * fp8w::gemv_wide_seg_rounds(descs[i].k, 4096);
+    }
+    if (rounds4 < rounds3) seg_cols = 4096;
+  }
   if (valu_stream || r == 2) {
     int slots = 0;
     int64_t want = 0;
@@ -408,14 +418,15 @@ FP8W_API fp8w_status fp8w_gemv_grouped(const fp8w_grouped_plan* plan, void* stre
     return from_hip(fp8w::launch_gemv_mfma_stream(table, plan->count, plan->blocks, plan->tiles,
                                                   plan->tiles_per_block, plan->m, seg, mx, s));
   }
-  if (plan->seg_cols != 0) return FP8W_ERR_SHAPE;
+  if (plan->seg_cols != 0 && !(plan->seg_cols == 4096 && plan->m == 1 && plan->tiles_per_block == 0))
+    return FP8W_ERR_SHAPE;
   if (plan->tiles_per_block > 0) {
     if (plan->m != 1) return FP8W_ERR_SHAPE;
     return from_hip(fp8w::launch_gemv_stream(table, plan->count, plan->blocks, plan->tiles,
                                              plan->tiles_per_block, mx, s));
   }
   if (plan->blocks != plan->tiles) return FP8W_ERR_SHAPE;
-  return from_hip(fp8w::launch_gemv_grouped(table, plan->count, plan->blocks, plan->m, mx, s));
+  return from_hip(fp8w::launch_gemv_grouped(table, plan->count, plan->blocks, plan->m, mx, plan->seg_cols, s));
 }
 
 // ------------------------------------------------------------- helpers --

@@ -1269,11 +1269,13 @@ hipError_t run_valu(const GemvJob& job, const GemvJob* table, int njobs, int64_t
 // per wave, fewer and larger workgroups; otherwise 1 or 2 rows per wave, the
 // most workgroups for small N.
 template <bool MX, bool G>
-hipError_t dispatch_valu(int m, bool wide, const GemvJob& job, const GemvJob* table, int njobs,
+hipError_t dispatch_valu(int m, bool wide, bool seg4096, const GemvJob& job, const GemvJob* table, int njobs,
                          int64_t blocks, hipStream_t s) {
   if (wide) {
     switch (m) {
-      case 1: return run_valu<1, 4, 3, MX, G>(job, table, njobs, blocks, s);
+      case 1:
+        return seg4096 ? run_valu<1, 4, 4, MX, G>(job, table, njobs, blocks, s)
+                       : run_valu<1, 4, 3, MX, G>(job, table, njobs, blocks, s);
       case 2: return run_valu<2, 4, 2, MX, G>(job, table, njobs, blocks, s);
       case 3: return run_valu<3, 4, 2, MX, G>(job, table, njobs, blocks, s);
       case 4: return run_valu<4, 4, 2, MX, G>(job, table, njobs, blocks, s);
@@ -1388,6 +1390,12 @@ int gemv_rows_per_block(int route, int m, bool grouped) {
 }
 
 int gemv_stream_max_k() { return 1024 * kStreamC; }
+
+int gemv_wide_seg_rounds(int64_t k, int seg_cols) { return (int)((k + seg_cols - 1) / seg_cols); }
+
+int gemv_wide_seg_cols(int64_t k) {
+  return gemv_wide_seg_rounds(k, 4096) < gemv_wide_seg_rounds(k, 3072) ? 4096 : 3072;
+}
 int gemv_stream_rows() { return kWaves * kStreamR; }
 
 int gemv_mfma_stream_seg_cols(int m, int64_t max_k) {
@@ -1435,8 +1443,9 @@ hipError_t launch_gemv(const GemvJob& job, int m, bool mx, int route, hipStream_
     }
     const int rows = wide ? gemv_rows_per_block(route, m, true) : gemv_rows_per_block(route, m, false);
     const int64_t blocks = (job.n + rows - 1) / rows;
-    return mx ? dispatch_valu<true, false>(m, wide, job, nullptr, 1, blocks, stream)
-              : dispatch_valu<false, false>(m, wide, job, nullptr, 1, blocks, stream);
+    const bool seg4096 = wide && m == 1 && gemv_wide_seg_cols(job.k) == 4096;
+    return mx ? dispatch_valu<true, false>(m, wide, seg4096, job, nullptr, 1, blocks, stream)
+              : dispatch_valu<false, false>(m, wide, seg4096, job, nullptr, 1, blocks, stream);
   }
   if (single_call_streams_mfma(job.n, m)) {
     StreamJobs l{nullptr, 1, job};
@@ -1489,11 +1498,12 @@ hipError_t launch_gemv_stream(const GemvJob* table, int njobs, int64_t blocks, i
             : run_valu_stream<false, false>(l, blocks, tiles, tiles_per_block, stream);
 }
 
-hipError_t launch_gemv_grouped(const GemvJob* table, int njobs, int64_t blocks, int m, bool mx,
+hipError_t launch_gemv_grouped(const GemvJob* table, int njobs, int64_t blocks, int m, bool mx, int seg_cols,
                                hipStream_t stream) {
   const GemvJob none{};
-  return mx ? dispatch_valu<true, true>(m, true, none, table, njobs, blocks, stream)
-            : dispatch_valu<false, true>(m, true, none, table, njobs, blocks, stream);
+  const bool seg4096 = m == 1 && seg_cols == 4096;
+  return mx ? dispatch_valu<true, true>(m, true, seg4096, none, table, njobs, blocks, stream)
+            : dispatch_valu<false, true>(m, true, seg4096, none, table, njobs, blocks, stream);
 }
 
 hipError_t gemv_mfma_stream_slots(int m, bool mx, int seg_cols, int* slots) {

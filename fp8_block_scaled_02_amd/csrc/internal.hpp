@@ -62,9 +62,17 @@ hipError_t launch_quantize_act(const uint16_t* x, int64_t count, uint8_t* codes,
 // route: 1 = VALU (m <= 8), 2 = MFMA (m <= 32).
 int gemv_rows_per_block(int route, int m, bool grouped);
 hipError_t launch_gemv(const GemvJob& job, int m, bool mx, int route, hipStream_t stream);
-// Grouped VALU launch, one tile of gemv_rows_per_block(1, m, true) rows per workgroup.
+// Grouped VALU launch, one tile of gemv_rows_per_block(1, m, true) rows per
+// workgroup.  At m = 1 the tiles walk K in segments of seg_cols columns:
+// 3072 (seg_cols 0 or 3072) or 4096.
 hipError_t launch_gemv_grouped(const GemvJob* device_table, int njobs, int64_t blocks, int m,
-                               bool mx, hipStream_t stream);
+                               bool mx, int seg_cols, hipStream_t stream);
+// Wide VALU tiles at m = 1 (single calls on many rows, grouped launches
+// with a K above the streaming limit): K segments of 3072 columns, or 4096
+// where those need fewer segments per tile (4096 holds more registers per
+// wave: fewer waves per SIMD).  gemv_wide_seg_rounds = segments per tile.
+int gemv_wide_seg_rounds(int64_t k, int seg_cols);
+int gemv_wide_seg_cols(int64_t k);
 
 // Streaming grouped VALU kernel (m = 1, every K <= gemv_stream_max_k(), MX
 // exponent arrays 4-byte aligned):

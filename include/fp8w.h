@@ -350,7 +350,9 @@ typedef struct fp8w_grouped_plan {
   int32_t tiles_per_block; /* 0: one tile per workgroup; else a contiguous
                               run of tiles per workgroup (streaming kernels) */
   int32_t seg_cols;        /* MFMA route: K columns of x staged per pass
-                              (multiple of 256); 0 on the VALU route       */
+                              (multiple of 256).  VALU route: 0, or 4096
+                              for m = 1 plans without streaming whose
+                              tiles walk K in 4096-column segments        */
 } fp8w_grouped_plan;
 
 /* Bytes of device memory a table for `count` GEMVs needs (0 if count < 1). */

@@ -203,6 +203,12 @@ def test_grouped_argument_errors(F):
     assert L.fp8w_gemv_grouped(ctypes.byref(bad), None) == F.ERR_SHAPE
     bad = F.GroupedPlanC(T, 1, 1, 0, 1, 4, 4, 1, 256)   # VALU plans carry no x segment
     assert L.fp8w_gemv_grouped(ctypes.byref(bad), None) == F.ERR_SHAPE
+    bad = F.GroupedPlanC(T, 1, 1, 0, 1, 4, 4, 0, 3072)  # VALU K segments: 0 (default) or 4096
+    assert L.fp8w_gemv_grouped(ctypes.byref(bad), None) == F.ERR_SHAPE
+    bad = F.GroupedPlanC(T, 1, 2, 0, 1, 4, 4, 0, 4096)  # 4096-column VALU segments: m = 1 only
+    assert L.fp8w_gemv_grouped(ctypes.byref(bad), None) == F.ERR_SHAPE
+    bad = F.GroupedPlanC(T, 1, 1, 0, 1, 4, 100, 25, 4096)  # ... and only on the per-tile kernel
+    assert L.fp8w_gemv_grouped(ctypes.byref(bad), None) == F.ERR_SHAPE
     bad = F.GroupedPlanC(T, 1, 4, 0, 2, 4, 4, 0, 256)   # MFMA plans always stream
     assert L.fp8w_gemv_grouped(ctypes.byref(bad), None) == F.ERR_SHAPE
     bad = F.GroupedPlanC(T, 1, 4, 0, 2, 4, 4, 1, 0)     # MFMA: no x segment

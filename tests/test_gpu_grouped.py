@@ -199,3 +199,27 @@ def test_mx_exponent_alignment_paths(fp8w, oracle_mod, off, m, long_k):
         assert_within_bound(bf16_to_f64(ysg), y_ref, bound, f"single mx off={off} m={m} [{n}x{k}]")
         if ysv is not None:
             assert_within_bound(bf16_to_f64(ysv), y_ref, bound, f"single valu mx off={off} m={m} [{n}x{k}]")
+
+
+# Grouped M = 1 plans above the streaming K limit run the wide per-tile
+# tiles, with 4096-column K segments when that takes fewer segment rounds
+# over the group (seg_cols = 4096) and 3072-column ones otherwise.
+@pytest.mark.parametrize("fmt", ["block", "mx"])
+@pytest.mark.parametrize("shapes,seg", [([(300, 4096), (130, 3584), (257, 8176)], 4096),
+                                        ([(300, 4160), (129, 6144)], 0)])
+def test_grouped_wide_tiles_segment_width(fp8w, oracle_mod, fmt, shapes, seg):
+    jobs = []
+    for i, (n, k) in enumerate(shapes):
+        bits = W.gaussian_weight(37, i, n, k, outlier_rows=fmt == "block", heavy_tail=fmt == "mx")
+        codes, sc = oracle_mod.quantize_block(bits) if fmt == "block" else oracle_mod.quantize_mx(bits)
+        jobs.append((n, k, codes, sc))
+    xs_h = [W.activation(38, 1, k) for (_, k, _, _) in jobs]
+    plan = fp8w.fp8w_grouped_plan_init([to_dev_bf16(x) for x in xs_h], [to_dev(c) for (_, _, c, _) in jobs],
+                                       [to_dev(s) for (_, _, _, s) in jobs], fmt=fmt)
+    assert plan.route == fp8w.ROUTE_VALU and plan.plan.tiles_per_block == 0 and plan.plan.seg_cols == seg
+    ys = fp8w.fp8w_gemv_grouped(plan)
+    _sync()
+    ref = oracle_mod.gemv_block_f64 if fmt == "block" else oracle_mod.gemv_mx_f64
+    for (n, k, c, s), x, y in zip(jobs, xs_h, ys):
+        y_ref, bound = ref(x, c, s)
+        assert_within_bound(bf16_to_f64(y), y_ref, bound, f"grouped wide {fmt} seg={seg} [{n}x{k}]")

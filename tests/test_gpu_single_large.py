@@ -97,10 +97,11 @@ def test_valu_stream_single_job(fp8w, oracle_mod, weights, fmt):
     _check(fp8w, oracle_mod, weights, 16405, 2064, 1, fmt, 0)
 
 
-# VALU wide tiles without streaming: K above the streaming limit, m = 2
+# VALU wide tiles without streaming: K above the streaming limit (m = 1:
+# 4096-column K segments at K = 4096 and 8176, 3072-column ones at 4112), m = 2
 # (AUTO) and forced VALU up to m = 8
 @pytest.mark.parametrize("fmt", ("block", "mx", "row"))
-@pytest.mark.parametrize("m,k", [(1, 4112), (2, 2064), (3, 1040), (8, 4112)])
+@pytest.mark.parametrize("m,k", [(1, 4112), (1, 4096), (1, 8176), (2, 2064), (3, 1040), (8, 4112)])
 def test_valu_wide_single_call(fp8w, oracle_mod, weights, fmt, m, k):
     import fp8_block_scaled_02_amd as F
     _check(fp8w, oracle_mod, weights, 16405, k, m, fmt, F.ROUTE_VALU if m > 2 else 0)

@@ -91,7 +91,8 @@ class GroupedPlanC(ctypes.Structure):
     """fp8w_grouped_plan of include/fp8w.h."""
     _fields_ = [("table", _P), ("count", ctypes.c_int32), ("m", ctypes.c_int32),
                 ("format", ctypes.c_int32), ("route", ctypes.c_int32), ("blocks", _I64),
-                ("tiles", _I64), ("tiles_per_block", ctypes.c_int32), ("seg_cols", ctypes.c_int32)]
+                ("tiles", _I64), ("tiles_per_block", ctypes.c_int32), ("seg_cols", ctypes.c_int32),
+                ("mx_packed8", ctypes.c_int32)]
 
 
 _lib = None

@@ -388,11 +388,19 @@ FP8W_API fp8w_status fp8w_grouped_plan_init(const fp8w_gemv_desc* descs, int64_t
     per_block = (int32_t)((tiles + want - 1) / want);
     blocks = (tiles + per_block - 1) / per_block;
   }
+  // MFMA route, MX: one 8-byte exponent load per row and panel when every
+  // GEMV's exponent rows start 8-byte aligned
+  int32_t mx_packed8 = 0;
+  if (r == 2 && mx) {
+    mx_packed8 = 1;
+    for (int64_t i = 0; i < count; ++i)
+      if (!fp8w::mx_rows_packed8(descs[i].scales, descs[i].k)) mx_packed8 = 0;
+  }
   if (hipMemcpy(device_table, table.data(), table_bytes, hipMemcpyHostToDevice) != hipSuccess)
     return FP8W_ERR_HIP;
   *plan = fp8w_grouped_plan{device_table, (int32_t)count, (int32_t)m, (int32_t)format,
                             (int32_t)(r == 1 ? FP8W_ROUTE_VALU : FP8W_ROUTE_MFMA), blocks, tiles,
-                            per_block, seg_cols};
+                            per_block, seg_cols, mx_packed8};
   return FP8W_OK;
 }
 
@@ -405,6 +413,9 @@ FP8W_API fp8w_status fp8w_gemv_grouped(const fp8w_grouped_plan* plan, void* stre
       plan->tiles_per_block < 0 ||
       !format_ok(plan->format))
     return FP8W_ERR_SHAPE;
+  if (plan->mx_packed8 != 0 &&
+      (plan->mx_packed8 != 1 || plan->route != FP8W_ROUTE_MFMA || plan->format != FP8W_FORMAT_MX))
+    return FP8W_ERR_SHAPE;
   const bool mx = plan->format == FP8W_FORMAT_MX;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const fp8w::GemvJob* table = static_cast<const fp8w::GemvJob*>(plan->table);
@@ -416,7 +427,8 @@ FP8W_API fp8w_status fp8w_gemv_grouped(const fp8w_grouped_plan* plan, void* stre
         fp8w::gemv_mfma_stream_lds(plan->m, seg) > fp8w::gemv_mfma_stream_lds_limit())
       return FP8W_ERR_SHAPE;
     return from_hip(fp8w::launch_gemv_mfma_stream(table, plan->count, plan->blocks, plan->tiles,
-                                                  plan->tiles_per_block, plan->m, seg, mx, s));
+                                                  plan->tiles_per_block, plan->m, seg, mx,
+                                                  plan->mx_packed8 == 1, s));
   }
   if (plan->seg_cols != 0 && !(plan->seg_cols == 4096 && plan->m == 1 && plan->tiles_per_block == 0))
     return FP8W_ERR_SHAPE;

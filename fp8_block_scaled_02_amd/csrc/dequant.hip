@@ -33,6 +33,25 @@ __device__ __forceinline__ float weight_scale(const void* scales, int format, in
   return ld_global<float>(scales, 0);
 }
 
+// The stored scale of weight (row, col) as loaded, in any format (an e8m0
+// byte, bf16 bits or fp32 bits), and its value.  The vector kernel loads
+// every unit's raw scale before it converts any: a conversion right after
+// its load would wait for that load before the next unit's loads issue.
+__device__ __forceinline__ uint32_t raw_scale(const void* scales, int format, int64_t row, int col,
+                                              int scale_cols) {
+  if (format == kFmtMx) return ld_global<uint8_t>(scales, (size_t)row * scale_cols + col / kGroup);
+  const size_t tile = (size_t)(row / kTile) * scale_cols + col / kTile;
+  if (format == kFmtBlock) return ld_global<uint32_t>(scales, tile * 4);
+  if (format == kFmtBlockBf16) return ld_global<uint16_t>(scales, tile * 2);
+  return ld_global<uint32_t>(scales, (size_t)row * 4);   // kFmtRow (kFmtTensor: loaded once per thread)
+}
+
+__device__ __forceinline__ float scale_value(uint32_t raw, int format) {
+  if (format == kFmtMx) return pow2_e8m0((uint8_t)raw);
+  if (format == kFmtBlockBf16) return __uint_as_float(raw << 16);
+  return __uint_as_float(raw);
+}
+
 // Eight codes (two dwords) times s -> eight bf16, rounded to nearest even
 // by the hardware conversion (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ u32x4 dequant8(u32x2 d, float s) {
@@ -61,27 +80,26 @@ __global__ __launch_bounds__(kThreads) void k_dequant_vec(const uint8_t* __restr
                                                           const void* __restrict__ scales,
                                                           uint16_t* __restrict__ out, int64_t units,
                                                           int units_per_row, int scale_cols, int format) {
+  const int fmt = MX ? kFmtMx : format;
+  const uint32_t whole = fmt == kFmtTensor ? ld_global<uint32_t>(scales, 0) : 0u;
   u32x2 c[kUnitsPerThread];
-  float s[kUnitsPerThread];
+  uint32_t raw[kUnitsPerThread];
 #pragma unroll
   for (int i = 0; i < kUnitsPerThread; ++i) {
     const int64_t u = ((int64_t)blockIdx.x * kUnitsPerThread + i) * kThreads + threadIdx.x;
     c[i] = u32x2{0u, 0u};
-    s[i] = 0.0f;
+    raw[i] = 0u;
     if (u < units) {
       c[i] = __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x2*)(codes + (size_t)u * 8));
       const IDX row = (IDX)u / (IDX)units_per_row;
       const int col = (int)((IDX)u - row * (IDX)units_per_row) * 8;
-      if (MX)
-        s[i] = pow2_e8m0(ld_global<uint8_t>(scales, (size_t)row * scale_cols + col / kGroup));
-      else
-        s[i] = weight_scale(scales, format, (int64_t)row, col, scale_cols);
+      raw[i] = fmt == kFmtTensor ? whole : raw_scale(scales, fmt, (int64_t)row, col, scale_cols);
     }
   }
 #pragma unroll
   for (int i = 0; i < kUnitsPerThread; ++i) {
     const int64_t u = ((int64_t)blockIdx.x * kUnitsPerThread + i) * kThreads + threadIdx.x;
-    if (u < units) st_global<u32x4>(out, (size_t)u * 16, dequant8(c[i], s[i]));
+    if (u < units) st_global<u32x4>(out, (size_t)u * 16, dequant8(c[i], scale_value(raw[i], fmt)));
   }
 }
 

@@ -53,6 +53,7 @@
 
 #include <atomic>
 #include <stddef.h>
+#include <type_traits>
 
 #include "device.hpp"
 #include "internal.hpp"
@@ -654,12 +655,22 @@ constexpr int kPanelBytes = 16 * kPanelCols;    // LDS bytes of one wave's panel
 template <bool MX>
 struct Panel {
   uint4 v[4];                // lane l: row 4q + l/16 of the tile, bytes 16*(l%16)
-  float s[MX ? 4 : 2];       // block: per 128-column block; MX: per (block, chunk) of the A layout
+  // block: the scale of each 128-column block (a scalar load when fp32);
+  // MX: the exponent byte of each (block, chunk) of the A layout, as loaded
+  // (panel_scales converts it where the MFMA step uses it)
+  typename std::conditional<MX, uint32_t, float>::type s[MX ? 4 : 2];
+  u32x2 e8;                  // MX, packed rows: the row's 8 exponent bytes of the panel
 };
 
 // Request panel p (columns [256p, 256p + 256)) of the 16-row tile at row0,
-// with its scales.  Rows >= n and columns >= k load zeros.
-template <bool MX>
+// with its scales.  Rows >= n and columns >= k load zeros.  PK (MX only):
+// every exponent row starts 8-byte aligned (groups % 8 == 0 and an aligned
+// array; the host checks, mx_rows_packed8), so one 8-byte load per row
+// brings the panel's exponents.  It is a template choice, not a branch:
+// with both loads behind a runtime branch the compiler joins their results
+// with copies, and a copy waits for its load, and so for every weight load
+// the wave issued before it.
+template <bool MX, bool PK = false>
 __device__ __forceinline__ void panel_issue(const GemvJob& j, int row0, int p, bool live, int nkb,
                                             int groups, Panel<MX>& r) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -672,27 +683,22 @@ __device__ __forceinline__ void panel_issue(const GemvJob& j, int row0, int p, b
   }
   if (MX) {
     // Lane l needs the exponents of groups 8p + 2c + (l/16)/2, c = 0..3, of
-    // row l%16: all inside the row's 8 bytes for this panel.  When every row
-    // starts 8-byte aligned (groups % 8 == 0, aligned base) one 8-byte load
-    // brings them; otherwise one byte load per chunk.
-    const int row = row0 + (lane & 15);
+    // row l%16: all inside the row's 8 bytes for this panel (PK: one 8-byte
+    // load; otherwise one byte load per chunk).  The loads are
+    // unconditional, from a row and group clamped into the weight: rows and
+    // columns outside it have zero codes, so the exponent they borrow only
+    // multiplies zeros.  No select or copy follows a load, so nothing waits
+    // for one before the MFMA step converts it.
+    const int row = min(row0 + (lane & 15), j.n - 1);
     const uint8_t* __restrict__ e8 = static_cast<const uint8_t*>(j.scales);
-    if ((groups & 7) == 0 && (reinterpret_cast<uintptr_t>(e8) & 7) == 0) {
-      u32x2 w = {0u, 0u};
-      if (live && row < j.n && p * kPanelCols < j.k) w = ld_global<u32x2>(e8, (size_t)row * groups + 8 * p);
-      const int sh = 8 * ((lane >> 5) & 1);
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        r.s[c] = (live && row < j.n && p * kPanelCols < j.k)
-                     ? mx_scale((uint8_t)(((c < 2 ? w.x : w.y) >> (16 * (c & 1) + sh)) & 0xFF))
-                     : 0.0f;
+    if (PK) {
+      const int pc = min(p, (j.k - 1) / kPanelCols);
+      r.e8 = ld_global<u32x2>(e8, (size_t)row * groups + 8 * pc);
     } else {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const int kx = p * kPanelCols + 64 * c + 16 * (lane >> 4);   // block c/2, chunk c%2
-        r.s[c] = 0.0f;
-        if (live && row < j.n && kx < j.k)
-          r.s[c] = mx_scale(ld_global<uint8_t>(e8, (size_t)row * groups + kx / kGroup));
+        const int kx = min(p * kPanelCols + 64 * c + 16 * (lane >> 4), j.k - 1);   // block c/2, chunk c%2
+        r.s[c] = ld_global<uint8_t>(e8, (size_t)row * groups + kx / kGroup);
       }
     }
   } else {
@@ -701,6 +707,27 @@ __device__ __forceinline__ void panel_issue(const GemvJob& j, int row0, int p, b
       r.s[0] = block_scale(j, row0, 2 * p, nkb);
       if (2 * p + 1 < nkb) r.s[1] = block_scale(j, row0, 2 * p + 1, nkb);
     }
+  }
+}
+
+// The panel's scales as the MFMA step uses them: block: per 128-column
+// block; MX: 2^(E-127) per (block, chunk) of the A layout (lane l reads the
+// exponents of groups 8p + 2c + (l/16)/2, c = 0..3, of row l%16).
+template <bool MX, bool PK = false>
+__device__ __forceinline__ void panel_scales(const Panel<MX>& r, float (&sc)[MX ? 4 : 2]) {
+  if (MX) {
+    if (PK) {
+      const int sh = 8 * (((threadIdx.x & (kWave - 1)) >> 5) & 1);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        sc[c] = mx_scale((uint8_t)(((c < 2 ? r.e8.x : r.e8.y) >> (16 * (c & 1) + sh)) & 0xFF));
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) sc[c] = mx_scale((uint8_t)r.s[c]);
+    }
+  } else {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) sc[b] = r.s[b];
   }
 }
 
@@ -804,7 +831,7 @@ __device__ __forceinline__ void store_tile(const GemvJob& j, int row0, int m_row
 // (a multiple of 256, sized on the host so that two workgroups fit on a CU):
 // restaged when the run enters a new job, and at every segment of a tile
 // when K spans more than one segment.
-template <int MT, int NW, int D, bool MX, bool ONE>
+template <int MT, int NW, int D, bool MX, bool ONE, bool PK>
 __global__ __launch_bounds__(NW * kWave) void k_gemv_mfma_stream(const GemvJob* __restrict__ table,
                                                                  int njobs, GemvJob one, int total_tiles,
                                                                  int tiles_per_block, int m_rows,
@@ -836,7 +863,7 @@ __global__ __launch_bounds__(NW * kWave) void k_gemv_mfma_stream(const GemvJob* 
 
   auto issue = [&](Panel<MX>& r) {
     const bool live = it < t_end;
-    panel_issue<MX>(ij, (it - ij.item0) * kRows + 16 * wave, ip, live, (ij.k + kTile - 1) / kTile,
+    panel_issue<MX, PK>(ij, (it - ij.item0) * kRows + 16 * wave, ip, live, (ij.k + kTile - 1) / kTile,
                     (ij.k + kGroup - 1) / kGroup, r);
     if (!live) return;
     if (++ip == i_np) {
@@ -881,8 +908,7 @@ __global__ __launch_bounds__(NW * kWave) void k_gemv_mfma_stream(const GemvJob* 
       uint4 a[2][2];
       panel_to_a(slot[s].v, pbuf, a);
       float sc[MX ? 4 : 2];
-#pragma unroll
-      for (int c = 0; c < (MX ? 4 : 2); ++c) sc[c] = slot[s].s[c];
+      panel_scales<MX, PK>(slot[s], sc);
       issue(slot[s]);
       const int kseg = (cp % seg_panels) * kPanelCols;   // panel start within the staged segment
       const int kp = cp * kPanelCols;
@@ -938,7 +964,7 @@ struct DirectSlot {
   uint4 xb[MT][2][2][2];   // [m tile][block][chunk][first / last 8 K positions]
 };
 
-template <int MT, int D, bool MX, int NW>
+template <int MT, int D, bool MX, int NW, bool PK>
 __global__ __launch_bounds__(NW * kWave) void k_gemv_mfma_direct(GemvJob j, int m_rows) {
   __shared__ __align__(16) unsigned char pb[NW * kPanelBytes];
   __shared__ float red[NW * MT * 4 * kWave];
@@ -954,7 +980,7 @@ __global__ __launch_bounds__(NW * kWave) void k_gemv_mfma_direct(GemvJob j, int 
   auto issue = [&](int q, DirectSlot<MT, MX>& r) {
     const int p = wave + NW * q;
     const bool live = q < nq;
-    panel_issue<MX>(j, row0, p, live, nkb, groups, r.p);
+    panel_issue<MX, PK>(j, row0, p, live, nkb, groups, r.p);
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -984,7 +1010,9 @@ __global__ __launch_bounds__(NW * kWave) void k_gemv_mfma_direct(GemvJob j, int 
       if (q0 + s < nq) {
         uint4 a[2][2];
         panel_to_a(slot[s].p.v, pb + wave * kPanelBytes, a);
-        panel_mfma<MT, MX>(a, slot[s].p.s, [&](int t, int b, int c, uint4& B0, uint4& B1) {
+        float sc[MX ? 4 : 2];
+        panel_scales<MX, PK>(slot[s].p, sc);
+        panel_mfma<MT, MX>(a, sc, [&](int t, int b, int c, uint4& B0, uint4& B1) {
           B0 = slot[s].xb[t][b][c][0];
           B1 = slot[s].xb[t][b][c][1];
         }, acc);
@@ -1313,15 +1341,15 @@ constexpr int kStreamR = 4, kStreamC = 3;
 // per CU) split each tile's panels over 8 waves instead of 4.
 constexpr int64_t kDirect8MaxRows = 4096;
 
-template <int MT, bool MX, bool ONE>
+template <int MT, bool MX, bool ONE, bool PK>
 constexpr auto mfma_stream_kernel() {
-  return &k_gemv_mfma_stream<MT, kMfmaStreamWaves, 2, MX, ONE>;
+  return &k_gemv_mfma_stream<MT, kMfmaStreamWaves, 2, MX, ONE, PK>;
 }
 
 // The kernel needs more than the default 64 KB of dynamic LDS: raise the
 // limit once per device and variant.  Host threads may race here; setting
 // the attribute twice is harmless, so a relaxed flag suffices.
-template <int MT, bool MX, bool ONE>
+template <int MT, bool MX, bool ONE, bool PK>
 hipError_t allow_mfma_stream_lds() {
   static std::atomic<bool> done[64];
   int dev = 0;
@@ -1329,7 +1357,7 @@ hipError_t allow_mfma_stream_lds() {
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
   if (!done[dev].load(std::memory_order_relaxed)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(mfma_stream_kernel<MT, MX, ONE>()),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(mfma_stream_kernel<MT, MX, ONE, PK>()),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kMfmaStreamLds);
     if (e != hipSuccess) return e;
     done[dev].store(true, std::memory_order_relaxed);
@@ -1353,18 +1381,23 @@ hipError_t run_valu_stream(const StreamJobs& l, int64_t blocks, int64_t tiles, i
   return hipGetLastError();
 }
 
-template <int MT, bool MX, bool ONE>
+template <int MT, bool MX, bool ONE, bool PK>
 hipError_t run_mfma_stream(const StreamJobs& l, int64_t blocks, int64_t tiles, int tiles_per_block, int m,
                            int seg_cols, hipStream_t stream);
 
+template <int MT, bool ONE>
+hipError_t dispatch_mfma_stream_mt(const StreamJobs& l, int64_t blocks, int64_t tiles, int tiles_per_block,
+                                   int m, int seg_cols, bool mx, bool pk, hipStream_t s) {
+  if (!mx) return run_mfma_stream<MT, false, ONE, false>(l, blocks, tiles, tiles_per_block, m, seg_cols, s);
+  return pk ? run_mfma_stream<MT, true, ONE, true>(l, blocks, tiles, tiles_per_block, m, seg_cols, s)
+            : run_mfma_stream<MT, true, ONE, false>(l, blocks, tiles, tiles_per_block, m, seg_cols, s);
+}
+
 template <bool ONE>
 hipError_t dispatch_mfma_stream(const StreamJobs& l, int64_t blocks, int64_t tiles, int tiles_per_block,
-                                int m, int seg_cols, bool mx, hipStream_t s) {
-  if (m <= 16)
-    return mx ? run_mfma_stream<1, true, ONE>(l, blocks, tiles, tiles_per_block, m, seg_cols, s)
-              : run_mfma_stream<1, false, ONE>(l, blocks, tiles, tiles_per_block, m, seg_cols, s);
-  return mx ? run_mfma_stream<2, true, ONE>(l, blocks, tiles, tiles_per_block, m, seg_cols, s)
-            : run_mfma_stream<2, false, ONE>(l, blocks, tiles, tiles_per_block, m, seg_cols, s);
+                                int m, int seg_cols, bool mx, bool pk, hipStream_t s) {
+  return m <= 16 ? dispatch_mfma_stream_mt<1, ONE>(l, blocks, tiles, tiles_per_block, m, seg_cols, mx, pk, s)
+                 : dispatch_mfma_stream_mt<2, ONE>(l, blocks, tiles, tiles_per_block, m, seg_cols, mx, pk, s);
 }
 
 // Single calls with many rows take the wide VALU tiles (the streaming
@@ -1416,13 +1449,22 @@ int gemv_mfma_stream_lds_limit() { return kMfmaStreamLds; }
 
 namespace {
 
-template <int MT, bool MX, bool ONE>
+template <int MT, int NW>
+hipError_t launch_mfma_direct(dim3 grid, const GemvJob& job, int m, bool mx, bool pk, hipStream_t stream) {
+  const dim3 block(NW * kWave);
+  if (!mx) hipLaunchKernelGGL((k_gemv_mfma_direct<MT, 2, false, NW, false>), grid, block, 0, stream, job, m);
+  else if (pk) hipLaunchKernelGGL((k_gemv_mfma_direct<MT, 2, true, NW, true>), grid, block, 0, stream, job, m);
+  else hipLaunchKernelGGL((k_gemv_mfma_direct<MT, 2, true, NW, false>), grid, block, 0, stream, job, m);
+  return hipGetLastError();
+}
+
+template <int MT, bool MX, bool ONE, bool PK>
 hipError_t run_mfma_stream(const StreamJobs& l, int64_t blocks, int64_t tiles, int tiles_per_block, int m,
                            int seg_cols, hipStream_t stream) {
-  const hipError_t e = allow_mfma_stream_lds<MT, MX, ONE>();
+  const hipError_t e = allow_mfma_stream_lds<MT, MX, ONE, PK>();
   if (e != hipSuccess) return e;
   const size_t lds = (size_t)gemv_mfma_stream_lds(m, seg_cols);
-  hipLaunchKernelGGL((k_gemv_mfma_stream<MT, kMfmaStreamWaves, 2, MX, ONE>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((k_gemv_mfma_stream<MT, kMfmaStreamWaves, 2, MX, ONE, PK>), dim3((unsigned)blocks),
                      dim3(kMfmaStreamWaves * kWave), lds, stream, l.table, l.count, l.one, (int)tiles,
                      tiles_per_block, m, seg_cols);
   return hipGetLastError();
@@ -1453,29 +1495,20 @@ hipError_t launch_gemv(const GemvJob& job, int m, bool mx, int route, hipStream_
     const int rows = gemv_rows_per_block(route, m, true);
     const int64_t tiles = (job.n + rows - 1) / rows;
     return dispatch_mfma_stream<true>(l, tiles, tiles, 1, m, gemv_mfma_stream_seg_cols(m, job.k), mx,
-                                      stream);
+                                      mx && mx_rows_packed8(job.scales, job.k), stream);
   }
-  const int64_t blocks = (job.n + 15) / 16;
+  const dim3 grid((unsigned)((job.n + 15) / 16));
+  const bool pk = mx && mx_rows_packed8(job.scales, job.k);
   if (job.n <= kDirect8MaxRows) {
-    const dim3 grid((unsigned)blocks), block(8 * kWave);
-    if (m <= 16) {
-      if (mx) hipLaunchKernelGGL((k_gemv_mfma_direct<1, 2, true, 8>), grid, block, 0, stream, job, m);
-      else hipLaunchKernelGGL((k_gemv_mfma_direct<1, 2, false, 8>), grid, block, 0, stream, job, m);
-    } else {
-      if (mx) hipLaunchKernelGGL((k_gemv_mfma_direct<2, 2, true, 8>), grid, block, 0, stream, job, m);
-      else hipLaunchKernelGGL((k_gemv_mfma_direct<2, 2, false, 8>), grid, block, 0, stream, job, m);
-    }
-    return hipGetLastError();
+    return m <= 16 ? launch_mfma_direct<1, 8>(grid, job, m, mx, pk, stream)
+                   : launch_mfma_direct<2, 8>(grid, job, m, mx, pk, stream);
   }
-  const dim3 grid((unsigned)blocks), block(kThreads);
-  if (m <= 16) {
-    if (mx) hipLaunchKernelGGL((k_gemv_mfma_direct<1, 2, true, kWaves>), grid, block, 0, stream, job, m);
-    else hipLaunchKernelGGL((k_gemv_mfma_direct<1, 2, false, kWaves>), grid, block, 0, stream, job, m);
-  } else {
-    if (mx) hipLaunchKernelGGL((k_gemv_mfma_direct<2, 2, true, kWaves>), grid, block, 0, stream, job, m);
-    else hipLaunchKernelGGL((k_gemv_mfma_direct<2, 2, false, kWaves>), grid, block, 0, stream, job, m);
-  }
-  return hipGetLastError();
+  return m <= 16 ? launch_mfma_direct<1, kWaves>(grid, job, m, mx, pk, stream)
+                 : launch_mfma_direct<2, kWaves>(grid, job, m, mx, pk, stream);
+}
+
+bool mx_rows_packed8(const void* e8m0, int64_t k) {
+  return ((k + kGroup - 1) / kGroup) % 8 == 0 && reinterpret_cast<uintptr_t>(e8m0) % 8 == 0;
 }
 
 hipError_t gemv_stream_slots(bool mx, int* slots) {
@@ -1514,18 +1547,18 @@ hipError_t gemv_mfma_stream_slots(int m, bool mx, int seg_cols, int* slots) {
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess) {
     if (m <= 16) {
-      e = mx ? allow_mfma_stream_lds<1, true, false>() : allow_mfma_stream_lds<1, false, false>();
+      e = mx ? allow_mfma_stream_lds<1, true, false, false>() : allow_mfma_stream_lds<1, false, false, false>();
       if (e == hipSuccess)
-        e = mx ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_stream_kernel<1, true, false>(),
+        e = mx ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_stream_kernel<1, true, false, false>(),
                                                               threads, lds)
-               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_stream_kernel<1, false, false>(),
+               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_stream_kernel<1, false, false, false>(),
                                                               threads, lds);
     } else {
-      e = mx ? allow_mfma_stream_lds<2, true, false>() : allow_mfma_stream_lds<2, false, false>();
+      e = mx ? allow_mfma_stream_lds<2, true, false, false>() : allow_mfma_stream_lds<2, false, false, false>();
       if (e == hipSuccess)
-        e = mx ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_stream_kernel<2, true, false>(),
+        e = mx ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_stream_kernel<2, true, false, false>(),
                                                               threads, lds)
-               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_stream_kernel<2, false, false>(),
+               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_stream_kernel<2, false, false, false>(),
                                                               threads, lds);
     }
   }
@@ -1621,10 +1654,11 @@ hipError_t launch_gemv_w8a8(const GemvJob& job, const float* x_scale, int m, boo
 }
 
 hipError_t launch_gemv_mfma_stream(const GemvJob* table, int njobs, int64_t blocks, int64_t tiles,
-                                   int tiles_per_block, int m, int seg_cols, bool mx,
+                                   int tiles_per_block, int m, int seg_cols, bool mx, bool mx_packed8,
                                    hipStream_t stream) {
   const StreamJobs l{table, njobs, GemvJob{}};
-  return dispatch_mfma_stream<false>(l, blocks, tiles, tiles_per_block, m, seg_cols, mx, stream);
+  return dispatch_mfma_stream<false>(l, blocks, tiles, tiles_per_block, m, seg_cols, mx, mx && mx_packed8,
+                                     stream);
 }
 
 }  // namespace fp8w

@@ -90,9 +90,13 @@ int gemv_mfma_stream_seg_cols(int m, int64_t max_k);
 int gemv_mfma_stream_lds(int m, int seg_cols);      // LDS bytes per workgroup
 int gemv_mfma_stream_lds_limit();
 hipError_t gemv_mfma_stream_slots(int m, bool mx, int seg_cols, int* slots);
+// MX weights whose exponent rows all start 8-byte aligned (ceil(k/32) % 8
+// == 0 and an 8-byte aligned array): the MFMA kernels then read each row's
+// exponents for a 256-column panel with one 8-byte load.
+bool mx_rows_packed8(const void* e8m0, int64_t k);
 hipError_t launch_gemv_mfma_stream(const GemvJob* device_table, int njobs, int64_t blocks,
                                    int64_t tiles, int tiles_per_block, int m, int seg_cols,
-                                   bool mx, hipStream_t stream);
+                                   bool mx, bool mx_packed8, hipStream_t stream);
 
 // Read-only pass over `bytes` (a multiple of 16) of device memory, one
 // 32-bit XOR per workgroup into out[0 .. blocks).

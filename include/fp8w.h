@@ -353,6 +353,11 @@ typedef struct fp8w_grouped_plan {
                               (multiple of 256).  VALU route: 0, or 4096
                               for m = 1 plans without streaming whose
                               tiles walk K in 4096-column segments        */
+  int32_t mx_packed8;      /* MFMA route, MX format: 1 when every GEMV's
+                              exponent rows start 8-byte aligned
+                              (ceil(k/32) % 8 == 0, 8-byte aligned array),
+                              so its kernel reads 8 exponents per load;
+                              0 otherwise                                  */
 } fp8w_grouped_plan;
 
 /* Bytes of device memory a table for `count` GEMVs needs (0 if count < 1). */

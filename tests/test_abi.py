@@ -217,6 +217,12 @@ def test_grouped_argument_errors(F):
     assert L.fp8w_gemv_grouped(ctypes.byref(bad), None) == F.ERR_SHAPE
     bad = F.GroupedPlanC(T, 1, 32, 0, 2, 4, 4, 1, 4096)  # MFMA: x segment exceeds the LDS budget
     assert L.fp8w_gemv_grouped(ctypes.byref(bad), None) == F.ERR_SHAPE
+    bad = F.GroupedPlanC(T, 1, 4, 1, 2, 4, 4, 1, 256, 2)  # mx_packed8 is 0 or 1
+    assert L.fp8w_gemv_grouped(ctypes.byref(bad), None) == F.ERR_SHAPE
+    bad = F.GroupedPlanC(T, 1, 4, 0, 2, 4, 4, 1, 256, 1)  # ... 1 only for MX weights
+    assert L.fp8w_gemv_grouped(ctypes.byref(bad), None) == F.ERR_SHAPE
+    bad = F.GroupedPlanC(T, 1, 1, 1, 1, 4, 4, 0, 0, 1)    # ... on the MFMA route
+    assert L.fp8w_gemv_grouped(ctypes.byref(bad), None) == F.ERR_SHAPE
 
 
 def test_binding_refuses_cpu_tensors(F):

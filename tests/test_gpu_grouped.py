@@ -223,3 +223,26 @@ def test_grouped_wide_tiles_segment_width(fp8w, oracle_mod, fmt, shapes, seg):
     for (n, k, c, s), x, y in zip(jobs, xs_h, ys):
         y_ref, bound = ref(x, c, s)
         assert_within_bound(bf16_to_f64(y), y_ref, bound, f"grouped wide {fmt} seg={seg} [{n}x{k}]")
+
+
+# MFMA plans over MX weights read 8 exponents per load when every GEMV's
+# exponent rows start 8-byte aligned (ceil(k/32) % 8 == 0 and an aligned
+# array: mx_packed8 = 1), one per chunk otherwise; ragged N and K.
+@pytest.mark.parametrize("off", [0, 4])
+@pytest.mark.parametrize("m", [2, 9, 17, 32])
+def test_mx_packed_exponents_grouped(fp8w, oracle_mod, off, m):
+    shapes = [(37, 240), (130, 496), (300, 2048), (7, 3056), (129, 4352)]
+    jobs = []
+    for i, (n, k) in enumerate(shapes):
+        bits = W.gaussian_weight(45, i, n, k, heavy_tail=True)
+        c, e = oracle_mod.quantize_mx(bits)
+        jobs.append((n, k, c, e))
+    xs_h = [W.activation(46, m, k) for (_, k, _, _) in jobs]
+    plan = fp8w.fp8w_grouped_plan_init([to_dev_bf16(x) for x in xs_h], [to_dev(c) for (_, _, c, _) in jobs],
+                                       [_offset_dev(e, off) for (_, _, _, e) in jobs], fmt="mx")
+    assert plan.route == fp8w.ROUTE_MFMA and plan.plan.mx_packed8 == (1 if off == 0 else 0)
+    ys = fp8w.fp8w_gemv_grouped(plan)
+    _sync()
+    for (n, k, c, e), x, y in zip(jobs, xs_h, ys):
+        y_ref, bound = oracle_mod.gemv_mx_f64(x, c, e)
+        assert_within_bound(bf16_to_f64(y), y_ref, bound, f"grouped mx packed={off == 0} m={m} [{n}x{k}]")

@@ -187,6 +187,15 @@ def test_mfma_direct_wave_split(fp8w, oracle_mod, weights, fmt, n, m):
     _check(fp8w, oracle_mod, weights, n, 2320, m, fmt, 0)
 
 
+# MX single calls whose exponent rows start 8-byte aligned (K = 2304: 72
+# groups) read 8 exponents per load: the per-tile MFMA kernel on both sides
+# of its wave split and the streaming one (32813 rows)
+@pytest.mark.parametrize("n", [4096, 4112, 32813])
+@pytest.mark.parametrize("m", [3, 17, 32])
+def test_mx_packed_exponents_single(fp8w, oracle_mod, weights, n, m):
+    _check(fp8w, oracle_mod, weights, n, 2304, m, "mx", 0)
+
+
 # W8A8 single calls on either side of the same split (m >= 3 on fewer rows
 # than the 128-row W8A8 tiles take)
 @pytest.mark.parametrize("fmt", ("block", "mx"))

@@ -1076,16 +1076,21 @@ __device__ __forceinline__ void panel8_issue(const GemvJob& j, int row0, int p, 
     if (live && row < j.n && col < j.k) r.v[q] = ld_stream_u4(j.codes, (size_t)row * j.k + col);
   }
   r.s[0] = r.s[1] = 0.0f;
-  r.e[0] = r.e[1] = kE8m0One;
   if (MX) {
-    const int row = row0 + (lane & 15);
+    // Unconditional loads from a row and group clamped into the weight (as
+    // panel_issue): rows and columns outside it have zero codes.  A default
+    // joined with a conditional load would make the wave wait for the load.
+    const int row = min(row0 + (lane & 15), j.n - 1);
     const uint8_t* __restrict__ e8 = static_cast<const uint8_t*>(j.scales);
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      const int grp = 4 * (2 * p + b) + (lane >> 4);
-      if (live && row < j.n && grp < groups) r.e[b] = ld_global<uint8_t>(e8, (size_t)row * groups + grp);
+      const int grp = min(4 * (2 * p + b) + (lane >> 4), groups - 1);
+      r.e[b] = ld_global<uint8_t>(e8, (size_t)row * groups + grp);
     }
-  } else if (live && row0 < j.n) {
+  } else {
+    r.e[0] = r.e[1] = kE8m0One;
+  }
+  if (!MX && live && row0 < j.n) {
     r.s[0] = block_scale(j, row0, 2 * p, nkb);
     if (2 * p + 1 < nkb) r.s[1] = block_scale(j, row0, 2 * p + 1, nkb);
   }

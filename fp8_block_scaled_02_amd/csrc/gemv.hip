@@ -220,46 +220,6 @@ __device__ __forceinline__ void copy_batched(int total, Load load, Store store) 
 // Units of the staging copies in flight per thread.
 constexpr int kStageBatch = 4;
 
-// Copy x[0:rows, seg0 : seg0+len] (len a multiple of 16) into LDS rows of
-// stride `ld` elements, covering columns [0, len_pad); columns >= len and
-// rows rows..rows_pad-1 are zero-filled, so padded products are exact zeros.
-__device__ __forceinline__ void stage_x(const uint16_t* __restrict__ x, int rows, int rows_pad,
-                                        int k, int seg0, int len, int len_pad, uint16_t* xs,
-                                        int ld) {
-  const int units = len_pad / 8;   // 16-byte units per row
-  copy_batched<kStageBatch, kThreads, uint4>(
-      rows_pad * units,
-      [&](int u) {
-        const int r = u / units, c = (u - r * units) * 8;
-        return (r < rows && c < len) ? ld_global_u4(x, ((size_t)r * k + seg0 + c) * 2) : make_uint4(0, 0, 0, 0);
-      },
-      [&](int u, uint4 v) {
-        const int r = u / units, c = (u - r * units) * 8;
-        *reinterpret_cast<uint4*>(xs + r * ld + c) = v;
-      });
-}
-
-// As stage_x for e4m3 activation codes x[0:rows, ...] (1 byte each), each
-// code widened to bf16 (exact) on the way into LDS.  len and seg0 are
-// multiples of 16 and x is 16-byte aligned, so every 8-code load is aligned.
-__device__ __forceinline__ void stage_x8(const uint8_t* __restrict__ x, int rows, int k, int seg0, int len,
-                                         uint16_t* xs, int ld) {
-  const int units = len / 8;
-  copy_batched<kStageBatch, kThreads, u32x2>(
-      rows * units,
-      [&](int u) {
-        const int r = u / units, c = (u - r * units) * 8;
-        return ld_global<u32x2>(x, (size_t)r * k + seg0 + c);
-      },
-      [&](int u, u32x2 v) {
-        const int r = u / units, c = (u - r * units) * 8;
-        const bf16x2 a = cvt_lo(v.x), b = cvt_hi(v.x), d = cvt_lo(v.y), e = cvt_hi(v.y);
-        *reinterpret_cast<u32x4*>(xs + r * ld + c) =
-            u32x4{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, d),
-                  __builtin_bit_cast(uint32_t, e)};
-      });
-}
-
 // x[0, 0:k] (one activation row, k a multiple of 8) into LDS.
 __device__ __forceinline__ void stage_row(const uint16_t* __restrict__ x, int k, uint16_t* xs) {
   copy_batched<kStageBatch, kThreads, uint4>(
@@ -271,9 +231,10 @@ __device__ __forceinline__ void stage_row(const uint16_t* __restrict__ x, int k,
 //
 // Workgroup = 4 waves x R rows.  Wave w owns rows row0 + r (r < R); lane l
 // takes the 16-byte chunks l, l + 64, ..., of each K segment (C chunks per
-// lane, so a segment is 1024*C columns).  Per segment: the codes (and MX
-// scale bytes) of all R rows are requested, x and the block-scale row are
-// staged in LDS while they arrive, then the segment is accumulated.
+// lane, so a segment is 1024*C columns).  Per segment: x and the block
+// scales (or MX exponents) are requested, then the codes of all R rows;
+// the staged values reach LDS while the codes are in flight, and the
+// segment is accumulated chunk by chunk as its codes arrive.
 template <int M, int R, int C>
 struct ValuShape {
   static constexpr int kRows = kWaves * R;
@@ -282,49 +243,126 @@ struct ValuShape {
   static constexpr int kLdsX = M * kSeg * 2;
   static constexpr int kLdsScales = (kSeg / kTile) * 4;
   static constexpr int kLdsBytes = kLdsX + (kLdsScales > kRows * kSegGroups ? kLdsScales : kRows * kSegGroups);
+  // staging loads per thread and segment: 8-element x units (at most 8 in
+  // registers; a larger M stages the rest after the codes) and MX exponents
+  static constexpr int kXUnits = (M * kSeg / 8 + kThreads - 1) / kThreads;
+  static constexpr int kXPre = kXUnits < 8 ? kXUnits : 8;
+  static constexpr int kExpPre = (kRows * kSegGroups + kThreads - 1) / kThreads;
   static_assert(kTile % kRows == 0, "a workgroup must stay inside one 128-row block");
   static_assert(kLdsBytes <= 64 * 1024, "LDS budget");
 };
 
+// The segment's codes, every load unconditional: rows past n read row n-1
+// and chunks past nch read chunk nch-1; the accumulation skips those chunks
+// and the store skips those rows.  (A conditional load is one the compiler
+// cannot count, and it then waits for every load before the staged x can
+// be written to LDS; unconditional loads let it wait for exactly the ones
+// it needs.)
 template <int R, int C>
 __device__ __forceinline__ void valu_load(const GemvJob& j, int row0, int seg0, int nch, uint4 (&wv)[R][C]) {
   const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int row = row0 + r;
+    const int row = min(row0 + r, j.n - 1);
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-      const int ch = lane + kWave * c;
-      wv[r][c] = make_uint4(0, 0, 0, 0);
-      if (ch < nch && row < j.n) wv[r][c] = ld_stream_u4(j.codes, (size_t)row * j.k + seg0 + ch * 16);
+      const int ch = min(lane + kWave * c, nch - 1);
+      wv[r][c] = ld_stream_u4(j.codes, (size_t)row * j.k + seg0 + ch * 16);
     }
   }
 }
 
-// MX exponents of the workgroup's `rows` rows for the segment's `ng` groups
-// starting at group gs, into LDS rows of `ld` bytes (rows >= n read as 0).
-// When every row's exponents start 4-byte aligned (groups % 4 == 0, aligned
-// base; gs is a multiple of 4) they are read as dwords: each row's span then
-// ends on a dword inside the row.  Otherwise one byte per load.
-__device__ __forceinline__ void stage_exponents(const GemvJob& j, int row0, int rows, int groups, int gs, int ng,
-                                                unsigned char* ex, int ld) {
-  const uint8_t* __restrict__ e8 = static_cast<const uint8_t*>(j.scales);
-  if ((groups & 3) == 0 && (reinterpret_cast<uintptr_t>(e8) & 3) == 0) {
-    const int per_row = (ng + 3) / 4;
-    for (int u = threadIdx.x; u < rows * per_row; u += kThreads) {
-      const int r = u / per_row, d = u - r * per_row;
-      const int row = row0 + r;
-      const uint32_t v = row < j.n ? ld_global<uint32_t>(e8, (size_t)row * groups + gs + 4 * d) : 0u;
-      *reinterpret_cast<uint32_t*>(ex + r * ld + 4 * d) = v;
+// What one K segment stages in LDS besides the codes: x (bf16, or e4m3
+// codes widened to bf16 for X8) and the block scales or MX exponents.  The
+// loads are issued before the segment's codes (load) and written to LDS
+// after them (commit): vector-memory waits count in issue order, so staging
+// loads issued after the codes could only be written once every code had
+// arrived; issued first, x and the scales reach LDS while the codes are
+// still in flight.  Loads are unconditional, from indices clamped into
+// their arrays; commit writes only the valid ones.
+template <int M, int R, int C, bool MX, bool X8>
+struct SegStage {
+  using S = ValuShape<M, R, C>;
+  using XU = typename std::conditional<X8, u32x2, uint4>::type;   // 8 elements of x
+  XU x[S::kXPre];
+  uint32_t e[MX ? S::kExpPre : 1];      // MX: exponent bytes
+  uint16_t lo, hi;                      // block grids: the scale's 16-bit halves
+
+  __device__ __forceinline__ void load(const GemvJob& j, int tile, int seg0, int len, int tiles_k, int groups) {
+    const int units = len / 8, total = M * units;
+#pragma unroll
+    for (int q = 0; q < S::kXPre; ++q) {
+      const int u = min((int)threadIdx.x + q * kThreads, total - 1);
+      const int r = u / units, c = (u - r * units) * 8;
+      if constexpr (X8) x[q] = ld_x8(j, (size_t)r * j.k + seg0 + c);
+      else x[q] = ld_x16(j, ((size_t)r * j.k + seg0 + c) * 2);
     }
-  } else {
-    for (int u = threadIdx.x; u < rows * ng; u += kThreads) {
-      const int r = u / ng, g = u - r * ng;
-      const int row = row0 + r;
-      ex[r * ld + g] = row < j.n ? ld_global<uint8_t>(e8, (size_t)row * groups + gs + g) : (uint8_t)0;
+    if (MX) {
+      const int ng = (len + kGroup - 1) / kGroup, gs = seg0 / kGroup;
+#pragma unroll
+      for (int q = 0; q < S::kExpPre; ++q) {
+        const int u = min((int)threadIdx.x + q * kThreads, S::kRows * ng - 1);
+        const int r = u / ng, g = u - r * ng;
+        const int row = min(tile * S::kRows + r, j.n - 1);
+        e[q] = ld_global<uint8_t>(j.scales, (size_t)row * groups + gs + g);
+      }
+    } else {
+      // fp32 grid: both halves of the scale; bf16 grid: its bits are the
+      // high half; row and tensor scales (applied at the store) read the
+      // array's first word and stage 1
+      const int nkb = (len + kTile - 1) / kTile;
+      const size_t at = (size_t)((tile * S::kRows) / kTile) * tiles_k + seg0 / kTile +
+                        min((int)threadIdx.x, nkb - 1);
+      const bool f32 = j.format == kFmtBlock, b16 = j.format == kFmtBlockBf16;
+      lo = ld_global<uint16_t>(j.scales, f32 ? at * 4 : 0);
+      hi = ld_global<uint16_t>(j.scales, f32 ? at * 4 + 2 : (b16 ? at * 2 : 0));
     }
   }
-}
+
+  __device__ __forceinline__ void commit(const GemvJob& j, int tile, int seg0, int len, int groups,
+                                         uint16_t* xs, float* ss, unsigned char* ex) const {
+    const int units = len / 8, total = M * units;
+#pragma unroll
+    for (int q = 0; q < S::kXPre; ++q) {
+      const int u = (int)threadIdx.x + q * kThreads;
+      const int r = u / units, c = (u - r * units) * 8;
+      if (u < total) *reinterpret_cast<uint4*>(xs + r * S::kSeg + c) = widen(x[q]);
+    }
+    for (int u = (int)threadIdx.x + S::kXPre * kThreads; u < total; u += kThreads) {   // M beyond the registers
+      const int r = u / units, c = (u - r * units) * 8;
+      if constexpr (X8) *reinterpret_cast<uint4*>(xs + r * S::kSeg + c) = widen(ld_x8(j, (size_t)r * j.k + seg0 + c));
+      else *reinterpret_cast<uint4*>(xs + r * S::kSeg + c) = ld_x16(j, ((size_t)r * j.k + seg0 + c) * 2);
+    }
+    if (MX) {
+      const int ng = (len + kGroup - 1) / kGroup;
+#pragma unroll
+      for (int q = 0; q < S::kExpPre; ++q) {
+        const int u = (int)threadIdx.x + q * kThreads;
+        const int r = u / ng, g = u - r * ng;
+        if (u < S::kRows * ng) ex[r * S::kSegGroups + g] = (unsigned char)e[q];
+      }
+    } else {
+      const int nkb = (len + kTile - 1) / kTile;
+      if ((int)threadIdx.x < nkb)
+        ss[threadIdx.x] = j.format == kFmtBlock       ? __uint_as_float((uint32_t)hi << 16 | lo)
+                          : j.format == kFmtBlockBf16 ? __uint_as_float((uint32_t)hi << 16)
+                                                      : 1.0f;
+    }
+    (void)tile;
+    (void)groups;
+  }
+
+ private:
+  static __device__ __forceinline__ u32x2 ld_x8(const GemvJob& j, size_t off) { return ld_global<u32x2>(j.x, off); }
+  static __device__ __forceinline__ uint4 ld_x16(const GemvJob& j, size_t off) { return ld_global_u4(j.x, off); }
+  // x as staged: bf16 passes through; e4m3 codes widen to bf16 (exact)
+  static __device__ __forceinline__ uint4 widen(uint4 v) { return v; }
+  static __device__ __forceinline__ uint4 widen(u32x2 v) {
+    const bf16x2 a = cvt_lo(v.x), b = cvt_hi(v.x), d = cvt_lo(v.y), f = cvt_hi(v.y);
+    return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                      __builtin_bit_cast(uint32_t, d), __builtin_bit_cast(uint32_t, f));
+  }
+};
 
 // X8: the activation is e4m3 codes (j.x points at bytes) with the fp32
 // tensor scale at *xscale (the W8A8 path at small m): the codes are widened
@@ -355,18 +393,12 @@ __global__ __launch_bounds__(kThreads) void k_gemv_valu(GemvJob arg, const GemvJ
   for (int seg0 = 0; seg0 < j.k; seg0 += S::kSeg) {
     const int len = min(S::kSeg, j.k - seg0);
     const int nch = len / 16;
+    SegStage<M, R, C, MX, X8> st;
+    st.load(j, tile, seg0, len, tiles_k, groups);
     uint4 cw[R][C];
     valu_load<R, C>(j, row0, seg0, nch, cw);
     if (seg0 > 0) __syncthreads();   // the previous segment's LDS reads are done
-    if (X8) stage_x8(reinterpret_cast<const uint8_t*>(j.x), M, j.k, seg0, len, xs, S::kSeg);
-    else stage_x(j.x, M, M, j.k, seg0, len, len, xs, S::kSeg);
-    if (MX) {
-      stage_exponents(j, tile * S::kRows, S::kRows, groups, seg0 / kGroup, (len + kGroup - 1) / kGroup, ex,
-                      S::kSegGroups);
-    } else {
-      const int nkb = (len + kTile - 1) / kTile;
-      if ((int)threadIdx.x < nkb) ss[threadIdx.x] = block_scale(j, tile * S::kRows, seg0 / kTile + threadIdx.x, tiles_k);
-    }
+    st.commit(j, tile, seg0, len, groups, xs, ss, ex);
     __syncthreads();
 
     for (int c = 0; c < C; ++c) {

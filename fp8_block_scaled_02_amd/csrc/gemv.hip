@@ -28,8 +28,11 @@
 //    the activation codes widened to bf16 at M <= 2.
 //
 // Each call is a few microseconds of HBM traffic, so latency decides the
-// time: every kernel issues its weight loads first (non-temporal: each code
-// byte is read once) and stages x while they are in flight.
+// time: every kernel keeps its weight loads (non-temporal: each code byte
+// is read once) in flight while x is staged.  Vector-memory waits count in
+// issue order, so what must be ready first is requested first: the
+// per-tile VALU kernel requests x and the scales just before the codes,
+// and scale bytes are kept as loaded and converted where they are used.
 //
 // A launch covers either one GEMV (the job travels as a kernel argument) or
 // a group of independent GEMVs (a job table in device memory; a workgroup

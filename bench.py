@@ -41,7 +41,7 @@ PEAK_BF16 = 2.5e15         # MI355X dense bf16 MFMA, flop/s
 # kernel, launch-plan and helper sources); any change to those reports
 # traffic as null until the counters are retaken.
 COUNTED_TRAFFIC = {
-    "sources_sha256": "be958026f361dcff5773f630e55d738f8aec980dda013e4d7ea99fbb6fc702c7",
+    "sources_sha256": "8db196d5d109fcae6563d154694c7be7e88adb9cfc1b4017323382d31038298e",
     "bytes_per_launch": 1340.38e6,
 }
 TRAFFIC_SOURCES = ('gemv.hip', 'device.hpp', 'internal.hpp', 'api.cpp')

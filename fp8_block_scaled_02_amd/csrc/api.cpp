@@ -344,9 +344,10 @@ FP8W_API fp8w_status fp8w_grouped_plan_init(const fp8w_gemv_desc* descs, int64_t
   // runs of tiles per workgroup); other VALU plans take one tile per
   // workgroup; MFMA plans always stream, x staged by K segments.
   // (the streaming VALU kernel reads MX exponents as aligned dwords)
-  bool scales_aligned4 = true;
-  for (int64_t i = 0; i < count; ++i) scales_aligned4 = scales_aligned4 && aligned(descs[i].scales, 4);
-  const bool valu_stream = r == 1 && m == 1 && max_k <= fp8w::gemv_stream_max_k() && (!mx || scales_aligned4);
+  bool mx_dwords = true;
+  for (int64_t i = 0; i < count; ++i)
+    mx_dwords = mx_dwords && fp8w::mx_rows_stream(descs[i].scales, descs[i].n, descs[i].k);
+  const bool valu_stream = r == 1 && m == 1 && max_k <= fp8w::gemv_stream_max_k() && (!mx || mx_dwords);
   const int rows = valu_stream ? fp8w::gemv_stream_rows() : fp8w::gemv_rows_per_block(r, (int)m, true);
   std::vector<fp8w::GemvJob> table((size_t)count);
   int64_t tiles = 0;

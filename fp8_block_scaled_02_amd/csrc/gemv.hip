@@ -467,25 +467,19 @@ struct TileRegs {
 // [n, groups] array, R * groups <= 512 bytes, read as dwords (lane l: bytes
 // 4l and 256 + 4l of the span) instead of one byte load per row and chunk.
 // row0 is a multiple of R = 4, so with a 4-byte aligned base every dword is
-// aligned; the last dword of a job is assembled from bytes when it would
-// reach past row n-1.
+// aligned, and the host streams MX weights only when the whole array is a
+// whole number of dwords (n * groups % 4 == 0, mx_rows_stream): each dword
+// lies inside the array or wholly past its end.  Those past the end load the
+// array's last dword instead (rows >= n, whose sums are never stored), so
+// the loads are unconditional and the compiler can count them.
 __device__ __forceinline__ void mx_span_issue(const GemvJob& j, int row0, int rows, int groups,
                                               uint32_t (&e)[2]) {
+  (void)rows;
   const int lane = threadIdx.x & (kWave - 1);
-  const uint8_t* __restrict__ e8 = static_cast<const uint8_t*>(j.scales);
-  const int valid = max(0, min(j.n - row0, rows)) * groups;   // bytes of the span inside the array
+  const size_t total = (size_t)j.n * groups;
   const size_t base = (size_t)row0 * groups;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int off = 4 * (lane + kWave * h);
-    uint32_t v = 0;
-    if (off + 4 <= valid) {
-      v = ld_global<uint32_t>(e8, base + off);
-    } else if (off < valid) {
-      for (int b = 0; b < valid - off; ++b) v |= (uint32_t)ld_global<uint8_t>(e8, base + off + b) << (8 * b);
-    }
-    e[h] = v;
-  }
+  for (int h = 0; h < 2; ++h) e[h] = ld_global<uint32_t>(j.scales, min(base + 4 * (lane + kWave * h), total - 4));
 }
 
 __device__ __forceinline__ void load_job_row(const GemvJob* __restrict__ jobs, int jn, GemvJob& job) {
@@ -1515,8 +1509,7 @@ hipError_t run_mfma_stream(const StreamJobs& l, int64_t blocks, int64_t tiles, i
 hipError_t launch_gemv(const GemvJob& job, int m, bool mx, int route, hipStream_t stream) {
   if (route == 1) {
     const bool wide = job.n >= kSingleWideMinRowsValu;
-    if (wide && m == 1 && job.k <= gemv_stream_max_k() &&
-        (!mx || reinterpret_cast<uintptr_t>(job.scales) % 4 == 0)) {
+    if (wide && m == 1 && job.k <= gemv_stream_max_k() && (!mx || mx_rows_stream(job.scales, job.n, job.k))) {
       StreamJobs l{nullptr, 1, job};
       l.one.item0 = 0;
       const int64_t tiles = (job.n + gemv_stream_rows() - 1) / gemv_stream_rows();
@@ -1545,6 +1538,10 @@ hipError_t launch_gemv(const GemvJob& job, int m, bool mx, int route, hipStream_
   }
   return m <= 16 ? launch_mfma_direct<1, kWaves>(grid, job, m, mx, pk, stream)
                  : launch_mfma_direct<2, kWaves>(grid, job, m, mx, pk, stream);
+}
+
+bool mx_rows_stream(const void* e8m0, int64_t n, int64_t k) {
+  return reinterpret_cast<uintptr_t>(e8m0) % 4 == 0 && (n * ((k + kGroup - 1) / kGroup)) % 4 == 0;
 }
 
 bool mx_rows_packed8(const void* e8m0, int64_t k) {

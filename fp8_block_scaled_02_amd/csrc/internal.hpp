@@ -75,7 +75,7 @@ int gemv_wide_seg_rounds(int64_t k, int seg_cols);
 int gemv_wide_seg_cols(int64_t k);
 
 // Streaming grouped VALU kernel (m = 1, every K <= gemv_stream_max_k(), MX
-// exponent arrays 4-byte aligned):
+// exponent arrays as mx_rows_stream requires):
 // tiles of gemv_stream_rows() rows, a contiguous run of tiles per workgroup.
 int gemv_stream_max_k();
 int gemv_stream_rows();
@@ -94,6 +94,9 @@ hipError_t gemv_mfma_stream_slots(int m, bool mx, int seg_cols, int* slots);
 // == 0 and an 8-byte aligned array): the MFMA kernels then read each row's
 // exponents for a 256-column panel with one 8-byte load.
 bool mx_rows_packed8(const void* e8m0, int64_t k);
+// MX weights the streaming VALU kernel reads exponents of as dwords: a
+// 4-byte aligned array of a whole number of dwords (n * ceil(k/32) % 4 == 0).
+bool mx_rows_stream(const void* e8m0, int64_t n, int64_t k);
 hipError_t launch_gemv_mfma_stream(const GemvJob* device_table, int njobs, int64_t blocks,
                                    int64_t tiles, int tiles_per_block, int m, int seg_cols,
                                    bool mx, bool mx_packed8, hipStream_t stream);

@@ -131,12 +131,16 @@ def test_grouped_and_single_calls_replay_in_a_graph(fp8w, oracle_mod):
 @pytest.mark.parametrize("case", ["projection_like", "many_small_jobs"])
 def test_grouped_streaming_kernel_matches_oracle(fp8w, oracle_mod, fmt, case):
     """m = 1 with every K <= 3072 takes the streaming kernel (runs of tiles
-    per workgroup that cross job boundaries)."""
+    per workgroup that cross job boundaries).  MX weights stream when every
+    exponent array is a whole number of dwords: their N is rounded up to a
+    multiple of 4 here (still ragged against the 16-row tiles)."""
     rng = np.random.default_rng(40)
     if case == "projection_like":
         shapes = [(300, 1008), (130, 272), (8192, 2560), (257, 2560), (64, 16), (2560, 3072), (17, 3072)]
     else:
         shapes = [(int(rng.integers(1, 300)), int(rng.integers(1, 193)) * 16) for _ in range(60)]
+    if fmt == "mx":
+        shapes = [((n + 3) // 4 * 4, k) for n, k in shapes]
     jobs = []
     for i, (n, k) in enumerate(shapes):
         bits = W.gaussian_weight(41, i, n, k, outlier_rows=fmt == "block", heavy_tail=fmt == "mx")
@@ -168,11 +172,11 @@ def _offset_dev(a: np.ndarray, off: int):
 @pytest.mark.parametrize("off", [0, 1, 4])
 @pytest.mark.parametrize("m", [1, 2, 8, 17])
 def test_mx_exponent_alignment_paths(fp8w, oracle_mod, off, m, long_k):
-    """MX exponents at every alignment: the streaming VALU kernel and the
-    per-call VALU kernel read them as dwords only when each row starts 4-byte
-    aligned; the MFMA panels read 8 bytes at once only when 8-byte aligned
-    with groups % 8 == 0 (K = 240 and 496 have groups % 8 == 0 without K %
-    256 == 0).  Grouped plans, single calls and forced-VALU single calls."""
+    """MX exponents at every alignment: the streaming VALU kernel reads them
+    as dwords only from a 4-byte aligned array of whole dwords; the MFMA
+    panels read 8 bytes at once only when 8-byte aligned with groups % 8 == 0
+    (K = 240 and 496 have groups % 8 == 0 without K % 256 == 0).  Grouped
+    plans, single calls and forced-VALU single calls."""
     shapes = [(37, 240), (130, 496), (300, 2048), (61, 2064), (129, 1040), (7, 3056)]
     if long_k:   # several K segments in the per-call VALU kernel; no streaming plan
         shapes.append((19, 4240))
@@ -186,8 +190,9 @@ def test_mx_exponent_alignment_paths(fp8w, oracle_mod, off, m, long_k):
     codes = [to_dev(c) for (_, _, c, _) in jobs]
     exps = [_offset_dev(e, off) for (_, _, _, e) in jobs]
     plan = fp8w.fp8w_grouped_plan_init(xs, codes, exps, fmt="mx")
-    if m == 1:   # streaming only with aligned exponents and every K <= 3072
-        assert (plan.plan.tiles_per_block > 0) == (off % 4 == 0 and max(k for _, k in shapes) <= 3072)
+    if m == 1:   # streaming only with aligned exponent arrays of whole dwords and every K <= 3072
+        dwords = all(n * ((k + 31) // 32) % 4 == 0 for n, k in shapes)
+        assert (plan.plan.tiles_per_block > 0) == (off % 4 == 0 and dwords and max(k for _, k in shapes) <= 3072)
     ys = fp8w.fp8w_gemv_grouped(plan)
     ys_single = [fp8w.fp8w_gemv_mx(x, c, e) for x, c, e in zip(xs, codes, exps)]
     ys_valu = [fp8w.fp8w_gemv_mx(x, c, e, route=fp8w.ROUTE_VALU) if m <= 8 else None
@@ -246,3 +251,26 @@ def test_mx_packed_exponents_grouped(fp8w, oracle_mod, off, m):
     for (n, k, c, e), x, y in zip(jobs, xs_h, ys):
         y_ref, bound = oracle_mod.gemv_mx_f64(x, c, e)
         assert_within_bound(bf16_to_f64(y), y_ref, bound, f"grouped mx packed={off == 0} m={m} [{n}x{k}]")
+
+
+# Streaming MX plans at M = 1 with ragged N: exponent arrays of whole dwords
+# (groups % 4 == 0, so any n) stream, the span of the last tile reaching past
+# row n - 1; one array of n * groups % 4 != 0 in the group keeps the plan on
+# the per-tile kernel.
+@pytest.mark.parametrize("odd", [False, True])
+def test_mx_streaming_ragged_rows(fp8w, oracle_mod, odd):
+    shapes = [(37, 256), (130, 2048), (301, 3072), (5, 128)] + ([(61, 2064)] if odd else [])
+    jobs = []
+    for i, (n, k) in enumerate(shapes):
+        bits = W.gaussian_weight(47, i, n, k, heavy_tail=True)
+        c, e = oracle_mod.quantize_mx(bits)
+        jobs.append((n, k, c, e))
+    xs_h = [W.activation(48, 1, k) for (_, k, _, _) in jobs]
+    plan = fp8w.fp8w_grouped_plan_init([to_dev_bf16(x) for x in xs_h], [to_dev(c) for (_, _, c, _) in jobs],
+                                       [to_dev(e) for (_, _, _, e) in jobs], fmt="mx")
+    assert (plan.plan.tiles_per_block > 0) == (not odd)
+    ys = fp8w.fp8w_gemv_grouped(plan)
+    _sync()
+    for (n, k, c, e), x, y in zip(jobs, xs_h, ys):
+        y_ref, bound = oracle_mod.gemv_mx_f64(x, c, e)
+        assert_within_bound(bf16_to_f64(y), y_ref, bound, f"streaming mx odd={odd} [{n}x{k}]")

@@ -85,8 +85,13 @@ typedef enum fp8w_status {
  * in single calls and for m = 1 in grouped launches, MFMA above: the
  * crossovers measured on MI355X (gfx950 matrix cores win from 3 activation
  * rows on in single calls, from 2 in grouped launches).  Within a route the
- * kernel also depends on n (weights with many rows take the streaming
- * kernels), never on values.  Every route meets the same error bound. */
+ * kernel also depends on n and k (weights with many rows take the streaming
+ * kernels; K above 3072 is walked in 3072- or 4096-column segments) and, for
+ * MX, on how the exponent array is laid out (4-byte aligned with n *
+ * ceil(k/32) % 4 == 0: the M = 1 streaming kernel; 8-byte aligned with
+ * ceil(k/32) % 8 == 0: one 8-byte exponent load per row and panel in the
+ * MFMA kernels) -- never on values.  Every route meets the same error
+ * bound. */
 typedef enum fp8w_route {
   FP8W_ROUTE_AUTO = 0,
   FP8W_ROUTE_VALU = 1,

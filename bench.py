@@ -186,6 +186,14 @@ def pct(v, q):
     return v[min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))]
 
 
+def route_names(fp8w, m, calls):
+    """The kernel families AUTO takes for these single calls ("valu", "mfma")."""
+    names = {fp8w.ROUTE_VALU: "valu", fp8w.ROUTE_MFMA: "mfma"}
+    L = fp8w.lib()
+    got = sorted({names[L.fp8w_gemv_auto_route(m, c.shape[0], c.shape[1])] for (_, c, _, _) in calls})
+    return "+".join(got)
+
+
 def summarize(per_ms, calls, nbytes):
     med = statistics.median(per_ms)
     return {
@@ -320,7 +328,9 @@ def bench_proj(torch, fp8w, lean, timer, W, args, state, log):
         per_s, _ = timer.run(lean.gemv_block(calls, route), stream_steps, min(args.warmup, 20), hold_ms=20.0)
         row["per_call_stream"] = dict(summarize(per_s, len(calls), nbytes), launches_per_pass=len(calls),
                                       ms_per_pass=round(statistics.median(per_s), 4), graph=False)
-        row.update({"bytes_per_pass": nbytes, "route": "valu" if plan.route == fp8w.ROUTE_VALU else "mfma"})
+        per_call_route = route_names(fp8w, m, calls) if route == fp8w.ROUTE_AUTO else args.route
+        row.update({"bytes_per_pass": nbytes, "route": "valu" if plan.route == fp8w.ROUTE_VALU else "mfma",
+                    "per_call_route": per_call_route})
         if m == 1 and route == fp8w.ROUTE_AUTO:
             head = {"per": per, "total_ms": total, "bytes": nbytes, "calls": len(calls), "row": row}
         rows[f"m{m}"] = row
@@ -394,7 +404,7 @@ def bench_dense(torch, fp8w, lean, timer, W, args, log):
         nbytes = sum(gemv_bytes_block(m, c.shape[0], c.shape[1]) for (_, c, _, _) in calls)
         g = graph_of(torch, lean.gemv_block(calls))
         per, _ = timer.run(g.replay, args.steps, args.warmup)
-        row = {"per_call": summarize(per, len(calls), nbytes), "route": "valu" if m <= 2 else "mfma"}
+        row = {"per_call": summarize(per, len(calls), nbytes), "route": route_names(fp8w, m, calls)}
         del g
         plan = fp8w.fp8w_grouped_plan_init([c[0] for c in calls], [c[1] for c in calls],
                                            [c[2] for c in calls], [c[3] for c in calls])

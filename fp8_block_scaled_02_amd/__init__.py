@@ -46,6 +46,7 @@ MX_GROUP = 32
 _P, _I64, _I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
 SIGNATURES = {
     "fp8w_scale_bytes": (_I64, [_I, _I64, _I64]),
+    "fp8w_gemv_auto_route": (_I, [_I64, _I64, _I64]),
     "fp8w_quantize": (_I, [_P, _I64, _I64, _I, _P, _P, _P, _I64, _P]),
     "fp8w_dequantize": (_I, [_P, _P, _I, _I64, _I64, _P, _P]),
     "fp8w_gemv": (_I, [_P, _I64, _P, _P, _I, _I64, _I64, _P, _I, _P]),

@@ -21,11 +21,17 @@ namespace {
 
 constexpr int64_t kMaxDim = 0x7FFFFFFF;   // kernels index rows and columns with int
 constexpr int kValuMaxM = 8;
-// AUTO route: VALU up to this m, MFMA above, measured on MI355X over the
-// 96-GEMV projection set.  Single calls: VALU is faster at m <= 2.  Grouped:
-// the streaming MFMA kernel is faster from m = 2 on (6.4 against 5.5 TB/s).
-constexpr int kAutoValuMaxM = 2;
-constexpr int kAutoValuMaxMGrouped = 1;
+// AUTO route, from the VALU / MFMA crossovers measured on MI355X.
+//  - Single calls: VALU up to m = 3 on every weight shape measured (block
+//    and MX, N 2560..151936, K 2048..12288; MX loses up to 4 % at m = 3 on
+//    the largest shapes, block gains 3-25 %); at m = 4 VALU still wins on
+//    weights up to 8192 x 4096 and loses on more rows or longer K.
+//  - Grouped: the streaming VALU kernel at m = 1; VALU tiles at m = 2 for
+//    block-scaled formats (+4 % on the projection set, +16 % on dense
+//    layers), while MX at m = 2 is 6 % faster on the streaming MFMA kernel.
+constexpr int kAutoValuMaxM = 3;
+constexpr int kAutoValuM4MaxN = 8192;
+constexpr int kAutoValuM4MaxK = 4096;
 
 bool aligned(const void* p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
 
@@ -96,13 +102,30 @@ fp8w_status check_gemv(const uint16_t* x, int64_t m, const uint8_t* codes, const
 fp8w_status gemv_any(const uint16_t* x, int64_t m, const uint8_t* codes, const void* scales, int format,
                      int64_t n, int64_t k, uint16_t* y, fp8w_route route, void* stream);
 
-int resolve_route(fp8w_route route, int64_t m, bool grouped) {
+bool auto_valu_single(int64_t m, int64_t n, int64_t k) {
+  return m <= kAutoValuMaxM || (m == 4 && n <= kAutoValuM4MaxN && k <= kAutoValuM4MaxK);
+}
+
+bool auto_valu_grouped(int64_t m, bool mx) { return m == 1 || (m == 2 && !mx); }
+
+int resolve_route(fp8w_route route, int64_t m, int64_t n, int64_t k) {
   if (route == FP8W_ROUTE_VALU) return 1;
   if (route == FP8W_ROUTE_MFMA) return 2;
-  return m <= (grouped ? kAutoValuMaxMGrouped : kAutoValuMaxM) ? 1 : 2;
+  return auto_valu_single(m, n, k) ? 1 : 2;
+}
+
+int resolve_route_grouped(fp8w_route route, int64_t m, bool mx) {
+  if (route == FP8W_ROUTE_VALU) return 1;
+  if (route == FP8W_ROUTE_MFMA) return 2;
+  return auto_valu_grouped(m, mx) ? 1 : 2;
 }
 
 }  // namespace
+
+FP8W_API fp8w_route fp8w_gemv_auto_route(int64_t m, int64_t n, int64_t k) {
+  if (m < 1 || m > FP8W_MAX_M || !dims_ok(n, k)) return FP8W_ROUTE_AUTO;
+  return auto_valu_single(m, n, k) ? FP8W_ROUTE_VALU : FP8W_ROUTE_MFMA;
+}
 
 FP8W_API int64_t fp8w_scale_bytes(fp8w_format format, int64_t n, int64_t k) {
   return (!format_ok(format) || n < 1 || k < 1) ? 0 : (int64_t)scale_bytes(format, n, k);
@@ -156,7 +179,7 @@ fp8w_status gemv_any(const uint16_t* x, int64_t m, const uint8_t* codes, const v
   const fp8w_status st = check_gemv(x, m, codes, scales, format, n, k, y, route);
   if (st != FP8W_OK) return st;
   const fp8w::GemvJob job{x, codes, scales, y, (int32_t)n, (int32_t)k, 0, format};
-  return from_hip(fp8w::launch_gemv(job, (int)m, format == FP8W_FORMAT_MX, resolve_route(route, m, false),
+  return from_hip(fp8w::launch_gemv(job, (int)m, format == FP8W_FORMAT_MX, resolve_route(route, m, n, k),
                                     static_cast<hipStream_t>(stream)));
 }
 
@@ -337,7 +360,7 @@ FP8W_API fp8w_status fp8w_grouped_plan_init(const fp8w_gemv_desc* descs, int64_t
   ins.push_back({device_table, table_bytes});
   if (any_overlap(outs.data(), (int)outs.size(), ins.data(), (int)ins.size()))
     return FP8W_ERR_OVERLAP;
-  const int r = resolve_route(route, m, true);
+  const int r = resolve_route_grouped(route, m, mx);
   int64_t max_k = 0;
   for (int64_t i = 0; i < count; ++i) max_k = descs[i].k > max_k ? descs[i].k : max_k;
   // Kernels: VALU at m = 1 with every K in one segment streams (contiguous

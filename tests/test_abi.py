@@ -59,6 +59,22 @@ def test_helpers(F):
         assert F.status_string(st).startswith("FP8W_")
 
 
+def test_auto_route_rule(F):
+    L = F.lib()
+    # single calls: VALU through m = 3 on any weight, at m = 4 only up to
+    # 8192 rows and K = 4096, MFMA from m = 5
+    for n, k in ((1, 16), (2560, 3072), (151936, 2048), (4096, 12288)):
+        for m in (1, 2, 3):
+            assert L.fp8w_gemv_auto_route(m, n, k) == F.ROUTE_VALU
+        for m in (5, 8, 9, 32):
+            assert L.fp8w_gemv_auto_route(m, n, k) == F.ROUTE_MFMA
+    assert L.fp8w_gemv_auto_route(4, 8192, 4096) == F.ROUTE_VALU
+    assert L.fp8w_gemv_auto_route(4, 8193, 4096) == F.ROUTE_MFMA
+    assert L.fp8w_gemv_auto_route(4, 8192, 4112) == F.ROUTE_MFMA
+    for m, n, k in ((0, 1, 16), (33, 1, 16), (1, 0, 16), (1, 16, 0), (1, 1 << 31, 16)):
+        assert L.fp8w_gemv_auto_route(m, n, k) == F.ROUTE_AUTO
+
+
 # Fake, well-aligned "device" addresses: every call below fails validation
 # before any HIP call, so they are never dereferenced.
 A, B, C, D = 0x10000, 0x2000000, 0x4000000, 0x8000000

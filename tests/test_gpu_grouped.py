@@ -43,7 +43,7 @@ def test_grouped_matches_oracle(fp8w, oracle_mod, fmt, m):
     plan = fp8w.fp8w_grouped_plan_init([to_dev_bf16(x) for x in xs_h],
                                        [to_dev(c) for (_, _, c, _) in jobs],
                                        [to_dev(s) for (_, _, _, s) in jobs], fmt=fmt)
-    assert plan.route == (fp8w.ROUTE_VALU if m == 1 else fp8w.ROUTE_MFMA)
+    assert plan.route == (fp8w.ROUTE_VALU if m == 1 or (m == 2 and fmt != "mx") else fp8w.ROUTE_MFMA)
     if plan.route == fp8w.ROUTE_MFMA:   # streaming kernel, x staged by K segments
         assert plan.plan.tiles_per_block > 0 and plan.plan.seg_cols % 256 == 0 and plan.plan.seg_cols > 0
     ys = fp8w.fp8w_gemv_grouped(plan)

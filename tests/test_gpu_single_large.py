@@ -101,8 +101,8 @@ def test_valu_stream_single_job(fp8w, oracle_mod, weights, fmt, k):
 
 
 # VALU wide tiles without streaming: K above the streaming limit (m = 1:
-# 4096-column K segments at K = 4096 and 8176, 3072-column ones at 4112), m = 2
-# (AUTO) and forced VALU up to m = 8
+# 4096-column K segments at K = 4096 and 8176, 3072-column ones at 4112),
+# m = 2 and 3 (AUTO) and forced VALU up to m = 8
 @pytest.mark.parametrize("fmt", ("block", "mx", "row"))
 @pytest.mark.parametrize("m,k", [(1, 4112), (1, 4096), (1, 8176), (2, 2064), (3, 1040), (8, 4112)])
 def test_valu_wide_single_call(fp8w, oracle_mod, weights, fmt, m, k):

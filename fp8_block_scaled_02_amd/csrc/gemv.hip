@@ -589,7 +589,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv_valu_stream(const GemvJob* __
 
   TileRegs<R, C, MX> cur, nxt;
   stream_issue<R, C, MX>(j, t_begin - j.item0, cur);
-  stage_row(j.x, j.k, xs);
+  stage_row(j.x, min(j.k, kSeg), xs);   // the host streams only K <= kSeg
   __syncthreads();
 
   for (int t = t_begin; t < t_end; ++t) {
@@ -651,7 +651,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv_valu_stream(const GemvJob* __
     if (!more) break;
     if (jn_next != jn) {   // restage x for the next job
       __syncthreads();
-      stage_row(jnext.x, jnext.k, xs);
+      stage_row(jnext.x, min(jnext.k, kSeg), xs);
       __syncthreads();
     }
     j = jnext;

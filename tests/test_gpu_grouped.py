@@ -274,3 +274,30 @@ def test_mx_streaming_ragged_rows(fp8w, oracle_mod, odd):
     for (n, k, c, e), x, y in zip(jobs, xs_h, ys):
         y_ref, bound = oracle_mod.gemv_mx_f64(x, c, e)
         assert_within_bound(bf16_to_f64(y), y_ref, bound, f"streaming mx odd={odd} [{n}x{k}]")
+
+
+# Grouped MFMA plans run several 128-row tiles per workgroup when the group
+# has more tiles than eight per resident workgroup slot; every run length is
+# exercised here by rewriting the plan's run length (a valid plan: blocks *
+# tiles_per_block >= tiles), runs that cross job boundaries included. Outputs are poisoned first so a
+# tile that no workgroup sums shows.
+@pytest.mark.parametrize("fmt", ["block", "mx"])
+@pytest.mark.parametrize("m", [4, 17])
+def test_grouped_mfma_run_lengths(fp8w, oracle_mod, fmt, m):
+    jobs = _jobs(oracle_mod, fmt, 2)
+    xs_h = [W.activation(50, m, k) for (_, k, _, _) in jobs]
+    plan = fp8w.fp8w_grouped_plan_init([to_dev_bf16(x) for x in xs_h], [to_dev(c) for (_, _, c, _) in jobs],
+                                       [to_dev(s) for (_, _, _, s) in jobs], fmt=fmt, route=fp8w.ROUTE_MFMA)
+    tiles = plan.plan.tiles
+    assert tiles == sum(-(-n // 128) for n, _, _, _ in jobs)
+    ref = oracle_mod.gemv_block_f64 if fmt == "block" else oracle_mod.gemv_mx_f64
+    refs = [ref(x, c, s) for x, (_, _, c, s) in zip(xs_h, jobs)]
+    for run in (2, 3, 7, tiles):
+        plan.plan.tiles_per_block = run
+        plan.plan.blocks = -(-tiles // run)
+        for y in plan.ys:
+            y.fill_(float("nan"))
+        ys = fp8w.fp8w_gemv_grouped(plan)
+        _sync()
+        for (n, k, _, _), (y_ref, bound), y in zip(jobs, refs, ys):
+            assert_within_bound(bf16_to_f64(y), y_ref, bound, f"mfma runs {fmt} m={m} run={run} [{n}x{k}]")

@@ -189,8 +189,7 @@ def pct(v, q):
 def route_names(fp8w, m, calls):
     """The kernel families AUTO takes for these single calls ("valu", "mfma")."""
     names = {fp8w.ROUTE_VALU: "valu", fp8w.ROUTE_MFMA: "mfma"}
-    L = fp8w.lib()
-    got = sorted({names[L.fp8w_gemv_auto_route(m, c.shape[0], c.shape[1])] for (_, c, _, _) in calls})
+    got = sorted({names[fp8w.fp8w_gemv_auto_route(m, c.shape[0], c.shape[1])] for (_, c, _, _) in calls})
     return "+".join(got)
 
 

@@ -240,6 +240,12 @@ def fp8w_gemv(x, codes, scales, fmt: str = "block", y=None, route=0, stream=None
     return y
 
 
+def fp8w_gemv_auto_route(m: int, n: int, k: int) -> int:
+    """The kernel family AUTO takes for a single GEMV of m activation rows on an
+    [n, k] weight: ROUTE_VALU or ROUTE_MFMA (ROUTE_AUTO when out of range)."""
+    return int(lib().fp8w_gemv_auto_route(int(m), int(n), int(k)))
+
+
 def fp8w_gemm(x, codes, scales, fmt: str = "block", y=None, workspace=None, stream=None):
     torch = _torch()
     _require(x, _bf16_like(torch), "x", 2)

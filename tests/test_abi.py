@@ -73,6 +73,8 @@ def test_auto_route_rule(F):
     assert L.fp8w_gemv_auto_route(4, 8192, 4112) == F.ROUTE_MFMA
     for m, n, k in ((0, 1, 16), (33, 1, 16), (1, 0, 16), (1, 16, 0), (1, 1 << 31, 16)):
         assert L.fp8w_gemv_auto_route(m, n, k) == F.ROUTE_AUTO
+    assert F.fp8w_gemv_auto_route(4, 24576, 4096) == F.ROUTE_MFMA
+    assert F.fp8w_gemv_auto_route(3, 151936, 2048) == F.ROUTE_VALU
 
 
 # Fake, well-aligned "device" addresses: every call below fails validation

@@ -215,3 +215,22 @@ def test_w8a8_direct_wave_split(fp8w, oracle_mod, weights, fmt, n, m):
     xb = (oracle_mod.e4m3_decode(xc).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
     y_ref, bound = oracle_mod.gemv_format_f64(xb, c, s, fmt, rows=rows)
     assert_within_bound(bf16_to_f64(y)[:, rows], xs * y_ref, xs * bound, f"w8a8 direct {fmt} m={m} [{n}x{k}]")
+
+
+# Single calls at M = 1 with 4096 < K <= 16384 on fewer than 16384 rows (one
+# row per wave, K walked in 4096-column segments, ragged last segment, rows
+# past the end of a 4-row workgroup), in every non-MX scale format.
+@pytest.mark.parametrize("fmt", ("block", "block_bf16", "row", "tensor"))
+@pytest.mark.parametrize("n,k", [(1, 4112), (5, 5008), (129, 8176), (300, 12288), (17, 16384), (4099, 9232)])
+def test_long_k_single_call_m1(fp8w, oracle_mod, fmt, n, k):
+    import torch
+    bits = W.gaussian_weight(61, n % 7, n, k, outlier_rows=True)
+    c, s = oracle_mod.quantize_format(bits, fmt)
+    x = W.activation(62, 1, k)
+    sd = to_dev(np.ascontiguousarray(s))
+    if fmt == "block_bf16":
+        sd = sd.view(torch.bfloat16)
+    y = fp8w.fp8w_gemv(to_dev_bf16(x), to_dev(c), sd, fmt)
+    torch.cuda.synchronize()
+    y_ref, bound = oracle_mod.gemv_format_f64(x, c, s, fmt)
+    assert_within_bound(bf16_to_f64(y), y_ref, bound, f"long-K single {fmt} [{n}x{k}]")

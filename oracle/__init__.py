@@ -30,7 +30,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "fp8w_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# FP8W_ORACLE_LIB names another build of the oracle to load instead (the
+# mutation test loads deliberately broken builds through it, to show that
+# the pins catch each planted mistake).
+_LIB = os.environ.get("FP8W_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lock = threading.Lock()
 _lib = None
 
@@ -39,17 +42,24 @@ TILE = 128
 MX_GROUP = 32
 
 
-def build(force: bool = True) -> str:
-    """Compile ``fp8w_oracle.c`` into ``liboracle.so`` with gcc (no fast-math)."""
-    if not force and os.path.exists(_LIB):
-        return _LIB
-    tmp = _LIB + ".tmp%d" % os.getpid()
+def compile_source(src: str, out: str) -> str:
+    """Compile an oracle C source into the shared library ``out`` with gcc
+    (no fast-math, fp contraction off: every fp32 operation is the IEEE one)."""
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-std=gnu11", "-fopenmp", "-ffp-contract=off",
            "-fno-fast-math", "-Wall", "-Wextra", "-Werror", "-fPIC", "-shared",
-           _SRC, "-o", tmp, "-lm"]
+           src, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, _LIB)
-    return _LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    """Compile ``fp8w_oracle.c`` into ``liboracle.so`` (or the library named
+    by FP8W_ORACLE_LIB)."""
+    if not force and os.path.exists(_LIB):
+        return _LIB
+    return compile_source(_SRC, _LIB)
 
 
 def _load():

@@ -126,3 +126,54 @@ def test_generic_dequant_and_gemv(oracle_mod, fmt):
     xf = _f32(x).astype(np.float64)
     assert np.allclose(y, xf @ exact.T, rtol=1e-12, atol=1e-300)
     assert np.allclose(bound, np.abs(xf) @ np.abs(exact).T, rtol=1e-12, atol=1e-300)
+
+
+def test_block_bf16_scale_floor_on_tiny_tiles(oracle_mod):
+    """bf16 block scales of tiles whose amax/448 rounds to zero in bf16.
+
+    "feat(quant): opt-in fp8-block QAT for the lm_head" (How it works) stores
+    the 128-block scale in bf16.  The smallest positive bf16 is 2^-133 (bits
+    0x0001); amax/448 at or below half of it, 2^-134, rounds to zero (the
+    exact half ties to the even pattern 0x0000).  448 * 2^-134 = 1.75 * 2^-126
+    is the normal bf16 0x00E0, so every tile with amax <= 0x00E0 is such a
+    tile.  Reading (design notes, reading 19): the scale is kept positive at
+    2^-133 and the codes divide by it, so dequantizing with the stored scale
+    inverts them.  Tiles just above the edge round to 0x0001 by themselves,
+    so the floor equals what the rounding gives one ulp of amax higher.  The
+    expected values below are fixed by hand: scale bits 0x0001 and codes from
+    torch's e4m3 cast of w / 2^-133 (an exact power-of-two scaling here).
+    """
+    n, k = 256, 384                                      # 2 x 3 tiles
+    rng = np.random.default_rng(76)
+    bits = np.zeros((n, k), np.uint16)
+    # every tile: random bf16 subnormals (|w| < 2^-126) of both signs, zeros
+    sub = rng.integers(0, 0x80, size=(n, k)).astype(np.uint16)
+    sub |= (rng.integers(0, 2, size=(n, k)).astype(np.uint16) << 15)
+    bits[:] = sub
+    tiny_amax = {(0, 0): 0x0080,    # 2^-126: amax/448 = 2^-134.81, rounds to 0
+                 (0, 1): 0x0001,    # 2^-133, the smallest subnormal (tile holds +-2^-133, 0)
+                 (0, 2): 0x00E0,    # 1.75 * 2^-126: amax/448 = 2^-134 exactly, ties to 0
+                 (1, 0): 0x007F}    # largest subnormal
+    above = {(1, 1): 0x00E1,        # one ulp above the edge: rounds up to 0x0001
+             (1, 2): 0x0100}        # 2^-125: amax/448 = 2^-133.81, nearest is 0x0001
+    for (ti, tj), a in {**tiny_amax, **above}.items():
+        tile = bits[128 * ti:128 * ti + 128, 128 * tj:128 * tj + 128]
+        tile &= np.uint16(0x8000) | np.uint16(min(a, 0x7F))   # keep |w| <= amax
+        tile[5, 7] = a                                          # the tile's amax
+        tile[9, 3] = a | 0x8000                                 # and its negative
+    codes, sb = oracle_mod.quantize_block_bf16(bits)
+    assert sb.shape == (2, 3)
+    assert np.all(sb == 0x0001), sb                      # floored and naturally rounded alike
+    w = _f32(bits)
+    expect = _torch_e4m3(w / np.float32(2.0 ** -133))
+    assert np.array_equal(codes, expect)
+    # the tiles' largest codes are the exact multiples a / 2^-133
+    assert oracle_mod.e4m3_decode(codes[5, 7]) == 128.0     # 2^-126 / 2^-133
+    assert oracle_mod.e4m3_decode(codes[5, 128 + 7]) == 1.0  # 2^-133 / 2^-133
+    assert oracle_mod.e4m3_decode(codes[9, 128 + 3]) == -1.0
+    # dequantizing with the stored scale gives back every weight exactly
+    # (|w| / 2^-133 is an integer below 256, which e4m3 holds exactly up to 16
+    # and within its rounding above)
+    deq = oracle_mod.dequant_format_bf16(codes, sb, "block_bf16")
+    small = np.abs(w) <= np.float32(16 * 2.0 ** -133)
+    assert np.array_equal(deq[small] & 0x7FFF, bits[small] & 0x7FFF)

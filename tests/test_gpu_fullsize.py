@@ -1,11 +1,10 @@
 """GPU parity at the workloads' full sizes, in the launch configurations the
 benchmark times (grouped launches and single calls).
 
-Codes and scales are compared bit for bit with the oracle on every weight
-where the oracle finishes in seconds, else on sampled 128-row blocks (tiles
-are independent, so a block quantized alone by the oracle is the reference
-for the same rows of the full weight).  GEMV outputs are compared on sampled
-rows, the oracle computing them from its own codes and scales.
+Codes and scales are compared bit for bit with the oracle on every weight,
+the [151936 x 2048] lm_head included.  GEMV outputs are compared on sampled
+rows (all rows for the MX workload), the oracle computing them from its own
+codes and scales.
 """
 import numpy as np
 import pytest
@@ -85,12 +84,13 @@ def test_projection_set_gemv_grouped_and_single(fp8w, oracle_mod, projection, m)
 # --------------------------------------------------------------- lm_head --
 
 @pytest.fixture(scope="module")
-def lm_head(fp8w):
+def lm_head(fp8w, oracle_mod):
     w = W.WORKLOADS[3].weights[0]
     bits = w.bits(3)
     codes, scales = fp8w.fp8w_quantize_block(to_dev_bf16(bits))
     _sync()
-    return w, bits, codes, scales
+    ref = oracle_mod.quantize_block(bits)        # the whole head: about 1 s on 16 threads
+    return w, bits, codes, scales, ref
 
 
 def _lm_blocks(n):
@@ -99,28 +99,30 @@ def _lm_blocks(n):
     return sorted({0, 1, nb // 2, nb - 2, nb - 1} | set(int(b) for b in rng.choice(nb, 6, replace=False)))
 
 
-def test_lm_head_quantize_sampled_blocks_bit_exact(oracle_mod, lm_head):
-    w, bits, codes, scales = lm_head
+def test_lm_head_quantize_all_blocks_bit_exact(lm_head):
+    """Every code and every scale of the [151936 x 2048] head (1187 x 16
+    tiles) against the oracle's whole-weight pass."""
+    w, bits, codes, scales, (rc, rs) = lm_head
     gc, gs = codes.cpu().numpy(), scales.cpu().numpy()
-    for b in _lm_blocks(w.n):
-        r0, r1 = 128 * b, min(w.n, 128 * b + 128)
-        rc, rs = oracle_mod.quantize_block(bits[r0:r1])
-        assert np.array_equal(gc[r0:r1], rc), b
-        assert np.array_equal(gs[b:b + 1].view(np.uint32), rs.view(np.uint32)), b
+    assert gs.shape == rs.shape == (1187, 16)
+    assert np.array_equal(gs.view(np.uint32), rs.view(np.uint32))
+    bad = np.flatnonzero((gc != rc).any(axis=1))
+    assert bad.size == 0, f"{bad.size} rows differ; first row {bad[:1]}"
 
 
 @pytest.mark.parametrize("m", [1, 4, 16, 32])
 def test_lm_head_gemv_sampled_rows(fp8w, oracle_mod, lm_head, m):
-    w, bits, codes, scales = lm_head
+    w, bits, codes, scales, (rc, rs) = lm_head
     x = W.activation(3, m, w.k)
     y = bf16_to_f64(fp8w.fp8w_gemv_block(to_dev_bf16(x), codes, scales))
     rng = np.random.default_rng(m)
+    rows = []
     for b in _lm_blocks(w.n):
         r0, r1 = 128 * b, min(w.n, 128 * b + 128)
-        rc, rs = oracle_mod.quantize_block(bits[r0:r1])
-        rows = _sample_rows(r1 - r0, rng, 8)
-        y_ref, bound = oracle_mod.gemv_block_f64(x, rc, rs, rows=rows)
-        assert_within_bound(y[:, r0 + rows], y_ref, bound, f"lm_head m={m} block {b}")
+        rows.extend(r0 + _sample_rows(r1 - r0, rng, 8))
+    rows = np.array(sorted(set(int(r) for r in rows)), dtype=np.int64)
+    y_ref, bound = oracle_mod.gemv_block_f64(x, rc, rs, rows=rows)
+    assert_within_bound(y[:, rows], y_ref, bound, f"lm_head m={m}")
 
 
 # ----------------------------------------------------------- dense layer --

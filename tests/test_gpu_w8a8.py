@@ -115,8 +115,15 @@ def test_w8a8_mx_scale_mapping_every_code_and_scale_byte(fp8w, oracle_mod):
 @pytest.mark.parametrize("fmt", ["block", "mx"])
 def test_w8a8_end_to_end_against_bf16_reference(fp8w, oracle_mod, fmt):
     """GPU activation quantization + GPU W8A8 GEMV against the bf16 oracle
-    GEMV: the GEMV bound plus the activation's quantization error, at most
-    2^-4 |x| (normal range) or 2^-10 x_scale (subnormal codes) per element."""
+    GEMV y_ref.  With y_q the oracle's fp64 product of the quantized operands
+    (its own activation codes, bit-equal to the GPU's), the triangle
+    inequality gives |y - y_ref| <= |y - y_q| + |y_q - y_ref|: the first term
+    is the W8A8 GEMV bound 2^-7 * sum |x_q| |deq| + 1e-6 on the quantized
+    operands, the second the activation's own e4m3 error carried through
+    the weight, exact in fp64 and itself at most sum (2^-4 |x| + 2^-10
+    x_scale) |deq| (half an ulp of a normal code relative to |x|, half the
+    subnormal step 2^-9 x_scale).  No other slack than the fp64 rounding of
+    the references themselves."""
     n, k = 2560, 3072
     bits = W.gaussian_weight(64, 0, n, k, outlier_rows=False, heavy_tail=fmt == "mx")
     c, s = oracle_mod.quantize_block(bits) if fmt == "block" else oracle_mod.quantize_mx(bits)
@@ -124,10 +131,19 @@ def test_w8a8_end_to_end_against_bf16_reference(fp8w, oracle_mod, fmt):
     for m in (1, 8, 16, 32):
         x = W.activation(64, m, k)
         xc, xs = fp8w.fp8w_quantize_act(to_dev_bf16(x))
+        xc_ref, xs_ref = oracle_mod.quantize_act_tensor(x)
+        assert np.array_equal(xc.cpu().numpy(), xc_ref) and float(xs.item()) == xs_ref, f"{fmt} m={m}"
         gemv = fp8w.fp8w_gemv_block_w8a8 if fmt == "block" else fp8w.fp8w_gemv_mx_w8a8
         y = bf16_to_f64(gemv(xc, xs, to_dev(c), to_dev(s)))
         y_ref, bound = (oracle_mod.gemv_block_f64 if fmt == "block" else oracle_mod.gemv_mx_f64)(x, c, s)
+        y_q, bound_q = (oracle_mod.gemv_w8a8_block_f64 if fmt == "block"
+                        else oracle_mod.gemv_w8a8_mx_f64)(xc_ref, xs_ref, c, s)
         xf = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-        act_err = (np.ldexp(np.abs(xf), -4) + np.ldexp(float(xs.item()), -10)) @ np.abs(deq).T
+        act_err = (np.ldexp(np.abs(xf), -4) + np.ldexp(xs_ref, -10)) @ np.abs(deq).T
+        act_dev = np.abs(y_q - y_ref)
+        # rounding of the two fp64 reference sums (k terms each): at most
+        # k * 2^-53 of each sum of magnitudes, doubled for safety
+        fp64 = k * 2.0 ** -52 * (bound + bound_q)
+        assert np.all(act_dev <= act_err + fp64), f"{fmt} m={m}: activation error bound"
         err = np.abs(y - y_ref)
-        assert np.all(err <= np.ldexp(bound, -7) * 1.1 + act_err + 1e-6), f"{fmt} m={m}"
+        assert np.all(err <= np.ldexp(bound_q, -7) + 1e-6 + act_dev + fp64), f"{fmt} m={m}"

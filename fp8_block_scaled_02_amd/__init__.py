@@ -65,6 +65,7 @@ SIGNATURES = {
     "fp8w_gemm_mx": (_I, [_P, _I64, _P, _P, _I64, _I64, _P, _P, _I64, _P]),
     "fp8w_quantize_act_workspace_bytes": (_I64, []),
     "fp8w_quantize_act": (_I, [_P, _I64, _I64, _P, _P, _P, _I64, _P]),
+    "fp8w_quantize_act_noalloc": (_I, [_P, _I64, _I64, _P, _P, _P]),
     "fp8w_gemv_block_w8a8": (_I, [_P, _P, _I64, _P, _P, _I64, _I64, _P, _P]),
     "fp8w_gemv_mx_w8a8": (_I, [_P, _P, _I64, _P, _P, _I64, _I64, _P, _P]),
     "fp8w_read_ceiling": (_I, [_P, _I64, _P, _I64, _P]),
@@ -467,6 +468,22 @@ def fp8w_quantize_act(x, codes=None, scale=None, workspace=None, stream=None):
     _check(lib().fp8w_quantize_act(x.data_ptr(), m, k, codes.data_ptr(), scale.data_ptr(),
                                    workspace.data_ptr(), workspace.numel(), _stream_handle(stream)),
            "fp8w_quantize_act")
+    return codes, scale
+
+
+def fp8w_quantize_act_noalloc(x, codes, scale, stream=None):
+    """fp8w_quantize_act with its partial maxima in the library's own device
+    array: no workspace and no allocation.  The outputs are the caller's
+    (codes u8 [m,k], scale fp32 [1])."""
+    torch = _torch()
+    _require(x, _bf16_like(torch), "x", 2)
+    _require(codes, (torch.uint8,), "codes", 2)
+    _require(scale, (torch.float32,), "scale", 1)
+    m, k = x.shape
+    if tuple(codes.shape) != (m, k) or scale.numel() != 1:
+        raise ValueError("fp8w_quantize_act_noalloc: codes must be [m, k] and scale one element")
+    _check(lib().fp8w_quantize_act_noalloc(x.data_ptr(), m, k, codes.data_ptr(), scale.data_ptr(),
+                                           _stream_handle(stream)), "fp8w_quantize_act_noalloc")
     return codes, scale
 
 

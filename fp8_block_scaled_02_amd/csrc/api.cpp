@@ -298,6 +298,19 @@ FP8W_API fp8w_status fp8w_quantize_act(const uint16_t* x, int64_t m, int64_t k, 
                                             static_cast<hipStream_t>(stream)));
 }
 
+FP8W_API fp8w_status fp8w_quantize_act_noalloc(const uint16_t* x, int64_t m, int64_t k, uint8_t* codes,
+                                               float* scale, void* stream) {
+  if (!x || !codes || !scale) return FP8W_ERR_NULL;
+  if (m < 1 || k < 1 || m > kMaxDim || k > kMaxDim) return FP8W_ERR_SHAPE;
+  const int64_t count = m * k;
+  if (!aligned(x, 2) || !aligned(scale, 4)) return FP8W_ERR_ALIGN;
+  const Span out[2] = {{codes, (uint64_t)count}, {scale, 4}};
+  const Span in[1] = {{x, (uint64_t)count * 2}};
+  if (any_overlap(out, 2, in, 1)) return FP8W_ERR_OVERLAP;
+  const hipError_t e = fp8w::launch_quantize_act_noalloc(x, count, codes, scale, static_cast<hipStream_t>(stream));
+  return e == hipErrorInvalidValue ? FP8W_ERR_SHAPE : from_hip(e);
+}
+
 FP8W_API fp8w_status fp8w_gemv_w8a8(const uint8_t* x_codes, const float* x_scale, int64_t m,
                                     const uint8_t* codes, const void* scales, fp8w_format format,
                                     int64_t n, int64_t k, uint16_t* y, void* stream) {

@@ -58,6 +58,10 @@ hipError_t launch_gemv_w8a8(const GemvJob& job, const float* x_scale, int m, boo
 int act_quant_partials();
 hipError_t launch_quantize_act(const uint16_t* x, int64_t count, uint8_t* codes, float* scale,
                                uint32_t* workspace, hipStream_t stream);
+// The same with the partial maxima in a file-scope device array of
+// act_quant_partials() words (one per device, shared by every call on it).
+hipError_t launch_quantize_act_noalloc(const uint16_t* x, int64_t count, uint8_t* codes, float* scale,
+                                       hipStream_t stream);
 
 // route: 1 = VALU (m <= 8), 2 = MFMA (m <= 32).
 int gemv_rows_per_block(int route, int m, bool grouped);

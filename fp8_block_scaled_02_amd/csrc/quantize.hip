@@ -11,6 +11,9 @@
 // any chunking, so the kernel streams rows with no transient.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -353,9 +356,60 @@ __global__ __launch_bounds__(kThreads) void k_act_quant_cast(const uint16_t* __r
   if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = scale;
 }
 
+// Partial maxima of fp8w_quantize_act_noalloc, for callers that cannot
+// allocate: a file-scope array, one copy per device for the life of the
+// process.  Host code never passes the name itself to a kernel (on the host
+// it is a stand-in, not a device address): act_scratch() resolves the
+// device's own address once and every launch takes that pointer.
+static __device__ __align__(256) uint32_t scratch[kActPartials];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+std::atomic<uint32_t*> g_scratch[kMaxDevices];
+
+// This device's address of `scratch`, resolved on the first call with the
+// device current (hipGetSymbolAddress) and kept per device.
+hipError_t act_scratch(uint32_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  uint32_t* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void* addr = nullptr;
+      e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!addr) return hipErrorInvalidSymbol;
+      p = static_cast<uint32_t*>(addr);
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+// Workgroups of the amax pass (= partial maxima written) for `count` elements.
+int act_partials_for(int64_t count) {
+  const int64_t want = (count + kThreads * kActVec - 1) / (kThreads * kActVec);
+  return (int)(want < kActPartials ? want : kActPartials);
+}
+
 }  // namespace
 
 int act_quant_partials() { return kActPartials; }
+
+hipError_t launch_quantize_act_noalloc(const uint16_t* x, int64_t count, uint8_t* codes, float* scale,
+                                       hipStream_t stream) {
+  uint32_t* ws = nullptr;
+  const hipError_t e = act_scratch(&ws);
+  if (e != hipSuccess) return e;
+  // every size fits: the amax pass never uses more partials than the array holds
+  if (count > kActSmall && act_partials_for(count) > kActPartials) return hipErrorInvalidValue;
+  return launch_quantize_act(x, count, codes, scale, ws, stream);
+}
 
 hipError_t launch_quantize_act(const uint16_t* x, int64_t count, uint8_t* codes, float* scale,
                                uint32_t* workspace, hipStream_t stream) {
@@ -365,8 +419,7 @@ hipError_t launch_quantize_act(const uint16_t* x, int64_t count, uint8_t* codes,
     return hipGetLastError();
   }
   // about one 16-byte vector per thread per pass: the passes are latency-bound
-  const int64_t want = (count + kThreads * kActVec - 1) / (kThreads * kActVec);
-  const int partials = (int)(want < kActPartials ? want : kActPartials);
+  const int partials = act_partials_for(count);
   hipLaunchKernelGGL(k_act_amax_partial, dim3(partials), dim3(kThreads), 0, stream, x, count, vec, workspace);
   const int64_t per_block = (int64_t)kThreads * kActVec;
   const int64_t cast_blocks = (count + per_block - 1) / per_block;

@@ -282,6 +282,22 @@ fp8w_status fp8w_quantize_act(const uint16_t* x, int64_t m, int64_t k, uint8_t* 
                               float* scale, void* workspace, int64_t workspace_bytes,
                               void* stream);
 
+/* fp8w_quantize_act without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, result bits and errors as
+ * fp8w_quantize_act, minus the workspace; any m * k (the partial maxima of
+ * every size fit the array).  The partial maxima live in a file-scope device
+ * array of 256 32-bit words (1 KiB) that each device holds until the process
+ * ends; the first call on a device resolves that device's address of it
+ * (hipGetSymbolAddress), so make that first call outside stream capture.
+ * Every call on one device shares the array and leaves its partial maxima
+ * in it: each launch writes every word it later reads, so nothing needs
+ * clearing, but calls that overlap in time on one device (concurrent
+ * streams, or host threads) race on it and must be serialized by the
+ * caller.  Allocates nothing.  Errors: NULL, SHAPE, ALIGN, OVERLAP, HIP. */
+fp8w_status fp8w_quantize_act_noalloc(const uint16_t* x, int64_t m, int64_t k, uint8_t* codes,
+                                      float* scale, void* stream);
+
 /* W8A8 GEMV on a quantized activation:
  *   y[i][j] = bf16_rne( x_scale * sum_k dec(x_codes[i][k]) * deq[j][k] )
  * with fp32 accumulation.  From m = 3 the products are fp8 x fp8 on the

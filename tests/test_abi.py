@@ -169,6 +169,34 @@ def test_gemm_argument_errors(F):
     assert m(A, 64, B, C + 1, 16, 16, D, C, 512, None) == F.ERR_OVERLAP    # workspace over e8m0
 
 
+def test_quantize_act_argument_errors(F):
+    L = F.lib()
+    ws = int(L.fp8w_quantize_act_workspace_bytes())
+    assert ws == 256 * 4
+    q = L.fp8w_quantize_act
+    assert q(None, 1, 64, B, C, None, 0, None) == F.ERR_NULL
+    assert q(A, 0, 64, B, C, None, 0, None) == F.ERR_SHAPE
+    assert q(A, 1, 1 << 31, B, C, None, 0, None) == F.ERR_SHAPE
+    assert q(A, 4, 8192, B, C, None, 0, None) == F.ERR_NULL            # above 16384 elements: workspace
+    assert q(A, 4, 8192, B, C, D, ws - 4, None) == F.ERR_SHAPE         # workspace too small
+    assert q(A + 1, 1, 64, B, C, None, 0, None) == F.ERR_ALIGN
+    assert q(A, 1, 64, B, C + 2, None, 0, None) == F.ERR_ALIGN
+    assert q(A, 1, 64, A + 64, C, None, 0, None) == F.ERR_OVERLAP      # codes over x
+    assert q(A, 4, 8192, B, C, B + 16, ws, None) == F.ERR_OVERLAP      # workspace over codes
+    # the allocation-free variant: the same checks, no workspace argument
+    n = L.fp8w_quantize_act_noalloc
+    assert n(None, 1, 64, B, C, None) == F.ERR_NULL
+    assert n(A, 1, 64, None, C, None) == F.ERR_NULL
+    assert n(A, 1, 64, B, None, None) == F.ERR_NULL
+    assert n(A, 0, 64, B, C, None) == F.ERR_SHAPE
+    assert n(A, 1, 0, B, C, None) == F.ERR_SHAPE
+    assert n(A, 1 << 31, 1, B, C, None) == F.ERR_SHAPE
+    assert n(A + 1, 1, 64, B, C, None) == F.ERR_ALIGN
+    assert n(A, 1, 64, B, C + 1, None) == F.ERR_ALIGN
+    assert n(A, 1, 64, A + 127, C, None) == F.ERR_OVERLAP              # codes over x's last byte
+    assert n(A, 1, 64, B, B + 60, None) == F.ERR_OVERLAP               # scale over codes
+
+
 def test_generic_format_calls_argument_errors(F):
     L = F.lib()
     assert [L.fp8w_scale_bytes(f, 129, 257) for f in range(5)] == [24, 129 * 9, 12, 129 * 4, 4]

@@ -36,7 +36,7 @@ from typing import Optional
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfp8w.so")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_OVERLAP, ERR_HIP = range(7)
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_OVERLAP, ERR_HIP, ERR_CAPTURE = range(8)
 ROUTE_AUTO, ROUTE_VALU, ROUTE_MFMA = 0, 1, 2
 MAX_M = 32
 TILE = 128
@@ -61,6 +61,7 @@ SIGNATURES = {
     "fp8w_dequantize_block": (_I, [_P, _P, _I64, _I64, _P, _P]),
     "fp8w_dequantize_mx": (_I, [_P, _P, _I64, _I64, _P, _P]),
     "fp8w_gemm_workspace_bytes": (_I64, [_I64, _I64]),
+    "fp8w_gemm_prepare": (_I, []),
     "fp8w_gemm_block": (_I, [_P, _I64, _P, _P, _I64, _I64, _P, _P, _I64, _P]),
     "fp8w_gemm_mx": (_I, [_P, _I64, _P, _P, _I64, _I64, _P, _P, _I64, _P]),
     "fp8w_quantize_act_workspace_bytes": (_I64, []),
@@ -428,6 +429,12 @@ def fp8w_gemm_block(x, codes, scales, y=None, workspace=None, stream=None):
 def fp8w_gemm_mx(x, codes, e8m0, y=None, workspace=None, stream=None):
     torch = _torch()
     return _gemm("fp8w_gemm_mx", x, codes, e8m0, mx_scale_shape, torch.uint8, y, workspace, stream)
+
+
+def fp8w_gemm_prepare() -> None:
+    """Create the current device's rocBLAS handle for the GEMM calls (outside
+    stream capture), so that GEMM calls can then be captured in a graph."""
+    _check(lib().fp8w_gemm_prepare(), "fp8w_gemm_prepare")
 
 
 # ------------------------------------------------------------------- W8A8 --

@@ -257,10 +257,14 @@ FP8W_API fp8w_status fp8w_gemm(const uint16_t* x, int64_t m, const uint8_t* code
   const Span out[2] = {{y, (uint64_t)m * n * 2}, {workspace, (uint64_t)n * k * 2}};
   const Span in[3] = {{x, (uint64_t)m * k * 2}, {codes, (uint64_t)n * k}, {scales, scale_bytes(format, n, k)}};
   if (any_overlap(out, 2, in, 3)) return FP8W_ERR_OVERLAP;
-  return from_hip(fp8w::launch_gemm_dequant(x, m, codes, scales, format, n, k, y,
-                                            static_cast<uint16_t*>(workspace),
-                                            static_cast<hipStream_t>(stream)));
+  bool capture_blocked = false;
+  const hipError_t e = fp8w::launch_gemm_dequant(x, m, codes, scales, format, n, k, y,
+                                                 static_cast<uint16_t*>(workspace),
+                                                 static_cast<hipStream_t>(stream), &capture_blocked);
+  return capture_blocked ? FP8W_ERR_CAPTURE : from_hip(e);
 }
+
+FP8W_API fp8w_status fp8w_gemm_prepare(void) { return from_hip(fp8w::gemm_prepare()); }
 
 FP8W_API fp8w_status fp8w_gemm_block(const uint16_t* x, int64_t m, const uint8_t* codes,
                                      const float* scales, int64_t n, int64_t k, uint16_t* y,
@@ -509,6 +513,9 @@ FP8W_API const char* fp8w_status_string(fp8w_status status) {
     case FP8W_ERR_UNSUPPORTED: return "FP8W_ERR_UNSUPPORTED: route cannot serve this m";
     case FP8W_ERR_OVERLAP: return "FP8W_ERR_OVERLAP: an output overlaps another buffer";
     case FP8W_ERR_HIP: return "FP8W_ERR_HIP: the HIP runtime rejected the launch";
+    case FP8W_ERR_CAPTURE:
+      return "FP8W_ERR_CAPTURE: first GEMM call on this device made under stream capture "
+             "(call fp8w_gemm_prepare first)";
   }
   return "FP8W_ERR_UNKNOWN";
 }

@@ -44,10 +44,14 @@ hipError_t launch_dequantize_block(const uint8_t* codes, const float* scales, in
                                    uint16_t* out, hipStream_t stream);
 hipError_t launch_dequantize_mx(const uint8_t* codes, const uint8_t* e8m0, int64_t n, int64_t k,
                                 uint16_t* out, hipStream_t stream);
-// Dequantize into w_bf16 [n, k], then y = x . w^T with rocBLAS.
+// Dequantize into w_bf16 [n, k], then y = x . w^T with rocBLAS.  When the
+// device has no rocBLAS handle yet and `stream` is capturing, nothing is
+// enqueued and *capture_blocked is set.
 hipError_t launch_gemm_dequant(const uint16_t* x, int64_t m, const uint8_t* codes,
                                const void* scales, int format, int64_t n, int64_t k, uint16_t* y,
-                               uint16_t* w_bf16, hipStream_t stream);
+                               uint16_t* w_bf16, hipStream_t stream, bool* capture_blocked);
+// Create the current device's rocBLAS handle now (outside capture).
+hipError_t gemm_prepare();
 
 // W8A8 GEMV: job.x points at e4m3 activation codes [m, k]; x_scale is a
 // device pointer to the activation's fp32 scale.

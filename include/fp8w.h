@@ -42,12 +42,17 @@
  * Memory and ownership: every tensor pointer is a DEVICE pointer on the
  * current HIP device.  The caller allocates and frees every buffer; the
  * library keeps no pointer after a call returns and never allocates (the
- * GEMM calls alone create one rocBLAS handle per device on first use).
+ * GEMM calls alone create one rocBLAS handle per device, in
+ * fp8w_gemm_prepare or on their first use).
  *
  * Execution: every call only enqueues work on `stream` (a hipStream_t;
  * NULL means the default stream) and returns without synchronizing.  Calls
  * never read tensor values on the host, and the kernel chosen depends on the
- * shape only, so the calls may be captured in a HIP graph.  Results are
+ * shape only, so the calls may be captured in a HIP graph, with two
+ * exceptions that need a set-up call outside capture first: the GEMM calls
+ * (fp8w_gemm_prepare, or one GEMM call, on the device) and grouped GEMVs
+ * (fp8w_grouped_plan_init).  fp8w_quantize_act_noalloc resolves its device
+ * array on its first call on a device; make that call outside capture too.  Results are
  * bitwise reproducible run to run (no atomics, fixed reduction order).
  *
  * Errors: arguments are checked on the host before anything is enqueued; on
@@ -75,7 +80,9 @@ typedef enum fp8w_status {
                             /* or a scale pointer not 4-B aligned               */
   FP8W_ERR_UNSUPPORTED = 4, /* the requested route cannot serve this m          */
   FP8W_ERR_OVERLAP = 5,     /* an output byte range overlaps another buffer     */
-  FP8W_ERR_HIP = 6          /* the HIP runtime rejected the launch              */
+  FP8W_ERR_HIP = 6,         /* the HIP runtime rejected the launch              */
+  FP8W_ERR_CAPTURE = 7      /* GEMM: the device's rocBLAS handle would have to  */
+                            /* be created under stream capture                  */
 } fp8w_status;
 
 /* GEMV kernel family.  The two routes follow the fused W8A16 GEMM of "feat:
@@ -247,12 +254,20 @@ fp8w_status fp8w_dequantize_mx(const uint8_t* codes, const uint8_t* e8m0,
  *               16-byte aligned; overwritten (holds deq(W) afterwards)
  * Bound, with y_ref in fp64 from the exact dequantized weight:
  * |y - y_ref| <= 2^-7 * sum_k |x[i][k]| |deq[j][k]| + 1e-6 (the bf16 weight
- * adds at most 2^-8 of that sum).  The first call on a device creates the
- * device's rocBLAS handle (rocBLAS allocates its own workspace then): make
- * that call outside graph capture.  Calls on one device are serialized
- * around its handle.  m, n, k <= 2^31 - 1.
- * Errors: NULL, SHAPE (also: workspace too small), ALIGN, OVERLAP, HIP. */
+ * adds at most 2^-8 of that sum).  The calls use one rocBLAS handle per
+ * device, created by fp8w_gemm_prepare or by the first GEMM call on the
+ * device (rocBLAS allocates its own workspace then); if that first call's
+ * stream is capturing, it fails with FP8W_ERR_CAPTURE and enqueues nothing,
+ * and once the handle exists the calls may be captured.  Calls on one
+ * device are serialized around its handle.  m, n, k <= 2^31 - 1.
+ * Errors: NULL, SHAPE (also: workspace too small), ALIGN, OVERLAP, CAPTURE,
+ * HIP. */
 int64_t fp8w_gemm_workspace_bytes(int64_t n, int64_t k);
+
+/* Create the current device's rocBLAS handle for the GEMM calls now, so that
+ * later GEMM calls can be captured in a HIP graph.  Not for use under
+ * capture; idempotent.  Errors: HIP (no device, or rocBLAS failed). */
+fp8w_status fp8w_gemm_prepare(void);
 fp8w_status fp8w_gemm_block(const uint16_t* x, int64_t m, const uint8_t* codes,
                             const float* scales, int64_t n, int64_t k, uint16_t* y,
                             void* workspace, int64_t workspace_bytes, void* stream);

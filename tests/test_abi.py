@@ -55,7 +55,7 @@ def test_helpers(F):
     assert L.fp8w_grouped_table_bytes(96) == 96 * 48
     assert L.fp8w_grouped_table_bytes(0) == 0
     assert L.fp8w_version() >= 100
-    for st in range(7):
+    for st in range(8):
         assert F.status_string(st).startswith("FP8W_")
 
 

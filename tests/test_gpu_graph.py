@@ -3,8 +3,13 @@ quantization and W8A8 GEMVs, W8A16 single calls on the streaming kernels
 (one job passed by value), MX single and grouped calls and dequantization.
 The graph is replayed several times, with eager work and synchronizations
 between replays, and every replay must reproduce the eager results bit for
-bit; the eager results themselves are checked against the oracle.  (The
-large-M route, which calls rocBLAS, is not captured here.)"""
+bit; the eager results themselves are checked against the oracle.  The
+large-M route (dequantize + rocBLAS) is captured on its own once its
+rocBLAS handle exists, and refuses to create one under capture."""
+import os
+import subprocess
+import sys
+
 import numpy as np
 import pytest
 
@@ -151,3 +156,66 @@ def test_calls_on_concurrent_streams(fp8w, oracle_mod):
             assert torch.equal(outs[i].view(torch.int16), alone[i][0].view(torch.int16)), f"stream {i} rep {rep}"
             if res[i] is not None:
                 assert torch.equal(res[i].view(torch.int16), alone[i][1].view(torch.int16)), f"w8a8 {i} rep {rep}"
+
+
+_FIRST_GEMM_UNDER_CAPTURE = r"""
+import torch, fp8_block_scaled_02_amd as F
+L = F.lib()
+m, n, k = 64, 256, 512
+x = torch.zeros((m, k), dtype=torch.bfloat16, device="cuda")
+c = torch.zeros((n, k), dtype=torch.uint8, device="cuda")
+s = torch.ones((2, 4), dtype=torch.float32, device="cuda")
+y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+ws = torch.empty(n * k * 2, dtype=torch.uint8, device="cuda")
+torch.cuda.synchronize()
+side = torch.cuda.Stream()
+g = torch.cuda.CUDAGraph()
+with torch.cuda.graph(g, stream=side):
+    y.fill_(1.0)
+    st = L.fp8w_gemm_block(x.data_ptr(), m, c.data_ptr(), s.data_ptr(), n, k, y.data_ptr(),
+                           ws.data_ptr(), ws.numel(), side.cuda_stream)
+torch.cuda.synchronize()
+print("status", st, flush=True)
+"""
+
+
+def test_first_gemm_call_under_capture_is_refused():
+    """In a fresh process (no rocBLAS handle yet), a GEMM call on a capturing
+    stream returns FP8W_ERR_CAPTURE and enqueues nothing, instead of letting
+    rocBLAS allocate inside the capture."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    print("fresh process: first fp8w_gemm_block under capture", flush=True)
+    r = subprocess.run([sys.executable, "-c", _FIRST_GEMM_UNDER_CAPTURE], cwd=root, capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
+    assert "status 7" in r.stdout, r.stdout[-2000:]
+
+
+def test_gemm_route_replays_in_a_graph(fp8w, oracle_mod):
+    import torch
+    fp8w.fp8w_gemm_prepare()
+    m, n, k = 96, 1280, 1024
+    bits = W.gaussian_weight(96, 0, n, k, outlier_rows=True)
+    c, s = oracle_mod.quantize_block(bits)
+    x = W.activation(96, m, k)
+    cd, sd, xd = to_dev(c), to_dev(s), to_dev_bf16(x)
+    y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(int(fp8w.lib().fp8w_gemm_workspace_bytes(n, k)), dtype=torch.uint8, device="cuda")
+    fp8w.fp8w_gemm_block(xd, cd, sd, y=y, workspace=ws)
+    _sync()
+    eager = y.clone()
+    rows = np.array([0, 1, 127, 128, 700, n - 1])
+    y_ref, bound = oracle_mod.gemv_block_f64(x, c, s, rows=rows)
+    assert_within_bound(bf16_to_f64(eager)[:, rows], y_ref, bound, "gemm eager")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        fp8w.fp8w_gemm_block(xd, cd, sd, y=y, workspace=ws, stream=side)
+    for rep in range(4):
+        y.fill_(rep + 3)
+        ws.fill_(rep + 1)                     # eager work between replays
+        _sync()
+        g.replay()
+        _sync()
+        assert torch.equal(y.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"

@@ -57,7 +57,7 @@ def counted_traffic():
         return None
     return COUNTED_TRAFFIC["bytes_per_launch"]
 TILE, GROUP = 128, 32
-ALL_ROWS = ("proj", "quant", "lm_head", "dense", "mx", "single", "dequant", "gemm", "w8a8", "row")
+ALL_ROWS = ("proj", "quant", "lm_head", "dense", "mx", "single", "dequant", "gemm", "w8a8", "row", "route")
 
 
 def parse():
@@ -71,18 +71,22 @@ def parse():
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--rows", default=",".join(ALL_ROWS))
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--ms", default="1,8,16", help="M values of the projection-set rows")
-    p.add_argument("--cpu-sweep", action="store_true",
-                   help="also time the oracle's quantizers and GEMV (M = 1, 8, 16) on one "
-                        "[8192x2560] weight, on 1 thread and on all host threads")
+    p.add_argument("--ms", default=None,
+                   help="M values of the GEMV rows (default: projection set 1,8,16; the other "
+                        "workloads their own)")
     p.add_argument("--route", default="auto", choices=("auto", "valu", "mfma"),
                    help="route of the projection-set rows (auto: the library's choice per M)")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="also run one device copy of this many MiB (counter calibration)")
     a = p.parse_args()
-    if a.route == "valu" and any(int(v) > 8 for v in a.ms.split(",") if v):
+    if a.route == "valu" and any(int(v) > 8 for v in (a.ms or "1,8,16").split(",") if v):
         p.error("--route valu serves m <= 8 only")
     return a
+
+
+def row_ms(args, default):
+    """M values of a GEMV row: --ms when given, else the workload's own."""
+    return tuple(int(v) for v in args.ms.split(",") if v) if args.ms else tuple(default)
 
 
 # ------------------------------------------------------------ byte counts --
@@ -301,7 +305,7 @@ def bench_proj(torch, fp8w, lean, timer, W, args, state, log):
     """The projection pass at M = 1, 8, 16: one grouped launch per pass, and
     96 single-GEMV launches per pass (both captured in a HIP graph)."""
     wl, bf, codes, scales = state
-    ms = tuple(int(v) for v in args.ms.split(","))
+    ms = row_ms(args, (1, 8, 16))
     xs = activations(torch, W, 2, ms, (2560, 3072))
     rows, head = {}, None
     route = {"auto": fp8w.ROUTE_AUTO, "valu": fp8w.ROUTE_VALU, "mfma": fp8w.ROUTE_MFMA}[args.route]
@@ -361,7 +365,7 @@ def bench_lm_head(torch, fp8w, lean, timer, W, args, log):
     del bf
     copies = [(c0, s0)] + [(c0.clone(), s0.clone()) for _ in range(3)]
     lib = fp8w.lib()
-    for m in wl.ms:
+    for m in row_ms(args, wl.ms):
         x = upload_bf16(torch, W.activation(3, m, k))
         calls = [(x, c, s, torch.empty((m, n), dtype=torch.bfloat16, device="cuda")) for c, s in copies]
         g = graph_of(torch, lean.gemv_block(calls))
@@ -396,7 +400,7 @@ def bench_dense(torch, fp8w, lean, timer, W, args, log):
         del bf
     copies = [layer] + [[(c.clone(), s.clone()) for c, s in layer] for _ in range(5)]
     out = {}
-    for m in wl.ms:
+    for m in row_ms(args, wl.ms):
         xs = {k: upload_bf16(torch, W.activation(4, m, k)) for k in (4096, 12288)}
         calls = [(xs[c.shape[1]], c, s, torch.empty((m, c.shape[0]), dtype=torch.bfloat16, device="cuda"))
                  for cp in copies for c, s in cp]
@@ -426,7 +430,7 @@ def bench_mx(torch, fp8w, lean, timer, W, args, log):
         out[f"quantize_mx_{key}"] = summarize(qper, 1, quant_bytes_mx(w.n, w.k))
         del bf
         copies = [(c0, e0)] + [(c0.clone(), e0.clone()) for _ in range(copies_n - 1)]
-        for m in wl.ms:
+        for m in row_ms(args, wl.ms):
             x = upload_bf16(torch, W.activation(5, m, w.k))
             calls = [(x, c, e, torch.empty((m, w.n), dtype=torch.bfloat16, device="cuda")) for c, e in copies]
             nb = len(calls) * gemv_bytes_mx(m, w.n, w.k)
@@ -643,6 +647,34 @@ def bench_single(torch, fp8w, lean, timer, W, args, log):
     return {"single_1024x1024": out}
 
 
+def bench_route(torch, fp8w, lean, timer, W, args, log):
+    """The single-call VALU / MFMA crossover behind the AUTO rule: a
+    graph-captured pass of single calls over ~1 GB of rotating copies of a
+    projection weight [8192x2560] and of a dense o-projection [4096x4096],
+    at M = 3, 4, 5 on each route forced, next to the route AUTO takes."""
+    out = {}
+    names = {fp8w.ROUTE_VALU: "valu", fp8w.ROUTE_MFMA: "mfma"}
+    for wl_id, widx in ((2, 12), (4, 1)):
+        w = W.WORKLOADS[wl_id].weights[widx]
+        c0, s0 = fp8w.fp8w_quantize_block(upload_bf16(torch, w.bits(wl_id)))
+        copies = [(c0, s0)] + [(c0.clone(), s0.clone()) for _ in range(max(1, (1 << 30) // (w.n * w.k)) - 1)]
+        key = f"{w.n}x{w.k}"
+        for m in row_ms(args, (3, 4, 5)):
+            x = upload_bf16(torch, W.activation(wl_id, m, w.k))
+            calls = [(x, c, s, torch.empty((m, w.n), dtype=torch.bfloat16, device="cuda")) for c, s in copies]
+            nb = len(calls) * gemv_bytes_block(m, w.n, w.k)
+            row = {"auto": names[fp8w.fp8w_gemv_auto_route(m, w.n, w.k)], "calls_per_pass": len(calls)}
+            for rname, r in (("valu", fp8w.ROUTE_VALU), ("mfma", fp8w.ROUTE_MFMA)):
+                g = graph_of(torch, lean.gemv_block(calls, r))
+                per, _ = timer.run(g.replay, max(10, args.steps // 4), min(args.warmup, 20))
+                row[rname] = summarize(per, len(calls), nb)
+                del g
+            out[f"{key}_m{m}"] = row
+        del copies
+    log(f"route crossover: {out}")
+    return {"route_crossover_single_calls": out}
+
+
 # ------------------------------------------------------ HBM read ceiling --
 
 def read_ceiling(torch, fp8w, timer, log, gib=2, reps=100, warmup=150):
@@ -671,12 +703,28 @@ def read_ceiling(torch, fp8w, timer, log, gib=2, reps=100, warmup=150):
 
 # ------------------------------------------------------------ CPU baseline --
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            return next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+    except OSError:
+        return ""
+
+
 def cpu_baseline(W, log, min_seconds=10.0, max_passes=40):
-    """The CPU oracle (unchanged) on the projection set: its own block
-    quantization of the 96 weights once, then fp64 GEMV passes at M = 1 over
-    all 96 weights, repeated until about `min_seconds` of GEMV time."""
+    """The CPU oracle (unchanged, plain C driven through ctypes) on the host
+    cores of this run, as GB/s of the same algorithmic bytes as the GPU rows:
+
+    * value: fp64 GEMV passes at M = 1 over the whole projection set on all
+      host threads (its own block quantization of the 96 weights first),
+      repeated until about `min_seconds`;
+    * per_op: on one [8192x2560] projection weight, block quantization and
+      the fp64 GEMV at M = 1, 8, 16, and MX quantization of the MXFP8
+      workload's [8192x2560] weight, each on 1 thread and on all threads."""
+    import platform
     import oracle
     wl = W.WORKLOADS[2]
+    threads = oracle.max_threads()
     x = {k: W.activation(2, 1, k) for k in (2560, 3072)}
     t_q = 0.0
     quantized = []
@@ -693,57 +741,49 @@ def cpu_baseline(W, log, min_seconds=10.0, max_passes=40):
             oracle.gemv_block_f64(x[k], c, s)
         t_g += time.perf_counter() - t
         passes += 1
+    del quantized
     qbytes = sum(quant_bytes_block(w.n, w.k) for w in wl.weights)
-    res = {"value": round(passes * pass_bytes / t_g / 1e9, 3), "unit": "GB/s", "cores": oracle.max_threads(),
-           "kind": "oracle",
-           "sample": f"{passes} fp64 GEMV passes at M=1 over the 48-layer projection set "
-                     f"({len(wl.weights)} weights, {pass_bytes} algorithmic bytes per pass) on the "
-                     f"oracle's own codes",
-           "seconds": round(t_g, 3),
-           "quantize_block_GBps": round(qbytes / t_q / 1e9, 3), "quantize_seconds": round(t_q, 3)}
-    log(f"cpu baseline: {res}")
-    return res
-
-
-def cpu_sweep(W, log):
-    """The oracle on one [8192x2560] projection weight: block and MX
-    quantization and the fp64 GEMV at M = 1, 8, 16, each on one thread and on
-    all host threads, as GB/s of algorithmic bytes."""
-    import platform
-    import oracle
-    w = W.WORKLOADS[2].weights[12]
-    n, k = w.n, w.k
-    bits = w.bits(2)
-    all_threads = oracle.max_threads()
-    model = ""
-    try:
-        with open("/proc/cpuinfo") as fh:
-            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
-    except OSError:
-        pass
-    out = {"weight": [n, k], "host_threads": all_threads, "cpu": model or platform.processor(), "ops": {}}
 
     def timed(fn, nbytes):
         t = time.perf_counter()
         r = fn()
         dt = time.perf_counter() - t
-        return r, {"seconds": round(dt, 3), "GBps": round(nbytes / dt / 1e9, 3)}
+        return r, round(nbytes / dt / 1e9, 4)
 
+    w = wl.weights[12]
+    n, k = w.n, w.k
+    bits = w.bits(2)
+    wmx = W.WORKLOADS[5].weights[0]
+    bits_mx = wmx.bits(5)
+    per_op = {}
     try:
-        for threads in (1, all_threads):
-            oracle.set_threads(threads)
-            (c, s), a = timed(lambda: oracle.quantize_block(bits), quant_bytes_block(n, k))
-            _, b = timed(lambda: oracle.quantize_mx(bits), quant_bytes_mx(n, k))
-            out["ops"][f"quantize_block_t{threads}"] = a
-            out["ops"][f"quantize_mx_t{threads}"] = b
+        for th in (1, threads):
+            oracle.set_threads(th)
+            (c, s), per_op.setdefault("quantize_block", {})[f"t{th}"] = timed(
+                lambda: oracle.quantize_block(bits), quant_bytes_block(n, k))
+            _, per_op.setdefault("quantize_mx", {})[f"t{th}"] = timed(
+                lambda: oracle.quantize_mx(bits_mx), quant_bytes_mx(wmx.n, wmx.k))
             for m in (1, 8, 16):
-                x = W.activation(2, m, k)
-                _, g = timed(lambda: oracle.gemv_block_f64(x, c, s), gemv_bytes_block(m, n, k))
-                out["ops"][f"gemv_block_m{m}_t{threads}"] = g
+                xm = W.activation(2, m, k)
+                _, per_op.setdefault(f"gemv_block_m{m}", {})[f"t{th}"] = timed(
+                    lambda: oracle.gemv_block_f64(xm, c, s), gemv_bytes_block(m, n, k))
     finally:
-        oracle.set_threads(all_threads)
-    log(f"cpu sweep: {out}")
-    return out
+        oracle.set_threads(threads)
+    res = {"value": round(passes * pass_bytes / t_g / 1e9, 3), "unit": "GB/s", "cores": threads,
+           "kind": "oracle",
+           "sample": f"{passes} fp64 GEMV passes at M=1 over the 48-layer projection set "
+                     f"({len(wl.weights)} weights, {pass_bytes} algorithmic bytes per pass) on the "
+                     f"oracle's own codes, {threads} threads",
+           "seconds": round(t_g, 3),
+           "nproc": os.cpu_count(), "cpu_model": cpu_model() or platform.processor(),
+           "quantize_block_projection_set_GBps": round(qbytes / t_q / 1e9, 3),
+           "quantize_block_projection_set_seconds": round(t_q, 3),
+           "per_op_GBps": per_op,
+           "per_op_weights": {"quantize_block, gemv": f"projection [{n}x{k}]",
+                              "quantize_mx": f"MXFP8 workload [{wmx.n}x{wmx.k}]",
+                              "t1 / tN": f"1 thread / {threads} threads"}}
+    log(f"cpu baseline: {res}")
+    return res
 
 
 # -------------------------------------------------------------------- main --
@@ -794,14 +834,13 @@ def main():
         del state
         torch.cuda.empty_cache()
     for name, fn in (("lm_head", bench_lm_head), ("dense", bench_dense), ("mx", bench_mx),
-                     ("single", bench_single), ("dequant", bench_dequant), ("gemm", bench_gemm)):
+                     ("single", bench_single), ("dequant", bench_dequant), ("gemm", bench_gemm),
+                     ("route", bench_route)):
         if name in rows_wanted:
             rows.update(fn(torch, fp8w, lean, timer, W, args, log))
             torch.cuda.empty_cache()
     ceiling = None if headline is None else read_ceiling(torch, fp8w, timer, log)
     cpu = None if args.no_cpu or headline is None else cpu_baseline(W, log)
-    if args.cpu_sweep:
-        rows["oracle_cpu_sweep"] = cpu_sweep(W, log)
 
     if headline is None:
         print(json.dumps({"rows": rows}))
@@ -824,9 +863,11 @@ def main():
                               "note": "96 single-GEMV launches per pass, graph-captured"},
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": round(3.78 / ms_per_step, 2),
-        "vs_baseline_basis": "block-FP8 Triton GEMV, 3.78 ms per 48-layer pass at M=1 on an "
-                             "RTX 6000 Ada (other hardware: context only)",
+        "vs_baseline": round(value / ceiling["GBps"], 4),
+        "vs_baseline_basis": "the pass's GB/s over fp8w_read_ceiling's in this session (a pure 2 GiB "
+                             "HBM read with the GEMV's 16-byte non-temporal loads)",
+        "pages_context": {"block-FP8 Triton, 48-layer pass at M=1, RTX 6000 Ada (other hardware)": "3.78 ms",
+                          "this pass": f"{ms_per_step:.4f} ms"},
         "dtype": "bf16",
         "weights": "fp8_e4m3fn, fp32 128x128 block scales",
         "data": "synthetic",

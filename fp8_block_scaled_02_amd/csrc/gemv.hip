@@ -860,8 +860,72 @@ __device__ __forceinline__ void store_tile(const GemvJob& j, int row0, int m_row
 // (a multiple of 256, sized on the host so that two workgroups fit on a CU):
 // restaged when the run enters a new job, and at every segment of a tile
 // when K spans more than one segment.
+// Where a wave's panel loads point inside one 16-row tile: base is the
+// tile's first row (uniform), off[q] the lane's byte offset of row 4q + l/16
+// plus its 16-byte column (rows past the weight's last row are clamped to
+// it: their sums are never stored).  Computed once per tile, so a panel
+// load costs one 64-bit add instead of a row multiply and bounds checks.
+struct TileLoads {
+  const uint8_t* base;
+  uint64_t off[4];
+};
+
+__device__ __forceinline__ void tile_loads(const GemvJob& j, int row0, TileLoads& t) {
+  const int lane = threadIdx.x & (kWave - 1);
+  t.base = j.codes + (size_t)row0 * j.k;
+  const int last = j.n - 1 - row0;   // >= 0 for a live tile
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    t.off[q] = (uint64_t)min(4 * q + (lane >> 4), last) * (uint64_t)j.k + 16 * (lane & 15);
+}
+
+// Panel p of the tile: as panel_issue, with the row offsets of `t`.  Every
+// load is in bounds: a partial last panel clamps its columns to the row's
+// last 16 bytes, whose codes then meet the zeros that pad x past k in LDS.
+template <bool MX, bool PK>
+__device__ __forceinline__ void panel_issue_tile(const GemvJob& j, const TileLoads& t, int row0, int p, bool live,
+                                                 int nkb, int groups, Panel<MX>& r) {
+  const int lane = threadIdx.x & (kWave - 1);
+  if (live) {
+    const uint8_t* pb = t.base + (size_t)p * kPanelCols;
+    if ((p + 1) * kPanelCols <= j.k) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) r.v[q] = ld_stream_u4(pb, t.off[q]);
+    } else {
+      const int over = max(0, p * kPanelCols + 16 * (lane & 15) + 16 - j.k);   // bytes past the row's end
+#pragma unroll
+      for (int q = 0; q < 4; ++q) r.v[q] = ld_stream_u4(pb, t.off[q] - (uint64_t)over);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r.v[q] = make_uint4(0, 0, 0, 0);
+  }
+  if (MX) {
+    const int row = min(row0 + (lane & 15), j.n - 1);
+    const uint8_t* __restrict__ e8 = static_cast<const uint8_t*>(j.scales);
+    if (PK) {
+      const int pc = min(p, (j.k - 1) / kPanelCols);
+      r.e8 = ld_global<u32x2>(e8, (size_t)row * groups + 8 * pc);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int kx = min(p * kPanelCols + 64 * c + 16 * (lane >> 4), j.k - 1);
+        r.s[c] = ld_global<uint8_t>(e8, (size_t)row * groups + kx / kGroup);
+      }
+    }
+  } else {
+    r.s[0] = r.s[1] = 0.0f;
+    if (live && row0 < j.n) {
+      r.s[0] = block_scale(j, row0, 2 * p, nkb);
+      if (2 * p + 1 < nkb) r.s[1] = block_scale(j, row0, 2 * p + 1, nkb);
+    }
+  }
+}
+
+// Four waves per SIMD (at most 128 VGPRs): two 8-wave workgroups per CU, so
+// one workgroup's staging barriers are covered by the other's loads.
 template <int MT, int NW, int D, bool MX, bool ONE, bool PK>
-__global__ __launch_bounds__(NW * kWave) void k_gemv_mfma_stream(const GemvJob* __restrict__ table,
+__global__ __launch_bounds__(NW * kWave, 4) void k_gemv_mfma_stream(const GemvJob* __restrict__ table,
                                                                  int njobs, GemvJob one, int total_tiles,
                                                                  int tiles_per_block, int m_rows,
                                                                  int seg_cols) {
@@ -875,9 +939,29 @@ __global__ __launch_bounds__(NW * kWave) void k_gemv_mfma_stream(const GemvJob* 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int i = lane & 15, g = lane >> 4;
   unsigned char* pbuf = smem + wave * kPanelBytes;
+  // x rows of seg_cols bf16, the 16-byte units of row r XOR-swizzled by
+  // r % 16 inside each group of 16 units: the 16 rows a B read spans then
+  // hit 16 different bank groups, with no padding (so more columns fit)
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem + NW * kPanelBytes);
-  const int ldx = seg_cols + 8;   // +16 B per row spreads the B reads over the banks
   const int seg_panels = seg_cols / kPanelCols;
+  // B operands: lane (i, g) reads x row 16t + i (rows past m_rows read row
+  // m_rows - 1: their products land in output columns that are not stored),
+  // units 32 * panel + 16b + 8c + 2g + h, swizzled: the panel's units keep
+  // their group of 32, 16b is an offset, and (8c + 2g + h) ^ i for c, h in
+  // {0, 1} is one of four per-lane unit offsets
+  int brow[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) brow[t] = min(16 * t + i, m_rows - 1) * seg_cols;
+  int bunit[2][2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) bunit[c][h] = 8 * ((8 * c + 2 * g + h) ^ (min(i, m_rows - 1) & 15));
+  // staging: this thread's first unit of the [m_rows][seg_cols / 8] grid of
+  // 8-element units, and the stride in rows and units between its units
+  const int units_row = seg_cols / 8;
+  const int st_r0 = threadIdx.x / units_row, st_c0 = threadIdx.x % units_row;
+  const int st_dr = (NW * kWave) / units_row, st_dc = (NW * kWave) % units_row;
 
   int jn = job_of_tile<ONE>(jobs, t_begin);
   // compute cursor: tile ct, panel cp of job cj
@@ -889,35 +973,50 @@ __global__ __launch_bounds__(NW * kWave) void k_gemv_mfma_stream(const GemvJob* 
   // issue cursor: tile it, panel ip of job ij, D panels ahead
   GemvJob ij = cj;
   int ijn = jn, i_bound = c_bound, i_np = c_np, it = t_begin, ip = 0;
+  TileLoads tl;
+  tile_loads(ij, (it - ij.item0) * kRows + 16 * wave, tl);
 
   auto issue = [&](Panel<MX>& r) {
     const bool live = it < t_end;
-    panel_issue<MX, PK>(ij, (it - ij.item0) * kRows + 16 * wave, ip, live, (ij.k + kTile - 1) / kTile,
-                    (ij.k + kGroup - 1) / kGroup, r);
+    panel_issue_tile<MX, PK>(ij, tl, (it - ij.item0) * kRows + 16 * wave, ip, live, (ij.k + kTile - 1) / kTile,
+                             (ij.k + kGroup - 1) / kGroup, r);
     if (!live) return;
     if (++ip == i_np) {
       ip = 0;
-      if (++it < t_end && it >= i_bound) {
-        load_job<ONE>(jobs, ++ijn, ij);
-        i_bound = job_end<ONE>(jobs, ijn);
-        i_np = (ij.k + kPanelCols - 1) / kPanelCols;
+      if (++it < t_end) {
+        if (it >= i_bound) {
+          load_job<ONE>(jobs, ++ijn, ij);
+          i_bound = job_end<ONE>(jobs, ijn);
+          i_np = (ij.k + kPanelCols - 1) / kPanelCols;
+        }
+        tile_loads(ij, (it - ij.item0) * kRows + 16 * wave, tl);
       }
     }
   };
-  // x[:, seg0 : seg0 + seg_cols) of job j into LDS (columns < k only: the B
-  // reads never look past k)
+  // x[:, seg0 : seg0 + seg_cols) of job j into LDS, zeros past k (the codes
+  // of a clamped last panel meet zeros there)
   auto stage = [&](const GemvJob& j, int seg0) {
-    const int units = min(seg_cols, j.k - seg0) / 8;
-    copy_batched<kStageBatch, NW * kWave, uint4>(
-        m_rows * units,
-        [&](int u) {
-          const int r = u / units, c = (u - r * units) * 8;
-          return ld_global_u4(j.x, ((size_t)r * j.k + seg0 + c) * 2);
-        },
-        [&](int u, uint4 v) {
-          const int r = u / units, c = (u - r * units) * 8;
-          *reinterpret_cast<uint4*>(xs + r * ldx + c) = v;
-        });
+    const int valid = min(seg_cols, j.k - seg0) / 8;
+    int r = st_r0, c = st_c0;
+    while (r < m_rows) {
+      uint4 v[kStageBatch];
+      int dst[kStageBatch];
+#pragma unroll
+      for (int q = 0; q < kStageBatch; ++q) {
+        dst[q] = r < m_rows ? r * seg_cols + 8 * (c ^ (r & 15)) : -1;
+        v[q] = make_uint4(0, 0, 0, 0);
+        if (r < m_rows && c < valid) v[q] = ld_global_u4(j.x, ((size_t)r * j.k + seg0 + 8 * c) * 2);
+        c += st_dc;
+        r += st_dr;
+        if (c >= units_row) {
+          c -= units_row;
+          ++r;
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < kStageBatch; ++q)
+        if (dst[q] >= 0) *reinterpret_cast<uint4*>(xs + dst[q]) = v[q];
+    }
   };
 
   Panel<MX> slot[D];
@@ -940,15 +1039,10 @@ __global__ __launch_bounds__(NW * kWave) void k_gemv_mfma_stream(const GemvJob* 
       panel_scales<MX, PK>(slot[s], sc);
       issue(slot[s]);
       const int kseg = (cp % seg_panels) * kPanelCols;   // panel start within the staged segment
-      const int kp = cp * kPanelCols;
       panel_mfma<MT, MX>(a, sc, [&](int t, int b, int c, uint4& B0, uint4& B1) {
-        const int m = 16 * t + i;
-        const int kx = 128 * b + 64 * c + 16 * g;
-        B0 = B1 = make_uint4(0, 0, 0, 0);
-        if (m < m_rows && kp + kx < cj.k) {
-          B0 = *reinterpret_cast<const uint4*>(xs + m * ldx + kseg + kx);
-          B1 = *reinterpret_cast<const uint4*>(xs + m * ldx + kseg + kx + 8);
-        }
+        const uint16_t* bp = xs + brow[t] + kseg + 128 * b;
+        B0 = *reinterpret_cast<const uint4*>(bp + bunit[c][0]);
+        B1 = *reinterpret_cast<const uint4*>(bp + bunit[c][1]);
       }, acc);
       if (++cp == c_np) {   // tile done
         store_tile<MT>(cj, (ct - cj.item0) * kRows + 16 * wave, m_rows, acc);
@@ -1466,8 +1560,10 @@ int gemv_wide_seg_cols(int64_t k) {
 int gemv_stream_rows() { return kWaves * kStreamR; }
 
 int gemv_mfma_stream_seg_cols(int m, int64_t max_k) {
-  const int x_budget = kMfmaStreamLds - kMfmaStreamWaves * kPanelBytes;
-  const int cap = (x_budget / (2 * m) - 8) / kPanelCols * kPanelCols;
+  // 1 KB under the per-workgroup share: at exactly half of the CU's LDS the
+  // measured rates fall as if only one workgroup fitted per CU
+  const int x_budget = kMfmaStreamLds - kMfmaStreamWaves * kPanelBytes - 1024;
+  const int cap = x_budget / (2 * m) / kPanelCols * kPanelCols;
   const int64_t kmax = (max_k + kPanelCols - 1) / kPanelCols * kPanelCols;
   if (kmax <= cap) return (int)kmax;
   const int64_t nseg = (kmax + cap - 1) / cap;
@@ -1476,7 +1572,7 @@ int gemv_mfma_stream_seg_cols(int m, int64_t max_k) {
 }
 
 int gemv_mfma_stream_lds(int m, int seg_cols) {
-  return kMfmaStreamWaves * kPanelBytes + m * (seg_cols + 8) * 2;
+  return kMfmaStreamWaves * kPanelBytes + m * seg_cols * 2;
 }
 
 int gemv_mfma_stream_lds_limit() { return kMfmaStreamLds; }

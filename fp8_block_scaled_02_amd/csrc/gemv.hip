@@ -261,18 +261,24 @@ struct ValuShape {
 // cannot count, and it then waits for every load before the staged x can
 // be written to LDS; unconditional loads let it wait for exactly the ones
 // it needs.)
+// rows[r]: the codes of row min(row0 + r, n - 1), computed once per tile.
 template <int R, int C>
-__device__ __forceinline__ void valu_load(const GemvJob& j, int row0, int seg0, int nch, uint4 (&wv)[R][C]) {
+__device__ __forceinline__ void valu_load(const uint8_t* const (&rows)[R], int seg0, int nch, uint4 (&wv)[R][C]) {
   const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int row = min(row0 + r, j.n - 1);
+  for (int c = 0; c < C; ++c) {
+    const int off = seg0 + 16 * min(lane + kWave * c, nch - 1);
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-      const int ch = min(lane + kWave * c, nch - 1);
-      wv[r][c] = ld_stream_u4(j.codes, (size_t)row * j.k + seg0 + ch * 16);
-    }
+    for (int r = 0; r < R; ++r) wv[r][c] = ld_stream_u4(rows[r], off);
   }
+}
+
+// u / d for a d that is the compile-time D on every full segment (only the
+// last segment of a row has another length): the constant divides with a
+// multiply, and the runtime divide runs once per launch at most.
+template <int D>
+__device__ __forceinline__ int div_seg(int u, int d) {
+  return d == D ? u / D : u / d;
 }
 
 // What one K segment stages in LDS besides the codes: x (bf16, or e4m3
@@ -291,12 +297,24 @@ struct SegStage {
   uint32_t e[MX ? S::kExpPre : 1];      // MX: exponent bytes
   uint16_t lo, hi;                      // block grids: the scale's 16-bit halves
 
+  // unit u of the segment's [M][len / 8] grid of 8-element x units
+  static __device__ __forceinline__ void unit_rc(int u, int units, int& r, int& c) {
+    if constexpr (M == 1) {
+      r = 0;
+      c = u * 8;
+    } else {
+      r = div_seg<S::kSeg / 8>(u, units);
+      c = (u - r * units) * 8;
+    }
+  }
+
   __device__ __forceinline__ void load(const GemvJob& j, int tile, int seg0, int len, int tiles_k, int groups) {
     const int units = len / 8, total = M * units;
 #pragma unroll
     for (int q = 0; q < S::kXPre; ++q) {
       const int u = min((int)threadIdx.x + q * kThreads, total - 1);
-      const int r = u / units, c = (u - r * units) * 8;
+      int r, c;
+      unit_rc(u, units, r, c);
       if constexpr (X8) x[q] = ld_x8(j, (size_t)r * j.k + seg0 + c);
       else x[q] = ld_x16(j, ((size_t)r * j.k + seg0 + c) * 2);
     }
@@ -305,7 +323,7 @@ struct SegStage {
 #pragma unroll
       for (int q = 0; q < S::kExpPre; ++q) {
         const int u = min((int)threadIdx.x + q * kThreads, S::kRows * ng - 1);
-        const int r = u / ng, g = u - r * ng;
+        const int r = div_seg<S::kSegGroups>(u, ng), g = u - r * ng;
         const int row = min(tile * S::kRows + r, j.n - 1);
         e[q] = ld_global<uint8_t>(j.scales, (size_t)row * groups + gs + g);
       }
@@ -328,11 +346,13 @@ struct SegStage {
 #pragma unroll
     for (int q = 0; q < S::kXPre; ++q) {
       const int u = (int)threadIdx.x + q * kThreads;
-      const int r = u / units, c = (u - r * units) * 8;
+      int r, c;
+      unit_rc(u, units, r, c);
       if (u < total) *reinterpret_cast<uint4*>(xs + r * S::kSeg + c) = widen(x[q]);
     }
     for (int u = (int)threadIdx.x + S::kXPre * kThreads; u < total; u += kThreads) {   // M beyond the registers
-      const int r = u / units, c = (u - r * units) * 8;
+      int r, c;
+      unit_rc(u, units, r, c);
       if constexpr (X8) *reinterpret_cast<uint4*>(xs + r * S::kSeg + c) = widen(ld_x8(j, (size_t)r * j.k + seg0 + c));
       else *reinterpret_cast<uint4*>(xs + r * S::kSeg + c) = ld_x16(j, ((size_t)r * j.k + seg0 + c) * 2);
     }
@@ -341,7 +361,7 @@ struct SegStage {
 #pragma unroll
       for (int q = 0; q < S::kExpPre; ++q) {
         const int u = (int)threadIdx.x + q * kThreads;
-        const int r = u / ng, g = u - r * ng;
+        const int r = div_seg<S::kSegGroups>(u, ng), g = u - r * ng;
         if (u < S::kRows * ng) ex[r * S::kSegGroups + g] = (unsigned char)e[q];
       }
     } else {
@@ -392,6 +412,9 @@ __global__ __launch_bounds__(kThreads) void k_gemv_valu(GemvJob arg, const GemvJ
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+  const uint8_t* rows[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) rows[r] = j.codes + (size_t)min(row0 + r, j.n - 1) * j.k;
 
   for (int seg0 = 0; seg0 < j.k; seg0 += S::kSeg) {
     const int len = min(S::kSeg, j.k - seg0);
@@ -399,7 +422,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv_valu(GemvJob arg, const GemvJ
     SegStage<M, R, C, MX, X8> st;
     st.load(j, tile, seg0, len, tiles_k, groups);
     uint4 cw[R][C];
-    valu_load<R, C>(j, row0, seg0, nch, cw);
+    valu_load<R, C>(rows, seg0, nch, cw);
     if (seg0 > 0) __syncthreads();   // the previous segment's LDS reads are done
     st.commit(j, tile, seg0, len, groups, xs, ss, ex);
     __syncthreads();
@@ -880,9 +903,11 @@ __device__ __forceinline__ void tile_loads(const GemvJob& j, int row0, TileLoads
 }
 
 // Panel p of the tile: as panel_issue, with the row offsets of `t`.  Every
-// load is in bounds: a partial last panel clamps its columns to the row's
-// last 16 bytes, whose codes then meet the zeros that pad x past k in LDS.
-template <bool MX, bool PK>
+// load is in bounds.  A partial last panel either clamps its columns to the
+// row's last 16 bytes, whose codes then meet the zeros that pad x past k in
+// LDS (ZT = false: the streaming kernel), or loads zeros past k (ZT = true:
+// kernels whose x operands are not zero there).
+template <bool MX, bool PK, bool ZT = false>
 __device__ __forceinline__ void panel_issue_tile(const GemvJob& j, const TileLoads& t, int row0, int p, bool live,
                                                  int nkb, int groups, Panel<MX>& r) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -891,6 +916,13 @@ __device__ __forceinline__ void panel_issue_tile(const GemvJob& j, const TileLoa
     if ((p + 1) * kPanelCols <= j.k) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) r.v[q] = ld_stream_u4(pb, t.off[q]);
+    } else if (ZT) {
+      const bool in = p * kPanelCols + 16 * (lane & 15) < j.k;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        r.v[q] = make_uint4(0, 0, 0, 0);
+        if (in) r.v[q] = ld_stream_u4(pb, t.off[q]);
+      }
     } else {
       const int over = max(0, p * kPanelCols + 16 * (lane & 15) + 16 - j.k);   // bytes past the row's end
 #pragma unroll
@@ -1100,25 +1132,47 @@ __global__ __launch_bounds__(NW * kWave) void k_gemv_mfma_direct(GemvJob j, int 
   const int groups = (j.k + kGroup - 1) / kGroup;
   const int nq = (np - wave + NW - 1) / NW;   // this wave's panels
 
+  // the tile's row offsets, and each lane's x rows (rows past m_rows read
+  // row m_rows - 1: their products land in output columns not stored)
+  TileLoads tl;
+  tile_loads(j, row0, tl);
+  const uint8_t* xrow[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+    xrow[t] = reinterpret_cast<const uint8_t*>(j.x) + ((size_t)min(16 * t + i, m_rows - 1) * j.k + 16 * g) * 2;
+
   auto issue = [&](int q, DirectSlot<MT, MX>& r) {
     const int p = wave + NW * q;
     const bool live = q < nq;
-    panel_issue<MX, PK>(j, row0, p, live, nkb, groups, r.p);
+    panel_issue_tile<MX, PK, true>(j, tl, row0, p, live, nkb, groups, r.p);
+    if (live && (p + 1) * kPanelCols <= j.k) {   // a whole panel: every x load in bounds
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int kx = p * kPanelCols + 128 * b + 64 * c + 16 * g;
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-          const int m = 16 * t + i;
-          r.xb[t][b][c][0] = r.xb[t][b][c][1] = make_uint4(0, 0, 0, 0);
-          if (live && m < m_rows && kx < j.k) {
-            r.xb[t][b][c][0] = ld_global_u4(j.x, ((size_t)m * j.k + kx) * 2);
-            r.xb[t][b][c][1] = ld_global_u4(j.x, ((size_t)m * j.k + kx + 8) * 2);
+          for (int t = 0; t < MT; ++t) {
+            const size_t off = (size_t)(p * kPanelCols + 128 * b + 64 * c) * 2;
+            r.xb[t][b][c][0] = ld_global_u4(xrow[t], off);
+            r.xb[t][b][c][1] = ld_global_u4(xrow[t], off + 16);
+          }
+    } else {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int kx = p * kPanelCols + 128 * b + 64 * c + 16 * g;
+#pragma unroll
+          for (int t = 0; t < MT; ++t) {
+            const int m = 16 * t + i;
+            r.xb[t][b][c][0] = r.xb[t][b][c][1] = make_uint4(0, 0, 0, 0);
+            if (live && m < m_rows && kx < j.k) {
+              r.xb[t][b][c][0] = ld_global_u4(j.x, ((size_t)m * j.k + kx) * 2);
+              r.xb[t][b][c][1] = ld_global_u4(j.x, ((size_t)m * j.k + kx + 8) * 2);
+            }
           }
         }
-      }
+    }
   };
 
   f32x4 acc[MT];

@@ -151,29 +151,43 @@ __global__ __launch_bounds__(kThreads) void k_quant_block_any(const uint16_t* __
 __device__ __forceinline__ float pow2_neg(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
 
 // MX vector path: k % 32 == 0, w 16-B aligned, codes 8-B aligned.  With k a
-// multiple of 32 the groups tile the flat [n*k] array, so thread t takes
-// elements 8t .. 8t+7 and the four lanes 4g .. 4g+3 form group g.
+// multiple of 32 the groups tile the flat [n*k] array of 8-element units;
+// a workgroup takes kMxUnits * 256 consecutive units, thread t units t,
+// t + 256, ... (every load instruction reads 4 KB contiguous), and the four
+// lanes 4g .. 4g+3 of a pass form one group.  All of a thread's loads are
+// issued before any encode, so each wave keeps kMxUnits * 1 KB in flight.
+constexpr int kMxUnits = 4;
+
 __global__ __launch_bounds__(kThreads) void k_quant_mx_vec(const uint16_t* __restrict__ w,
                                                            uint8_t* __restrict__ codes,
                                                            uint8_t* __restrict__ e8m0,
                                                            size_t threads_total) {
-  const size_t t = (size_t)blockIdx.x * kThreads + threadIdx.x;
-  const bool ok = t < threads_total;
-  uint4 v = make_uint4(0, 0, 0, 0);
-  if (ok) v = ld_stream_u4(w, 16 * t);
-  uint32_t amax = abs_max_pair(v.x, 0);
-  amax = abs_max_pair(v.y, amax);
-  amax = abs_max_pair(v.z, amax);
-  amax = abs_max_pair(v.w, amax);
-  amax = group_max_u32<4>(amax);
-  const int e = e8m0_exponent(amax << 16);
-  if (!ok) return;
-  if ((t & 3) == 0) e8m0[t >> 2] = (uint8_t)(e + 127);
-  const float mul = pow2_neg(e);
-  uint2 out;
-  out.x = encode4_mul(v.x, v.y, mul);
-  out.y = encode4_mul(v.z, v.w, mul);
-  st_stream_u2(codes, 8 * t, out);
+  const size_t t0 = (size_t)blockIdx.x * (kThreads * kMxUnits) + threadIdx.x;
+  uint4 v[kMxUnits];
+#pragma unroll
+  for (int u = 0; u < kMxUnits; ++u) {
+    const size_t t = t0 + (size_t)u * kThreads;
+    v[u] = make_uint4(0, 0, 0, 0);
+    if (t < threads_total) v[u] = ld_stream_u4(w, 16 * t);
+  }
+#pragma unroll
+  for (int u = 0; u < kMxUnits; ++u) {
+    const size_t t = t0 + (size_t)u * kThreads;
+    uint32_t amax = abs_max_pair(v[u].x, 0);
+    amax = abs_max_pair(v[u].y, amax);
+    amax = abs_max_pair(v[u].z, amax);
+    amax = abs_max_pair(v[u].w, amax);
+    amax = group_max_u32<4>(amax);
+    const int e = e8m0_exponent(amax << 16);
+    if (t < threads_total) {
+      if ((t & 3) == 0) e8m0[t >> 2] = (uint8_t)(e + 127);
+      const float mul = pow2_neg(e);
+      uint2 out;
+      out.x = encode4_mul(v[u].x, v[u].y, mul);
+      out.y = encode4_mul(v[u].z, v[u].w, mul);
+      st_stream_u2(codes, 8 * t, out);
+    }
+  }
 }
 
 // MX, any shape: one thread per (row, group), 2-byte loads.
@@ -466,7 +480,7 @@ hipError_t launch_quantize_mx(const uint16_t* w, int64_t n, int64_t k, uint8_t* 
   const int64_t groups = (k + kGroup - 1) / kGroup;
   if (k % kGroup == 0 && aligned(w, 16) && aligned(codes, 8)) {
     const size_t threads_total = (size_t)n * k / 8;
-    const dim3 grid((unsigned)((threads_total + kThreads - 1) / kThreads));
+    const dim3 grid((unsigned)((threads_total + kThreads * kMxUnits - 1) / (kThreads * kMxUnits)));
     hipLaunchKernelGGL(k_quant_mx_vec, grid, dim3(kThreads), 0, stream, w, codes, e8m0,
                        threads_total);
   } else {

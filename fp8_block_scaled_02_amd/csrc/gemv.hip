@@ -470,6 +470,80 @@ __global__ __launch_bounds__(kThreads) void k_gemv_valu(GemvJob arg, const GemvJ
   }
 }
 
+// ------------------------------------------------- VALU, rows per wave --
+//
+// Single calls at M = 1 on weights with fewer rows than the streaming
+// threshold and K <= 4096: one wave per workgroup, R rows per wave, and
+// each lane's x chunks (32 bytes per 16-code chunk) loaded straight into
+// registers, shared by the wave's R rows.  No LDS and no barrier: on
+// MI355X, staging x through LDS with a workgroup barrier cost about 0.8 us
+// of a 4.6 us call over a bare read of the same codes (graph-captured
+// projection-set calls), and loading x per wave costs about half of that
+// once R >= 2 rows share it.  x is requested before the codes.
+template <int R, int C, bool MX>
+__global__ __launch_bounds__(kWave) void k_gemv_valu_rows(GemvJob j) {
+  static_assert(kTile % R == 0, "a wave's rows stay inside one 128-row block");
+  const int lane = threadIdx.x & (kWave - 1);
+  const int row0 = blockIdx.x * R;
+  const int nch = j.k / 16;
+  const int nkb = (j.k + kTile - 1) / kTile, groups = (j.k + kGroup - 1) / kGroup;
+  int ch[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) ch[c] = min(lane + kWave * c, nch - 1);
+  uint4 x0[C], x1[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    x0[c] = ld_global_u4(j.x, (size_t)ch[c] * 32);
+    x1[c] = ld_global_u4(j.x, (size_t)ch[c] * 32 + 16);
+  }
+  const uint8_t* rows[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) rows[r] = j.codes + (size_t)min(row0 + r, j.n - 1) * j.k;
+  uint4 w[R][C];
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+#pragma unroll
+    for (int r = 0; r < R; ++r) w[r][c] = ld_stream_u4(rows[r], 16 * ch[c]);
+  float sc[MX ? 1 : C];
+  uint32_t e[MX ? R : 1][MX ? C : 1];
+  if (MX) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+        e[r][c] = ld_global<uint8_t>(j.scales, (size_t)min(row0 + r, j.n - 1) * groups + ch[c] / 2);
+  } else {
+#pragma unroll
+    for (int c = 0; c < C; ++c) sc[c] = block_scale(j, min(row0, j.n - 1), ch[c] >> 3, nkb);
+  }
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    if (lane + kWave * c < nch) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const uint4 d = w[r][c];
+        const bf16x2 wv[8] = {cvt_lo(d.x), cvt_hi(d.x), cvt_lo(d.y), cvt_hi(d.y),
+                              cvt_lo(d.z), cvt_hi(d.z), cvt_lo(d.w), cvt_hi(d.w)};
+        const float s = MX ? mx_scale((uint8_t)e[MX ? r : 0][MX ? c : 0]) : sc[MX ? 0 : c];
+        acc[r] = __builtin_fmaf(s, dot16(wv, x0[c], x1[c]), acc[r]);
+      }
+    }
+  }
+  const WaveSums<R> sums(acc);
+  if ((lane & 15) == 0) {
+#pragma unroll
+    for (int q = 0; q < WaveSums<R>::kGroups; ++q) {
+      const int r = 4 * q + (lane >> 4);
+      if (r < R && row0 + r < j.n)
+        st_global<uint16_t>(j.y, (size_t)(row0 + r) * 2,
+                            (uint16_t)f32_to_bf16_rne(sums.g[q] * output_scale(j, row0 + r)));
+    }
+  }
+}
+
 // ------------------------------------------------------- VALU streaming --
 //
 // Grouped launches at M = 1 whose GEMVs all have K <= 1024*C: each
@@ -1592,6 +1666,32 @@ hipError_t dispatch_mfma_stream(const StreamJobs& l, int64_t blocks, int64_t til
 // (1.1-2.5x, the gain growing with m), and from N = 16384 when m > 16.
 constexpr int64_t kSingleWideMinRowsValu = 16384;
 
+// M = 1 single calls below that many rows, K <= 1024 * kRowsMaxC: the
+// one-wave kernel with kRowsR rows per wave.
+constexpr int kRowsR = 2, kRowsMaxC = 4;
+
+template <int C, bool MX>
+hipError_t run_valu_rows(const GemvJob& job, hipStream_t stream) {
+  hipLaunchKernelGGL((k_gemv_valu_rows<kRowsR, C, MX>), dim3((unsigned)((job.n + kRowsR - 1) / kRowsR)),
+                     dim3(kWave), 0, stream, job);
+  return hipGetLastError();
+}
+
+template <bool MX>
+hipError_t dispatch_valu_rows(const GemvJob& job, hipStream_t stream) {
+  switch ((job.k + 1023) / 1024) {
+    case 1: return run_valu_rows<1, MX>(job, stream);
+    case 2: return run_valu_rows<2, MX>(job, stream);
+    case 3: return run_valu_rows<3, MX>(job, stream);
+    case 4: return run_valu_rows<4, MX>(job, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_valu_rows(const GemvJob& job, bool mx, hipStream_t stream) {
+  return mx ? dispatch_valu_rows<true>(job, stream) : dispatch_valu_rows<false>(job, stream);
+}
+
 bool single_call_streams_mfma(int64_t n, int m) { return n >= 32768 || (n >= 16384 && m > 16); }
 
 }  // namespace
@@ -1666,6 +1766,7 @@ hipError_t launch_gemv(const GemvJob& job, int m, bool mx, int route, hipStream_
       return mx ? run_valu_stream<true, true>(l, tiles, tiles, 1, stream)
                 : run_valu_stream<false, true>(l, tiles, tiles, 1, stream);
     }
+    if (!wide && m == 1 && job.k <= 1024 * kRowsMaxC) return launch_valu_rows(job, mx, stream);
     const int rows = wide ? gemv_rows_per_block(route, m, true) : gemv_rows_per_block(route, m, false);
     const int64_t blocks = (job.n + rows - 1) / rows;
     const bool seg4096 = wide && m == 1 && gemv_wide_seg_cols(job.k) == 4096;

@@ -76,6 +76,9 @@ def parse():
                         "workloads their own)")
     p.add_argument("--route", default="auto", choices=("auto", "valu", "mfma"),
                    help="route of the projection-set rows (auto: the library's choice per M)")
+    p.add_argument("--route-shapes", default=None,
+                   help="weights of the route row, as NxK,NxK (default: every workload shape)")
+    p.add_argument("--route-formats", default="block,mx", help="scale formats of the route row")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="also run one device copy of this many MiB (counter calibration)")
     a = p.parse_args()
@@ -647,30 +650,58 @@ def bench_single(torch, fp8w, lean, timer, W, args, log):
     return {"single_1024x1024": out}
 
 
+# Every weight shape of the workloads: the projection set, the dense layer
+# and the lm_head.
+ROUTE_SHAPES = ((6656, 2560), (8192, 2560), (2560, 3072), (4096, 4096), (6144, 4096), (24576, 4096),
+                (4096, 12288), (151936, 2048))
+
+
 def bench_route(torch, fp8w, lean, timer, W, args, log):
-    """The single-call VALU / MFMA crossover behind the AUTO rule: a
-    graph-captured pass of single calls over ~1 GB of rotating copies of a
-    projection weight [8192x2560] and of a dense o-projection [4096x4096],
-    at M = 3, 4, 5 on each route forced, next to the route AUTO takes."""
-    out = {}
+    """The single-call VALU / MFMA crossover behind the AUTO rule: for every
+    weight shape of the workloads, block and MX scales, a graph-captured pass
+    of single calls over ~0.5 GB of weight copies at M = 2..8 on each route
+    forced, next to the route AUTO takes.  Codes and scales are random
+    (finite codes; the time does not depend on the values)."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
     names = {fp8w.ROUTE_VALU: "valu", fp8w.ROUTE_MFMA: "mfma"}
-    for wl_id, widx in ((2, 12), (4, 1)):
-        w = W.WORKLOADS[wl_id].weights[widx]
-        c0, s0 = fp8w.fp8w_quantize_block(upload_bf16(torch, w.bits(wl_id)))
-        copies = [(c0, s0)] + [(c0.clone(), s0.clone()) for _ in range(max(1, (1 << 30) // (w.n * w.k)) - 1)]
-        key = f"{w.n}x{w.k}"
-        for m in row_ms(args, (3, 4, 5)):
-            x = upload_bf16(torch, W.activation(wl_id, m, w.k))
-            calls = [(x, c, s, torch.empty((m, w.n), dtype=torch.bfloat16, device="cuda")) for c, s in copies]
-            nb = len(calls) * gemv_bytes_block(m, w.n, w.k)
-            row = {"auto": names[fp8w.fp8w_gemv_auto_route(m, w.n, w.k)], "calls_per_pass": len(calls)}
-            for rname, r in (("valu", fp8w.ROUTE_VALU), ("mfma", fp8w.ROUTE_MFMA)):
-                g = graph_of(torch, lean.gemv_block(calls, r))
-                per, _ = timer.run(g.replay, max(10, args.steps // 4), min(args.warmup, 20))
-                row[rname] = summarize(per, len(calls), nb)
-                del g
-            out[f"{key}_m{m}"] = row
-        del copies
+    out = {}
+    shapes = ROUTE_SHAPES
+    if args.route_shapes:
+        shapes = tuple(tuple(int(v) for v in sh.split("x")) for sh in args.route_shapes.split(",") if sh)
+    for fmt in (f for f in args.route_formats.split(",") if f):
+        if fmt not in ("block", "mx"):
+            raise SystemExit(f"--route-formats: unknown format {fmt}")
+        for n, k in shapes:
+            copies = []
+            for _ in range(max(2, (1 << 29) // (n * k))):
+                c = torch.randint(0, 0x7E, (n, k), dtype=torch.uint8, device="cuda", generator=gen)
+                if fmt == "block":
+                    s = torch.rand(((n + TILE - 1) // TILE, (k + TILE - 1) // TILE), device="cuda",
+                                   generator=gen) * 1e-3 + 1e-4
+                else:
+                    s = torch.randint(110, 125, (n, (k + GROUP - 1) // GROUP), dtype=torch.uint8, device="cuda",
+                                      generator=gen)
+                copies.append((c, s))
+            for m in row_ms(args, (2, 3, 4, 5, 6, 7, 8)):
+                x = (torch.randn((m, k), device="cuda", generator=gen)).to(torch.bfloat16)
+                calls = [(x, c, s, torch.empty((m, n), dtype=torch.bfloat16, device="cuda")) for c, s in copies]
+                nb = len(calls) * (gemv_bytes_block(m, n, k) if fmt == "block" else gemv_bytes_mx(m, n, k))
+                row = {"auto": names[fp8w.fp8w_gemv_auto_route(m, n, k)], "calls_per_pass": len(calls)}
+                for rname, r in (("valu", fp8w.ROUTE_VALU), ("mfma", fp8w.ROUTE_MFMA)):
+                    if r == fp8w.ROUTE_VALU and m > 8:
+                        continue
+                    fn = lean.gemv_block(calls, r) if fmt == "block" else lean.gemv_mx(calls, r)
+                    g = graph_of(torch, fn)
+                    per, _ = timer.run(g.replay, max(10, args.steps // 4), min(args.warmup, 20))
+                    row[rname] = summarize(per, len(calls), nb)
+                    del g
+                if "valu" in row:
+                    t = {rn: row[rn]["us_per_call_p50"] for rn in ("valu", "mfma")}
+                    row["auto_vs_best_pct"] = round(100 * (t[row["auto"]] / min(t.values()) - 1), 1)
+                out[f"{fmt}_{n}x{k}_m{m}"] = row
+            del copies
+            torch.cuda.empty_cache()
     log(f"route crossover: {out}")
     return {"route_crossover_single_calls": out}
 

@@ -22,16 +22,30 @@ namespace {
 constexpr int64_t kMaxDim = 0x7FFFFFFF;   // kernels index rows and columns with int
 constexpr int kValuMaxM = 8;
 // AUTO route, from the VALU / MFMA crossovers measured on MI355X.
-//  - Single calls: VALU up to m = 3 on every weight shape measured (block
-//    and MX, N 2560..151936, K 2048..12288; MX loses up to 4 % at m = 3 on
-//    the largest shapes, block gains 3-25 %); at m = 4 VALU still wins on
-//    weights up to 8192 x 4096 and loses on more rows or longer K.
+//  - Single calls.  The MFMA kernel's time hardly moves with m: one 16-row
+//    MFMA tile serves every m <= 16 (rocprofv3 kernel traces and counters
+//    at m = 3, 4, 5: 8.0-8.2 us per call on [8192x2560] and 7.9-8.0 us on
+//    [4096x4096], VALU issue 9-11 %, MFMA busy under 2 %).  The VALU
+//    kernel's instructions grow with m (VALU issue 18 / 22 / 25 % on
+//    [4096x4096] and 29 / 34 / 37 % on [8192x2560] at m = 3 / 4 / 5, both
+//    kernels within 1.5 % of the same HBM bytes), so every shape has one
+//    crossover, later on shorter weights.  Graph-captured passes over every
+//    workload shape (N 2560..151936, K 2048..12288, block and MX scales,
+//    m = 2..8) put it after m = 2 on weights of 32768 rows or more (where
+//    the MFMA route streams: the [151936x2048] lm_head at m = 3 is 2 %
+//    (block) and 4-14 % (MX) faster on MFMA), after m = 3 on the rest,
+//    after m = 4 on weights up to 8192 x 4096, and after m = 5 on K = 4096
+//    weights up to 6144 rows (+2 to +13 % at m = 5; at m = 6 they lose up
+//    to 4 %).
 //  - Grouped: the streaming VALU kernel at m = 1; VALU tiles at m = 2 for
 //    block-scaled formats (+4 % on the projection set, +16 % on dense
 //    layers), while MX at m = 2 is 6 % faster on the streaming MFMA kernel.
 constexpr int kAutoValuMaxM = 3;
+constexpr int64_t kAutoValuM3MaxN = 32768 - 1;
 constexpr int kAutoValuM4MaxN = 8192;
 constexpr int kAutoValuM4MaxK = 4096;
+constexpr int kAutoValuM5MaxN = 6144;
+constexpr int kAutoValuM5MinK = 3072 + 16;   // K in (3072, 4096]
 
 bool aligned(const void* p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
 
@@ -103,7 +117,9 @@ fp8w_status gemv_any(const uint16_t* x, int64_t m, const uint8_t* codes, const v
                      int64_t n, int64_t k, uint16_t* y, fp8w_route route, void* stream);
 
 bool auto_valu_single(int64_t m, int64_t n, int64_t k) {
-  return m <= kAutoValuMaxM || (m == 4 && n <= kAutoValuM4MaxN && k <= kAutoValuM4MaxK);
+  return m < kAutoValuMaxM || (m == kAutoValuMaxM && n <= kAutoValuM3MaxN) ||
+         (m == 4 && n <= kAutoValuM4MaxN && k <= kAutoValuM4MaxK) ||
+         (m == 5 && n <= kAutoValuM5MaxN && k >= kAutoValuM5MinK && k <= kAutoValuM4MaxK);
 }
 
 bool auto_valu_grouped(int64_t m, bool mx) { return m == 1 || (m == 2 && !mx); }

@@ -73,6 +73,9 @@ SIGNATURES = {
     "fp8w_grouped_table_bytes": (_I64, [_I64]),
     "fp8w_grouped_plan_init": (_I, [_P, _I64, _I64, _I, _I, _P, _P]),
     "fp8w_gemv_grouped": (_I, [_P, _P]),
+    "fp8w_quant_table_bytes": (_I64, [_I64]),
+    "fp8w_quant_plan_init": (_I, [_P, _I64, _I, _P, _P]),
+    "fp8w_quantize_grouped": (_I, [_P, _P]),
     "fp8w_block_scale_count": (_I64, [_I64, _I64]),
     "fp8w_mx_scale_count": (_I64, [_I64, _I64]),
     "fp8w_status_string": (ctypes.c_char_p, [_I]),
@@ -96,6 +99,16 @@ class GroupedPlanC(ctypes.Structure):
                 ("format", ctypes.c_int32), ("route", ctypes.c_int32), ("blocks", _I64),
                 ("tiles", _I64), ("tiles_per_block", ctypes.c_int32), ("seg_cols", ctypes.c_int32),
                 ("mx_packed8", ctypes.c_int32)]
+
+
+class QuantDesc(ctypes.Structure):
+    """fp8w_quant_desc of include/fp8w.h."""
+    _fields_ = [("w", _P), ("codes", _P), ("scales", _P), ("n", _I64), ("k", _I64)]
+
+
+class QuantPlanC(ctypes.Structure):
+    """fp8w_quant_plan of include/fp8w.h."""
+    _fields_ = [("table", _P), ("count", ctypes.c_int32), ("format", ctypes.c_int32), ("blocks", _I64)]
 
 
 _lib = None
@@ -586,6 +599,61 @@ def fp8w_gemv_grouped(plan: GroupedPlan, stream=None):
     _check(lib().fp8w_gemv_grouped(ctypes.byref(plan.plan), _stream_handle(stream)),
            "fp8w_gemv_grouped")
     return plan.ys
+
+
+# ------------------------------------------------------- grouped quantize --
+
+class QuantPlan:
+    """Many weights quantized by one kernel launch (load time).
+
+    Holds the device table and references to every buffer it names; codes
+    and scales are allocated here when not given."""
+
+    def __init__(self, ws, fmt: str = "block", codes=None, scales=None):
+        torch = _torch()
+        if not ws:
+            raise ValueError("ws must be a non-empty list of bf16 [n, k] weights")
+        fid = _format_id(fmt)
+        if codes is None:
+            codes = [torch.empty(tuple(w.shape), dtype=torch.uint8, device=w.device) for w in ws]
+        if scales is None:
+            scales = [torch.empty(scale_shape(fmt, *w.shape), dtype=_scale_dtype(torch, fmt), device=w.device)
+                      for w in ws]
+        if not (len(ws) == len(codes) == len(scales)):
+            raise ValueError("ws, codes and scales must have equal lengths")
+        descs = (QuantDesc * len(ws))()
+        for i, (w, c, sc) in enumerate(zip(ws, codes, scales)):
+            _require(w, _bf16_like(torch), "w", 2)
+            _require(c, (torch.uint8,), "codes", 2)
+            n, k = w.shape
+            if tuple(c.shape) != (n, k):
+                raise ValueError(f"grouped quantize {i}: codes shape {tuple(c.shape)} != {(n, k)}")
+            _check_scales(torch, fmt, sc, n, k, "fp8w_quant_plan_init")
+            descs[i] = QuantDesc(w.data_ptr(), c.data_ptr(), sc.data_ptr(), n, k)
+        nbytes = int(lib().fp8w_quant_table_bytes(len(ws)))
+        self.table = torch.empty(nbytes, dtype=torch.uint8, device=ws[0].device)
+        self.plan = QuantPlanC()
+        _check(lib().fp8w_quant_plan_init(descs, len(ws), fid, self.table.data_ptr(), ctypes.byref(self.plan)),
+               "fp8w_quant_plan_init")
+        self.ws, self.codes, self.scales, self.fmt = list(ws), list(codes), list(scales), fmt
+
+    @property
+    def blocks(self) -> int:
+        return int(self.plan.blocks)
+
+
+def fp8w_quant_plan_init(ws, fmt="block", codes=None, scales=None) -> QuantPlan:
+    """Validate a group of weights to quantize and write its device table
+    (set-up call)."""
+    return QuantPlan(ws, fmt, codes, scales)
+
+
+def fp8w_quantize_grouped(plan: QuantPlan, stream=None):
+    """Enqueue the quantization of every weight of ``plan`` in one launch;
+    returns (codes list, scales list)."""
+    _check(lib().fp8w_quantize_grouped(ctypes.byref(plan.plan), _stream_handle(stream)),
+           "fp8w_quantize_grouped")
+    return plan.codes, plan.scales
 
 
 # ----------------------------------------------------------- tagged weight --

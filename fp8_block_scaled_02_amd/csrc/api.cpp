@@ -498,6 +498,63 @@ FP8W_API fp8w_status fp8w_gemv_grouped(const fp8w_grouped_plan* plan, void* stre
   return from_hip(fp8w::launch_gemv_grouped(table, plan->count, plan->blocks, plan->m, mx, plan->seg_cols, s));
 }
 
+// ---------------------------------------------------- grouped quantize --
+
+FP8W_API int64_t fp8w_quant_table_bytes(int64_t count) {
+  return (count < 1 || count > kMaxDim) ? 0 : count * (int64_t)sizeof(fp8w::QuantJob);
+}
+
+namespace {
+
+bool quant_grouped_format(int f) {
+  return f == FP8W_FORMAT_BLOCK || f == FP8W_FORMAT_MX || f == FP8W_FORMAT_BLOCK_BF16;
+}
+
+}  // namespace
+
+FP8W_API fp8w_status fp8w_quant_plan_init(const fp8w_quant_desc* descs, int64_t count, fp8w_format format,
+                                          void* device_table, fp8w_quant_plan* plan) {
+  if (!descs || !device_table || !plan) return FP8W_ERR_NULL;
+  if (count < 1 || count > kMaxDim) return FP8W_ERR_SHAPE;
+  if (!quant_grouped_format(format)) return FP8W_ERR_UNSUPPORTED;
+  if (!aligned(device_table, 16)) return FP8W_ERR_ALIGN;
+  std::vector<Span> ins, outs;
+  ins.reserve(count + 1);
+  outs.reserve(2 * count);
+  std::vector<fp8w::QuantJob> table((size_t)count);
+  int64_t blocks = 0;
+  for (int64_t i = 0; i < count; ++i) {
+    const fp8w_quant_desc& d = descs[i];
+    if (!d.w || !d.codes || !d.scales) return FP8W_ERR_NULL;
+    if (!dims_ok(d.n, d.k)) return FP8W_ERR_SHAPE;
+    if (!aligned(d.w, 2) || !aligned(d.scales, scale_align(format))) return FP8W_ERR_ALIGN;
+    ins.push_back({d.w, (uint64_t)d.n * d.k * 2});
+    outs.push_back({d.codes, (uint64_t)d.n * d.k});
+    outs.push_back({d.scales, scale_bytes(format, d.n, d.k)});
+    const bool vec = fp8w::quant_job_vec(format, d.w, d.k, d.codes);
+    table[i] = fp8w::QuantJob{d.w, d.codes, d.scales, (int32_t)d.n, (int32_t)d.k, (int32_t)blocks,
+                              vec ? 1 : 0, {0, 0}};
+    blocks += fp8w::quant_job_blocks(format, d.n, d.k, vec);
+    if (blocks > kMaxDim) return FP8W_ERR_SHAPE;
+  }
+  const uint64_t table_bytes = (uint64_t)count * sizeof(fp8w::QuantJob);
+  ins.push_back({device_table, table_bytes});
+  if (any_overlap(outs.data(), (int)outs.size(), ins.data(), (int)ins.size())) return FP8W_ERR_OVERLAP;
+  if (hipMemcpy(device_table, table.data(), table_bytes, hipMemcpyHostToDevice) != hipSuccess)
+    return FP8W_ERR_HIP;
+  *plan = fp8w_quant_plan{device_table, (int32_t)count, (int32_t)format, blocks};
+  return FP8W_OK;
+}
+
+FP8W_API fp8w_status fp8w_quantize_grouped(const fp8w_quant_plan* plan, void* stream) {
+  if (!plan || !plan->table) return FP8W_ERR_NULL;
+  if (plan->count < 1 || plan->blocks < plan->count || plan->blocks > kMaxDim ||
+      !quant_grouped_format(plan->format) || !aligned(plan->table, 16))
+    return FP8W_ERR_SHAPE;
+  return from_hip(fp8w::launch_quantize_grouped(static_cast<const fp8w::QuantJob*>(plan->table), plan->count,
+                                                plan->blocks, plan->format, static_cast<hipStream_t>(stream)));
+}
+
 // ------------------------------------------------------------- helpers --
 
 FP8W_API int64_t fp8w_block_scale_count(int64_t n, int64_t k) {

@@ -29,6 +29,26 @@ struct GemvJob {
 };
 static_assert(sizeof(GemvJob) == 48, "device table row");
 
+// One weight of a grouped quantize launch (device table row).
+struct QuantJob {
+  const uint16_t* w;        // bf16 [n, k]
+  uint8_t* codes;           // e4m3fn [n, k]
+  void* scales;             // the launch's format: f32 / bf16 block grid or e8m0 [n, ceil(k/32)]
+  int32_t n, k;             // validated to fit int32 on the host
+  int32_t item0;            // first workgroup of this weight in the launch
+  int32_t vec;              // 1: the 16-byte path (quant_job_vec)
+  int32_t pad[2];
+};
+static_assert(sizeof(QuantJob) == 48, "device table row");
+
+// Workgroups of one weight in a grouped quantize launch, and whether its
+// shape and alignment take the 16-byte path (format: kFmtBlock,
+// kFmtBlockBf16 or kFmtMx).
+int64_t quant_job_blocks(int format, int64_t n, int64_t k, bool vec);
+bool quant_job_vec(int format, const void* w, int64_t k, const void* codes);
+hipError_t launch_quantize_grouped(const QuantJob* device_table, int njobs, int64_t blocks, int format,
+                                   hipStream_t stream);
+
 hipError_t launch_quantize_block(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,
                                  float* scales, hipStream_t stream);
 hipError_t launch_quantize_mx(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,

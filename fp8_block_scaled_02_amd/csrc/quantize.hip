@@ -13,6 +13,7 @@
 
 #include <atomic>
 #include <mutex>
+#include <stddef.h>
 
 #include "device.hpp"
 #include "internal.hpp"
@@ -58,31 +59,29 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v) {
 // scale ("feat(quant): opt-in fp8-block QAT for the lm_head", How it works:
 // a bf16 128-block scale).
 template <bool BF16S>
-__device__ __forceinline__ float tile_scale(float amax_f, void* scales) {
+__device__ __forceinline__ float tile_scale(float amax_f, void* scales, size_t at) {
   float scale = amax_f > 0.0f ? amax_f / 448.0f : 1.0f;
   if (BF16S) {
     uint32_t bits = f32_to_bf16_rne(scale);
     if (bits == 0) bits = 1;
     scale = bf16_lo(bits);
-    if (threadIdx.x == 0) st_global<uint16_t>(scales, (size_t)blockIdx.x * 2, (uint16_t)bits);
+    if (threadIdx.x == 0) st_global<uint16_t>(scales, at * 2, (uint16_t)bits);
   } else if (threadIdx.x == 0) {
-    st_global<float>(scales, (size_t)blockIdx.x * 4, scale);
+    st_global<float>(scales, at * 4, scale);
   }
   return scale;
 }
 
-// One 256-thread block per 128x128 tile; flat block index b -> tile
-// (b / tiles_k, b % tiles_k).  Vector path: k % 8 == 0, w 16-B aligned and
-// codes 8-B aligned.  Thread t owns columns 8*(t%16) .. +7 of rows
+// One 256-thread block per 128x128 tile (ti, tj), whose scale is element
+// ti * tiles_k + tj of the grid.  Vector path: k % 8 == 0, w 16-B aligned
+// and codes 8-B aligned.  Thread t owns columns 8*(t%16) .. +7 of rows
 // t/16 + 16*i (i = 0..7): each row of the tile is read as 16 x 16 B and
 // written as 16 x 8 B, and the tile stays in registers between the amax and
 // the encode pass (the bf16 source is read from HBM once).
 template <bool BF16S>
-__global__ __launch_bounds__(kThreads) void k_quant_block_vec(const uint16_t* __restrict__ w,
-                                                              uint8_t* __restrict__ codes,
-                                                              void* __restrict__ scales, int n,
-                                                              int k, int tiles_k) {
-  const int ti = blockIdx.x / tiles_k, tj = blockIdx.x % tiles_k;
+__device__ __forceinline__ void block_tile_vec(const uint16_t* __restrict__ w, uint8_t* __restrict__ codes,
+                                               void* __restrict__ scales, int n, int k, int ti, int tj,
+                                               size_t at) {
   const int col = tj * kTile + (threadIdx.x & 15) * 8;
   const int row0 = ti * kTile + (threadIdx.x >> 4);
   const bool col_ok = col < k;
@@ -103,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_block_vec(const uint16_t* __
   }
   amax = block_max_u32(amax);
   const float amax_f = __uint_as_float(amax << 16);
-  const float scale = tile_scale<BF16S>(amax_f, scales);
+  const float scale = tile_scale<BF16S>(amax_f, scales, at);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int row = row0 + 16 * i;
@@ -117,34 +116,52 @@ __global__ __launch_bounds__(kThreads) void k_quant_block_vec(const uint16_t* __
 }
 
 // Any shape and alignment: element e = t + 256*j (j = 0..63) of the tile,
-// row e/128, column e%128, 2-byte loads and 1-byte stores.
+// row e/128, column e%128, 2-byte loads and 1-byte stores.  The tile is
+// read twice (amax, then encode; the second read hits L2) so that the
+// grouped kernel, which also runs the 16-byte body, keeps its registers.
+template <bool BF16S>
+__device__ __forceinline__ void block_tile_any(const uint16_t* __restrict__ w, uint8_t* __restrict__ codes,
+                                               void* __restrict__ scales, int n, int k, int ti, int tj,
+                                               size_t at) {
+  uint32_t amax = 0;
+  for (int j = 0; j < 64; ++j) {
+    const int e = threadIdx.x + kThreads * j;
+    const int row = ti * kTile + (e >> 7), col = tj * kTile + (e & 127);
+    if (row < n && col < k) {
+      const uint32_t a = w[(size_t)row * k + col] & 0x7FFFu;
+      amax = a > amax ? a : amax;
+    }
+  }
+  amax = block_max_u32(amax);
+  const float amax_f = __uint_as_float(amax << 16);
+  const float scale = tile_scale<BF16S>(amax_f, scales, at);
+  for (int j = 0; j < 64; ++j) {
+    const int e = threadIdx.x + kThreads * j;
+    const int row = ti * kTile + (e >> 7), col = tj * kTile + (e & 127);
+    if (row < n && col < k) {
+      const size_t i = (size_t)row * k + col;
+      codes[i] = (uint8_t)e4m3_code(__uint_as_float((uint32_t)w[i] << 16) / scale);
+    }
+  }
+}
+
+// Single weight: flat block index b -> tile (b / tiles_k, b % tiles_k).
+template <bool BF16S>
+__global__ __launch_bounds__(kThreads) void k_quant_block_vec(const uint16_t* __restrict__ w,
+                                                              uint8_t* __restrict__ codes,
+                                                              void* __restrict__ scales, int n,
+                                                              int k, int tiles_k) {
+  const int ti = blockIdx.x / tiles_k, tj = blockIdx.x % tiles_k;
+  block_tile_vec<BF16S>(w, codes, scales, n, k, ti, tj, blockIdx.x);
+}
+
 template <bool BF16S>
 __global__ __launch_bounds__(kThreads) void k_quant_block_any(const uint16_t* __restrict__ w,
                                                               uint8_t* __restrict__ codes,
                                                               void* __restrict__ scales, int n,
                                                               int k, int tiles_k) {
   const int ti = blockIdx.x / tiles_k, tj = blockIdx.x % tiles_k;
-  uint16_t v[64];
-  uint32_t amax = 0;
-#pragma unroll
-  for (int j = 0; j < 64; ++j) {
-    const int e = threadIdx.x + kThreads * j;
-    const int row = ti * kTile + (e >> 7), col = tj * kTile + (e & 127);
-    v[j] = 0;
-    if (row < n && col < k) v[j] = w[(size_t)row * k + col];
-    const uint32_t a = v[j] & 0x7FFFu;
-    amax = a > amax ? a : amax;
-  }
-  amax = block_max_u32(amax);
-  const float amax_f = __uint_as_float(amax << 16);
-  const float scale = tile_scale<BF16S>(amax_f, scales);
-#pragma unroll
-  for (int j = 0; j < 64; ++j) {
-    const int e = threadIdx.x + kThreads * j;
-    const int row = ti * kTile + (e >> 7), col = tj * kTile + (e & 127);
-    if (row < n && col < k)
-      codes[(size_t)row * k + col] = (uint8_t)e4m3_code(__uint_as_float((uint32_t)v[j] << 16) / scale);
-  }
+  block_tile_any<BF16S>(w, codes, scales, n, k, ti, tj, blockIdx.x);
 }
 
 // 2^-e as an fp32 (e in [-127, 120], so the result is a normal number).
@@ -158,11 +175,10 @@ __device__ __forceinline__ float pow2_neg(int e) { return __uint_as_float((uint3
 // issued before any encode, so each wave keeps kMxUnits * 1 KB in flight.
 constexpr int kMxUnits = 4;
 
-__global__ __launch_bounds__(kThreads) void k_quant_mx_vec(const uint16_t* __restrict__ w,
-                                                           uint8_t* __restrict__ codes,
-                                                           uint8_t* __restrict__ e8m0,
-                                                           size_t threads_total) {
-  const size_t t0 = (size_t)blockIdx.x * (kThreads * kMxUnits) + threadIdx.x;
+// Units t0, t0 + 256, ..., t0 + 256 * (kMxUnits - 1) of the flat unit array
+// (threads_total units).
+__device__ __forceinline__ void mx_units_vec(const uint16_t* __restrict__ w, uint8_t* __restrict__ codes,
+                                             uint8_t* __restrict__ e8m0, size_t t0, size_t threads_total) {
   uint4 v[kMxUnits];
 #pragma unroll
   for (int u = 0; u < kMxUnits; ++u) {
@@ -190,12 +206,17 @@ __global__ __launch_bounds__(kThreads) void k_quant_mx_vec(const uint16_t* __res
   }
 }
 
-// MX, any shape: one thread per (row, group), 2-byte loads.
-__global__ __launch_bounds__(kThreads) void k_quant_mx_any(const uint16_t* __restrict__ w,
+__global__ __launch_bounds__(kThreads) void k_quant_mx_vec(const uint16_t* __restrict__ w,
                                                            uint8_t* __restrict__ codes,
-                                                           uint8_t* __restrict__ e8m0, int n,
-                                                           int k, int groups) {
-  const size_t t = (size_t)blockIdx.x * kThreads + threadIdx.x;
+                                                           uint8_t* __restrict__ e8m0,
+                                                           size_t threads_total) {
+  mx_units_vec(w, codes, e8m0, (size_t)blockIdx.x * (kThreads * kMxUnits) + threadIdx.x, threads_total);
+}
+
+// MX, any shape: one thread per (row, group), 2-byte loads; t is the flat
+// (row, group) index.
+__device__ __forceinline__ void mx_group_any(const uint16_t* __restrict__ w, uint8_t* __restrict__ codes,
+                                             uint8_t* __restrict__ e8m0, int n, int k, int groups, size_t t) {
   if (t >= (size_t)n * groups) return;
   const size_t row = t / groups;
   const int c0 = (int)(t % groups) * kGroup;
@@ -211,6 +232,68 @@ __global__ __launch_bounds__(kThreads) void k_quant_mx_any(const uint16_t* __res
   const float mul = pow2_neg(e);
   for (int c = c0; c < c1; ++c)
     codes[row * k + c] = (uint8_t)e4m3_code(__uint_as_float((uint32_t)src[c] << 16) * mul);
+}
+
+__global__ __launch_bounds__(kThreads) void k_quant_mx_any(const uint16_t* __restrict__ w,
+                                                           uint8_t* __restrict__ codes,
+                                                           uint8_t* __restrict__ e8m0, int n,
+                                                           int k, int groups) {
+  mx_group_any(w, codes, e8m0, n, k, groups, (size_t)blockIdx.x * kThreads + threadIdx.x);
+}
+
+// ------------------------------------------------------------- grouped --
+//
+// Many weights in one launch, for load time: the launch's fixed cost (about
+// 1.7 us of a graph-captured launch on MI355X) is paid once, and the chip
+// streams the whole set as it does one large weight.  Workgroups are dealt
+// to the weights in table order (job j owns workgroups [item0_j,
+// item0_{j+1})); each workgroup finds its weight by a binary search of the
+// table and runs the single-weight body on its tile (block formats) or
+// chunk (MX).
+__device__ __forceinline__ void find_quant_job(const QuantJob* __restrict__ jobs, int njobs, QuantJob& job,
+                                               int& item) {
+  const int b = blockIdx.x;
+  int lo = 0, hi = njobs - 1;   // last job whose first workgroup is <= b
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (ld_global<int32_t>(jobs, (size_t)mid * sizeof(QuantJob) + offsetof(QuantJob, item0)) <= b)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  const size_t row = (size_t)lo * sizeof(QuantJob);
+  job.w = (const uint16_t*)ld_global<uint64_t>(jobs, row + offsetof(QuantJob, w));
+  job.codes = (uint8_t*)ld_global<uint64_t>(jobs, row + offsetof(QuantJob, codes));
+  job.scales = (void*)ld_global<uint64_t>(jobs, row + offsetof(QuantJob, scales));
+  job.n = ld_global<int32_t>(jobs, row + offsetof(QuantJob, n));
+  job.k = ld_global<int32_t>(jobs, row + offsetof(QuantJob, k));
+  job.item0 = ld_global<int32_t>(jobs, row + offsetof(QuantJob, item0));
+  job.vec = ld_global<int32_t>(jobs, row + offsetof(QuantJob, vec));
+  item = b - job.item0;
+}
+
+template <bool BF16S>
+__global__ __launch_bounds__(kThreads) void k_quant_block_grouped(const QuantJob* __restrict__ jobs, int njobs) {
+  QuantJob j;
+  int t;
+  find_quant_job(jobs, njobs, j, t);
+  const int tiles_k = (j.k + kTile - 1) / kTile;
+  const int ti = t / tiles_k, tj = t - ti * tiles_k;
+  if (j.vec)
+    block_tile_vec<BF16S>(j.w, j.codes, j.scales, j.n, j.k, ti, tj, (size_t)t);
+  else
+    block_tile_any<BF16S>(j.w, j.codes, j.scales, j.n, j.k, ti, tj, (size_t)t);
+}
+
+__global__ __launch_bounds__(kThreads) void k_quant_mx_grouped(const QuantJob* __restrict__ jobs, int njobs) {
+  QuantJob j;
+  int t;
+  find_quant_job(jobs, njobs, j, t);
+  uint8_t* e8m0 = static_cast<uint8_t*>(j.scales);
+  if (j.vec)
+    mx_units_vec(j.w, j.codes, e8m0, (size_t)t * (kThreads * kMxUnits) + threadIdx.x, (size_t)j.n * j.k / 8);
+  else
+    mx_group_any(j.w, j.codes, e8m0, j.n, j.k, (j.k + kGroup - 1) / kGroup, (size_t)t * kThreads + threadIdx.x);
 }
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -488,6 +571,38 @@ hipError_t launch_quantize_mx(const uint16_t* w, int64_t n, int64_t k, uint8_t* 
     const dim3 grid((unsigned)((total + kThreads - 1) / kThreads));
     hipLaunchKernelGGL(k_quant_mx_any, grid, dim3(kThreads), 0, stream, w, codes, e8m0, (int)n,
                        (int)k, (int)groups);
+  }
+  return hipGetLastError();
+}
+
+int64_t quant_job_blocks(int format, int64_t n, int64_t k, bool vec) {
+  if (format == kFmtMx) {
+    if (vec) return (n * k / 8 + kThreads * kMxUnits - 1) / (kThreads * kMxUnits);
+    return (n * ((k + kGroup - 1) / kGroup) + kThreads - 1) / kThreads;
+  }
+  return ((n + kTile - 1) / kTile) * ((k + kTile - 1) / kTile);
+}
+
+bool quant_job_vec(int format, const void* w, int64_t k, const void* codes) {
+  if (format == kFmtMx) return k % kGroup == 0 && aligned(w, 16) && aligned(codes, 8);
+  return k % 8 == 0 && aligned(w, 16) && aligned(codes, 8);
+}
+
+hipError_t launch_quantize_grouped(const QuantJob* table, int njobs, int64_t blocks, int format,
+                                   hipStream_t stream) {
+  const dim3 grid((unsigned)blocks), block(kThreads);
+  switch (format) {
+    case kFmtBlock:
+      hipLaunchKernelGGL(k_quant_block_grouped<false>, grid, block, 0, stream, table, njobs);
+      break;
+    case kFmtBlockBf16:
+      hipLaunchKernelGGL(k_quant_block_grouped<true>, grid, block, 0, stream, table, njobs);
+      break;
+    case kFmtMx:
+      hipLaunchKernelGGL(k_quant_mx_grouped, grid, block, 0, stream, table, njobs);
+      break;
+    default:
+      return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -425,6 +425,53 @@ fp8w_status fp8w_grouped_plan_init(const fp8w_gemv_desc* descs, int64_t count, i
  * produced by fp8w_grouped_plan_init), HIP. */
 fp8w_status fp8w_gemv_grouped(const fp8w_grouped_plan* plan, void* stream);
 
+/* ---------------------------------------------------- grouped quantize -- */
+
+/* Load-time quantization of many weights in one kernel launch: every bf16
+ * weight of a checkpoint is requantized when it is loaded ("Load-time MXFP8
+ * requantization of bf16 dense, hyper-connection and lm_head weights",
+ * Proposed solution), and a launch per weight pays a fixed cost (about
+ * 1.7 us on MI355X) that is as long as the whole of a small weight's pass.
+ * One grouped launch streams the set as one large weight.  Each weight's
+ * codes and scales are bit-identical to those of fp8w_quantize in the same
+ * format.  Formats: BLOCK, BLOCK_BF16 and MX; ROW and TENSOR are
+ * UNSUPPORTED. */
+typedef struct fp8w_quant_desc {
+  const uint16_t* w;     /* bf16 [n, k], 2-byte aligned              input  */
+  uint8_t* codes;        /* e4m3fn [n, k]                             output */
+  void* scales;          /* the format's scale buffer, aligned to its element
+                            (f32 or bf16 block grid, e8m0 [n, ceil(k/32)]) output */
+  int64_t n, k;          /* n, k >= 1                                        */
+} fp8w_quant_desc;
+
+/* What fp8w_quant_plan_init fills in; pass it to fp8w_quantize_grouped. */
+typedef struct fp8w_quant_plan {
+  const void* table;     /* the caller's device table buffer      */
+  int32_t count;         /* weights in the group                  */
+  int32_t format;        /* fp8w_format                           */
+  int64_t blocks;        /* workgroups of one launch              */
+} fp8w_quant_plan;
+
+/* Bytes of device memory a table for `count` weights needs (0 if count < 1). */
+int64_t fp8w_quant_table_bytes(int64_t count);
+
+/* Set-up call (not for graph capture): validates every descriptor as
+ * fp8w_quantize would, rejects any output that overlaps another output or
+ * any input (the bf16 weights and the table), and writes the group's table
+ * into `device_table` (caller-owned device memory of
+ * fp8w_quant_table_bytes(count) bytes, 16-byte aligned) with a blocking
+ * host-to-device copy.  The descriptors are not retained.
+ * Errors: NULL, SHAPE (count < 1, n or k out of range, too many
+ * workgroups), ALIGN, UNSUPPORTED (format), OVERLAP, HIP. */
+fp8w_status fp8w_quant_plan_init(const fp8w_quant_desc* descs, int64_t count, fp8w_format format,
+                                 void* device_table, fp8w_quant_plan* plan);
+
+/* Enqueue the quantization of every weight of the plan in one launch on
+ * `stream`.  Asynchronous, allocation-free and safe to capture in a HIP
+ * graph; the buffers the descriptors named must still be live.
+ * Errors: NULL, SHAPE (a plan not produced by fp8w_quant_plan_init), HIP. */
+fp8w_status fp8w_quantize_grouped(const fp8w_quant_plan* plan, void* stream);
+
 /* ------------------------------------------------------------- helpers -- */
 
 /* Number of fp32 block scales for [n, k]: ceil(n/128) * ceil(k/128); 0 if

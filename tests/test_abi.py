@@ -279,6 +279,46 @@ def test_grouped_argument_errors(F):
     assert L.fp8w_gemv_grouped(ctypes.byref(bad), None) == F.ERR_SHAPE
 
 
+def test_grouped_quantize_argument_errors(F):
+    L = F.lib()
+    assert L.fp8w_quant_table_bytes(96) == 96 * 48
+    assert L.fp8w_quant_table_bytes(0) == 0
+    descs = (F.QuantDesc * 2)(F.QuantDesc(A, B, C, 64, 64), F.QuantDesc(A + 8192, B + 4096, C + 64, 64, 64))
+    plan = F.QuantPlanC()
+    T = 0x10000000
+    init = L.fp8w_quant_plan_init
+    assert init(None, 2, F.FORMAT_BLOCK, T, ctypes.byref(plan)) == F.ERR_NULL
+    assert init(descs, 2, F.FORMAT_BLOCK, None, ctypes.byref(plan)) == F.ERR_NULL
+    assert init(descs, 0, F.FORMAT_BLOCK, T, ctypes.byref(plan)) == F.ERR_SHAPE
+    for fmt in (F.FORMAT_ROW, F.FORMAT_TENSOR, 7):
+        assert init(descs, 2, fmt, T, ctypes.byref(plan)) == F.ERR_UNSUPPORTED
+    assert init(descs, 2, F.FORMAT_BLOCK, T + 8, ctypes.byref(plan)) == F.ERR_ALIGN
+    for d in (F.QuantDesc(None, B, C, 64, 64), F.QuantDesc(A, None, C, 64, 64), F.QuantDesc(A, B, None, 64, 64)):
+        assert init((F.QuantDesc * 1)(d), 1, F.FORMAT_BLOCK, T, ctypes.byref(plan)) == F.ERR_NULL
+    for d in (F.QuantDesc(A, B, C, 0, 64), F.QuantDesc(A, B, C, 64, 1 << 31)):
+        assert init((F.QuantDesc * 1)(d), 1, F.FORMAT_BLOCK, T, ctypes.byref(plan)) == F.ERR_SHAPE
+    assert init((F.QuantDesc * 1)(F.QuantDesc(A + 1, B, C, 64, 64)), 1, F.FORMAT_BLOCK, T,
+                ctypes.byref(plan)) == F.ERR_ALIGN                               # w alignment
+    assert init((F.QuantDesc * 1)(F.QuantDesc(A, B, C + 2, 64, 64)), 1, F.FORMAT_BLOCK, T,
+                ctypes.byref(plan)) == F.ERR_ALIGN                               # f32 scale alignment
+    assert init((F.QuantDesc * 1)(F.QuantDesc(A, B, C + 1, 64, 64)), 1, F.FORMAT_BLOCK_BF16, T,
+                ctypes.byref(plan)) == F.ERR_ALIGN                               # bf16 scale alignment
+    clash = (F.QuantDesc * 2)(F.QuantDesc(A, B, C, 64, 64), F.QuantDesc(A + 8192, B + 64, C + 64, 64, 64))
+    assert init(clash, 2, F.FORMAT_BLOCK, T, ctypes.byref(plan)) == F.ERR_OVERLAP   # codes overlap
+    onto_w = (F.QuantDesc * 1)(F.QuantDesc(A, A + 100, C, 64, 64))
+    assert init(onto_w, 1, F.FORMAT_MX, T, ctypes.byref(plan)) == F.ERR_OVERLAP     # codes inside w
+    into_table = (F.QuantDesc * 1)(F.QuantDesc(A, B, T + 16, 64, 64))
+    assert init(into_table, 1, F.FORMAT_BLOCK, T, ctypes.byref(plan)) == F.ERR_OVERLAP
+    assert L.fp8w_quantize_grouped(None, None) == F.ERR_NULL
+    assert L.fp8w_quantize_grouped(ctypes.byref(F.QuantPlanC(None, 1, 0, 1)), None) == F.ERR_NULL
+    for bad in (F.QuantPlanC(T, 0, 0, 1),            # no weights
+                F.QuantPlanC(T, 2, 0, 1),            # fewer workgroups than weights
+                F.QuantPlanC(T, 1, 3, 4),            # ROW is not a grouped format
+                F.QuantPlanC(T + 8, 1, 0, 4),        # table alignment
+                F.QuantPlanC(T, 1, 0, 1 << 31)):     # too many workgroups
+        assert L.fp8w_quantize_grouped(ctypes.byref(bad), None) == F.ERR_SHAPE
+
+
 def test_binding_refuses_cpu_tensors(F):
     import torch
     w = torch.zeros((4, 4), dtype=torch.bfloat16)

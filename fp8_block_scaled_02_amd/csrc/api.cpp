@@ -6,7 +6,8 @@
 // the fail-loudly bounds contract of "feat: add FP8 blockwise weight
 // quantization and FP8(E4M3) KV cache support" (Security and Safety).
 // The kernel family is chosen from the shape only (never from values), so
-// the calls are safe to capture in a HIP graph.
+// the enqueueing calls can be captured in a HIP graph once their set-up
+// calls (GEMM handle, grouped tables) have run outside capture.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

@@ -1667,25 +1667,35 @@ hipError_t dispatch_mfma_stream(const StreamJobs& l, int64_t blocks, int64_t til
 constexpr int64_t kSingleWideMinRowsValu = 16384;
 
 // M = 1 single calls below that many rows, K <= 1024 * kRowsMaxC: the
-// one-wave kernel with kRowsR rows per wave.
-constexpr int kRowsR = 2, kRowsMaxC = 4;
+// one-wave kernel.
+constexpr int kRowsMaxC = 4;
+// Rows per wave: one up to 4096 rows, where the call has too few rows to
+// keep every SIMD busy with two (graph-captured single calls on MI355X:
+// [2560x3072] 1.4 % faster with block scales and 2.5 % with MX; two rows
+// per wave stay faster on [6656x2560] and [8192x2560], by 7-8 %).
+constexpr int64_t kRowsOneMaxN = 4096;
 
-template <int C, bool MX>
+template <int R, int C, bool MX>
 hipError_t run_valu_rows(const GemvJob& job, hipStream_t stream) {
-  hipLaunchKernelGGL((k_gemv_valu_rows<kRowsR, C, MX>), dim3((unsigned)((job.n + kRowsR - 1) / kRowsR)),
+  hipLaunchKernelGGL((k_gemv_valu_rows<R, C, MX>), dim3((unsigned)((job.n + R - 1) / R)),
                      dim3(kWave), 0, stream, job);
   return hipGetLastError();
 }
 
-template <bool MX>
-hipError_t dispatch_valu_rows(const GemvJob& job, hipStream_t stream) {
+template <int R, bool MX>
+hipError_t dispatch_valu_rows_r(const GemvJob& job, hipStream_t stream) {
   switch ((job.k + 1023) / 1024) {
-    case 1: return run_valu_rows<1, MX>(job, stream);
-    case 2: return run_valu_rows<2, MX>(job, stream);
-    case 3: return run_valu_rows<3, MX>(job, stream);
-    case 4: return run_valu_rows<4, MX>(job, stream);
+    case 1: return run_valu_rows<R, 1, MX>(job, stream);
+    case 2: return run_valu_rows<R, 2, MX>(job, stream);
+    case 3: return run_valu_rows<R, 3, MX>(job, stream);
+    case 4: return run_valu_rows<R, 4, MX>(job, stream);
   }
   return hipErrorInvalidValue;
+}
+
+template <bool MX>
+hipError_t dispatch_valu_rows(const GemvJob& job, hipStream_t stream) {
+  return job.n <= kRowsOneMaxN ? dispatch_valu_rows_r<1, MX>(job, stream) : dispatch_valu_rows_r<2, MX>(job, stream);
 }
 
 hipError_t launch_valu_rows(const GemvJob& job, bool mx, hipStream_t stream) {

@@ -50,10 +50,11 @@
  * never read tensor values on the host, and the kernel chosen depends on the
  * shape only, so the calls may be captured in a HIP graph, with two
  * exceptions that need a set-up call outside capture first: the GEMM calls
- * (fp8w_gemm_prepare, or one GEMM call, on the device) and grouped GEMVs
- * (fp8w_grouped_plan_init).  fp8w_quantize_act_noalloc resolves its device
- * array on its first call on a device; make that call outside capture too.  Results are
- * bitwise reproducible run to run (no atomics, fixed reduction order).
+ * (fp8w_gemm_prepare, or one GEMM call, on the device) and the grouped
+ * calls (fp8w_grouped_plan_init, fp8w_quant_plan_init).
+ * fp8w_quantize_act_noalloc resolves its device array on its first call on
+ * a device; make that call outside capture too.  Results are bitwise
+ * reproducible run to run (no atomics, fixed reduction order).
  *
  * Errors: arguments are checked on the host before anything is enqueued; on
  * any error nothing is launched and no output byte is written.  A fault

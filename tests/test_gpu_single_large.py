@@ -100,6 +100,16 @@ def test_valu_stream_single_job(fp8w, oracle_mod, weights, fmt, k):
     _check(fp8w, oracle_mod, weights, 16405, k, 1, fmt, 0)
 
 
+# M = 1 single calls below 16384 rows with K <= 4096 run the one-wave kernel:
+# one row per wave up to 4096 rows, two above (an odd N leaves a wave's
+# second row past the end), for every chunk count K <= 1024 * C, C = 1..4
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("n", [4095, 4096, 4097, 16383])
+@pytest.mark.parametrize("k", [1008, 2048, 3056, 4096])
+def test_rows_kernel_either_side_of_the_row_split(fp8w, oracle_mod, weights, fmt, n, k):
+    _check(fp8w, oracle_mod, weights, n, k, 1, fmt, 0)
+
+
 # VALU wide tiles without streaming: K above the streaming limit (m = 1:
 # 4096-column K segments at K = 4096 and 8176, 3072-column ones at 4112),
 # m = 2 and 3 (AUTO) and forced VALU up to m = 8

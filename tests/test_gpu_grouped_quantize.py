@@ -121,3 +121,23 @@ def test_grouped_quantize_rejects_bad_groups(fp8w):
     s = torch.empty((1, 1), dtype=torch.float32, device="cuda")
     with pytest.raises(fp8w.Fp8wError, match="OVERLAP"):   # two weights write the same codes
         fp8w.fp8w_quant_plan_init([w, w.clone()], codes=[c, c], scales=[s, s.clone()])
+
+
+@pytest.mark.parametrize("fmt", ["block", "mx"])
+def test_grouped_quantize_many_small_weights(fp8w, fmt):
+    """300 weights of mixed tiny and ragged shapes in one launch: every
+    workgroup finds its weight by the table search, including weights of a
+    single workgroup next to each other."""
+    import torch
+    rng = np.random.default_rng(17)
+    shapes = [(int(rng.integers(1, 300)), int(rng.choice([1, 7, 16, 32, 40, 96, 130, 256, 272]))) for _ in range(300)]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    ws = [(torch.randn((n, k), device="cuda", generator=gen) * 0.05).to(torch.bfloat16) for n, k in shapes]
+    plan = fp8w.fp8w_quant_plan_init(ws, fmt=fmt)
+    codes, scales = fp8w.fp8w_quantize_grouped(plan)
+    _sync()
+    for i, (w, c, s) in enumerate(zip(ws, codes, scales)):
+        c1, s1 = fp8w.fp8w_quantize(w, fmt)
+        _sync()
+        assert torch.equal(c, c1) and torch.equal(s, s1), f"{fmt} weight {i} {tuple(w.shape)}"

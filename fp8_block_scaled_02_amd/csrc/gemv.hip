@@ -1187,38 +1187,49 @@ __global__ __launch_bounds__(NW * kWave, 4) void k_gemv_mfma_stream(const GemvJo
 // sums meet in LDS at the end.  A call is latency-bound when its grid is
 // small: with one workgroup or less per CU (N <= 4096 on MI355X), 8 waves
 // per tile halve the panels each wave waits for in turn.
-template <int MT, bool MX>
+template <int MT, bool MX, int T>
 struct DirectSlot {
-  Panel<MX> p;
-  uint4 xb[MT][2][2][2];   // [m tile][block][chunk][first / last 8 K positions]
+  Panel<MX> p[T];          // the panel of each of the workgroup's T 16-row tiles
+  uint4 xb[MT][2][2][2];   // [m tile][block][chunk][first / last 8 K positions], shared by the T tiles
 };
 
-template <int MT, int D, bool MX, int NW, bool PK>
+// T 16-row tiles per workgroup (T = 2: 32 rows) share each x^T fragment a
+// wave loads, so x costs 1/T of the fragment reads per weight byte.
+template <int MT, int D, bool MX, int NW, bool PK, int T>
 __global__ __launch_bounds__(NW * kWave) void k_gemv_mfma_direct(GemvJob j, int m_rows) {
   __shared__ __align__(16) unsigned char pb[NW * kPanelBytes];
-  __shared__ float red[NW * MT * 4 * kWave];
+  __shared__ float red[NW * T * MT * 4 * kWave];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int i = lane & 15, g = lane >> 4;
-  const int row0 = blockIdx.x * 16;
   const int np = (j.k + kPanelCols - 1) / kPanelCols;
   const int nkb = (j.k + kTile - 1) / kTile;
   const int groups = (j.k + kGroup - 1) / kGroup;
   const int nq = (np - wave + NW - 1) / NW;   // this wave's panels
 
-  // the tile's row offsets, and each lane's x rows (rows past m_rows read
-  // row m_rows - 1: their products land in output columns not stored)
-  TileLoads tl;
-  tile_loads(j, row0, tl);
+  // each tile's row offsets (tiles past the last row load nothing), and
+  // each lane's x rows (rows past m_rows read row m_rows - 1: their
+  // products land in output columns not stored)
+  int row0[T];
+  bool tlive[T];
+  TileLoads tl[T];
+#pragma unroll
+  for (int u = 0; u < T; ++u) {
+    row0[u] = (blockIdx.x * T + u) * 16;
+    tlive[u] = row0[u] < j.n;
+    if (tlive[u]) tile_loads(j, row0[u], tl[u]);
+  }
   const uint8_t* xrow[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t)
     xrow[t] = reinterpret_cast<const uint8_t*>(j.x) + ((size_t)min(16 * t + i, m_rows - 1) * j.k + 16 * g) * 2;
 
-  auto issue = [&](int q, DirectSlot<MT, MX>& r) {
+  auto issue = [&](int q, DirectSlot<MT, MX, T>& r) {
     const int p = wave + NW * q;
     const bool live = q < nq;
-    panel_issue_tile<MX, PK, true>(j, tl, row0, p, live, nkb, groups, r.p);
+#pragma unroll
+    for (int u = 0; u < T; ++u)
+      panel_issue_tile<MX, PK, true>(j, tl[u], row0[u], p, live && tlive[u], nkb, groups, r.p[u]);
     if (live && (p + 1) * kPanelCols <= j.k) {   // a whole panel: every x load in bounds
 #pragma unroll
       for (int b = 0; b < 2; ++b)
@@ -1249,42 +1260,54 @@ __global__ __launch_bounds__(NW * kWave) void k_gemv_mfma_direct(GemvJob j, int 
     }
   };
 
-  f32x4 acc[MT];
+  f32x4 acc[T][MT];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  DirectSlot<MT, MX> slot[D];
+  for (int u = 0; u < T; ++u)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[u][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  DirectSlot<MT, MX, T> slot[D];
 #pragma unroll
   for (int s = 0; s < D; ++s) issue(s, slot[s]);
   for (int q0 = 0; q0 < nq; q0 += D) {
 #pragma unroll
     for (int s = 0; s < D; ++s) {
       if (q0 + s < nq) {
-        uint4 a[2][2];
-        panel_to_a(slot[s].p.v, pb + wave * kPanelBytes, a);
-        float sc[MX ? 4 : 2];
-        panel_scales<MX, PK>(slot[s].p, sc);
-        panel_mfma<MT, MX>(a, sc, [&](int t, int b, int c, uint4& B0, uint4& B1) {
-          B0 = slot[s].xb[t][b][c][0];
-          B1 = slot[s].xb[t][b][c][1];
-        }, acc);
+#pragma unroll
+        for (int u = 0; u < T; ++u) {
+          if (!tlive[u]) continue;
+          uint4 a[2][2];
+          panel_to_a(slot[s].p[u].v, pb + wave * kPanelBytes, a);
+          float sc[MX ? 4 : 2];
+          panel_scales<MX, PK>(slot[s].p[u], sc);
+          panel_mfma<MT, MX>(a, sc, [&](int t, int b, int c, uint4& B0, uint4& B1) {
+            B0 = slot[s].xb[t][b][c][0];
+            B1 = slot[s].xb[t][b][c][1];
+          }, acc[u]);
+        }
       }
       issue(q0 + s + D, slot[s]);
     }
   }
 
 #pragma unroll
-  for (int t = 0; t < MT; ++t)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) red[((wave * MT + t) * 4 + jj) * kWave + lane] = acc[t][jj];
-  __syncthreads();
-  if (wave == 0) {
+  for (int u = 0; u < T; ++u)
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
+      for (int jj = 0; jj < 4; ++jj) red[(((wave * T + u) * MT + t) * 4 + jj) * kWave + lane] = acc[u][t][jj];
+  __syncthreads();
+  if (wave == 0) {
 #pragma unroll
-        for (int w = 1; w < NW; ++w) acc[t][jj] += red[((w * MT + t) * 4 + jj) * kWave + lane];
-    store_tile<MT>(j, row0, m_rows, acc);
+    for (int u = 0; u < T; ++u) {
+      if (!tlive[u]) continue;
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int w = 1; w < NW; ++w) acc[u][t][jj] += red[(((w * T + u) * MT + t) * 4 + jj) * kWave + lane];
+      store_tile<MT>(j, row0[u], m_rows, acc[u]);
+    }
   }
 }
 
@@ -1596,6 +1619,9 @@ constexpr int kStreamR = 4, kStreamC = 3;
 // Single MFMA calls on at most this many rows (one 16-row workgroup or less
 // per CU) split each tile's panels over 8 waves instead of 4.
 constexpr int64_t kDirect8MaxRows = 4096;
+// Two-tile single MFMA calls at 9 <= M <= 16 on at most this many rows
+// split each workgroup's panels over 8 waves, on more rows over 4.
+constexpr int64_t kDirectT2Wave8MaxRows = 8192;
 
 template <int MT, bool MX, bool ONE, bool PK>
 constexpr auto mfma_stream_kernel() {
@@ -1743,12 +1769,12 @@ int gemv_mfma_stream_lds_limit() { return kMfmaStreamLds; }
 
 namespace {
 
-template <int MT, int NW>
-hipError_t launch_mfma_direct(dim3 grid, const GemvJob& job, int m, bool mx, bool pk, hipStream_t stream) {
-  const dim3 block(NW * kWave);
-  if (!mx) hipLaunchKernelGGL((k_gemv_mfma_direct<MT, 2, false, NW, false>), grid, block, 0, stream, job, m);
-  else if (pk) hipLaunchKernelGGL((k_gemv_mfma_direct<MT, 2, true, NW, true>), grid, block, 0, stream, job, m);
-  else hipLaunchKernelGGL((k_gemv_mfma_direct<MT, 2, true, NW, false>), grid, block, 0, stream, job, m);
+template <int MT, int NW, int T>
+hipError_t launch_mfma_direct(const GemvJob& job, int m, bool mx, bool pk, hipStream_t stream) {
+  const dim3 grid((unsigned)((job.n + 16 * T - 1) / (16 * T))), block(NW * kWave);
+  if (!mx) hipLaunchKernelGGL((k_gemv_mfma_direct<MT, 2, false, NW, false, T>), grid, block, 0, stream, job, m);
+  else if (pk) hipLaunchKernelGGL((k_gemv_mfma_direct<MT, 2, true, NW, true, T>), grid, block, 0, stream, job, m);
+  else hipLaunchKernelGGL((k_gemv_mfma_direct<MT, 2, true, NW, false, T>), grid, block, 0, stream, job, m);
   return hipGetLastError();
 }
 
@@ -1791,14 +1817,23 @@ hipError_t launch_gemv(const GemvJob& job, int m, bool mx, int route, hipStream_
     return dispatch_mfma_stream<true>(l, tiles, tiles, 1, m, gemv_mfma_stream_seg_cols(m, job.k), mx,
                                       mx && mx_rows_packed8(job.scales, job.k), stream);
   }
-  const dim3 grid((unsigned)((job.n + 15) / 16));
   const bool pk = mx && mx_rows_packed8(job.scales, job.k);
   if (job.n <= kDirect8MaxRows) {
-    return m <= 16 ? launch_mfma_direct<1, 8>(grid, job, m, mx, pk, stream)
-                   : launch_mfma_direct<2, 8>(grid, job, m, mx, pk, stream);
+    return m <= 16 ? launch_mfma_direct<1, 8, 1>(job, m, mx, pk, stream)
+                   : launch_mfma_direct<2, 8, 1>(job, m, mx, pk, stream);
   }
-  return m <= 16 ? launch_mfma_direct<1, kWaves>(grid, job, m, mx, pk, stream)
-                 : launch_mfma_direct<2, kWaves>(grid, job, m, mx, pk, stream);
+  // Above M = 8 two 16-row tiles per workgroup share each x^T fragment
+  // (graph-captured single calls on MI355X, block / MX: M = 16 on
+  // [8192x2560] +6 / +6 % with 8 waves, [6144x4096] +15 / +12 %,
+  // [24576x4096] +4 / +7 % with 4 waves; M = 32 +6..+21 / +4..+28 % with 4
+  // waves).  At M <= 8 the fragments are half duplicates (rows past M) and
+  // the shared tiles lose 3-9 %.
+  if (m <= 8) return launch_mfma_direct<1, kWaves, 1>(job, m, mx, pk, stream);
+  if (m <= 16) {
+    return job.n <= kDirectT2Wave8MaxRows ? launch_mfma_direct<1, 8, 2>(job, m, mx, pk, stream)
+                                          : launch_mfma_direct<1, kWaves, 2>(job, m, mx, pk, stream);
+  }
+  return launch_mfma_direct<2, kWaves, 2>(job, m, mx, pk, stream);
 }
 
 bool mx_rows_stream(const void* e8m0, int64_t n, int64_t k) {

@@ -41,7 +41,7 @@ PEAK_BF16 = 2.5e15         # MI355X dense bf16 MFMA, flop/s
 # kernel, launch-plan and helper sources); any change to those reports
 # traffic as null until the counters are retaken.
 COUNTED_TRAFFIC = {
-    "sources_sha256": "2eaeb09690be67b3e11af7159989d29c6834dea3f2c850e11915eb9ffc220e3e",
+    "sources_sha256": "34a4a7b91e2973e518940e5fd911460b50ee1f26b2f3529cc27ddf788853a52b",
     "bytes_per_launch": 1340.30e6,
 }
 TRAFFIC_SOURCES = ('gemv.hip', 'device.hpp', 'internal.hpp', 'api.cpp')

@@ -15,12 +15,15 @@
 //    k_gemv_valu: one tile of rows per workgroup, K in segments staged
 //    with x in LDS.  k_gemv_valu_stream (M = 1, K <= 3072): a contiguous
 //    run of 16-row tiles per workgroup, the next tile's codes requested
-//    before the current one is computed.
+//    before the current one is computed.  k_gemv_valu_rows (single calls,
+//    M <= 4, fewer than 16384 rows): one wave per workgroup, a few rows per
+//    wave, x held in registers.
 //  * MFMA (M <= 32): v_mfma_f32_16x16x32_bf16 on 16-row tiles of W against
 //    x^T padded to 16 or 32 columns.  Codes reach the A layout through a
 //    per-wave LDS transpose of 16-row x 256-byte panels.  k_gemv_mfma_direct
-//    (single calls): one 16-row tile per workgroup, its 4 waves (8 when
-//    N <= 4096) splitting the panels, x fragments from L2.
+//    (single calls): one 16-row tile per workgroup (two above M = 8,
+//    sharing each x^T fragment), its 4 or 8 waves splitting the panels, x
+//    fragments from L2.
 //    k_gemv_mfma_stream: runs of 128-row tiles, one 16-row tile per wave,
 //    x staged in LDS by K segments.
 //  * W8A8: fp8 x fp8 v_mfma_scale_f32_16x16x128_f8f6f4 (k_gemv_w8a8_direct,
@@ -472,15 +475,16 @@ __global__ __launch_bounds__(kThreads) void k_gemv_valu(GemvJob arg, const GemvJ
 
 // ------------------------------------------------- VALU, rows per wave --
 //
-// Single calls at M = 1 on weights with fewer rows than the streaming
-// threshold and K <= 4096: one wave per workgroup, R rows per wave, and
-// each lane's x chunks (32 bytes per 16-code chunk) loaded straight into
-// registers, shared by the wave's R rows.  No LDS and no barrier: on
+// Single calls at M <= 4 on weights with fewer rows than the streaming
+// threshold and K <= 4096 (K <= 3072 at M > 1): one wave per workgroup, R
+// rows per wave, and each lane's x chunks (32 bytes per 16-code chunk and
+// activation row) loaded straight into registers, shared by the wave's R
+// rows.  No LDS and no barrier: on
 // MI355X, staging x through LDS with a workgroup barrier cost about 0.8 us
 // of a 4.6 us call over a bare read of the same codes (graph-captured
 // projection-set calls), and loading x per wave costs about half of that
 // once R >= 2 rows share it.  x is requested before the codes.
-template <int R, int C, bool MX>
+template <int R, int C, bool MX, int M>
 __global__ __launch_bounds__(kWave) void k_gemv_valu_rows(GemvJob j) {
   static_assert(kTile % R == 0, "a wave's rows stay inside one 128-row block");
   const int lane = threadIdx.x & (kWave - 1);
@@ -490,12 +494,15 @@ __global__ __launch_bounds__(kWave) void k_gemv_valu_rows(GemvJob j) {
   int ch[C];
 #pragma unroll
   for (int c = 0; c < C; ++c) ch[c] = min(lane + kWave * c, nch - 1);
-  uint4 x0[C], x1[C];
+  uint4 x0[M][C], x1[M][C];
 #pragma unroll
-  for (int c = 0; c < C; ++c) {
-    x0[c] = ld_global_u4(j.x, (size_t)ch[c] * 32);
-    x1[c] = ld_global_u4(j.x, (size_t)ch[c] * 32 + 16);
-  }
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const size_t off = ((size_t)m * j.k + 16 * (size_t)ch[c]) * 2;
+      x0[m][c] = ld_global_u4(j.x, off);
+      x1[m][c] = ld_global_u4(j.x, off + 16);
+    }
   const uint8_t* rows[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) rows[r] = j.codes + (size_t)min(row0 + r, j.n - 1) * j.k;
@@ -516,9 +523,9 @@ __global__ __launch_bounds__(kWave) void k_gemv_valu_rows(GemvJob j) {
 #pragma unroll
     for (int c = 0; c < C; ++c) sc[c] = block_scale(j, min(row0, j.n - 1), ch[c] >> 3, nkb);
   }
-  float acc[R];
+  float acc[R * M];   // row r, activation row m at r * M + m
 #pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+  for (int f = 0; f < R * M; ++f) acc[f] = 0.0f;
 #pragma unroll
   for (int c = 0; c < C; ++c) {
     if (lane + kWave * c < nch) {
@@ -528,17 +535,18 @@ __global__ __launch_bounds__(kWave) void k_gemv_valu_rows(GemvJob j) {
         const bf16x2 wv[8] = {cvt_lo(d.x), cvt_hi(d.x), cvt_lo(d.y), cvt_hi(d.y),
                               cvt_lo(d.z), cvt_hi(d.z), cvt_lo(d.w), cvt_hi(d.w)};
         const float s = MX ? mx_scale((uint8_t)e[MX ? r : 0][MX ? c : 0]) : sc[MX ? 0 : c];
-        acc[r] = __builtin_fmaf(s, dot16(wv, x0[c], x1[c]), acc[r]);
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r * M + m] = __builtin_fmaf(s, dot16(wv, x0[m][c], x1[m][c]), acc[r * M + m]);
       }
     }
   }
-  const WaveSums<R> sums(acc);
+  const WaveSums<R * M> sums(acc);
   if ((lane & 15) == 0) {
 #pragma unroll
-    for (int q = 0; q < WaveSums<R>::kGroups; ++q) {
-      const int r = 4 * q + (lane >> 4);
-      if (r < R && row0 + r < j.n)
-        st_global<uint16_t>(j.y, (size_t)(row0 + r) * 2,
+    for (int q = 0; q < WaveSums<R * M>::kGroups; ++q) {
+      const int f = 4 * q + (lane >> 4), r = f / M, m = f % M;
+      if (f < R * M && row0 + r < j.n)
+        st_global<uint16_t>(j.y, ((size_t)m * j.n + row0 + r) * 2,
                             (uint16_t)f32_to_bf16_rne(sums.g[q] * output_scale(j, row0 + r)));
     }
   }
@@ -1692,40 +1700,69 @@ hipError_t dispatch_mfma_stream(const StreamJobs& l, int64_t blocks, int64_t til
 // (1.1-2.5x, the gain growing with m), and from N = 16384 when m > 16.
 constexpr int64_t kSingleWideMinRowsValu = 16384;
 
-// M = 1 single calls below that many rows, K <= 1024 * kRowsMaxC: the
-// one-wave kernel.
+// Single calls below that many rows with M <= kRowsMaxM run the one-wave
+// kernel up to K = 1024 * kRowsMaxC (M = 1) or 1024 * kRowsMultiMaxC (M > 1).
 constexpr int kRowsMaxC = 4;
-// Rows per wave: one up to 4096 rows, where the call has too few rows to
-// keep every SIMD busy with two (graph-captured single calls on MI355X:
-// [2560x3072] 1.4 % faster with block scales and 2.5 % with MX; two rows
-// per wave stay faster on [6656x2560] and [8192x2560], by 7-8 %).
+constexpr int kRowsMaxM = 4;
+constexpr int kRowsMultiMaxC = 3;
+// Rows per wave at M = 1: one up to 4096 rows, where the call has too few
+// rows to keep every SIMD busy with two (graph-captured single calls on
+// MI355X: [2560x3072] 1.4 % faster with block scales and 2.5 % with MX; two
+// rows per wave stay faster on [6656x2560] and [8192x2560], by 7-8 %).
 constexpr int64_t kRowsOneMaxN = 4096;
 
-template <int R, int C, bool MX>
+template <int R, int C, bool MX, int M>
 hipError_t run_valu_rows(const GemvJob& job, hipStream_t stream) {
-  hipLaunchKernelGGL((k_gemv_valu_rows<R, C, MX>), dim3((unsigned)((job.n + R - 1) / R)),
+  hipLaunchKernelGGL((k_gemv_valu_rows<R, C, MX, M>), dim3((unsigned)((job.n + R - 1) / R)),
                      dim3(kWave), 0, stream, job);
   return hipGetLastError();
 }
 
-template <int R, bool MX>
+template <int R, bool MX, int M>
 hipError_t dispatch_valu_rows_r(const GemvJob& job, hipStream_t stream) {
   switch ((job.k + 1023) / 1024) {
-    case 1: return run_valu_rows<R, 1, MX>(job, stream);
-    case 2: return run_valu_rows<R, 2, MX>(job, stream);
-    case 3: return run_valu_rows<R, 3, MX>(job, stream);
-    case 4: return run_valu_rows<R, 4, MX>(job, stream);
+    case 1: return run_valu_rows<R, 1, MX, M>(job, stream);
+    case 2: return run_valu_rows<R, 2, MX, M>(job, stream);
+    case 3: return run_valu_rows<R, 3, MX, M>(job, stream);
+    case 4:
+      if constexpr (M == 1) return run_valu_rows<R, 4, MX, M>(job, stream);
+      break;
   }
   return hipErrorInvalidValue;
 }
 
-template <bool MX>
-hipError_t dispatch_valu_rows(const GemvJob& job, hipStream_t stream) {
-  return job.n <= kRowsOneMaxN ? dispatch_valu_rows_r<1, MX>(job, stream) : dispatch_valu_rows_r<2, MX>(job, stream);
+// One wave reads R rows against M activation rows held in registers.  Each
+// wave loads all of x from L2, so more rows per wave pay off as M grows.
+// Graph-captured single calls on MI355X, M = 2..4, block / MX scales,
+// against the LDS-staging kernel: [2560x3072] with 2 rows per wave +7..+9 /
+// +17..+21 %; [6656x2560] with 4 rows +0.5..+6.5 / +7..+12 %; [8192x2560]
+// -4.6 (block, M = 3)..+3 / -2..+8 %.  One row per wave loses 10-40 %.  At
+// K = 4096 the registers for x cut occupancy and the LDS-staging kernel
+// stays 10-25 % ahead, hence M > 1 stops at K = 3072.
+template <bool MX, int M>
+hipError_t dispatch_valu_rows_m(const GemvJob& job, hipStream_t stream) {
+  if constexpr (M == 1) {
+    return job.n <= kRowsOneMaxN ? dispatch_valu_rows_r<1, MX, M>(job, stream)
+                                 : dispatch_valu_rows_r<2, MX, M>(job, stream);
+  } else {
+    return job.n <= kRowsOneMaxN ? dispatch_valu_rows_r<2, MX, M>(job, stream)
+                                 : dispatch_valu_rows_r<4, MX, M>(job, stream);
+  }
 }
 
-hipError_t launch_valu_rows(const GemvJob& job, bool mx, hipStream_t stream) {
-  return mx ? dispatch_valu_rows<true>(job, stream) : dispatch_valu_rows<false>(job, stream);
+template <bool MX>
+hipError_t dispatch_valu_rows(const GemvJob& job, int m, hipStream_t stream) {
+  switch (m) {
+    case 1: return dispatch_valu_rows_m<MX, 1>(job, stream);
+    case 2: return dispatch_valu_rows_m<MX, 2>(job, stream);
+    case 3: return dispatch_valu_rows_m<MX, 3>(job, stream);
+    case 4: return dispatch_valu_rows_m<MX, 4>(job, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_valu_rows(const GemvJob& job, int m, bool mx, hipStream_t stream) {
+  return mx ? dispatch_valu_rows<true>(job, m, stream) : dispatch_valu_rows<false>(job, m, stream);
 }
 
 bool single_call_streams_mfma(int64_t n, int m) { return n >= 32768 || (n >= 16384 && m > 16); }
@@ -1802,7 +1839,8 @@ hipError_t launch_gemv(const GemvJob& job, int m, bool mx, int route, hipStream_
       return mx ? run_valu_stream<true, true>(l, tiles, tiles, 1, stream)
                 : run_valu_stream<false, true>(l, tiles, tiles, 1, stream);
     }
-    if (!wide && m == 1 && job.k <= 1024 * kRowsMaxC) return launch_valu_rows(job, mx, stream);
+    if (!wide && m <= kRowsMaxM && job.k <= 1024 * (m == 1 ? kRowsMaxC : kRowsMultiMaxC))
+      return launch_valu_rows(job, m, mx, stream);
     const int rows = wide ? gemv_rows_per_block(route, m, true) : gemv_rows_per_block(route, m, false);
     const int64_t blocks = (job.n + rows - 1) / rows;
     const bool seg4096 = wide && m == 1 && gemv_wide_seg_cols(job.k) == 4096;

@@ -110,6 +110,18 @@ def test_rows_kernel_either_side_of_the_row_split(fp8w, oracle_mod, weights, fmt
     _check(fp8w, oracle_mod, weights, n, k, 1, fmt, 0)
 
 
+# the same kernel with two to four activation rows held in registers: two
+# rows per wave up to 4096 rows, four above, K <= 3072 (K = 3088 and 4096
+# take the LDS-staging kernel); forced VALU, as AUTO sends some to MFMA
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("n", [4095, 4097, 16383])
+@pytest.mark.parametrize("k", [1008, 2048, 3056, 3072, 3088, 4096])
+@pytest.mark.parametrize("m", [2, 3, 4])
+def test_rows_kernel_several_activation_rows(fp8w, oracle_mod, weights, fmt, n, k, m):
+    import fp8_block_scaled_02_amd as F
+    _check(fp8w, oracle_mod, weights, n, k, m, fmt, F.ROUTE_VALU)
+
+
 # VALU wide tiles without streaming: K above the streaming limit (m = 1:
 # 4096-column K segments at K = 4096 and 8176, 3072-column ones at 4112),
 # m = 2 and 3 (AUTO) and forced VALU up to m = 8

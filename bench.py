@@ -41,7 +41,7 @@ PEAK_BF16 = 2.5e15         # MI355X dense bf16 MFMA, flop/s
 # kernel, launch-plan and helper sources); any change to those reports
 # traffic as null until the counters are retaken.
 COUNTED_TRAFFIC = {
-    "sources_sha256": "34a4a7b91e2973e518940e5fd911460b50ee1f26b2f3529cc27ddf788853a52b",
+    "sources_sha256": "ab4dc1228a92308ea9c01f5b71b5aec176ac3f0f6ad85711bf119aa339b8b18f",
     "bytes_per_launch": 1340.30e6,
 }
 TRAFFIC_SOURCES = ('gemv.hip', 'device.hpp', 'internal.hpp', 'api.cpp')
@@ -195,10 +195,10 @@ def pct(v, q):
     return v[min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))]
 
 
-def route_names(fp8w, m, calls):
+def route_names(fp8w, m, calls, fmt="block"):
     """The kernel families AUTO takes for these single calls ("valu", "mfma")."""
     names = {fp8w.ROUTE_VALU: "valu", fp8w.ROUTE_MFMA: "mfma"}
-    got = sorted({names[fp8w.fp8w_gemv_auto_route(m, c.shape[0], c.shape[1])] for (_, c, _, _) in calls})
+    got = sorted({names[fp8w.fp8w_gemv_auto_route(m, c.shape[0], c.shape[1], fmt)] for (_, c, _, _) in calls})
     return "+".join(got)
 
 
@@ -715,7 +715,7 @@ def bench_route(torch, fp8w, lean, timer, W, args, log):
                 x = (torch.randn((m, k), device="cuda", generator=gen)).to(torch.bfloat16)
                 calls = [(x, c, s, torch.empty((m, n), dtype=torch.bfloat16, device="cuda")) for c, s in copies]
                 nb = len(calls) * (gemv_bytes_block(m, n, k) if fmt == "block" else gemv_bytes_mx(m, n, k))
-                row = {"auto": names[fp8w.fp8w_gemv_auto_route(m, n, k)], "calls_per_pass": len(calls)}
+                row = {"auto": names[fp8w.fp8w_gemv_auto_route(m, n, k, fmt)], "calls_per_pass": len(calls)}
                 for rname, r in (("valu", fp8w.ROUTE_VALU), ("mfma", fp8w.ROUTE_MFMA)):
                     if r == fp8w.ROUTE_VALU and m > 8:
                         continue

@@ -46,7 +46,7 @@ MX_GROUP = 32
 _P, _I64, _I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
 SIGNATURES = {
     "fp8w_scale_bytes": (_I64, [_I, _I64, _I64]),
-    "fp8w_gemv_auto_route": (_I, [_I64, _I64, _I64]),
+    "fp8w_gemv_auto_route": (_I, [_I, _I64, _I64, _I64]),
     "fp8w_quantize": (_I, [_P, _I64, _I64, _I, _P, _P, _P, _I64, _P]),
     "fp8w_dequantize": (_I, [_P, _P, _I, _I64, _I64, _P, _P]),
     "fp8w_gemv": (_I, [_P, _I64, _P, _P, _I, _I64, _I64, _P, _I, _P]),
@@ -255,10 +255,11 @@ def fp8w_gemv(x, codes, scales, fmt: str = "block", y=None, route=0, stream=None
     return y
 
 
-def fp8w_gemv_auto_route(m: int, n: int, k: int) -> int:
+def fp8w_gemv_auto_route(m: int, n: int, k: int, fmt: str = "block") -> int:
     """The kernel family AUTO takes for a single GEMV of m activation rows on an
-    [n, k] weight: ROUTE_VALU or ROUTE_MFMA (ROUTE_AUTO when out of range)."""
-    return int(lib().fp8w_gemv_auto_route(int(m), int(n), int(k)))
+    [n, k] weight with `fmt` scales: ROUTE_VALU or ROUTE_MFMA (ROUTE_AUTO when
+    out of range)."""
+    return int(lib().fp8w_gemv_auto_route(_format_id(fmt), int(m), int(n), int(k)))
 
 
 def fp8w_gemm(x, codes, scales, fmt: str = "block", y=None, workspace=None, stream=None):

@@ -37,7 +37,9 @@ constexpr int kValuMaxM = 8;
 //    (block) and 4-14 % (MX) faster on MFMA), after m = 3 on the rest,
 //    after m = 4 on weights up to 8192 x 4096, and after m = 5 on K = 4096
 //    weights up to 6144 rows (+2 to +13 % at m = 5; at m = 6 they lose up
-//    to 4 %).
+//    to 4 %).  With MX scales the VALU route keeps m = 4 on every weight
+//    below 32768 rows: [24576x4096] 5-7 % and [4096x12288] 3-4 % faster in
+//    three runs of the sweep, where block scales are 1-5 % faster on MFMA.
 //  - Grouped: the streaming VALU kernel at m = 1; VALU tiles at m = 2 for
 //    block-scaled formats (+4 % on the projection set, +16 % on dense
 //    layers), while MX at m = 2 is 6 % faster on the streaming MFMA kernel.
@@ -117,18 +119,18 @@ fp8w_status check_gemv(const uint16_t* x, int64_t m, const uint8_t* codes, const
 fp8w_status gemv_any(const uint16_t* x, int64_t m, const uint8_t* codes, const void* scales, int format,
                      int64_t n, int64_t k, uint16_t* y, fp8w_route route, void* stream);
 
-bool auto_valu_single(int64_t m, int64_t n, int64_t k) {
+bool auto_valu_single(int64_t m, int64_t n, int64_t k, bool mx) {
   return m < kAutoValuMaxM || (m == kAutoValuMaxM && n <= kAutoValuM3MaxN) ||
-         (m == 4 && n <= kAutoValuM4MaxN && k <= kAutoValuM4MaxK) ||
+         (m == 4 && (mx ? n <= kAutoValuM3MaxN : n <= kAutoValuM4MaxN && k <= kAutoValuM4MaxK)) ||
          (m == 5 && n <= kAutoValuM5MaxN && k >= kAutoValuM5MinK && k <= kAutoValuM4MaxK);
 }
 
 bool auto_valu_grouped(int64_t m, bool mx) { return m == 1 || (m == 2 && !mx); }
 
-int resolve_route(fp8w_route route, int64_t m, int64_t n, int64_t k) {
+int resolve_route(fp8w_route route, int64_t m, int64_t n, int64_t k, bool mx) {
   if (route == FP8W_ROUTE_VALU) return 1;
   if (route == FP8W_ROUTE_MFMA) return 2;
-  return auto_valu_single(m, n, k) ? 1 : 2;
+  return auto_valu_single(m, n, k, mx) ? 1 : 2;
 }
 
 int resolve_route_grouped(fp8w_route route, int64_t m, bool mx) {
@@ -139,9 +141,9 @@ int resolve_route_grouped(fp8w_route route, int64_t m, bool mx) {
 
 }  // namespace
 
-FP8W_API fp8w_route fp8w_gemv_auto_route(int64_t m, int64_t n, int64_t k) {
-  if (m < 1 || m > FP8W_MAX_M || !dims_ok(n, k)) return FP8W_ROUTE_AUTO;
-  return auto_valu_single(m, n, k) ? FP8W_ROUTE_VALU : FP8W_ROUTE_MFMA;
+FP8W_API fp8w_route fp8w_gemv_auto_route(fp8w_format format, int64_t m, int64_t n, int64_t k) {
+  if (!format_ok(format) || m < 1 || m > FP8W_MAX_M || !dims_ok(n, k)) return FP8W_ROUTE_AUTO;
+  return auto_valu_single(m, n, k, format == FP8W_FORMAT_MX) ? FP8W_ROUTE_VALU : FP8W_ROUTE_MFMA;
 }
 
 FP8W_API int64_t fp8w_scale_bytes(fp8w_format format, int64_t n, int64_t k) {
@@ -196,7 +198,7 @@ fp8w_status gemv_any(const uint16_t* x, int64_t m, const uint8_t* codes, const v
   const fp8w_status st = check_gemv(x, m, codes, scales, format, n, k, y, route);
   if (st != FP8W_OK) return st;
   const fp8w::GemvJob job{x, codes, scales, y, (int32_t)n, (int32_t)k, 0, format};
-  return from_hip(fp8w::launch_gemv(job, (int)m, format == FP8W_FORMAT_MX, resolve_route(route, m, n, k),
+  return from_hip(fp8w::launch_gemv(job, (int)m, format == FP8W_FORMAT_MX, resolve_route(route, m, n, k, format == FP8W_FORMAT_MX),
                                     static_cast<hipStream_t>(stream)));
 }
 

@@ -91,10 +91,10 @@ typedef enum fp8w_status {
  * SIMT for M <= 8, tensor-core mma for 9 <= M <= 32): VALU serves
  * 1 <= m <= 8 only; MFMA serves 1 <= m <= 32.  AUTO follows the crossovers
  * measured on MI355X: single calls take VALU for m <= 2, for m = 3 on
- * weights of fewer than 32768 rows, for m = 4 on
- * weights of at most 8192 rows and K <= 4096, and for m = 5 on weights of
- * at most 6144 rows and 3072 < K <= 4096 (fp8w_gemv_auto_route gives the
- * choice); grouped launches take VALU for m = 1, and for m = 2 on every
+ * weights of fewer than 32768 rows, for m = 4 on weights of at most 8192
+ * rows and K <= 4096 (MX: fewer than 32768 rows), and for m = 5 on weights
+ * of at most 6144 rows and 3072 < K <= 4096 (fp8w_gemv_auto_route gives
+ * the choice); grouped launches take VALU for m = 1, and for m = 2 on every
  * format but MX; MFMA otherwise.  Within a route the
  * kernel also depends on n and k (weights with many rows take the streaming
  * kernels; K above 3072 is walked in 3072- or 4096-column segments) and, for
@@ -202,10 +202,11 @@ fp8w_status fp8w_gemv_mx(const uint16_t* x, int64_t m, const uint8_t* codes,
                          uint16_t* y, void* stream);
 
 /* The route AUTO takes for a single-call GEMV of m activation rows on an
- * [n, k] weight (any scale format): FP8W_ROUTE_VALU or FP8W_ROUTE_MFMA, or
- * FP8W_ROUTE_AUTO when m, n or k is out of range (m outside 1..32, n or k
- * outside 1..2^31-1).  Pure host function; touches no device state. */
-fp8w_route fp8w_gemv_auto_route(int64_t m, int64_t n, int64_t k);
+ * [n, k] weight with scales of the given format: FP8W_ROUTE_VALU or
+ * FP8W_ROUTE_MFMA, or FP8W_ROUTE_AUTO when the format is unknown or m, n or
+ * k is out of range (m outside 1..32, n or k outside 1..2^31-1).  Pure host
+ * function; touches no device state. */
+fp8w_route fp8w_gemv_auto_route(fp8w_format format, int64_t m, int64_t n, int64_t k);
 
 /* The same two GEMVs with an explicit kernel family, for A/B measurement
  * and for testing every route at every m.  FP8W_ROUTE_AUTO is identical to

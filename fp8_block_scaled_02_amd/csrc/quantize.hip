@@ -173,7 +173,11 @@ __device__ __forceinline__ float pow2_neg(int e) { return __uint_as_float((uint3
 // t + 256, ... (every load instruction reads 4 KB contiguous), and the four
 // lanes 4g .. 4g+3 of a pass form one group.  All of a thread's loads are
 // issued before any encode, so each wave keeps kMxUnits * 1 KB in flight.
-constexpr int kMxUnits = 4;
+// Two units per thread, graph-captured single calls on MI355X (µs per call,
+// 1 / 2 / 3 / 4 / 5 units): [8192x2560] 13.47 / 12.09 / 12.44 / 12.72 /
+// 12.97, [2560x3072] 6.48 / 5.91 / 6.07 / 6.17 / 5.97, [6656x2560] 11.37 /
+// 10.25 / 10.75 / 10.92 / 11.14; grouped launches +1-2 % over four.
+constexpr int kMxUnits = 2;
 
 // Units t0, t0 + 256, ..., t0 + 256 * (kMxUnits - 1) of the flat unit array
 // (threads_total units).

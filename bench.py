@@ -41,7 +41,7 @@ PEAK_BF16 = 2.5e15         # MI355X dense bf16 MFMA, flop/s
 # kernel, launch-plan and helper sources); any change to those reports
 # traffic as null until the counters are retaken.
 COUNTED_TRAFFIC = {
-    "sources_sha256": "ab4dc1228a92308ea9c01f5b71b5aec176ac3f0f6ad85711bf119aa339b8b18f",
+    "sources_sha256": "db5809d2bd54c569976fb5ef800504cd512b54428f817fe010356446afe70e04",
     "bytes_per_launch": 1340.30e6,
 }
 TRAFFIC_SOURCES = ('gemv.hip', 'device.hpp', 'internal.hpp', 'api.cpp')

@@ -32,19 +32,19 @@ constexpr int kValuMaxM = 8;
 //    kernels within 1.5 % of the same HBM bytes), so every shape has one
 //    crossover, later on shorter weights.  Graph-captured passes over every
 //    workload shape (N 2560..151936, K 2048..12288, block and MX scales,
-//    m = 2..8) put it after m = 2 on weights of 32768 rows or more (where
-//    the MFMA route streams: the [151936x2048] lm_head at m = 3 is 2 %
-//    (block) and 4-14 % (MX) faster on MFMA), after m = 3 on the rest,
-//    after m = 4 on weights up to 8192 x 4096, and after m = 5 on K = 4096
-//    weights up to 6144 rows (+2 to +13 % at m = 5; at m = 6 they lose up
-//    to 4 %).  With MX scales the VALU route keeps m = 4 on every weight
-//    below 32768 rows: [24576x4096] 5-7 % and [4096x12288] 3-4 % faster in
-//    three runs of the sweep, where block scales are 1-5 % faster on MFMA.
+//    m = 2..8) put it after m = 3, after m = 4 on weights up to 8192 x
+//    4096, and after m = 5 on K = 4096 weights up to 6144 rows (+2 to +13 %
+//    at m = 5; at m = 6 they lose up to 4 %).  With MX scales it falls
+//    after m = 2 on weights of 32768 rows or more, where the MFMA route
+//    streams (the [151936x2048] lm_head at m = 3: 4 % faster on MFMA, where
+//    block scales are 1.6-4.4 % faster on VALU in six runs), and after
+//    m = 4 on every weight below that ([24576x4096] 5 % and [4096x12288]
+//    4 % faster on VALU in repeated runs, where block scales are 1-5 %
+//    faster on MFMA).
 //  - Grouped: the streaming VALU kernel at m = 1; VALU tiles at m = 2 for
 //    block-scaled formats (+4 % on the projection set, +16 % on dense
 //    layers), while MX at m = 2 is 6 % faster on the streaming MFMA kernel.
-constexpr int kAutoValuMaxM = 3;
-constexpr int64_t kAutoValuM3MaxN = 32768 - 1;
+constexpr int64_t kAutoValuMxMaxN = 32768 - 1;
 constexpr int kAutoValuM4MaxN = 8192;
 constexpr int kAutoValuM4MaxK = 4096;
 constexpr int kAutoValuM5MaxN = 6144;
@@ -120,9 +120,14 @@ fp8w_status gemv_any(const uint16_t* x, int64_t m, const uint8_t* codes, const v
                      int64_t n, int64_t k, uint16_t* y, fp8w_route route, void* stream);
 
 bool auto_valu_single(int64_t m, int64_t n, int64_t k, bool mx) {
-  return m < kAutoValuMaxM || (m == kAutoValuMaxM && n <= kAutoValuM3MaxN) ||
-         (m == 4 && (mx ? n <= kAutoValuM3MaxN : n <= kAutoValuM4MaxN && k <= kAutoValuM4MaxK)) ||
-         (m == 5 && n <= kAutoValuM5MaxN && k >= kAutoValuM5MinK && k <= kAutoValuM4MaxK);
+  switch (m) {
+    case 1:
+    case 2: return true;
+    case 3: return !mx || n <= kAutoValuMxMaxN;
+    case 4: return mx ? n <= kAutoValuMxMaxN : n <= kAutoValuM4MaxN && k <= kAutoValuM4MaxK;
+    case 5: return n <= kAutoValuM5MaxN && k >= kAutoValuM5MinK && k <= kAutoValuM4MaxK;
+    default: return false;
+  }
 }
 
 bool auto_valu_grouped(int64_t m, bool mx) { return m == 1 || (m == 2 && !mx); }

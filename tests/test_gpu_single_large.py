@@ -134,11 +134,20 @@ def test_valu_wide_single_call(fp8w, oracle_mod, weights, fmt, m, k):
 
 # MFMA: the streaming kernel with one job from 32768 rows, and from 16384
 # rows when m > 16; m = 16 at 16405 rows stays on the single-call kernel
+# (forced MFMA: AUTO takes VALU at m = 3 outside MX; the same as AUTO above)
 @pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("n,m", [(32813, 3), (32813, 9), (32813, 16), (32813, 17), (32813, 32),
                                  (16405, 16), (16405, 17), (16405, 32)])
 def test_mfma_stream_single_job(fp8w, oracle_mod, weights, fmt, n, m):
-    _check(fp8w, oracle_mod, weights, n, 1040, m, fmt, 0)
+    import fp8_block_scaled_02_amd as F
+    _check(fp8w, oracle_mod, weights, n, 1040, m, fmt, F.ROUTE_MFMA)
+
+
+# AUTO at m = 3 on many rows: the VALU wide tiles outside MX, the streaming
+# MFMA kernel with MX
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_auto_m3_many_rows(fp8w, oracle_mod, weights, fmt):
+    _check(fp8w, oracle_mod, weights, 32813, 1040, 3, fmt, 0)
 
 
 # forced MFMA at m = 1 and 2 on the streaming kernel, K over several

@@ -492,7 +492,7 @@ FP8W_API fp8w_status fp8w_gemv_grouped(const fp8w_grouped_plan* plan, void* stre
         fp8w::gemv_mfma_stream_lds(plan->m, seg) > fp8w::gemv_mfma_stream_lds_limit())
       return FP8W_ERR_SHAPE;
     return from_hip(fp8w::launch_gemv_mfma_stream(table, plan->count, plan->blocks, plan->tiles,
-                                                  plan->tiles_per_block, plan->m, seg, mx,
+                                                  plan->tiles_per_block, plan->m, seg, plan->format,
                                                   plan->mx_packed8 == 1, s));
   }
   if (plan->seg_cols != 0 && !(plan->seg_cols == 4096 && plan->m == 1 && plan->tiles_per_block == 0))

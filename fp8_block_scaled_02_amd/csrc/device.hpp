@@ -52,6 +52,10 @@ __device__ __forceinline__ void st_stream_u2(void* p, size_t byte_offset, uint2 
                               (__attribute__((address_space(1))) u32x2*)((char*)p + byte_offset));
 }
 
+// s_waitcnt vmcnt(0), leaving the LDS/scalar and export counters alone
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+__device__ __forceinline__ void vm_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // bf16 halves of a packed dword, widened exactly to fp32.
 __device__ __forceinline__ float bf16_lo(uint32_t d) { return __uint_as_float(d << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }

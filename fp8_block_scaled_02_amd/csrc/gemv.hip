@@ -112,6 +112,16 @@ __device__ __forceinline__ float output_scale(const GemvJob& j, int row) {
   return 1.0f;
 }
 
+// Index into the block-scale grid of 128-column block kb for the 128-row
+// block holding row0, both clamped into the grid: kernels that request the
+// scale ahead of its use load it unconditionally from here (a load behind a
+// branch, or joined with a default, gets a copy after the join, and the copy
+// waits for the load -- and, since vector-memory waits count in issue order,
+// for every load the wave issued before it).
+__device__ __forceinline__ size_t block_scale_at(const GemvJob& j, int row0, int kb, int nkb) {
+  return (size_t)(min(row0, j.n - 1) / kTile) * nkb + min(kb, nkb - 1);
+}
+
 // sum_j x[j] * dec(code[j]) over one 16-byte chunk (16 codes, 16 bf16 x).
 __device__ __forceinline__ float dot16(const bf16x2 (&w)[8], uint4 x0, uint4 x1) {
   float p = 0.0f;
@@ -789,65 +799,27 @@ constexpr int kPanelBytes = 16 * kPanelCols;    // LDS bytes of one wave's panel
 template <bool MX>
 struct Panel {
   uint4 v[4];                // lane l: row 4q + l/16 of the tile, bytes 16*(l%16)
-  // block: the scale of each 128-column block (a scalar load when fp32);
-  // MX: the exponent byte of each (block, chunk) of the A layout, as loaded
-  // (panel_scales converts it where the MFMA step uses it)
-  typename std::conditional<MX, uint32_t, float>::type s[MX ? 4 : 2];
+  // the scales as loaded (panel_scales converts them where the MFMA step
+  // uses them): MX: the exponent byte of each (block, chunk) of the A layout;
+  // otherwise the scale of each 128-column block, fp32 (f) or bf16 bits (h)
+  uint32_t s[4];
+  float f[2];
+  uint16_t h[2];
   u32x2 e8;                  // MX, packed rows: the row's 8 exponent bytes of the panel
 };
 
-// Request panel p (columns [256p, 256p + 256)) of the 16-row tile at row0,
-// with its scales.  Rows >= n and columns >= k load zeros.  PK (MX only):
-// every exponent row starts 8-byte aligned (groups % 8 == 0 and an aligned
-// array; the host checks, mx_rows_packed8), so one 8-byte load per row
-// brings the panel's exponents.  It is a template choice, not a branch:
-// with both loads behind a runtime branch the compiler joins their results
-// with copies, and a copy waits for its load, and so for every weight load
-// the wave issued before it.
-template <bool MX, bool PK = false>
-__device__ __forceinline__ void panel_issue(const GemvJob& j, int row0, int p, bool live, int nkb,
-                                            int groups, Panel<MX>& r) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int col = p * kPanelCols + 16 * (lane & 15);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int row = row0 + 4 * q + (lane >> 4);
-    r.v[q] = make_uint4(0, 0, 0, 0);
-    if (live && row < j.n && col < j.k) r.v[q] = ld_stream_u4(j.codes, (size_t)row * j.k + col);
-  }
-  if (MX) {
-    // Lane l needs the exponents of groups 8p + 2c + (l/16)/2, c = 0..3, of
-    // row l%16: all inside the row's 8 bytes for this panel (PK: one 8-byte
-    // load; otherwise one byte load per chunk).  The loads are
-    // unconditional, from a row and group clamped into the weight: rows and
-    // columns outside it have zero codes, so the exponent they borrow only
-    // multiplies zeros.  No select or copy follows a load, so nothing waits
-    // for one before the MFMA step converts it.
-    const int row = min(row0 + (lane & 15), j.n - 1);
-    const uint8_t* __restrict__ e8 = static_cast<const uint8_t*>(j.scales);
-    if (PK) {
-      const int pc = min(p, (j.k - 1) / kPanelCols);
-      r.e8 = ld_global<u32x2>(e8, (size_t)row * groups + 8 * pc);
-    } else {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int kx = min(p * kPanelCols + 64 * c + 16 * (lane >> 4), j.k - 1);   // block c/2, chunk c%2
-        r.s[c] = ld_global<uint8_t>(e8, (size_t)row * groups + kx / kGroup);
-      }
-    }
-  } else {
-    r.s[0] = r.s[1] = 0.0f;
-    if (live && row0 < j.n) {
-      r.s[0] = block_scale(j, row0, 2 * p, nkb);
-      if (2 * p + 1 < nkb) r.s[1] = block_scale(j, row0, 2 * p + 1, nkb);
-    }
-  }
-}
+// The scale format of a panel request.  kSfAny: any non-MX format, chosen at
+// run time, each block scale loaded only where it exists (kernels that
+// request every panel of a call up front).  kFmtBlock, kFmtBlockBf16: that
+// block grid, loaded unconditionally from a clamped index (kernels that
+// pipeline panels in a loop).  kFmtRow: no block scale (row and tensor
+// scales multiply the outputs).
+constexpr int kSfAny = -1;
 
 // The panel's scales as the MFMA step uses them: block: per 128-column
 // block; MX: 2^(E-127) per (block, chunk) of the A layout (lane l reads the
 // exponents of groups 8p + 2c + (l/16)/2, c = 0..3, of row l%16).
-template <bool MX, bool PK = false>
+template <bool MX, bool PK = false, int SF = kSfAny>
 __device__ __forceinline__ void panel_scales(const Panel<MX>& r, float (&sc)[MX ? 4 : 2]) {
   if (MX) {
     if (PK) {
@@ -859,9 +831,23 @@ __device__ __forceinline__ void panel_scales(const Panel<MX>& r, float (&sc)[MX 
 #pragma unroll
       for (int c = 0; c < 4; ++c) sc[c] = mx_scale((uint8_t)r.s[c]);
     }
-  } else {
+    // The scales are built here, not where the MFMA step uses them: left to
+    // the compiler, the conversion moves after the slot's next request, the
+    // exponent registers stay live across it, the request loads elsewhere,
+    // and the copy back at the loop's end waits for it.
 #pragma unroll
-    for (int b = 0; b < 2; ++b) sc[b] = r.s[b];
+    for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(sc[c]));
+  } else {
+    // A block scale is the same in every lane (one 16-row tile, one
+    // block): taken into a scalar register here, its vector register is free
+    // before the slot's next request, which can then load into it (a request
+    // into another register would need a copy back at the loop's end, and
+    // the copy would wait for it).
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const float v = SF == kFmtBlockBf16 ? __uint_as_float((uint32_t)r.h[b] << 16) : r.f[b];
+      sc[b] = SF == kFmtRow ? 1.0f : __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+    }
   }
 }
 
@@ -936,8 +922,14 @@ __device__ __forceinline__ void panel_mfma(const uint4 (&a)[2][2], const float* 
 }
 
 // y^T of a 16-row tile from the D layout; columns (activation rows) >= m_rows
-// and rows >= n are not written.
-template <int MT>
+// and rows >= n are not written.  OS: the format may scale rows or the whole
+// weight (kFmtRow, kFmtTensor), whose scales are loaded here and used under
+// the bounds branches; the explicit wait at the end (where those formats have
+// just waited for their scale loads anyway) keeps the compiler from treating
+// a load on a path that skipped its use as still pending, which would make
+// it wait for all vector memory at the top of a caller's panel loop.  Kernels
+// that pipeline panels across tiles take OS = false for the other formats.
+template <int MT, bool OS = true>
 __device__ __forceinline__ void store_tile(const GemvJob& j, int row0, int m_rows, const f32x4 (&acc)[MT],
                                            float factor = 1.0f) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -946,7 +938,7 @@ __device__ __forceinline__ void store_tile(const GemvJob& j, int row0, int m_row
   for (int jj = 0; jj < 4; ++jj) {
     const int r = row0 + 4 * g + jj;
     if (r >= j.n) continue;
-    const float os = factor * output_scale(j, r);
+    const float os = OS ? factor * output_scale(j, r) : factor;
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       const int mcol = 16 * t + i;
@@ -954,6 +946,7 @@ __device__ __forceinline__ void store_tile(const GemvJob& j, int row0, int m_row
         st_global<uint16_t>(j.y, ((size_t)mcol * j.n + r) * 2, (uint16_t)f32_to_bf16_rne(acc[t][jj] * os));
     }
   }
+  if (OS) vm_wait_all();
 }
 
 // ------------------------------------------------------- MFMA streaming --
@@ -984,12 +977,18 @@ __device__ __forceinline__ void tile_loads(const GemvJob& j, int row0, TileLoads
     t.off[q] = (uint64_t)min(4 * q + (lane >> 4), last) * (uint64_t)j.k + 16 * (lane & 15);
 }
 
-// Panel p of the tile: as panel_issue, with the row offsets of `t`.  Every
-// load is in bounds.  A partial last panel either clamps its columns to the
-// row's last 16 bytes, whose codes then meet the zeros that pad x past k in
-// LDS (ZT = false: the streaming kernel), or loads zeros past k (ZT = true:
-// kernels whose x operands are not zero there).
-template <bool MX, bool PK, bool ZT = false>
+// Request panel p (columns [256p, 256p + 256)) of the 16-row tile at row0,
+// with its scales, through the row offsets of `t`.  Every load is in bounds.
+// A partial last panel either clamps its columns to the row's last 16 bytes,
+// whose codes then meet the zeros that pad x past k in LDS (ZT = false: the
+// streaming kernel), or loads zeros past k (ZT = true: kernels whose x
+// operands are not zero there).  PK (MX only): every exponent row starts
+// 8-byte aligned (groups % 8 == 0 and an aligned array; the host checks,
+// mx_rows_packed8), so one 8-byte load per row brings the panel's exponents.
+// It is a template choice, not a branch: with both loads behind a runtime
+// branch the compiler joins their results with copies, and a copy waits for
+// its load, and so for every weight load the wave issued before it.
+template <bool MX, bool PK, bool ZT = false, int SF = kSfAny>
 __device__ __forceinline__ void panel_issue_tile(const GemvJob& j, const TileLoads& t, int row0, int p, bool live,
                                                  int nkb, int groups, Panel<MX>& r) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -1027,18 +1026,27 @@ __device__ __forceinline__ void panel_issue_tile(const GemvJob& j, const TileLoa
         r.s[c] = ld_global<uint8_t>(e8, (size_t)row * groups + kx / kGroup);
       }
     }
-  } else {
-    r.s[0] = r.s[1] = 0.0f;
+  } else if (SF == kFmtBlock) {
+    // a block past k (clamped to the last one) multiplies zero products,
+    // and the scale of a tile past the last row is never stored
+#pragma unroll
+    for (int b = 0; b < 2; ++b) r.f[b] = ld_global<float>(j.scales, block_scale_at(j, row0, 2 * p + b, nkb) * 4);
+  } else if (SF == kFmtBlockBf16) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+      r.h[b] = ld_global<uint16_t>(j.scales, block_scale_at(j, row0, 2 * p + b, nkb) * 2);
+  } else if (SF == kSfAny) {
+    r.f[0] = r.f[1] = 0.0f;
     if (live && row0 < j.n) {
-      r.s[0] = block_scale(j, row0, 2 * p, nkb);
-      if (2 * p + 1 < nkb) r.s[1] = block_scale(j, row0, 2 * p + 1, nkb);
+      r.f[0] = block_scale(j, row0, 2 * p, nkb);
+      if (2 * p + 1 < nkb) r.f[1] = block_scale(j, row0, 2 * p + 1, nkb);
     }
   }
 }
 
 // Four waves per SIMD (at most 128 VGPRs): two 8-wave workgroups per CU, so
 // one workgroup's staging barriers are covered by the other's loads.
-template <int MT, int NW, int D, bool MX, bool ONE, bool PK>
+template <int MT, int NW, int D, bool MX, bool ONE, bool PK, int SF>
 __global__ __launch_bounds__(NW * kWave, 4) void k_gemv_mfma_stream(const GemvJob* __restrict__ table,
                                                                  int njobs, GemvJob one, int total_tiles,
                                                                  int tiles_per_block, int m_rows,
@@ -1092,8 +1100,8 @@ __global__ __launch_bounds__(NW * kWave, 4) void k_gemv_mfma_stream(const GemvJo
 
   auto issue = [&](Panel<MX>& r) {
     const bool live = it < t_end;
-    panel_issue_tile<MX, PK>(ij, tl, (it - ij.item0) * kRows + 16 * wave, ip, live, (ij.k + kTile - 1) / kTile,
-                             (ij.k + kGroup - 1) / kGroup, r);
+    panel_issue_tile<MX, PK, false, SF>(ij, tl, (it - ij.item0) * kRows + 16 * wave, ip, live,
+                                        (ij.k + kTile - 1) / kTile, (ij.k + kGroup - 1) / kGroup, r);
     if (!live) return;
     if (++ip == i_np) {
       ip = 0;
@@ -1131,26 +1139,42 @@ __global__ __launch_bounds__(NW * kWave, 4) void k_gemv_mfma_stream(const GemvJo
       for (int q = 0; q < kStageBatch; ++q)
         if (dst[q] >= 0) *reinterpret_cast<uint4*>(xs + dst[q]) = v[q];
     }
+    // Every staged load has been waited for by its store, but the stores
+    // are conditional and the compiler cannot pair them with the loads: it
+    // would wait for all vector memory at the top of the panel loop, on
+    // every pass.  An explicit wait here (where staging has already drained
+    // the weight loads requested before it) tells it nothing is pending.
+    vm_wait_all();
   };
 
+  // Panel steps are fenced off from the scheduler (sched_barrier): left
+  // free, it gathers the requests of several slots in one place, so a wait
+  // for one slot would also wait for the next.
   Panel<MX> slot[D];
 #pragma unroll
-  for (int s = 0; s < D; ++s) issue(slot[s]);
+  for (int s = 0; s < D; ++s) {
+    issue(slot[s]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   stage(cj, 0);
   __syncthreads();
 
   f32x4 acc[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  bool done = false;
-  while (!done) {
+  // One exit, after every D panel steps: an exit between steps becomes a
+  // branch to a block shared with the loop's head, reached there with the
+  // slots' requests in another order, and the compiler, merging the two
+  // orders, would wait at the head for every request in flight.  So the last
+  // pass may consume up to D - 1 panels past the run: they were requested as
+  // dead (zero codes), and a tile past the run is neither stored nor staged.
+  for (;;) {
 #pragma unroll
     for (int s = 0; s < D; ++s) {
-      if (done) break;
       uint4 a[2][2];
       panel_to_a(slot[s].v, pbuf, a);
       float sc[MX ? 4 : 2];
-      panel_scales<MX, PK>(slot[s], sc);
+      panel_scales<MX, PK, SF>(slot[s], sc);
       issue(slot[s]);
       const int kseg = (cp % seg_panels) * kPanelCols;   // panel start within the staged segment
       panel_mfma<MT, MX>(a, sc, [&](int t, int b, int c, uint4& B0, uint4& B1) {
@@ -1159,30 +1183,32 @@ __global__ __launch_bounds__(NW * kWave, 4) void k_gemv_mfma_stream(const GemvJo
         B1 = *reinterpret_cast<const uint4*>(bp + bunit[c][1]);
       }, acc);
       if (++cp == c_np) {   // tile done
-        store_tile<MT>(cj, (ct - cj.item0) * kRows + 16 * wave, m_rows, acc);
+        if (ct < t_end) store_tile<MT, SF == kFmtRow>(cj, (ct - cj.item0) * kRows + 16 * wave, m_rows, acc);
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         cp = 0;
-        if (++ct >= t_end) {
-          done = true;
-        } else if (ct >= c_bound) {   // the run enters the next job
-          load_job<ONE>(jobs, ++jn, cj);
-          c_bound = job_end<ONE>(jobs, jn);
-          c_np = (cj.k + kPanelCols - 1) / kPanelCols;
-          __syncthreads();
-          stage(cj, 0);
-          __syncthreads();
-        } else if (c_np > seg_panels) {   // next tile of a multi-segment job
-          __syncthreads();
-          stage(cj, 0);
-          __syncthreads();
+        if (++ct < t_end) {
+          if (ct >= c_bound) {   // the run enters the next job
+            load_job<ONE>(jobs, ++jn, cj);
+            c_bound = job_end<ONE>(jobs, jn);
+            c_np = (cj.k + kPanelCols - 1) / kPanelCols;
+            __syncthreads();
+            stage(cj, 0);
+            __syncthreads();
+          } else if (c_np > seg_panels) {   // next tile of a multi-segment job
+            __syncthreads();
+            stage(cj, 0);
+            __syncthreads();
+          }
         }
-      } else if (cp % seg_panels == 0) {   // next segment of this tile
+      } else if (cp % seg_panels == 0 && ct < t_end) {   // next segment of this tile
         __syncthreads();
         stage(cj, cp * kPanelCols);
         __syncthreads();
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    if (ct >= t_end) return;
   }
 }
 
@@ -1631,15 +1657,15 @@ constexpr int64_t kDirect8MaxRows = 4096;
 // split each workgroup's panels over 8 waves, on more rows over 4.
 constexpr int64_t kDirectT2Wave8MaxRows = 8192;
 
-template <int MT, bool MX, bool ONE, bool PK>
+template <int MT, bool MX, bool ONE, bool PK, int SF>
 constexpr auto mfma_stream_kernel() {
-  return &k_gemv_mfma_stream<MT, kMfmaStreamWaves, 2, MX, ONE, PK>;
+  return &k_gemv_mfma_stream<MT, kMfmaStreamWaves, 2, MX, ONE, PK, SF>;
 }
 
 // The kernel needs more than the default 64 KB of dynamic LDS: raise the
 // limit once per device and variant.  Host threads may race here; setting
 // the attribute twice is harmless, so a relaxed flag suffices.
-template <int MT, bool MX, bool ONE, bool PK>
+template <int MT, bool MX, bool ONE, bool PK, int SF>
 hipError_t allow_mfma_stream_lds() {
   static std::atomic<bool> done[64];
   int dev = 0;
@@ -1647,7 +1673,7 @@ hipError_t allow_mfma_stream_lds() {
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
   if (!done[dev].load(std::memory_order_relaxed)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(mfma_stream_kernel<MT, MX, ONE, PK>()),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(mfma_stream_kernel<MT, MX, ONE, PK, SF>()),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kMfmaStreamLds);
     if (e != hipSuccess) return e;
     done[dev].store(true, std::memory_order_relaxed);
@@ -1671,23 +1697,33 @@ hipError_t run_valu_stream(const StreamJobs& l, int64_t blocks, int64_t tiles, i
   return hipGetLastError();
 }
 
-template <int MT, bool MX, bool ONE, bool PK>
+template <int MT, bool MX, bool ONE, bool PK, int SF>
 hipError_t run_mfma_stream(const StreamJobs& l, int64_t blocks, int64_t tiles, int tiles_per_block, int m,
                            int seg_cols, hipStream_t stream);
 
+// The scale format every job of the launch shares selects the variant.
 template <int MT, bool ONE>
 hipError_t dispatch_mfma_stream_mt(const StreamJobs& l, int64_t blocks, int64_t tiles, int tiles_per_block,
-                                   int m, int seg_cols, bool mx, bool pk, hipStream_t s) {
-  if (!mx) return run_mfma_stream<MT, false, ONE, false>(l, blocks, tiles, tiles_per_block, m, seg_cols, s);
-  return pk ? run_mfma_stream<MT, true, ONE, true>(l, blocks, tiles, tiles_per_block, m, seg_cols, s)
-            : run_mfma_stream<MT, true, ONE, false>(l, blocks, tiles, tiles_per_block, m, seg_cols, s);
+                                   int m, int seg_cols, int format, bool pk, hipStream_t s) {
+  switch (format) {
+    case kFmtMx:
+      return pk ? run_mfma_stream<MT, true, ONE, true, kFmtMx>(l, blocks, tiles, tiles_per_block, m, seg_cols, s)
+                : run_mfma_stream<MT, true, ONE, false, kFmtMx>(l, blocks, tiles, tiles_per_block, m, seg_cols, s);
+    case kFmtBlock:
+      return run_mfma_stream<MT, false, ONE, false, kFmtBlock>(l, blocks, tiles, tiles_per_block, m, seg_cols, s);
+    case kFmtBlockBf16:
+      return run_mfma_stream<MT, false, ONE, false, kFmtBlockBf16>(l, blocks, tiles, tiles_per_block, m,
+                                                                   seg_cols, s);
+    default:   // kFmtRow, kFmtTensor
+      return run_mfma_stream<MT, false, ONE, false, kFmtRow>(l, blocks, tiles, tiles_per_block, m, seg_cols, s);
+  }
 }
 
 template <bool ONE>
 hipError_t dispatch_mfma_stream(const StreamJobs& l, int64_t blocks, int64_t tiles, int tiles_per_block,
-                                int m, int seg_cols, bool mx, bool pk, hipStream_t s) {
-  return m <= 16 ? dispatch_mfma_stream_mt<1, ONE>(l, blocks, tiles, tiles_per_block, m, seg_cols, mx, pk, s)
-                 : dispatch_mfma_stream_mt<2, ONE>(l, blocks, tiles, tiles_per_block, m, seg_cols, mx, pk, s);
+                                int m, int seg_cols, int format, bool pk, hipStream_t s) {
+  return m <= 16 ? dispatch_mfma_stream_mt<1, ONE>(l, blocks, tiles, tiles_per_block, m, seg_cols, format, pk, s)
+                 : dispatch_mfma_stream_mt<2, ONE>(l, blocks, tiles, tiles_per_block, m, seg_cols, format, pk, s);
 }
 
 // Single calls with many rows take the wide VALU tiles (the streaming
@@ -1815,13 +1851,13 @@ hipError_t launch_mfma_direct(const GemvJob& job, int m, bool mx, bool pk, hipSt
   return hipGetLastError();
 }
 
-template <int MT, bool MX, bool ONE, bool PK>
+template <int MT, bool MX, bool ONE, bool PK, int SF>
 hipError_t run_mfma_stream(const StreamJobs& l, int64_t blocks, int64_t tiles, int tiles_per_block, int m,
                            int seg_cols, hipStream_t stream) {
-  const hipError_t e = allow_mfma_stream_lds<MT, MX, ONE, PK>();
+  const hipError_t e = allow_mfma_stream_lds<MT, MX, ONE, PK, SF>();
   if (e != hipSuccess) return e;
   const size_t lds = (size_t)gemv_mfma_stream_lds(m, seg_cols);
-  hipLaunchKernelGGL((k_gemv_mfma_stream<MT, kMfmaStreamWaves, 2, MX, ONE, PK>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((k_gemv_mfma_stream<MT, kMfmaStreamWaves, 2, MX, ONE, PK, SF>), dim3((unsigned)blocks),
                      dim3(kMfmaStreamWaves * kWave), lds, stream, l.table, l.count, l.one, (int)tiles,
                      tiles_per_block, m, seg_cols);
   return hipGetLastError();
@@ -1852,7 +1888,7 @@ hipError_t launch_gemv(const GemvJob& job, int m, bool mx, int route, hipStream_
     l.one.item0 = 0;
     const int rows = gemv_rows_per_block(route, m, true);
     const int64_t tiles = (job.n + rows - 1) / rows;
-    return dispatch_mfma_stream<true>(l, tiles, tiles, 1, m, gemv_mfma_stream_seg_cols(m, job.k), mx,
+    return dispatch_mfma_stream<true>(l, tiles, tiles, 1, m, gemv_mfma_stream_seg_cols(m, job.k), job.format,
                                       mx && mx_rows_packed8(job.scales, job.k), stream);
   }
   const bool pk = mx && mx_rows_packed8(job.scales, job.k);
@@ -1918,18 +1954,18 @@ hipError_t gemv_mfma_stream_slots(int m, bool mx, int seg_cols, int* slots) {
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess) {
     if (m <= 16) {
-      e = mx ? allow_mfma_stream_lds<1, true, false, false>() : allow_mfma_stream_lds<1, false, false, false>();
+      e = mx ? allow_mfma_stream_lds<1, true, false, false, kFmtMx>() : allow_mfma_stream_lds<1, false, false, false, kFmtBlock>();
       if (e == hipSuccess)
-        e = mx ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_stream_kernel<1, true, false, false>(),
+        e = mx ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_stream_kernel<1, true, false, false, kFmtMx>(),
                                                               threads, lds)
-               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_stream_kernel<1, false, false, false>(),
+               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_stream_kernel<1, false, false, false, kFmtBlock>(),
                                                               threads, lds);
     } else {
-      e = mx ? allow_mfma_stream_lds<2, true, false, false>() : allow_mfma_stream_lds<2, false, false, false>();
+      e = mx ? allow_mfma_stream_lds<2, true, false, false, kFmtMx>() : allow_mfma_stream_lds<2, false, false, false, kFmtBlock>();
       if (e == hipSuccess)
-        e = mx ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_stream_kernel<2, true, false, false>(),
+        e = mx ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_stream_kernel<2, true, false, false, kFmtMx>(),
                                                               threads, lds)
-               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_stream_kernel<2, false, false, false>(),
+               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_stream_kernel<2, false, false, false, kFmtBlock>(),
                                                               threads, lds);
     }
   }
@@ -2025,11 +2061,11 @@ hipError_t launch_gemv_w8a8(const GemvJob& job, const float* x_scale, int m, boo
 }
 
 hipError_t launch_gemv_mfma_stream(const GemvJob* table, int njobs, int64_t blocks, int64_t tiles,
-                                   int tiles_per_block, int m, int seg_cols, bool mx, bool mx_packed8,
+                                   int tiles_per_block, int m, int seg_cols, int format, bool mx_packed8,
                                    hipStream_t stream) {
   const StreamJobs l{table, njobs, GemvJob{}};
-  return dispatch_mfma_stream<false>(l, blocks, tiles, tiles_per_block, m, seg_cols, mx, mx && mx_packed8,
-                                     stream);
+  return dispatch_mfma_stream<false>(l, blocks, tiles, tiles_per_block, m, seg_cols, format,
+                                     format == kFmtMx && mx_packed8, stream);
 }
 
 }  // namespace fp8w

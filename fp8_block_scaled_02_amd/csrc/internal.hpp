@@ -125,9 +125,10 @@ bool mx_rows_packed8(const void* e8m0, int64_t k);
 // MX weights the streaming VALU kernel reads exponents of as dwords: a
 // 4-byte aligned array of a whole number of dwords (n * ceil(k/32) % 4 == 0).
 bool mx_rows_stream(const void* e8m0, int64_t n, int64_t k);
+// `format` is the format every job of the table shares.
 hipError_t launch_gemv_mfma_stream(const GemvJob* device_table, int njobs, int64_t blocks,
                                    int64_t tiles, int tiles_per_block, int m, int seg_cols,
-                                   bool mx, bool mx_packed8, hipStream_t stream);
+                                   int format, bool mx_packed8, hipStream_t stream);
 
 // Read-only pass over `bytes` (a multiple of 16) of device memory, one
 // 32-bit XOR per workgroup into out[0 .. blocks).

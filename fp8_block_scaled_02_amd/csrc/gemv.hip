@@ -1044,6 +1044,63 @@ __device__ __forceinline__ void panel_issue_tile(const GemvJob& j, const TileLoa
   }
 }
 
+// The order a wave walks a tile's panels in.  The tile's K splits into
+// segments of sp panels (the x segments staged in LDS; one segment when x
+// fits whole).  In plain order every wave walks them from the first panel.
+// Rotated, the workgroup visits them starting at segment s0 and wrapping,
+// and inside a segment of len panels each wave starts at its own offset,
+// wave * len / NW, and wraps, so at any moment the workgroups of the chip,
+// and the waves of a workgroup, read different column ranges.  With all of
+// them at the same columns, weights whose row stride is a multiple of 4 KB
+// read slowly: a read-only pass with this kernel's access pattern over
+// [8192 x K] weights on MI355X moves 5.7 / 5.5 / 6.4 TB/s at K = 4096 / 8192
+// / 12288 in plain order and 6.6 / 6.5 / 6.8 rotated (K = 2048..3072 and
+// 4608 / 6144 within 2 % either way).  In the GEMV the rotation gained 3-4 %
+// on the dense layer's K = 4096 / 12288 weights and 1-3 % on lm_head
+// (K = 2048) at M = 4..16, but lost 4 % on lm_head at M = 32, whose
+// segments are two panels long, and 1-2 % on K = 2560 / 3072; so only jobs
+// with K a multiple of 2048 and segments of at least four panels (or one
+// segment) are rotated.  Every field is uniform across the wave; stepping
+// needs no division.
+struct PanelWalk {
+  int sp, nseg, np;   // segment length, segments and panels of the job
+  int seg, len;       // current segment and its panel count
+  int off, pos, cnt;  // the wave's start in the segment, its current panel there, panels done there
+  int segs_done;      // segments of the tile done
+  bool rot;           // rotated order
+
+  __device__ __forceinline__ void start_segment(int wave, int nw) {
+    len = min(sp, np - seg * sp);
+    off = rot ? (wave * len) / nw : 0;
+    pos = off;
+    cnt = 0;
+  }
+  // A new job's first tile: s0 = the workgroup's starting segment if rotated.
+  __device__ __forceinline__ void start_job(int k, int seg_panels, int s0, int wave, int nw) {
+    np = (k + kPanelCols - 1) / kPanelCols;
+    sp = seg_panels;
+    nseg = (np + sp - 1) / sp;
+    rot = k % 2048 == 0 && (sp >= 4 || nseg == 1);
+    seg = rot ? s0 % nseg : 0;
+    segs_done = 0;
+    start_segment(wave, nw);
+  }
+  __device__ __forceinline__ int panel() const { return seg * sp + pos; }
+  __device__ __forceinline__ int seg_col0() const { return seg * sp * kPanelCols; }
+  // One panel on; returns 0 (same segment), 1 (next segment of the tile) or
+  // 2 (tile done: the walk restarts at the tile's first segment).
+  __device__ __forceinline__ int step(int wave, int nw) {
+    ++cnt;
+    if (++pos == len) pos = 0;
+    if (cnt < len) return 0;
+    if (++seg == nseg) seg = 0;
+    const int r = ++segs_done == nseg ? 2 : 1;
+    if (r == 2) segs_done = 0;
+    start_segment(wave, nw);
+    return r;
+  }
+};
+
 // Four waves per SIMD (at most 128 VGPRs): two 8-wave workgroups per CU, so
 // one workgroup's staging barriers are covered by the other's loads.
 template <int MT, int NW, int D, bool MX, bool ONE, bool PK, int SF>
@@ -1085,34 +1142,35 @@ __global__ __launch_bounds__(NW * kWave, 4) void k_gemv_mfma_stream(const GemvJo
   const int st_r0 = threadIdx.x / units_row, st_c0 = threadIdx.x % units_row;
   const int st_dr = (NW * kWave) / units_row, st_dc = (NW * kWave) % units_row;
 
+  // the workgroup's first segment in every tile
+  const int s0 = blockIdx.x;
   int jn = job_of_tile<ONE>(jobs, t_begin);
-  // compute cursor: tile ct, panel cp of job cj
+  // compute cursor: tile ct of job cj, the walk cw through its panels
   GemvJob cj;
   load_job<ONE>(jobs, jn, cj);
   int c_bound = job_end<ONE>(jobs, jn);
-  int c_np = (cj.k + kPanelCols - 1) / kPanelCols;
-  int ct = t_begin, cp = 0;
-  // issue cursor: tile it, panel ip of job ij, D panels ahead
+  PanelWalk cw;
+  cw.start_job(cj.k, seg_panels, s0, wave, NW);
+  int ct = t_begin;
+  // issue cursor: tile it of job ij, the walk iw, D panels ahead
   GemvJob ij = cj;
-  int ijn = jn, i_bound = c_bound, i_np = c_np, it = t_begin, ip = 0;
+  int ijn = jn, i_bound = c_bound, it = t_begin;
+  PanelWalk iw = cw;
   TileLoads tl;
   tile_loads(ij, (it - ij.item0) * kRows + 16 * wave, tl);
 
   auto issue = [&](Panel<MX>& r) {
     const bool live = it < t_end;
-    panel_issue_tile<MX, PK, false, SF>(ij, tl, (it - ij.item0) * kRows + 16 * wave, ip, live,
+    panel_issue_tile<MX, PK, false, SF>(ij, tl, (it - ij.item0) * kRows + 16 * wave, iw.panel(), live,
                                         (ij.k + kTile - 1) / kTile, (ij.k + kGroup - 1) / kGroup, r);
     if (!live) return;
-    if (++ip == i_np) {
-      ip = 0;
-      if (++it < t_end) {
-        if (it >= i_bound) {
-          load_job<ONE>(jobs, ++ijn, ij);
-          i_bound = job_end<ONE>(jobs, ijn);
-          i_np = (ij.k + kPanelCols - 1) / kPanelCols;
-        }
-        tile_loads(ij, (it - ij.item0) * kRows + 16 * wave, tl);
+    if (iw.step(wave, NW) == 2 && ++it < t_end) {
+      if (it >= i_bound) {
+        load_job<ONE>(jobs, ++ijn, ij);
+        i_bound = job_end<ONE>(jobs, ijn);
+        iw.start_job(ij.k, seg_panels, s0, wave, NW);
       }
+      tile_loads(ij, (it - ij.item0) * kRows + 16 * wave, tl);
     }
   };
   // x[:, seg0 : seg0 + seg_cols) of job j into LDS, zeros past k (the codes
@@ -1156,7 +1214,7 @@ __global__ __launch_bounds__(NW * kWave, 4) void k_gemv_mfma_stream(const GemvJo
     issue(slot[s]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  stage(cj, 0);
+  stage(cj, cw.seg_col0());
   __syncthreads();
 
   f32x4 acc[MT];
@@ -1176,34 +1234,34 @@ __global__ __launch_bounds__(NW * kWave, 4) void k_gemv_mfma_stream(const GemvJo
       float sc[MX ? 4 : 2];
       panel_scales<MX, PK, SF>(slot[s], sc);
       issue(slot[s]);
-      const int kseg = (cp % seg_panels) * kPanelCols;   // panel start within the staged segment
+      const int kseg = cw.pos * kPanelCols;   // panel start within the staged segment
       panel_mfma<MT, MX>(a, sc, [&](int t, int b, int c, uint4& B0, uint4& B1) {
         const uint16_t* bp = xs + brow[t] + kseg + 128 * b;
         B0 = *reinterpret_cast<const uint4*>(bp + bunit[c][0]);
         B1 = *reinterpret_cast<const uint4*>(bp + bunit[c][1]);
       }, acc);
-      if (++cp == c_np) {   // tile done
+      const int moved = cw.step(wave, NW);
+      if (moved == 2) {   // tile done
         if (ct < t_end) store_tile<MT, SF == kFmtRow>(cj, (ct - cj.item0) * kRows + 16 * wave, m_rows, acc);
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        cp = 0;
         if (++ct < t_end) {
           if (ct >= c_bound) {   // the run enters the next job
             load_job<ONE>(jobs, ++jn, cj);
             c_bound = job_end<ONE>(jobs, jn);
-            c_np = (cj.k + kPanelCols - 1) / kPanelCols;
+            cw.start_job(cj.k, seg_panels, s0, wave, NW);
             __syncthreads();
-            stage(cj, 0);
+            stage(cj, cw.seg_col0());
             __syncthreads();
-          } else if (c_np > seg_panels) {   // next tile of a multi-segment job
+          } else if (cw.nseg > 1) {   // next tile of a multi-segment job
             __syncthreads();
-            stage(cj, 0);
+            stage(cj, cw.seg_col0());
             __syncthreads();
           }
         }
-      } else if (cp % seg_panels == 0 && ct < t_end) {   // next segment of this tile
+      } else if (moved == 1 && ct < t_end) {   // next segment of this tile
         __syncthreads();
-        stage(cj, cp * kPanelCols);
+        stage(cj, cw.seg_col0());
         __syncthreads();
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -1240,6 +1298,7 @@ __global__ __launch_bounds__(NW * kWave) void k_gemv_mfma_direct(GemvJob j, int 
   const int nkb = (j.k + kTile - 1) / kTile;
   const int groups = (j.k + kGroup - 1) / kGroup;
   const int nq = (np - wave + NW - 1) / NW;   // this wave's panels
+  const int rot = j.k % 2048 == 0 ? blockIdx.x % np : 0;
 
   // each tile's row offsets (tiles past the last row load nothing), and
   // each lane's x rows (rows past m_rows read row m_rows - 1: their
@@ -1259,7 +1318,13 @@ __global__ __launch_bounds__(NW * kWave) void k_gemv_mfma_direct(GemvJob j, int 
     xrow[t] = reinterpret_cast<const uint8_t*>(j.x) + ((size_t)min(16 * t + i, m_rows - 1) * j.k + 16 * g) * 2;
 
   auto issue = [&](int q, DirectSlot<MT, MX, T>& r) {
-    const int p = wave + NW * q;
+    // panels rotated by the workgroup's index when K is a multiple of 2048
+    // (PanelWalk: weights whose row stride is a multiple of 4 KB read slowly
+    // when every workgroup starts at the same columns; single calls on the
+    // dense layer's K = 4096 weights gained 1-6 %, K = 2560 / 3072 lost 1 %);
+    // wave + NW * q < np, so one subtraction wraps it
+    int p = wave + NW * q + rot;
+    if (p >= np) p -= np;
     const bool live = q < nq;
 #pragma unroll
     for (int u = 0; u < T; ++u)

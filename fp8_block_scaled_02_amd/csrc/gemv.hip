@@ -1287,7 +1287,7 @@ struct DirectSlot {
 
 // T 16-row tiles per workgroup (T = 2: 32 rows) share each x^T fragment a
 // wave loads, so x costs 1/T of the fragment reads per weight byte.
-template <int MT, int D, bool MX, int NW, bool PK, int T>
+template <int MT, int D, bool MX, int NW, bool PK, int T, int SF>
 __global__ __launch_bounds__(NW * kWave) void k_gemv_mfma_direct(GemvJob j, int m_rows) {
   __shared__ __align__(16) unsigned char pb[NW * kPanelBytes];
   __shared__ float red[NW * T * MT * 4 * kWave];
@@ -1328,7 +1328,7 @@ __global__ __launch_bounds__(NW * kWave) void k_gemv_mfma_direct(GemvJob j, int 
     const bool live = q < nq;
 #pragma unroll
     for (int u = 0; u < T; ++u)
-      panel_issue_tile<MX, PK, true>(j, tl[u], row0[u], p, live && tlive[u], nkb, groups, r.p[u]);
+      panel_issue_tile<MX, PK, true, SF>(j, tl[u], row0[u], p, live && tlive[u], nkb, groups, r.p[u]);
     if (live && (p + 1) * kPanelCols <= j.k) {   // a whole panel: every x load in bounds
 #pragma unroll
       for (int b = 0; b < 2; ++b)
@@ -1377,7 +1377,7 @@ __global__ __launch_bounds__(NW * kWave) void k_gemv_mfma_direct(GemvJob j, int 
           uint4 a[2][2];
           panel_to_a(slot[s].p[u].v, pb + wave * kPanelBytes, a);
           float sc[MX ? 4 : 2];
-          panel_scales<MX, PK>(slot[s].p[u], sc);
+          panel_scales<MX, PK, SF>(slot[s].p[u], sc);
           panel_mfma<MT, MX>(a, sc, [&](int t, int b, int c, uint4& B0, uint4& B1) {
             B0 = slot[s].xb[t][b][c][0];
             B1 = slot[s].xb[t][b][c][1];
@@ -1405,7 +1405,7 @@ __global__ __launch_bounds__(NW * kWave) void k_gemv_mfma_direct(GemvJob j, int 
         for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
           for (int w = 1; w < NW; ++w) acc[u][t][jj] += red[(((w * T + u) * MT + t) * 4 + jj) * kWave + lane];
-      store_tile<MT>(j, row0[u], m_rows, acc[u]);
+      store_tile<MT, SF == kFmtRow>(j, row0[u], m_rows, acc[u]);
     }
   }
 }
@@ -1907,12 +1907,22 @@ int gemv_mfma_stream_lds_limit() { return kMfmaStreamLds; }
 
 namespace {
 
+// The job's scale format selects the variant (each loads its own scales
+// unconditionally, so no join waits for them).
 template <int MT, int NW, int T>
 hipError_t launch_mfma_direct(const GemvJob& job, int m, bool mx, bool pk, hipStream_t stream) {
   const dim3 grid((unsigned)((job.n + 16 * T - 1) / (16 * T))), block(NW * kWave);
-  if (!mx) hipLaunchKernelGGL((k_gemv_mfma_direct<MT, 2, false, NW, false, T>), grid, block, 0, stream, job, m);
-  else if (pk) hipLaunchKernelGGL((k_gemv_mfma_direct<MT, 2, true, NW, true, T>), grid, block, 0, stream, job, m);
-  else hipLaunchKernelGGL((k_gemv_mfma_direct<MT, 2, true, NW, false, T>), grid, block, 0, stream, job, m);
+  if (mx && pk)
+    hipLaunchKernelGGL((k_gemv_mfma_direct<MT, 2, true, NW, true, T, kFmtMx>), grid, block, 0, stream, job, m);
+  else if (mx)
+    hipLaunchKernelGGL((k_gemv_mfma_direct<MT, 2, true, NW, false, T, kFmtMx>), grid, block, 0, stream, job, m);
+  else if (job.format == kFmtBlock)
+    hipLaunchKernelGGL((k_gemv_mfma_direct<MT, 2, false, NW, false, T, kFmtBlock>), grid, block, 0, stream, job, m);
+  else if (job.format == kFmtBlockBf16)
+    hipLaunchKernelGGL((k_gemv_mfma_direct<MT, 2, false, NW, false, T, kFmtBlockBf16>), grid, block, 0, stream, job,
+                       m);
+  else
+    hipLaunchKernelGGL((k_gemv_mfma_direct<MT, 2, false, NW, false, T, kFmtRow>), grid, block, 0, stream, job, m);
   return hipGetLastError();
 }
 

@@ -1433,11 +1433,15 @@ constexpr int kE8m0One = 127;
 template <bool MX>
 struct Panel8 {
   uint4 v[4];     // as Panel: lane l holds row 4q + l/16, bytes 16*(l%16)
-  float s[2];     // block: scale of each 128-column block
+  float s[2];     // block: scale of each 128-column block (fp32 grid, or any format chosen at run time)
+  uint16_t h[2];  // bf16 block grid: the scale bits as loaded
   int e[2];       // MX: e8m0 byte of row l%16, group 4*(block) + l/16
 };
 
-template <bool MX>
+// SF as for panel_issue_tile: kSfAny picks the format at run time and loads
+// each block scale only where it exists; kFmtBlock / kFmtBlockBf16 load it
+// unconditionally from a clamped index; kFmtRow loads none.
+template <bool MX, int SF = kSfAny>
 __device__ __forceinline__ void panel8_issue(const GemvJob& j, int row0, int p, bool live, int nkb,
                                              int groups, Panel8<MX>& r) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -1463,9 +1467,31 @@ __device__ __forceinline__ void panel8_issue(const GemvJob& j, int row0, int p, 
   } else {
     r.e[0] = r.e[1] = kE8m0One;
   }
-  if (!MX && live && row0 < j.n) {
+  if (!MX && SF == kFmtBlock) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) r.s[b] = ld_global<float>(j.scales, block_scale_at(j, row0, 2 * p + b, nkb) * 4);
+  } else if (!MX && SF == kFmtBlockBf16) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+      r.h[b] = ld_global<uint16_t>(j.scales, block_scale_at(j, row0, 2 * p + b, nkb) * 2);
+  } else if (!MX && SF == kSfAny && live && row0 < j.n) {
     r.s[0] = block_scale(j, row0, 2 * p, nkb);
     if (2 * p + 1 < nkb) r.s[1] = block_scale(j, row0, 2 * p + 1, nkb);
+  } else if (!MX && SF == kFmtRow) {
+    r.s[0] = r.s[1] = 1.0f;
+  }
+}
+
+// A panel's block scales as the MFMA step uses them: the same in every lane
+// (one 16-row tile, one block), so taken into scalar registers where the
+// panel is consumed (panel_scales has the reason).
+template <bool MX, int SF>
+__device__ __forceinline__ void panel8_scales(Panel8<MX>& r) {
+  if (MX) return;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const float v = SF == kFmtBlockBf16 ? __uint_as_float((uint32_t)r.h[b] << 16) : r.s[b];
+    r.s[b] = SF == kFmtRow ? 1.0f : __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
   }
 }
 
@@ -1507,7 +1533,7 @@ struct Direct8Slot {
   uint4 xb[MT][2][2];   // [m tile][block][piece at 16g / at 64 + 16g]
 };
 
-template <int MT, int D, bool MX, int NW>
+template <int MT, int D, bool MX, int NW, int SF>
 __global__ __launch_bounds__(NW * kWave) void k_gemv_w8a8_direct(GemvJob j, const float* __restrict__ xs,
                                                                  int m_rows) {
   __shared__ __align__(16) unsigned char pb[NW * kPanelBytes];
@@ -1520,12 +1546,14 @@ __global__ __launch_bounds__(NW * kWave) void k_gemv_w8a8_direct(GemvJob j, cons
   const int nkb = (j.k + kTile - 1) / kTile;
   const int groups = (j.k + kGroup - 1) / kGroup;
   const int nq = (np - wave + NW - 1) / NW;
+  const int rot = j.k % 2048 == 0 ? blockIdx.x % np : 0;   // as k_gemv_mfma_direct
   const uint8_t* __restrict__ xc = reinterpret_cast<const uint8_t*>(j.x);
 
   auto issue = [&](int q, Direct8Slot<MT, MX>& r) {
-    const int p = wave + NW * q;
+    int p = wave + NW * q + rot;
+    if (p >= np) p -= np;
     const bool live = q < nq;
-    panel8_issue<MX>(j, row0, p, live, nkb, groups, r.p);
+    panel8_issue<MX, SF>(j, row0, p, live, nkb, groups, r.p);
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -1552,6 +1580,7 @@ __global__ __launch_bounds__(NW * kWave) void k_gemv_w8a8_direct(GemvJob j, cons
       if (q0 + s < nq) {
         uint4 a[2][2];
         panel_to_a(slot[s].p.v, pb + wave * kPanelBytes, a);
+        panel8_scales<MX, SF>(slot[s].p);
         panel8_mfma<MT, MX>(a, slot[s].p, [&](int t, int b, uint4& lo, uint4& hi) {
           lo = slot[s].xb[t][b][0];
           hi = slot[s].xb[t][b][1];
@@ -1573,7 +1602,7 @@ __global__ __launch_bounds__(NW * kWave) void k_gemv_w8a8_direct(GemvJob j, cons
       for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
         for (int w = 1; w < NW; ++w) acc[t][jj] += red[((w * MT + t) * 4 + jj) * kWave + lane];
-    store_tile<MT>(j, row0, m_rows, acc, ld_global<float>(xs, 0));
+    store_tile<MT, SF == kFmtRow>(j, row0, m_rows, acc, ld_global<float>(xs, 0));
   }
 }
 
@@ -2097,6 +2126,19 @@ hipError_t run_w8a8_tiles(const GemvJob& job, const float* x_scale, int m, hipSt
   return hipGetLastError();
 }
 
+// The non-MX W8A8 direct kernel for the job's scale format.
+template <int MT, int NW>
+void launch_w8a8_direct_fmt(dim3 grid, dim3 block, const GemvJob& job, const float* x_scale, int m,
+                            hipStream_t stream) {
+  if (job.format == kFmtBlock)
+    hipLaunchKernelGGL((k_gemv_w8a8_direct<MT, 2, false, NW, kFmtBlock>), grid, block, 0, stream, job, x_scale, m);
+  else if (job.format == kFmtBlockBf16)
+    hipLaunchKernelGGL((k_gemv_w8a8_direct<MT, 2, false, NW, kFmtBlockBf16>), grid, block, 0, stream, job, x_scale,
+                       m);
+  else
+    hipLaunchKernelGGL((k_gemv_w8a8_direct<MT, 2, false, NW, kFmtRow>), grid, block, 0, stream, job, x_scale, m);
+}
+
 }  // namespace
 
 // W8A8: m <= 2 on the VALU kernel with the codes widened while x is staged
@@ -2116,21 +2158,21 @@ hipError_t launch_gemv_w8a8(const GemvJob& job, const float* x_scale, int m, boo
   if (job.n <= kDirect8MaxRows) {   // as the bf16 single call: 8 waves per tile on few rows
     const dim3 block(8 * kWave);
     if (m <= 16) {
-      if (mx) hipLaunchKernelGGL((k_gemv_w8a8_direct<1, 2, true, 8>), grid, block, 0, stream, job, x_scale, m);
-      else hipLaunchKernelGGL((k_gemv_w8a8_direct<1, 2, false, 8>), grid, block, 0, stream, job, x_scale, m);
+      if (mx) hipLaunchKernelGGL((k_gemv_w8a8_direct<1, 2, true, 8, kFmtMx>), grid, block, 0, stream, job, x_scale, m);
+      else launch_w8a8_direct_fmt<1, 8>(grid, block, job, x_scale, m, stream);
     } else {
-      if (mx) hipLaunchKernelGGL((k_gemv_w8a8_direct<2, 2, true, 8>), grid, block, 0, stream, job, x_scale, m);
-      else hipLaunchKernelGGL((k_gemv_w8a8_direct<2, 2, false, 8>), grid, block, 0, stream, job, x_scale, m);
+      if (mx) hipLaunchKernelGGL((k_gemv_w8a8_direct<2, 2, true, 8, kFmtMx>), grid, block, 0, stream, job, x_scale, m);
+      else launch_w8a8_direct_fmt<2, 8>(grid, block, job, x_scale, m, stream);
     }
     return hipGetLastError();
   }
   const dim3 block(kThreads);
   if (m <= 16) {
-    if (mx) hipLaunchKernelGGL((k_gemv_w8a8_direct<1, 2, true, kWaves>), grid, block, 0, stream, job, x_scale, m);
-    else hipLaunchKernelGGL((k_gemv_w8a8_direct<1, 2, false, kWaves>), grid, block, 0, stream, job, x_scale, m);
+    if (mx) hipLaunchKernelGGL((k_gemv_w8a8_direct<1, 2, true, kWaves, kFmtMx>), grid, block, 0, stream, job, x_scale, m);
+    else launch_w8a8_direct_fmt<1, kWaves>(grid, block, job, x_scale, m, stream);
   } else {
-    if (mx) hipLaunchKernelGGL((k_gemv_w8a8_direct<2, 2, true, kWaves>), grid, block, 0, stream, job, x_scale, m);
-    else hipLaunchKernelGGL((k_gemv_w8a8_direct<2, 2, false, kWaves>), grid, block, 0, stream, job, x_scale, m);
+    if (mx) hipLaunchKernelGGL((k_gemv_w8a8_direct<2, 2, true, kWaves, kFmtMx>), grid, block, 0, stream, job, x_scale, m);
+    else launch_w8a8_direct_fmt<2, kWaves>(grid, block, job, x_scale, m, stream);
   }
   return hipGetLastError();
 }

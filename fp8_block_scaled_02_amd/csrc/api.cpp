@@ -25,30 +25,26 @@ constexpr int kValuMaxM = 8;
 // AUTO route, from the VALU / MFMA crossovers measured on MI355X.
 //  - Single calls.  The MFMA kernel's time hardly moves with m: one 16-row
 //    MFMA tile serves every m <= 16 (rocprofv3 kernel traces and counters
-//    at m = 3, 4, 5: 8.0-8.2 us per call on [8192x2560] and 7.9-8.0 us on
-//    [4096x4096], VALU issue 9-11 %, MFMA busy under 2 %).  The VALU
+//    at m = 3, 4, 5: VALU issue 9-11 %, MFMA busy under 2 %).  The VALU
 //    kernel's instructions grow with m (VALU issue 18 / 22 / 25 % on
 //    [4096x4096] and 29 / 34 / 37 % on [8192x2560] at m = 3 / 4 / 5, both
 //    kernels within 1.5 % of the same HBM bytes), so every shape has one
 //    crossover, later on shorter weights.  Graph-captured passes over every
 //    workload shape (N 2560..151936, K 2048..12288, block and MX scales,
-//    m = 2..8) put it after m = 3, after m = 4 on weights up to 8192 x
-//    4096, and after m = 5 on K = 4096 weights up to 6144 rows (+2 to +13 %
-//    at m = 5; at m = 6 they lose up to 4 %).  With MX scales it falls
-//    after m = 2 on weights of 32768 rows or more, where the MFMA route
-//    streams (the [151936x2048] lm_head at m = 3: 4 % faster on MFMA, where
-//    block scales are 1.6-4.4 % faster on VALU in six runs), and after
-//    m = 4 on every weight below that ([24576x4096] 5 % and [4096x12288]
-//    4 % faster on VALU in repeated runs, where block scales are 1-5 %
-//    faster on MFMA).
+//    m = 2..8; two runs on one box, `route_crossover_single_calls` rows)
+//    put it after m = 2 on weights of 32768 rows or more (lm_head at m = 3:
+//    MFMA 3-8 % faster with block scales, 9-14 % with MX), after m = 4 on
+//    weights up to 8192 rows and K = 4096 (VALU 2-16 % faster at m = 4),
+//    and after m = 3 elsewhere ([24576x4096] and [4096x12288] at m = 4:
+//    MFMA 0-10 % faster; m = 3 within 3 % either way on those two).  At
+//    m = 5 MFMA is as fast or faster on every shape (up to 9 %) but MX
+//    [6144x4096], 1 % slower there.  Block and MX scales now share the rule.
 //  - Grouped: the streaming VALU kernel at m = 1; VALU tiles at m = 2 for
 //    block-scaled formats (+4 % on the projection set, +16 % on dense
 //    layers), while MX at m = 2 is 6 % faster on the streaming MFMA kernel.
-constexpr int64_t kAutoValuMxMaxN = 32768 - 1;
+constexpr int64_t kAutoValuM3MaxN = 32768 - 1;
 constexpr int kAutoValuM4MaxN = 8192;
 constexpr int kAutoValuM4MaxK = 4096;
-constexpr int kAutoValuM5MaxN = 6144;
-constexpr int kAutoValuM5MinK = 3072 + 16;   // K in (3072, 4096]
 
 bool aligned(const void* p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
 
@@ -119,23 +115,22 @@ fp8w_status check_gemv(const uint16_t* x, int64_t m, const uint8_t* codes, const
 fp8w_status gemv_any(const uint16_t* x, int64_t m, const uint8_t* codes, const void* scales, int format,
                      int64_t n, int64_t k, uint16_t* y, fp8w_route route, void* stream);
 
-bool auto_valu_single(int64_t m, int64_t n, int64_t k, bool mx) {
+bool auto_valu_single(int64_t m, int64_t n, int64_t k) {
   switch (m) {
     case 1:
     case 2: return true;
-    case 3: return !mx || n <= kAutoValuMxMaxN;
-    case 4: return mx ? n <= kAutoValuMxMaxN : n <= kAutoValuM4MaxN && k <= kAutoValuM4MaxK;
-    case 5: return n <= kAutoValuM5MaxN && k >= kAutoValuM5MinK && k <= kAutoValuM4MaxK;
+    case 3: return n <= kAutoValuM3MaxN;
+    case 4: return n <= kAutoValuM4MaxN && k <= kAutoValuM4MaxK;
     default: return false;
   }
 }
 
 bool auto_valu_grouped(int64_t m, bool mx) { return m == 1 || (m == 2 && !mx); }
 
-int resolve_route(fp8w_route route, int64_t m, int64_t n, int64_t k, bool mx) {
+int resolve_route(fp8w_route route, int64_t m, int64_t n, int64_t k) {
   if (route == FP8W_ROUTE_VALU) return 1;
   if (route == FP8W_ROUTE_MFMA) return 2;
-  return auto_valu_single(m, n, k, mx) ? 1 : 2;
+  return auto_valu_single(m, n, k) ? 1 : 2;
 }
 
 int resolve_route_grouped(fp8w_route route, int64_t m, bool mx) {
@@ -148,7 +143,7 @@ int resolve_route_grouped(fp8w_route route, int64_t m, bool mx) {
 
 FP8W_API fp8w_route fp8w_gemv_auto_route(fp8w_format format, int64_t m, int64_t n, int64_t k) {
   if (!format_ok(format) || m < 1 || m > FP8W_MAX_M || !dims_ok(n, k)) return FP8W_ROUTE_AUTO;
-  return auto_valu_single(m, n, k, format == FP8W_FORMAT_MX) ? FP8W_ROUTE_VALU : FP8W_ROUTE_MFMA;
+  return auto_valu_single(m, n, k) ? FP8W_ROUTE_VALU : FP8W_ROUTE_MFMA;
 }
 
 FP8W_API int64_t fp8w_scale_bytes(fp8w_format format, int64_t n, int64_t k) {
@@ -203,7 +198,7 @@ fp8w_status gemv_any(const uint16_t* x, int64_t m, const uint8_t* codes, const v
   const fp8w_status st = check_gemv(x, m, codes, scales, format, n, k, y, route);
   if (st != FP8W_OK) return st;
   const fp8w::GemvJob job{x, codes, scales, y, (int32_t)n, (int32_t)k, 0, format};
-  return from_hip(fp8w::launch_gemv(job, (int)m, format == FP8W_FORMAT_MX, resolve_route(route, m, n, k, format == FP8W_FORMAT_MX),
+  return from_hip(fp8w::launch_gemv(job, (int)m, format == FP8W_FORMAT_MX, resolve_route(route, m, n, k),
                                     static_cast<hipStream_t>(stream)));
 }
 

@@ -90,12 +90,11 @@ typedef enum fp8w_status {
  * add FP8 blockwise weight quantization ..." (Summary; Notes for Reviewers:
  * SIMT for M <= 8, tensor-core mma for 9 <= M <= 32): VALU serves
  * 1 <= m <= 8 only; MFMA serves 1 <= m <= 32.  AUTO follows the crossovers
- * measured on MI355X: single calls take VALU for m <= 2, for m = 3, for
- * m = 4 on weights of at most 8192 rows and K <= 4096, and for m = 5 on
- * weights of at most 6144 rows and 3072 < K <= 4096, except that MX takes
- * VALU at m = 3 and 4 on every weight of fewer than 32768 rows and MFMA
- * above (fp8w_gemv_auto_route gives the choice); grouped launches take VALU for m = 1, and for m = 2 on every
- * format but MX; MFMA otherwise.  Within a route the
+ * measured on MI355X: single calls take VALU for m <= 2, for m = 3 on
+ * weights of fewer than 32768 rows, and for m = 4 on weights of at most
+ * 8192 rows and K <= 4096, in every scale format (fp8w_gemv_auto_route
+ * gives the choice); grouped launches take VALU for m = 1, and for m = 2 on
+ * every format but MX; MFMA otherwise.  Within a route the
  * kernel also depends on n and k (weights with many rows take the streaming
  * kernels; K above 3072 is walked in 3072- or 4096-column segments) and, for
  * MX, on how the exponent array is laid out (4-byte aligned with n *

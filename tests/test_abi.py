@@ -61,39 +61,26 @@ def test_helpers(F):
 
 def test_auto_route_rule(F):
     L = F.lib()
-    BLOCK, MX = 0, 1
-    assert F.FORMAT_IDS["block"] == BLOCK and F.FORMAT_IDS["mx"] == MX
-    # single calls: VALU through m = 3 on any weight, at m = 4 up to 8192
-    # rows and K = 4096, at m = 5 only on K = 4096 up to 6144 rows; MX takes
-    # VALU at m = 3 and 4 below 32768 rows and MFMA above; every format but
-    # MX follows the block rule
+    # single calls, every format: VALU through m = 2; at m = 3 below 32768
+    # rows; at m = 4 up to 8192 rows and K = 4096; MFMA from m = 5
     for fmt in range(len(F.FORMAT_IDS)):
-        mx = fmt == MX
         for n, k in ((1, 16), (2560, 3072), (151936, 2048), (4096, 12288)):
-            for m in (1, 2, 3) if n < 32768 or not mx else (1, 2):
+            for m in (1, 2):
                 assert L.fp8w_gemv_auto_route(fmt, m, n, k) == F.ROUTE_VALU, (fmt, m, n, k)
-            for m in (5, 8, 9, 32):
-                assert L.fp8w_gemv_auto_route(fmt, m, n, k) == F.ROUTE_MFMA
-        assert L.fp8w_gemv_auto_route(fmt, 3, 32768, 2048) == (F.ROUTE_MFMA if mx else F.ROUTE_VALU)
-        assert L.fp8w_gemv_auto_route(fmt, 4, 8192, 4096) == F.ROUTE_VALU
-        # m = 5: VALU only on K in (3072, 4096] up to 6144 rows
-        for n, k, want in ((6144, 4096, F.ROUTE_VALU), (4096, 3088, F.ROUTE_VALU), (6145, 4096, F.ROUTE_MFMA),
-                           (4096, 3072, F.ROUTE_MFMA), (4096, 4112, F.ROUTE_MFMA), (2560, 3072, F.ROUTE_MFMA)):
-            assert L.fp8w_gemv_auto_route(fmt, 5, n, k) == want, (fmt, n, k)
-            assert L.fp8w_gemv_auto_route(fmt, 6, n, k) == F.ROUTE_MFMA
+            for m in (5, 6, 8, 9, 32):
+                assert L.fp8w_gemv_auto_route(fmt, m, n, k) == F.ROUTE_MFMA, (fmt, m, n, k)
+        for n, want in ((1, F.ROUTE_VALU), (32767, F.ROUTE_VALU), (32768, F.ROUTE_MFMA), (151936, F.ROUTE_MFMA)):
+            assert L.fp8w_gemv_auto_route(fmt, 3, n, 2048) == want, (fmt, n)
+        for n, k, want in ((8192, 4096, F.ROUTE_VALU), (2560, 3072, F.ROUTE_VALU), (8193, 4096, F.ROUTE_MFMA),
+                           (8192, 4112, F.ROUTE_MFMA), (24576, 4096, F.ROUTE_MFMA), (4096, 12288, F.ROUTE_MFMA)):
+            assert L.fp8w_gemv_auto_route(fmt, 4, n, k) == want, (fmt, n, k)
         for m, n, k in ((0, 1, 16), (33, 1, 16), (1, 0, 16), (1, 16, 0), (1, 1 << 31, 16)):
             assert L.fp8w_gemv_auto_route(fmt, m, n, k) == F.ROUTE_AUTO
-        m4_wide = F.ROUTE_VALU if mx else F.ROUTE_MFMA
-        for n, k in ((8193, 4096), (8192, 4112), (24576, 4096), (4096, 12288), (32767, 2048)):
-            assert L.fp8w_gemv_auto_route(fmt, 4, n, k) == m4_wide, (fmt, n, k)
-        assert L.fp8w_gemv_auto_route(fmt, 4, 32768, 2048) == F.ROUTE_MFMA
     for fmt in (-1, len(F.FORMAT_IDS)):
         assert L.fp8w_gemv_auto_route(fmt, 1, 16, 16) == F.ROUTE_AUTO
-    assert F.fp8w_gemv_auto_route(4, 24576, 4096) == F.ROUTE_MFMA
-    assert F.fp8w_gemv_auto_route(4, 24576, 4096, "mx") == F.ROUTE_VALU
-    assert F.fp8w_gemv_auto_route(3, 151936, 2048) == F.ROUTE_VALU
-    assert F.fp8w_gemv_auto_route(3, 151936, 2048, "mx") == F.ROUTE_MFMA
-    assert F.fp8w_gemv_auto_route(3, 32767, 2048, "mx") == F.ROUTE_VALU
+    assert F.fp8w_gemv_auto_route(4, 24576, 4096, "mx") == F.ROUTE_MFMA
+    assert F.fp8w_gemv_auto_route(3, 151936, 2048) == F.ROUTE_MFMA
+    assert F.fp8w_gemv_auto_route(3, 4096, 12288, "mx") == F.ROUTE_VALU
 
 
 # Fake, well-aligned "device" addresses: every call below fails validation

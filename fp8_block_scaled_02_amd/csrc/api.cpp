@@ -483,9 +483,7 @@ FP8W_API fp8w_status fp8w_gemv_grouped(const fp8w_grouped_plan* plan, void* stre
     return FP8W_ERR_SHAPE;
   if (plan->route == FP8W_ROUTE_MFMA) {
     const int seg = plan->seg_cols;
-    if (plan->tiles_per_block < 1 || seg < 256 || seg % 256 != 0 ||
-        fp8w::gemv_mfma_stream_lds(plan->m, seg) > fp8w::gemv_mfma_stream_lds_limit())
-      return FP8W_ERR_SHAPE;
+    if (plan->tiles_per_block < 1 || !fp8w::gemv_mfma_stream_seg_ok(plan->m, seg)) return FP8W_ERR_SHAPE;
     return from_hip(fp8w::launch_gemv_mfma_stream(table, plan->count, plan->blocks, plan->tiles,
                                                   plan->tiles_per_block, plan->m, seg, plan->format,
                                                   plan->mx_packed8 == 1, s));

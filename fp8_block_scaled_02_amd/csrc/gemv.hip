@@ -24,8 +24,9 @@
 //    (single calls): one 16-row tile per workgroup (two above M = 8,
 //    sharing each x^T fragment), its 4 or 8 waves splitting the panels, x
 //    fragments from L2.
-//    k_gemv_mfma_stream: runs of 128-row tiles, one 16-row tile per wave,
-//    x staged in LDS by K segments.
+//    k_gemv_mfma_stream16 / k_gemv_mfma_stream32 (up to 16 / 17..32 rows):
+//    runs of 128-row tiles, one 16-row tile per wave, x staged in LDS by K
+//    segments (one buffer / two, the next segment prefetched).
 //  * W8A8: fp8 x fp8 v_mfma_scale_f32_16x16x128_f8f6f4 (k_gemv_w8a8_direct,
 //    and k_gemv_w8a8_tiles on weights with many rows), and k_gemv_valu with
 //    the activation codes widened to bf16 at M <= 2.
@@ -69,6 +70,15 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
+
+// The lane index, recomputed at every call (an opaque v_mbcnt pair): kernels
+// at the register limit otherwise keep lane-derived row indices live from the
+// start, and spill them.
+__device__ __forceinline__ int lane_fresh() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
 
 // 2^(e - 127) as an exact fp32: a normal number for e >= 1, the subnormal
 // 2^-127 for e == 0.
@@ -921,6 +931,57 @@ __device__ __forceinline__ void panel_mfma(const uint4 (&a)[2][2], const float* 
   }
 }
 
+// The panel half of panel_to_a: registers -> the wave's panel buffer.
+__device__ __forceinline__ void panel_write(const uint4 (&v)[4], unsigned char* buf) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int i = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = 4 * q + g;
+    *reinterpret_cast<uint4*>(buf + r * kPanelCols + 16 * (i ^ r)) = v[q];
+  }
+}
+
+// panel_mfma reading each A operand from the panel buffer where it is used,
+// with the scheduler fenced between the two 128-column blocks: the A
+// operands then hold 4 registers at a time instead of 16 (for kernels at the
+// register limit).
+template <int MT, bool MX, typename GetB>
+__device__ __forceinline__ void panel_mfma_lds(const unsigned char* buf, const float* s, GetB get_b,
+                                               f32x4 (&acc)[MT]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int i = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    f32x4 part[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) part[t] = MX ? acc[t] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const uint4 a = *reinterpret_cast<const uint4*>(buf + i * kPanelCols + 16 * ((8 * b + 4 * c + g) ^ i));
+      bf16x8 A0, A1;
+      a_operands<MX>(a, MX ? s[2 * b + c] : 0.0f, A0, A1);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        uint4 B0, B1;
+        get_b(t, b, c, B0, B1);
+        part[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, __builtin_bit_cast(bf16x8, B0), part[t], 0, 0, 0);
+        part[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, __builtin_bit_cast(bf16x8, B1), part[t], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      if (MX) {
+        acc[t] = part[t];
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) acc[t][jj] = __builtin_fmaf(s[b], part[t][jj], acc[t][jj]);
+      }
+    }
+    if (b == 0) __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // y^T of a 16-row tile from the D layout; columns (activation rows) >= m_rows
 // and rows >= n are not written.  OS: the format may scale rows or the whole
 // weight (kFmtRow, kFmtTensor), whose scales are loaded here and used under
@@ -929,10 +990,13 @@ __device__ __forceinline__ void panel_mfma(const uint4 (&a)[2][2], const float* 
 // a load on a path that skipped its use as still pending, which would make
 // it wait for all vector memory at the top of a caller's panel loop.  Kernels
 // that pipeline panels across tiles take OS = false for the other formats.
-template <int MT, bool OS = true>
+// FRESH: the lane index comes from lane_fresh, so the output offsets are
+// recomputed at each store (a kernel at the register limit otherwise keeps
+// them from the start, and spills).
+template <int MT, bool OS = true, bool FRESH = false>
 __device__ __forceinline__ void store_tile(const GemvJob& j, int row0, int m_rows, const f32x4 (&acc)[MT],
                                            float factor = 1.0f) {
-  const int lane = threadIdx.x & (kWave - 1);
+  const int lane = FRESH ? lane_fresh() : (int)(threadIdx.x & (kWave - 1));
   const int i = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
@@ -955,9 +1019,11 @@ __device__ __forceinline__ void store_tile(const GemvJob& j, int row0, int m_row
 // each workgroup owns a contiguous run of tiles across job boundaries (as the
 // VALU streaming kernel) and walks them panel by panel, the panel D ahead
 // already requested.  x is staged in LDS by K segments of seg_cols columns
-// (a multiple of 256, sized on the host so that two workgroups fit on a CU):
-// restaged when the run enters a new job, and at every segment of a tile
-// when K spans more than one segment.
+// (a multiple of 256).  Segments of at most kStreamXElems elements use two
+// buffers: while the workgroup works on one segment, the next one (of this
+// tile, the next tile or the next job) goes into the other buffer.  Larger
+// ones (chosen on the host only when every job's x fits one segment) use one
+// buffer, restaged at job changes behind a barrier.
 // Where a wave's panel loads point inside one 16-row tile: base is the
 // tile's first row (uniform), off[q] the lane's byte offset of row 4q + l/16
 // plus its 16-byte column (rows past the weight's last row are clamped to
@@ -977,6 +1043,66 @@ __device__ __forceinline__ void tile_loads(const GemvJob& j, int row0, TileLoads
     t.off[q] = (uint64_t)min(4 * q + (lane >> 4), last) * (uint64_t)j.k + 16 * (lane & 15);
 }
 
+// The streaming kernel's view of a 16-row tile: the address of the row each
+// of the lane's four loads reads (rows past the weight's last row clamped to
+// it: their sums are never stored).  Computed once per tile.
+struct TileRows {
+  const uint8_t* row[4];
+};
+
+__device__ __forceinline__ void tile_rows(const GemvJob& j, int row0, TileRows& t) {
+  const int lane = lane_fresh();
+  const int last = j.n - 1 - row0;   // >= 0 for a live tile
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    t.row[q] = j.codes + (size_t)(row0 + min(4 * q + (lane >> 4), last)) * (size_t)j.k;
+}
+
+// The streaming kernel's request of panel p: every lane loads, with no
+// branch.  A branch between full panels and a partial last one makes the
+// compiler count a path with fewer requests, and every wait it then sizes for
+// an earlier request also waits for requests issued after it.  Columns are
+// clamped to the row's last 16 bytes (a no-op on full panels; on a partial
+// last panel the clamped codes meet the zeros that pad x past k in LDS).
+// Scales as panel_issue_tile.
+// A dead request (live false: past the run) reads column 0 of the rows `t`
+// holds, which the caller points at one row: one cache line, not a panel.
+template <bool MX, bool PK, int SF>
+__device__ __forceinline__ void panel_issue_rows(const GemvJob& j, const TileRows& t, int row0, int p, bool live,
+                                                 int nkb, int groups, Panel<MX>& r) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint32_t col = live ? (uint32_t)min(p * kPanelCols + 16 * (lane & 15), j.k - 16) : 0u;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) r.v[q] = ld_stream_u4(t.row[q], col);
+  if (MX) {
+    // the tile's exponent rows from a uniform base: a 32-bit lane offset
+    // (16 rows of at most 2^26 bytes), so no 64-bit address stays live.
+    // row0 may lie past the last row (a wave's slice of a job's last tile, a
+    // dead request past the run): the base row is clamped, so every lane
+    // reads an existing row (n - 1 past the end; those sums are not stored).
+    const int r0 = min(row0, j.n - 1);
+    const uint8_t* __restrict__ e8 = static_cast<const uint8_t*>(j.scales) + (size_t)r0 * groups;
+    const uint32_t rofs = (uint32_t)min(lane & 15, j.n - 1 - r0) * (uint32_t)groups;
+    if (PK) {
+      const int pc = min(p, (j.k - 1) / kPanelCols);
+      r.e8 = ld_global<u32x2>(e8, rofs + 8 * pc);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int kx = min(p * kPanelCols + 64 * c + 16 * (lane >> 4), j.k - 1);
+        r.s[c] = ld_global<uint8_t>(e8, rofs + (uint32_t)(kx / kGroup));
+      }
+    }
+  } else if (SF == kFmtBlock) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) r.f[b] = ld_global<float>(j.scales, block_scale_at(j, row0, 2 * p + b, nkb) * 4);
+  } else if (SF == kFmtBlockBf16) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+      r.h[b] = ld_global<uint16_t>(j.scales, block_scale_at(j, row0, 2 * p + b, nkb) * 2);
+  }
+}
+
 // Request panel p (columns [256p, 256p + 256)) of the 16-row tile at row0,
 // with its scales, through the row offsets of `t`.  Every load is in bounds.
 // A partial last panel either clamps its columns to the row's last 16 bytes,
@@ -987,8 +1113,10 @@ __device__ __forceinline__ void tile_loads(const GemvJob& j, int row0, TileLoads
 // mx_rows_packed8), so one 8-byte load per row brings the panel's exponents.
 // It is a template choice, not a branch: with both loads behind a runtime
 // branch the compiler joins their results with copies, and a copy waits for
-// its load, and so for every weight load the wave issued before it.
-template <bool MX, bool PK, bool ZT = false, int SF = kSfAny>
+// its load, and so for every weight load the wave issued before it.  A dead
+// panel (live false) gets zero codes where its products reach a stored sum
+// (DZ); with DZ false its registers keep the codes they held (finite).
+template <bool MX, bool PK, bool ZT = false, int SF = kSfAny, bool DZ = true>
 __device__ __forceinline__ void panel_issue_tile(const GemvJob& j, const TileLoads& t, int row0, int p, bool live,
                                                  int nkb, int groups, Panel<MX>& r) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -1009,7 +1137,7 @@ __device__ __forceinline__ void panel_issue_tile(const GemvJob& j, const TileLoa
 #pragma unroll
       for (int q = 0; q < 4; ++q) r.v[q] = ld_stream_u4(pb, t.off[q] - (uint64_t)over);
     }
-  } else {
+  } else if (DZ) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) r.v[q] = make_uint4(0, 0, 0, 0);
   }
@@ -1101,13 +1229,24 @@ struct PanelWalk {
   }
 };
 
-// Four waves per SIMD (at most 128 VGPRs): two 8-wave workgroups per CU, so
-// one workgroup's staging barriers are covered by the other's loads.
-template <int MT, int NW, int D, bool MX, bool ONE, bool PK, int SF>
-__global__ __launch_bounds__(NW * kWave, 4) void k_gemv_mfma_stream(const GemvJob* __restrict__ table,
-                                                                 int njobs, GemvJob one, int total_tiles,
-                                                                 int tiles_per_block, int m_rows,
-                                                                 int seg_cols) {
+// x elements a double-buffered segment of the streaming MFMA kernel holds:
+// two 16-byte units per thread of its 512, so that a whole segment is in
+// flight in eight registers per thread.
+constexpr int kStreamXUnits = 2;
+constexpr int kStreamXElems = kStreamXUnits * 512 * 8;
+static_assert(32 * kPanelCols <= kStreamXElems, "a one-panel segment of 32 rows must fit the staging units");
+
+// Up to 16 activation rows: x^T is one 16-row m-tile, x is staged in one
+// buffer by segments as large as the workgroup's LDS share allows (x whole
+// for most shapes), restaged behind barriers.  Four waves per SIMD (at most
+// 128 VGPRs): two 8-wave workgroups per CU, so one workgroup's staging
+// barriers are covered by the other's loads.
+template <int NW, int D, bool MX, bool ONE, bool PK, int SF>
+__global__ __launch_bounds__(NW * kWave, 4) void k_gemv_mfma_stream16(const GemvJob* __restrict__ table,
+                                                                   int njobs, GemvJob one, int total_tiles,
+                                                                   int tiles_per_block, int m_rows,
+                                                                   int seg_cols) {
+  constexpr int MT = 1;
   const JobList jobs{table, njobs, one};
   constexpr int kRows = 16 * NW;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -1161,7 +1300,7 @@ __global__ __launch_bounds__(NW * kWave, 4) void k_gemv_mfma_stream(const GemvJo
 
   auto issue = [&](Panel<MX>& r) {
     const bool live = it < t_end;
-    panel_issue_tile<MX, PK, false, SF>(ij, tl, (it - ij.item0) * kRows + 16 * wave, iw.panel(), live,
+    panel_issue_tile<MX, PK, false, SF, false>(ij, tl, (it - ij.item0) * kRows + 16 * wave, iw.panel(), live,
                                         (ij.k + kTile - 1) / kTile, (ij.k + kGroup - 1) / kGroup, r);
     if (!live) return;
     if (iw.step(wave, NW) == 2 && ++it < t_end) {
@@ -1225,7 +1364,8 @@ __global__ __launch_bounds__(NW * kWave, 4) void k_gemv_mfma_stream(const GemvJo
   // slots' requests in another order, and the compiler, merging the two
   // orders, would wait at the head for every request in flight.  So the last
   // pass may consume up to D - 1 panels past the run: they were requested as
-  // dead (zero codes), and a tile past the run is neither stored nor staged.
+  // dead (not loaded: the slot keeps the codes it held, finite values), and
+  // a tile past the run is neither stored nor staged.
   for (;;) {
 #pragma unroll
     for (int s = 0; s < D; ++s) {
@@ -1263,6 +1403,247 @@ __global__ __launch_bounds__(NW * kWave, 4) void k_gemv_mfma_stream(const GemvJo
         __syncthreads();
         stage(cj, cw.seg_col0());
         __syncthreads();
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (ct >= t_end) return;
+  }
+}
+
+
+// 17..32 activation rows: x^T is two 16-row m-tiles, an x segment is one
+// panel (256 columns: m_rows * 256 <= kStreamXElems), double-buffered.  Four
+// waves per SIMD (at most 128 VGPRs): two 8-wave workgroups per CU, so one
+// workgroup's barriers are covered by the other's loads.
+//
+// Staging without a drain: vector memory requests complete in issue order,
+// so a wait for x loads issued after the weight requests in flight would wait
+// for those too, and stall the pipeline at every segment.  The next
+// segment's x is therefore requested at the start of the step that begins a
+// segment, before that step's weight request, and written into the other
+// buffer at the end of the step: its wait covers only the panel the next
+// step consumes anyway.  The buffers switch behind one barrier, which also
+// tells every wave that the buffer written next is no longer read.
+template <int NW, int D, bool MX, bool ONE, bool PK, int SF>
+__global__ __launch_bounds__(NW * kWave, 4) void k_gemv_mfma_stream32(const GemvJob* __restrict__ table,
+                                                                   int njobs, GemvJob one, int total_tiles,
+                                                                   int tiles_per_block, int m_rows, int) {
+  static_assert(NW * kWave == 512, "staging geometry assumes 512 threads");
+  constexpr int MT = 2;
+  constexpr int seg_cols = kPanelCols;   // one-panel segments (checked on the host)
+  const JobList jobs{table, njobs, one};
+  constexpr int kRows = 16 * NW;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int t_begin = blockIdx.x * tiles_per_block;
+  const int t_end = min(total_tiles, t_begin + tiles_per_block);
+  if (t_begin >= t_end) return;   // whole workgroup: no barrier is skipped by part of it
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int i = lane & 15, g = lane >> 4;
+  unsigned char* pbuf = smem + wave * kPanelBytes;
+  // two x buffers of m_rows rows of seg_cols bf16, the 16-byte units of row
+  // r XOR-swizzled by r % 16 inside each group of 16 units: the 16 rows a B
+  // read spans then hit 16 different bank groups, with no padding
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem + NW * kPanelBytes);
+  const int xbuf = m_rows * seg_cols;   // elements of one buffer
+  int xcur = 0;                         // the buffer in use: 0 or xbuf
+  const int seg_panels = seg_cols / kPanelCols;
+  // B operands: lane (i, g) reads x row 16t + i (rows past m_rows read row
+  // m_rows - 1: their products land in output columns that are not stored),
+  // units 32 * panel + 16b + 8c + 2g + h, swizzled: the panel's units keep
+  // their group of 32, 16b is an offset, and (8c + 2g + h) ^ i for c, h in
+  // {0, 1} is one of four per-lane unit offsets
+  int brow[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) brow[t] = min(16 * t + i, m_rows - 1) * seg_cols;
+  int bunit[2][2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) bunit[c][h] = 8 * ((8 * c + 2 * g + h) ^ (min(i, m_rows - 1) & 15));
+  // staging: this thread's units u = tid + 512q of the [m_rows][32] grid of
+  // 8-element units (one-panel segments): row r, unit c, LDS element offset
+  // dst (valid for r < m_rows); shifts of the thread index
+  auto x_unit = [&](int q, int& r, int& c, int& dst) {
+    r = (int)(threadIdx.x >> 5) + 16 * q;
+    c = threadIdx.x & 31;
+    dst = r * kPanelCols + 8 * (c ^ (r & 15));
+  };
+  // x[:, seg0 : seg0 + seg_cols) of a job (pointer, k) into registers.  The
+  // loads are unconditional (rows clamped to m_rows - 1, columns to k - 8):
+  // a load behind a branch would be joined by copies, and a copy waits for
+  // its load.  Units past k are zeroed where they are written (the codes of
+  // a clamped last panel meet zeros there).
+  auto x_request = [&](const uint16_t* x, int k, int seg0, uint4 (&v)[kStreamXUnits]) {
+#pragma unroll
+    for (int q = 0; q < kStreamXUnits; ++q) {
+      int r, c, dst;
+      x_unit(q, r, c, dst);
+      v[q] = ld_global_u4(x, ((size_t)min(r, m_rows - 1) * k + min(seg0 + 8 * c, k - 8)) * 2);
+    }
+  };
+  // to buffer `buf` (live), else, and for rows past m_rows, to the wave's
+  // panel buffer `spare`.  Every lane stores: a store under a lane mask gets
+  // its wait inside the masked block, and the compiler then takes the loads
+  // as still pending on the path that skips it.
+  // Units past k are zeroed only on a segment that reaches past k (a job's
+  // last one); both paths have waited for the loads where they join.
+  auto x_write = [&](uint4 (&v)[kStreamXUnits], int k, int seg0, bool live, int buf, unsigned char* spare) {
+    if (seg0 + seg_cols > k) {
+#pragma unroll
+      for (int q = 0; q < kStreamXUnits; ++q) {
+        int r, c, dst;
+        x_unit(q, r, c, dst);
+        if (seg0 + 8 * c + 8 > k) v[q] = make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kStreamXUnits; ++q) {
+      int r, c, dst;
+      x_unit(q, r, c, dst);
+      uint4* to = live && r < m_rows
+                      ? reinterpret_cast<uint4*>(xs + buf + dst)
+                      : reinterpret_cast<uint4*>(spare + 16 * (threadIdx.x & (kWave - 1)) + 1024 * q);
+      *to = v[q];
+    }
+  };
+
+  // the workgroup's first segment in every tile
+  const int s0 = blockIdx.x;
+  int jn = job_of_tile<ONE>(jobs, t_begin);
+  // compute cursor: tile ct of job cj, the walk cw through its panels
+  GemvJob cj;
+  load_job<ONE>(jobs, jn, cj);
+  int c_bound = job_end<ONE>(jobs, jn);
+  PanelWalk cw;
+  cw.start_job(cj.k, seg_panels, s0, wave, NW);
+  int ct = t_begin;
+  // issue cursor: tile it of job ij, the walk iw, D panels ahead
+  GemvJob ij = cj;
+  int ijn = jn, i_bound = c_bound, it = t_begin;
+  PanelWalk iw = cw;
+  TileRows tl;
+  tile_rows(ij, (it - ij.item0) * kRows + 16 * wave, tl);
+
+  // Requests past the run (dead: their sums are never stored) are loaded
+  // like live ones, all from the job's first 16 code bytes (one cache line).
+  auto issue = [&](Panel<MX>& r) {
+    const bool live = it < t_end;
+    panel_issue_rows<MX, PK, SF>(ij, tl, (it - ij.item0) * kRows + 16 * wave, iw.panel(), live,
+                                 (ij.k + kTile - 1) / kTile, (ij.k + kGroup - 1) / kGroup, r);
+    if (!live) return;
+    if (iw.step(wave, NW) == 2) {
+      if (++it < t_end) {
+        if (it >= i_bound) {
+          load_job<ONE>(jobs, ++ijn, ij);
+          i_bound = job_end<ONE>(jobs, ijn);
+          iw.start_job(ij.k, seg_panels, s0, wave, NW);
+        }
+        tile_rows(ij, (it - ij.item0) * kRows + 16 * wave, tl);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) tl.row[q] = ij.codes;
+      }
+    }
+  };
+
+  // Panel steps are fenced off from the scheduler (sched_barrier): left
+  // free, it gathers the requests of several slots in one place, so a wait
+  // for one slot would also wait for the next.
+  Panel<MX> slot[D];
+#pragma unroll
+  for (int s = 0; s < D; ++s) {
+    issue(slot[s]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  {
+    uint4 v[kStreamXUnits];
+    x_request(cj.x, cj.k, cw.seg_col0(), v);
+    x_write(v, cj.k, cw.seg_col0(), true, 0, pbuf);
+  }
+  __syncthreads();
+
+  f32x4 acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  bool staged = false;   // the next segment's x is in the other buffer
+  // One exit, after every D panel steps: an exit between steps becomes a
+  // branch to a block shared with the loop's head, reached there with the
+  // slots' requests in another order, and the compiler, merging the two
+  // orders, would wait at the head for every request in flight.  So the last
+  // pass may consume up to D - 1 panels past the run: they were requested as
+  // dead (loaded again from the run's last tile: finite codes), and a tile
+  // past the run is neither stored nor staged.
+  for (;;) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      // The step that begins a segment requests the segment after it: the
+      // next one of this tile, else the first one of the next tile (the same
+      // segment, and nothing to stage, when the job's x fits one segment),
+      // else that of the next job.  Uniform across the workgroup.
+      // The branches choose the segment (scalars only); one request follows.
+      uint4 xv[kStreamXUnits];
+      bool pre = false;
+      const uint16_t* xp = cj.x;
+      int xk = 0, xseg0 = 0;
+      if (cw.cnt == 0 && ct < t_end) {
+        const bool tile_end = cw.segs_done + 1 == cw.nseg;
+        if (!tile_end || (ct + 1 < t_end && (ONE || ct + 1 < c_bound))) {
+          if (cw.nseg > 1) {
+            pre = true;
+            xk = cj.k;
+            xseg0 = (cw.seg + 1 == cw.nseg ? 0 : cw.seg + 1) * seg_cols;
+          }
+        } else if (!ONE && ct + 1 < t_end) {
+          GemvJob nj;
+          load_job<ONE>(jobs, jn + 1, nj);
+          PanelWalk nw;
+          nw.start_job(nj.k, seg_panels, s0, wave, NW);
+          pre = true;
+          xp = nj.x;
+          xk = nj.k;
+          xseg0 = nw.seg_col0();
+        }
+      }
+      if (pre) x_request(xp, xk, xseg0, xv);
+      // the A operands are read from the panel buffer where the MFMAs use
+      // them (register limit)
+      panel_write(slot[s].v, pbuf);
+      float sc[MX ? 4 : 2];
+      panel_scales<MX, PK, SF>(slot[s], sc);
+      issue(slot[s]);
+      const uint16_t* xb = xs + xcur + cw.pos * kPanelCols;   // panel start within the staged segment
+      auto get_b = [&](int t, int b, int c, uint4& B0, uint4& B1) {
+        const uint16_t* bp = xb + brow[t] + 128 * b;
+        B0 = *reinterpret_cast<const uint4*>(bp + bunit[c][0]);
+        B1 = *reinterpret_cast<const uint4*>(bp + bunit[c][1]);
+      };
+      panel_mfma_lds<MT, MX>(pbuf, sc, get_b, acc);
+      // The write is unconditional: without a request it stores whatever the
+      // registers hold into the wave's own panel buffer (free until the next
+      // step).  Behind a branch of its own the compiler could not pair it
+      // with the request's branch, would take the loads as possibly pending
+      // after the step, and wait at the next request for them and for every
+      // weight request older than them.  Here its wait, at the end of a step
+      // without a request, covers only the panel the next step consumes.
+      x_write(xv, xk, xseg0, pre, xbuf - xcur, pbuf);
+      staged = staged || pre;
+      const int moved = cw.step(wave, NW);
+      if (moved == 2) {   // tile done
+        if (ct < t_end)
+          store_tile<MT, SF == kFmtRow, true>(cj, (ct - cj.item0) * kRows + 16 * wave, m_rows, acc);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (++ct < t_end && !ONE && ct >= c_bound) {   // the run enters the next job
+          load_job<ONE>(jobs, ++jn, cj);
+          c_bound = job_end<ONE>(jobs, jn);
+          cw.start_job(cj.k, seg_panels, s0, wave, NW);
+        }
+      }
+      if (moved != 0 && staged) {   // switch to the segment staged meanwhile
+        __syncthreads();
+        xcur = xbuf - xcur;
+        staged = false;
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1689,7 +2070,7 @@ __global__ __launch_bounds__(8 * kWave) void k_gemv_w8a8_tiles(GemvJob j, const 
 //     workgroups once many GEMVs share the launch).
 //   MFMA single call: k_gemv_mfma_direct, one 16-row tile per workgroup
 //     (4 waves; 8 on at most kDirect8MaxRows rows).
-//   MFMA grouped: k_gemv_mfma_stream, 8 waves, 128-row tiles.
+//   MFMA grouped: k_gemv_mfma_stream16 / 32, 8 waves, 128-row tiles.
 
 template <int M, int R, int C, bool MX, bool G>
 hipError_t run_valu(const GemvJob& job, const GemvJob* table, int njobs, int64_t blocks,
@@ -1751,9 +2132,12 @@ constexpr int64_t kDirect8MaxRows = 4096;
 // split each workgroup's panels over 8 waves, on more rows over 4.
 constexpr int64_t kDirectT2Wave8MaxRows = 8192;
 
+// MT = 1: up to 16 rows (k_gemv_mfma_stream16); MT = 2: 17..32 rows
+// (k_gemv_mfma_stream32).  Both take the same arguments.
 template <int MT, bool MX, bool ONE, bool PK, int SF>
 constexpr auto mfma_stream_kernel() {
-  return &k_gemv_mfma_stream<MT, kMfmaStreamWaves, 2, MX, ONE, PK, SF>;
+  if constexpr (MT == 1) return &k_gemv_mfma_stream16<kMfmaStreamWaves, 2, MX, ONE, PK, SF>;
+  else return &k_gemv_mfma_stream32<kMfmaStreamWaves, 2, MX, ONE, PK, SF>;
 }
 
 // The kernel needs more than the default 64 KB of dynamic LDS: raise the
@@ -1916,11 +2300,14 @@ int gemv_wide_seg_cols(int64_t k) {
 }
 int gemv_stream_rows() { return kWaves * kStreamR; }
 
+// Up to 16 rows: LDS bytes x may take, 1 KB under the per-workgroup share
+// (at exactly half of the CU's LDS the measured rates fall as if only one
+// workgroup fitted per CU).
+constexpr int kStream16XBytes = kMfmaStreamLds - kMfmaStreamWaves * kPanelBytes - 1024;
+
 int gemv_mfma_stream_seg_cols(int m, int64_t max_k) {
-  // 1 KB under the per-workgroup share: at exactly half of the CU's LDS the
-  // measured rates fall as if only one workgroup fitted per CU
-  const int x_budget = kMfmaStreamLds - kMfmaStreamWaves * kPanelBytes - 1024;
-  const int cap = x_budget / (2 * m) / kPanelCols * kPanelCols;
+  if (m > 16) return kPanelCols;   // k_gemv_mfma_stream32: one-panel segments
+  const int cap = kStream16XBytes / (2 * m) / kPanelCols * kPanelCols;
   const int64_t kmax = (max_k + kPanelCols - 1) / kPanelCols * kPanelCols;
   if (kmax <= cap) return (int)kmax;
   const int64_t nseg = (kmax + cap - 1) / cap;
@@ -1929,10 +2316,17 @@ int gemv_mfma_stream_seg_cols(int m, int64_t max_k) {
 }
 
 int gemv_mfma_stream_lds(int m, int seg_cols) {
-  return kMfmaStreamWaves * kPanelBytes + m * seg_cols * 2;
+  // up to 16 rows one x buffer, above two
+  return kMfmaStreamWaves * kPanelBytes + (m <= 16 ? 1 : 2) * m * seg_cols * 2;
 }
 
-int gemv_mfma_stream_lds_limit() { return kMfmaStreamLds; }
+bool gemv_mfma_stream_seg_ok(int m, int seg_cols) {
+  if (m < 1 || m > 32) return false;
+  if (m > 16) return seg_cols == kPanelCols;
+  return seg_cols >= kPanelCols && seg_cols % kPanelCols == 0 &&
+         (int64_t)m * seg_cols * 2 <= kStream16XBytes + 1024;
+}
+
 
 namespace {
 
@@ -1961,9 +2355,14 @@ hipError_t run_mfma_stream(const StreamJobs& l, int64_t blocks, int64_t tiles, i
   const hipError_t e = allow_mfma_stream_lds<MT, MX, ONE, PK, SF>();
   if (e != hipSuccess) return e;
   const size_t lds = (size_t)gemv_mfma_stream_lds(m, seg_cols);
-  hipLaunchKernelGGL((k_gemv_mfma_stream<MT, kMfmaStreamWaves, 2, MX, ONE, PK, SF>), dim3((unsigned)blocks),
-                     dim3(kMfmaStreamWaves * kWave), lds, stream, l.table, l.count, l.one, (int)tiles,
-                     tiles_per_block, m, seg_cols);
+  if constexpr (MT == 1)
+    hipLaunchKernelGGL((k_gemv_mfma_stream16<kMfmaStreamWaves, 2, MX, ONE, PK, SF>), dim3((unsigned)blocks),
+                       dim3(kMfmaStreamWaves * kWave), lds, stream, l.table, l.count, l.one, (int)tiles,
+                       tiles_per_block, m, seg_cols);
+  else
+    hipLaunchKernelGGL((k_gemv_mfma_stream32<kMfmaStreamWaves, 2, MX, ONE, PK, SF>), dim3((unsigned)blocks),
+                       dim3(kMfmaStreamWaves * kWave), lds, stream, l.table, l.count, l.one, (int)tiles,
+                       tiles_per_block, m, seg_cols);
   return hipGetLastError();
 }
 
@@ -2050,6 +2449,21 @@ hipError_t launch_gemv_grouped(const GemvJob* table, int njobs, int64_t blocks, 
             : dispatch_valu<false, true>(m, true, seg4096, none, table, njobs, blocks, stream);
 }
 
+namespace {
+
+// Resident workgroups per CU of a streaming MFMA variant at `lds` bytes.
+template <int MT, bool MX>
+hipError_t stream_occupancy(int threads, size_t lds, int* per_cu) {
+  constexpr int SF = MX ? kFmtMx : kFmtBlock;
+  hipError_t e = allow_mfma_stream_lds<MT, MX, false, false, SF>();
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, mfma_stream_kernel<MT, MX, false, false, SF>(),
+                                                     threads, lds);
+  return e;
+}
+
+}  // namespace
+
 hipError_t gemv_mfma_stream_slots(int m, bool mx, int seg_cols, int* slots) {
   const size_t lds = (size_t)gemv_mfma_stream_lds(m, seg_cols);
   const int threads = kMfmaStreamWaves * kWave;
@@ -2057,21 +2471,10 @@ hipError_t gemv_mfma_stream_slots(int m, bool mx, int seg_cols, int* slots) {
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess) {
-    if (m <= 16) {
-      e = mx ? allow_mfma_stream_lds<1, true, false, false, kFmtMx>() : allow_mfma_stream_lds<1, false, false, false, kFmtBlock>();
-      if (e == hipSuccess)
-        e = mx ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_stream_kernel<1, true, false, false, kFmtMx>(),
-                                                              threads, lds)
-               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_stream_kernel<1, false, false, false, kFmtBlock>(),
-                                                              threads, lds);
-    } else {
-      e = mx ? allow_mfma_stream_lds<2, true, false, false, kFmtMx>() : allow_mfma_stream_lds<2, false, false, false, kFmtBlock>();
-      if (e == hipSuccess)
-        e = mx ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_stream_kernel<2, true, false, false, kFmtMx>(),
-                                                              threads, lds)
-               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_stream_kernel<2, false, false, false, kFmtBlock>(),
-                                                              threads, lds);
-    }
+    if (m > 16)
+      e = mx ? stream_occupancy<2, true>(threads, lds, &per_cu) : stream_occupancy<2, false>(threads, lds, &per_cu);
+    else
+      e = mx ? stream_occupancy<1, true>(threads, lds, &per_cu) : stream_occupancy<1, false>(threads, lds, &per_cu);
   }
   *slots = cus * (per_cu > 0 ? per_cu : 1);
   return e;

@@ -116,7 +116,7 @@ hipError_t launch_gemv_stream(const GemvJob* device_table, int njobs, int64_t bl
 // seg_cols columns (a multiple of 256 chosen by gemv_mfma_stream_seg_cols).
 int gemv_mfma_stream_seg_cols(int m, int64_t max_k);
 int gemv_mfma_stream_lds(int m, int seg_cols);      // LDS bytes per workgroup
-int gemv_mfma_stream_lds_limit();
+bool gemv_mfma_stream_seg_ok(int m, int seg_cols);  // a segment the kernel can stage
 hipError_t gemv_mfma_stream_slots(int m, bool mx, int seg_cols, int* slots);
 // MX weights whose exponent rows all start 8-byte aligned (ceil(k/32) % 8
 // == 0 and an 8-byte aligned array): the MFMA kernels then read each row's

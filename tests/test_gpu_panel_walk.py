@@ -6,9 +6,15 @@ multiple of 2048 with x segments of at least four panels, and in plain order
 otherwise; a run of tiles ends after a whole group of pipeline slots, so a
 run whose panel count is odd consumes one dead panel past its last tile.  The
 direct single-call kernels rotate their panel assignment by workgroup on the
-same K.  Every kernel is compiled per scale format.  The cases below mix
-rotated and plain jobs in one grouped launch, cover whole-K, multi-segment
-and two-panel segments (M = 3 / 9..16 / 17..32), force every run length,
+same K.  Up to 16 rows x is staged in one buffer (x whole where it fits,
+else segments restaged behind barriers); above, by one-panel segments in two
+buffers, the next segment (of the tile, the next tile or the next job)
+prefetched while the current one is in use.  Every kernel is compiled per
+scale format.  The cases below mix rotated and plain jobs in one grouped
+launch, cover 16-, 8- and 5-panel segments (M = 3 / 9 / 16) and one-panel
+segments (M = 17..32), jobs whose x fits one segment next to jobs that need
+several, launches whose x fits whole (restaged at job changes), force every
+run length,
 run single calls on both kernels and on the fp8 x fp8 direct kernel, in
 every scale format.
 """
@@ -65,7 +71,7 @@ def test_grouped_walk_every_run_length(fp8w, oracle_mod, fmt, m):
                                        route=fp8w.ROUTE_MFMA)
     assert plan.route == fp8w.ROUTE_MFMA and plan.plan.tiles_per_block > 0
     seg = plan.plan.seg_cols
-    assert seg % 256 == 0 and (seg // 256 >= 4 if m <= 16 else seg // 256 >= 2)
+    assert seg % 256 == 0 and seg == {3: 4096, 9: 2048, 16: 1280, 17: 256, 32: 256}[m]
     tiles = plan.plan.tiles
     refs = [oracle_mod.gemv_format_f64(x, c, s, fmt) for x, (_, _, c, s) in zip(xs, jobs)]
     for run in (1, 2, 5, tiles):
@@ -77,6 +83,36 @@ def test_grouped_walk_every_run_length(fp8w, oracle_mod, fmt, m):
         _sync()
         for (n, k, _, _), (y_ref, bound), y in zip(jobs, refs, ys):
             assert_within_bound(bf16_to_f64(y), y_ref, bound, f"walk {fmt} m={m} run={run} [{n}x{k}] seg={seg}")
+
+
+# x of every job whole in one buffer (m * K * 2 bytes within the one-buffer
+# budget): x is restaged only where a run enters the next job
+ONE_BUFFER = {8: [(300, 2048), (257, 2560), (200, 1040), (129, 2048)],
+              12: [(300, 1024), (130, 784), (257, 512), (64, 1024)]}
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("m", sorted(ONE_BUFFER))
+def test_grouped_one_buffer_every_run_length(fp8w, oracle_mod, fmt, m):
+    jobs = _quantized(oracle_mod, fmt, ONE_BUFFER[m], 148)
+    xs = [W.activation(149, m, k) for (_, k, _, _) in jobs]
+    plan = fp8w.fp8w_grouped_plan_init([to_dev_bf16(x) for x in xs], [to_dev(c) for (_, _, c, _) in jobs],
+                                       [_dev_scales(fmt, s) for (_, _, _, s) in jobs], fmt=fmt,
+                                       route=fp8w.ROUTE_MFMA)
+    seg = plan.plan.seg_cols
+    kmax = max(k for (_, k, _, _) in jobs)
+    assert seg == -(-kmax // 256) * 256, seg
+    tiles = plan.plan.tiles
+    refs = [oracle_mod.gemv_format_f64(x, c, s, fmt) for x, (_, _, c, s) in zip(xs, jobs)]
+    for run in (1, 2, 3, tiles):
+        plan.plan.tiles_per_block = run
+        plan.plan.blocks = -(-tiles // run)
+        for y in plan.ys:
+            y.fill_(float("nan"))
+        ys = fp8w.fp8w_gemv_grouped(plan)
+        _sync()
+        for (n, k, _, _), (y_ref, bound), y in zip(jobs, refs, ys):
+            assert_within_bound(bf16_to_f64(y), y_ref, bound, f"one buffer {fmt} m={m} run={run} [{n}x{k}]")
 
 
 @pytest.mark.parametrize("fmt", FORMATS)

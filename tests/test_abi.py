@@ -269,6 +269,12 @@ def test_grouped_argument_errors(F):
     assert L.fp8w_gemv_grouped(ctypes.byref(bad), None) == F.ERR_SHAPE
     bad = F.GroupedPlanC(T, 1, 32, 0, 2, 4, 4, 1, 4096)  # MFMA: x segment exceeds the LDS budget
     assert L.fp8w_gemv_grouped(ctypes.byref(bad), None) == F.ERR_SHAPE
+    bad = F.GroupedPlanC(T, 1, 8, 0, 2, 4, 4, 1, 3328)   # m <= 16: m * seg * 2 bytes above 48 KB
+    assert L.fp8w_gemv_grouped(ctypes.byref(bad), None) == F.ERR_SHAPE
+    bad = F.GroupedPlanC(T, 1, 17, 0, 2, 4, 4, 1, 512)   # m > 16: one-panel segments only
+    assert L.fp8w_gemv_grouped(ctypes.byref(bad), None) == F.ERR_SHAPE
+    bad = F.GroupedPlanC(T, 1, 33, 0, 2, 4, 4, 1, 256)   # m above 32
+    assert L.fp8w_gemv_grouped(ctypes.byref(bad), None) == F.ERR_SHAPE
     bad = F.GroupedPlanC(T, 1, 4, 1, 2, 4, 4, 1, 256, 2)  # mx_packed8 is 0 or 1
     assert L.fp8w_gemv_grouped(ctypes.byref(bad), None) == F.ERR_SHAPE
     bad = F.GroupedPlanC(T, 1, 4, 0, 2, 4, 4, 1, 256, 1)  # ... 1 only for MX weights

@@ -115,6 +115,33 @@ def test_grouped_one_buffer_every_run_length(fp8w, oracle_mod, fmt, m):
             assert_within_bound(bf16_to_f64(y), y_ref, bound, f"one buffer {fmt} m={m} run={run} [{n}x{k}]")
 
 
+# above 16 rows: jobs of one panel (nothing to prefetch inside the job, the
+# next job's x prefetched at its tile ends), K below one panel and ragged
+SHORT_K = [(300, 256), (129, 16), (257, 512), (64, 272), (200, 256), (17, 784)]
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("m", [17, 32])
+def test_grouped_short_k_above_16_rows(fp8w, oracle_mod, fmt, m):
+    jobs = _quantized(oracle_mod, fmt, SHORT_K, 150)
+    xs = [W.activation(151, m, k) for (_, k, _, _) in jobs]
+    plan = fp8w.fp8w_grouped_plan_init([to_dev_bf16(x) for x in xs], [to_dev(c) for (_, _, c, _) in jobs],
+                                       [_dev_scales(fmt, s) for (_, _, _, s) in jobs], fmt=fmt,
+                                       route=fp8w.ROUTE_MFMA)
+    assert plan.plan.seg_cols == 256
+    tiles = plan.plan.tiles
+    refs = [oracle_mod.gemv_format_f64(x, c, s, fmt) for x, (_, _, c, s) in zip(xs, jobs)]
+    for run in (1, 2, 3, tiles):
+        plan.plan.tiles_per_block = run
+        plan.plan.blocks = -(-tiles // run)
+        for y in plan.ys:
+            y.fill_(float("nan"))
+        ys = fp8w.fp8w_gemv_grouped(plan)
+        _sync()
+        for (n, k, _, _), (y_ref, bound), y in zip(jobs, refs, ys):
+            assert_within_bound(bf16_to_f64(y), y_ref, bound, f"short K {fmt} m={m} run={run} [{n}x{k}]")
+
+
 @pytest.mark.parametrize("fmt", FORMATS)
 def test_direct_single_calls_rotated(fp8w, oracle_mod, fmt):
     # the direct kernel: 8 waves per tile up to 4096 rows, 4 above, one or

@@ -41,7 +41,7 @@ PEAK_BF16 = 2.5e15         # MI355X dense bf16 MFMA, flop/s
 # kernel, launch-plan and helper sources); any change to those reports
 # traffic as null until the counters are retaken.
 COUNTED_TRAFFIC = {
-    "sources_sha256": "5e7fbbeabe68dbd575fae86e9b20ad005e73071e4692bf71e5da22cd9b05a793",
+    "sources_sha256": "f18c3ad0fcdf04cb6cbaf46e2c14ac1271f9bad4e062183908c36d7571f564b3",
     "bytes_per_launch": 1340.30e6,
 }
 TRAFFIC_SOURCES = ('gemv.hip', 'device.hpp', 'internal.hpp', 'api.cpp')

@@ -1043,7 +1043,7 @@ __device__ __forceinline__ void tile_loads(const GemvJob& j, int row0, TileLoads
     t.off[q] = (uint64_t)min(4 * q + (lane >> 4), last) * (uint64_t)j.k + 16 * (lane & 15);
 }
 
-// The streaming kernel's view of a 16-row tile: the address of the row each
+// The 17..32-row streaming kernel's view of a 16-row tile: the address of the row each
 // of the lane's four loads reads (rows past the weight's last row clamped to
 // it: their sums are never stored).  Computed once per tile.
 struct TileRows {
@@ -1058,7 +1058,7 @@ __device__ __forceinline__ void tile_rows(const GemvJob& j, int row0, TileRows& 
     t.row[q] = j.codes + (size_t)(row0 + min(4 * q + (lane >> 4), last)) * (size_t)j.k;
 }
 
-// The streaming kernel's request of panel p: every lane loads, with no
+// The 17..32-row streaming kernel's request of panel p: every lane loads, with no
 // branch.  A branch between full panels and a partial last one makes the
 // compiler count a path with fewer requests, and every wait it then sizes for
 // an earlier request also waits for requests issued after it.  Columns are

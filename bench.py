@@ -41,7 +41,7 @@ PEAK_BF16 = 2.5e15         # MI355X dense bf16 MFMA, flop/s
 # kernel, launch-plan and helper sources); any change to those reports
 # traffic as null until the counters are retaken.
 COUNTED_TRAFFIC = {
-    "sources_sha256": "f18c3ad0fcdf04cb6cbaf46e2c14ac1271f9bad4e062183908c36d7571f564b3",
+    "sources_sha256": "da643c86f7ff702dad9247d891e2c9480ebec2cce44877578dd155c9968fdd93",
     "bytes_per_launch": 1340.30e6,
 }
 TRAFFIC_SOURCES = ('gemv.hip', 'device.hpp', 'internal.hpp', 'api.cpp')

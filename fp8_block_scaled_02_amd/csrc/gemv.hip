@@ -27,6 +27,9 @@
 //    k_gemv_mfma_stream16 / k_gemv_mfma_stream32 (up to 16 / 17..32 rows):
 //    runs of 128-row tiles, one 16-row tile per wave, x staged in LDS by K
 //    segments (one buffer / two, the next segment prefetched).
+//    k_gemv_mfma_xreg (single calls, 17..32 rows, K of eight panels): runs
+//    of 16-row tiles, wave w taking panel w of each, its x^T fragments held
+//    in registers for the whole run, partial sums met in LDS per tile.
 //  * W8A8: fp8 x fp8 v_mfma_scale_f32_16x16x128_f8f6f4 (k_gemv_w8a8_direct,
 //    and k_gemv_w8a8_tiles on weights with many rows), and k_gemv_valu with
 //    the activation codes widened to bf16 at M <= 2.
@@ -1791,6 +1794,113 @@ __global__ __launch_bounds__(NW * kWave) void k_gemv_mfma_direct(GemvJob j, int 
   }
 }
 
+// ------------------------------------------- MFMA, x in registers --
+//
+// Single calls on many rows whose K spans at most NW panels: wave w owns
+// panel w of every tile, so its x^T fragments are the same for the whole
+// run and are loaded once, into registers; the workgroup walks a
+// contiguous run of 16-row tiles (16 rows x K contiguous bytes each), the
+// panel of the tile D ahead in flight, and the waves' partial sums meet in
+// LDS once per tile (two buffers, one barrier per tile).
+template <int MT, int D, bool MX, int NW, bool PK, int SF>
+__global__ __launch_bounds__(NW * kWave, MT == 1 ? 4 : 2) void k_gemv_mfma_xreg(GemvJob j, int m_rows, int tiles_per_block) {
+  __shared__ __align__(16) unsigned char pb[NW * kPanelBytes];
+  __shared__ float red[2][NW * MT * 4 * kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int i = lane & 15, g = lane >> 4;
+  const int np = (j.k + kPanelCols - 1) / kPanelCols;
+  const int nkb = (j.k + kTile - 1) / kTile;
+  const int groups = (j.k + kGroup - 1) / kGroup;
+  const int ntiles = (j.n + 15) / 16;
+  const int t_begin = blockIdx.x * tiles_per_block;
+  const int t_end = min(ntiles, t_begin + tiles_per_block);
+  const bool pl = wave < np;          // waves past the last panel add zeros
+  const int p = min(wave, np - 1);    // every request in bounds
+
+  uint4 xb[MT][2][2][2];
+  if (pl && (p + 1) * kPanelCols <= j.k) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const uint8_t* xr =
+          reinterpret_cast<const uint8_t*>(j.x) + ((size_t)min(16 * t + i, m_rows - 1) * j.k + 16 * g) * 2;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const size_t off = (size_t)(p * kPanelCols + 128 * b + 64 * c) * 2;
+          xb[t][b][c][0] = ld_global_u4(xr, off);
+          xb[t][b][c][1] = ld_global_u4(xr, off + 16);
+        }
+    }
+  } else {
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int kx = p * kPanelCols + 128 * b + 64 * c + 16 * g;
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const int m = 16 * t + i;
+          xb[t][b][c][0] = xb[t][b][c][1] = make_uint4(0, 0, 0, 0);
+          if (pl && m < m_rows && kx < j.k) {
+            xb[t][b][c][0] = ld_global_u4(j.x, ((size_t)m * j.k + kx) * 2);
+            xb[t][b][c][1] = ld_global_u4(j.x, ((size_t)m * j.k + kx + 8) * 2);
+          }
+        }
+      }
+  }
+
+  auto issue = [&](int t, Panel<MX>& r) {
+    const int row0 = min(t, ntiles - 1) * 16;
+    TileLoads tl;
+    tile_loads(j, row0, tl);
+    panel_issue_tile<MX, PK, true, SF>(j, tl, row0, p, pl && t < t_end, nkb, groups, r);
+  };
+  Panel<MX> slot[D];
+#pragma unroll
+  for (int s = 0; s < D; ++s) issue(t_begin + s, slot[s]);
+  int buf = 0;
+  for (int t0 = t_begin; t0 < t_end; t0 += D) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      const int t = t0 + s;
+      if (t >= t_end) break;
+      f32x4 acc[MT];
+#pragma unroll
+      for (int u = 0; u < MT; ++u) acc[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      uint4 a[2][2];
+      panel_to_a(slot[s].v, pb + wave * kPanelBytes, a);
+      float sc[MX ? 4 : 2];
+      panel_scales<MX, PK, SF>(slot[s], sc);
+      panel_mfma<MT, MX>(a, sc, [&](int u, int b, int c, uint4& B0, uint4& B1) {
+        B0 = xb[u][b][c][0];
+        B1 = xb[u][b][c][1];
+      }, acc);
+      issue(t + D, slot[s]);
+#pragma unroll
+      for (int u = 0; u < MT; ++u)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) red[buf][((wave * MT + u) * 4 + jj) * kWave + lane] = acc[u][jj];
+      __syncthreads();
+      // thread (mcol, row): 16 consecutive threads store 16 consecutive rows
+      for (int v = threadIdx.x; v < MT * 16 * 16; v += NW * kWave) {
+        const int row = v & 15, mcol = v >> 4;
+        const int src = (((mcol >> 4) * 4 + (row & 3)) * kWave) + 16 * (row >> 2) + (mcol & 15);
+        float sum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) sum += red[buf][w * MT * 4 * kWave + src];
+        const int r = t * 16 + row;
+        if (r < j.n && mcol < m_rows) {
+          const float os = SF == kFmtRow ? output_scale(j, r) : 1.0f;
+          st_global<uint16_t>(j.y, ((size_t)mcol * j.n + r) * 2, (uint16_t)f32_to_bf16_rne(sum * os));
+        }
+      }
+      buf ^= 1;
+    }
+  }
+}
+
 // ------------------------------------------------------------------ W8A8 --
 //
 // The activation arrives quantized: e4m3fn codes xc[m, k] with one fp32
@@ -2175,6 +2285,47 @@ hipError_t run_valu_stream(const StreamJobs& l, int64_t blocks, int64_t tiles, i
   return hipGetLastError();
 }
 
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int c = cache[dev].load();
+  if (c == 0) {
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+    cache[dev].store(c);
+  }
+  return c;
+}
+
+// Waves per workgroup (one panel each) and panels in flight per wave of the
+// x-in-registers kernel: at 17..32 rows its x fragments take 64 VGPRs, so one
+// 8-wave workgroup runs per CU, and four panels in flight per wave keep HBM
+// busy (single calls on MI355X, [151936x2048] M = 32, % of 8 TB/s with two /
+// three / four: 57.5 / 59.3 / 59.8).
+constexpr int kXregWaves = 8;
+constexpr int kXregDepth = 4;
+
+template <int MT>
+hipError_t launch_mfma_xreg(const GemvJob& job, int m, bool mx, bool pk, hipStream_t stream) {
+  constexpr int D = kXregDepth, NW = kXregWaves;
+  const int64_t ntiles = (job.n + 15) / 16;
+  const int64_t slots = (MT == 1 ? 2 : 1) * (int64_t)device_cus();   // workgroups resident per CU
+  const int tpb = (int)((ntiles + slots - 1) / slots);
+  const dim3 grid((unsigned)((ntiles + tpb - 1) / tpb)), block(NW * kWave);
+  if (mx && pk)
+    hipLaunchKernelGGL((k_gemv_mfma_xreg<MT, D, true, NW, true, kFmtMx>), grid, block, 0, stream, job, m, tpb);
+  else if (mx)
+    hipLaunchKernelGGL((k_gemv_mfma_xreg<MT, D, true, NW, false, kFmtMx>), grid, block, 0, stream, job, m, tpb);
+  else if (job.format == kFmtBlock)
+    hipLaunchKernelGGL((k_gemv_mfma_xreg<MT, D, false, NW, false, kFmtBlock>), grid, block, 0, stream, job, m, tpb);
+  else if (job.format == kFmtBlockBf16)
+    hipLaunchKernelGGL((k_gemv_mfma_xreg<MT, D, false, NW, false, kFmtBlockBf16>), grid, block, 0, stream, job, m,
+                       tpb);
+  else
+    hipLaunchKernelGGL((k_gemv_mfma_xreg<MT, D, false, NW, false, kFmtRow>), grid, block, 0, stream, job, m, tpb);
+  return hipGetLastError();
+}
+
 template <int MT, bool MX, bool ONE, bool PK, int SF>
 hipError_t run_mfma_stream(const StreamJobs& l, int64_t blocks, int64_t tiles, int tiles_per_block, int m,
                            int seg_cols, hipStream_t stream);
@@ -2386,6 +2537,13 @@ hipError_t launch_gemv(const GemvJob& job, int m, bool mx, int route, hipStream_
     return mx ? dispatch_valu<true, false>(m, wide, seg4096, job, nullptr, 1, blocks, stream)
               : dispatch_valu<false, false>(m, wide, seg4096, job, nullptr, 1, blocks, stream);
   }
+  // Above 16 rows, on K of eight panels (1793..2048), each wave keeps its x^T
+  // fragments in registers for a whole run of tiles instead of staging x in
+  // LDS per tile (single calls on MI355X, [151936x2048] M = 32: 57.6 -> 59.8 %
+  // of 8 TB/s; at M = 4 / 16, two workgroups per CU, it lost 1-2 % to the
+  // streaming kernel).
+  if (m > 16 && single_call_streams_mfma(job.n, m) && (job.k + kPanelCols - 1) / kPanelCols == kXregWaves)
+    return launch_mfma_xreg<2>(job, m, mx, mx && mx_rows_packed8(job.scales, job.k), stream);
   if (single_call_streams_mfma(job.n, m)) {
     StreamJobs l{nullptr, 1, job};
     l.one.item0 = 0;

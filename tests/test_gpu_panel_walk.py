@@ -192,3 +192,20 @@ def test_w8a8_direct_rotated(fp8w, oracle_mod, fmt):
             xb = (oracle_mod.e4m3_decode(xc).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
             y_ref, bound = oracle_mod.gemv_format_f64(xb, c, s, fmt, rows=rows)
             assert_within_bound(y[:, rows], xs * y_ref, xs * bound, f"w8a8 {fmt} m={m} [{n}x{k}]")
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_single_calls_x_in_registers(fp8w, oracle_mod, fmt):
+    # single calls on many rows whose K spans eight panels keep each wave's
+    # x^T fragments in registers for a run of 16-row tiles: K = 2048 and a
+    # partial last panel (K = 1808), a ragged last tile; rows 53 apart, the
+    # last row of every 16-row tile near both ends and the last rows
+    for n, k in [(32768 + 37, 2048), (32768 + 200, 1808)]:
+        (_, _, c, s), = _quantized(oracle_mod, fmt, [(n, k)], 152)
+        cd, sd = to_dev(c), _dev_scales(fmt, s)
+        rows = np.unique(np.concatenate([np.arange(0, n, 53), np.arange(15, 4096, 16), np.arange(n - 300, n)]))
+        for m in (4, 9, 16, 17, 32):
+            x = W.activation(153, m, k)
+            y = bf16_to_f64(fp8w.fp8w_gemv(to_dev_bf16(x), cd, sd, fmt, route=fp8w.ROUTE_MFMA))
+            y_ref, bound = oracle_mod.gemv_format_f64(x, c, s, fmt, rows=rows)
+            assert_within_bound(y[:, rows], y_ref, bound, f"x in registers {fmt} m={m} [{n}x{k}]")
